@@ -1,0 +1,230 @@
+"""CPU float64 oracle for causal, normalized Hedgehog linear attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
+baseline may import this module.  It shares no code with the HIP library and
+imports nothing from it; the product path never calls it.
+
+Pages cited (by title and section):
+  [HM]  "HedgeMamba：融合线性注意力与状态空间模型的高效序列建模" (gsyq.cn news 1418924)
+        §2.1 Hedgehog feature map, §2.3 state expansion and normalization,
+        §3.1 stage-1 identity initialisation, §5.2 HedgeMambaMixer,
+        §5.3 HedgehogProjection.
+  [LA]  "线性注意力（Linear Attention）详解" (cnblogs ying-chease 22790249)
+        part 2 (kernel form of normalized attention, associativity),
+        part 3 (recurrent form), part 4.3 (RetNet scalar decay),
+        part 5 (chunk-wise parallel vs recurrent modes).
+  [SSM] "状态空间模型：Mamba、S4 的线性复杂度路径" (quant67.com, lecture 56)
+        §3.2 (softplus on the step size), §4.2 (associative affine scan).
+
+What is computed, per (batch b, head h), for tokens t = 0..n-1:
+  phi(x)  = softmax([x W, -x W]) over the feature axis          [HM §2.1, §5.3]
+  log a_t = -softplus(dt_t) * exp(A_log[h]);  a_t = 1 without dt [SSM §3.2; HM §3.1]
+  S_t = a_t S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t)
+  o_t = phi(q_t)^T S_t / phi(q_t)^T z_t                          [LA parts 2-3, 4.3; HM §2.3]
+S_{-1}, z_{-1} are the given initial state (zeros when absent); a_t scales the
+carried state only, never the current token (the RetNet form, [LA] 4.3).
+
+Readings where the pages are silent (listed with reasons in the design notes):
+one shared W per projection applied as x @ W with no bias or temperature;
+separate W_q, W_k; the u half precedes the -u half; no epsilon in the
+denominator; the denominator state is one F-vector because the decay is a
+per-head scalar.
+
+Every function here is pinned by tests/test_oracle.py against closed forms,
+library routines, brute force and invariants; there is no parity-unpinned
+function in this module.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# A2: Hedgehog feature map  [HM §2.1 (linear map, concat with its negation,
+# softmax over the feature axis), §5.3 HedgehogProjection.forward]
+# --------------------------------------------------------------------------
+def hedgehog_features(x, w):
+    """phi(x) = softmax([x W, -x W], axis=-1) in float64.
+
+    x: [..., d];  w: [d, f] shared, or [H, d, f] per head with x [B, H, n, d].
+    Returns [..., 2f]: the first f entries come from +xW, the last f from -xW.
+    The max shift is M = max|u| (the largest of u and -u); it cancels exactly.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    if w.ndim == 2:
+        u = x @ w
+    else:  # per-head weights
+        u = np.einsum("bhnd,hdf->bhnf", x, w)
+    both = np.concatenate([u, -u], axis=-1)
+    m = np.max(np.abs(u), axis=-1, keepdims=True)
+    e = np.exp(both - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# A1: per-head decay  [SSM §3.2: the step size passes through softplus;
+# decay a_t = exp(-softplus(dt_t) * exp(A_log)); HM §3.1: stage-1 init a = 1]
+# --------------------------------------------------------------------------
+def softplus(x):
+    """log(1 + e^x) without overflow: x + log1p(e^-x) for x > 0, log1p(e^x) otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x > 0
+    out[pos] = x[pos] + np.log1p(np.exp(-x[pos]))
+    out[~pos] = np.log1p(np.exp(x[~pos]))
+    return out
+
+
+def log_decay(dt, a_log):
+    """log a_t = -softplus(dt[b,h,t]) * exp(A_log[h]).  Returns [B, H, n] float64.
+
+    With dt absent the decay is the identity (log a_t = 0) and None is returned.
+    """
+    if dt is None:
+        return None
+    dt = np.asarray(dt, dtype=np.float64)
+    a_log = np.asarray(a_log, dtype=np.float64)
+    return -softplus(dt) * np.exp(a_log)[None, :, None]
+
+
+# --------------------------------------------------------------------------
+# Quadratic form: explicit causal n x n weights  [LA part 2: normalized kernel
+# attention o_i = sum_j sim(q_i,k_j) v_j / sum_j sim(q_i,k_j) with
+# sim = phi(q).phi(k); made causal and decayed as in LA 4.3]
+# --------------------------------------------------------------------------
+def decay_matrix(log_a_row):
+    """G[i, j] = prod_{s=j+1..i} a_s for j <= i, else 0, from one head's log a [n].
+
+    Formed as exp(L_i - L_j) with L the inclusive cumulative sum of log a.
+    """
+    n = log_a_row.shape[0]
+    L = np.cumsum(log_a_row)
+    diff = L[:, None] - L[None, :]
+    G = np.zeros((n, n))
+    mask = np.tril(np.ones((n, n), dtype=bool))
+    G[mask] = np.exp(diff[mask])
+    return G
+
+
+def linattn_quadratic(phiq, phik, v, log_a=None, s_init=None, z_init=None):
+    """Output o [B, H, n, dv] from explicit masked n x n weights, per (b, h).
+
+    phiq, phik: [B, H, n, F]; v: [B, H, n, dv]; log_a: [B, H, n] or None;
+    s_init: [B, H, F, dv] or None; z_init: [B, H, F] or None.
+    """
+    B, H, n, F = phiq.shape
+    dv = v.shape[-1]
+    o = np.empty((B, H, n, dv))
+    for b in range(B):
+        for h in range(H):
+            scores = phiq[b, h] @ phik[b, h].T                     # [n, n]
+            if log_a is None:
+                G = np.tril(np.ones((n, n)))
+                carry = np.ones(n)
+            else:
+                G = decay_matrix(log_a[b, h])
+                carry = np.exp(np.cumsum(log_a[b, h]))             # prod_{s<=i} a_s
+            wgt = G * scores
+            num = wgt @ v[b, h]
+            den = wgt.sum(axis=1)
+            if s_init is not None:
+                num = num + carry[:, None] * (phiq[b, h] @ s_init[b, h])
+                den = den + carry * (phiq[b, h] @ z_init[b, h])
+            o[b, h] = num / den[:, None]
+    return o
+
+
+# --------------------------------------------------------------------------
+# Recurrent form  [LA part 3: S_i = S_{i-1} + phi(k_i) v_i^T, o_i = phi(q_i)^T S_i;
+# LA 4.3: S_i = gamma S_{i-1} + ...; HM §2.3: numerator / denominator split]
+# --------------------------------------------------------------------------
+def linattn_recurrent(phiq, phik, v, log_a=None, s_init=None, z_init=None):
+    """Token-by-token scan, vectorized over (b, h).
+
+    Returns (o [B,H,n,dv], S [B,H,F,dv], z [B,H,F]): the outputs and the state
+    after the last token.
+    """
+    B, H, n, F = phiq.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, F, dv)) if s_init is None else np.array(s_init, dtype=np.float64)
+    z = np.zeros((B, H, F)) if z_init is None else np.array(z_init, dtype=np.float64)
+    o = np.empty((B, H, n, dv))
+    for t in range(n):
+        if log_a is not None:
+            a = np.exp(log_a[:, :, t])
+            S *= a[:, :, None, None]
+            z *= a[:, :, None]
+        S += phik[:, :, t, :, None] * v[:, :, t, None, :]
+        z += phik[:, :, t, :]
+        num = np.einsum("bhf,bhfd->bhd", phiq[:, :, t, :], S)
+        den = np.einsum("bhf,bhf->bh", phiq[:, :, t, :], z)
+        o[:, :, t, :] = num / den[:, :, None]
+    return o, S, z
+
+
+def prefix_state(phik, v, log_a=None):
+    """Closed form of the state after a prefix: S = sum_j (prod_{s>j} a_s) phi(k_j) v_j^T.
+
+    One matrix product per (b, h); z is the same sum with v_j replaced by 1.
+    """
+    B, H, n, F = phik.shape
+    dv = v.shape[-1]
+    S = np.empty((B, H, F, dv))
+    z = np.empty((B, H, F))
+    for b in range(B):
+        for h in range(H):
+            if log_a is None:
+                wgt = np.ones(n)
+            else:
+                tail = np.cumsum(log_a[b, h][::-1])[::-1]       # sum_{s>=j} log a_s
+                wgt = np.exp(tail - log_a[b, h])                 # sum_{s>j}
+            kw = phik[b, h] * wgt[:, None]
+            S[b, h] = kw.T @ v[b, h]
+            z[b, h] = kw.sum(axis=0)
+    return S, z
+
+
+# --------------------------------------------------------------------------
+# Whole path and decode step
+# --------------------------------------------------------------------------
+def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, form="recurrent"):
+    """Featurize q and k, then run the chosen form.  Returns (o, S_final, z_final);
+    the quadratic form returns None for the state."""
+    phiq = hedgehog_features(q, w_q)
+    phik = hedgehog_features(k, w_k)
+    v = np.asarray(v, dtype=np.float64)
+    la = log_decay(dt, a_log)
+    if form == "quadratic":
+        return linattn_quadratic(phiq, phik, v, la, s_init, z_init), None, None
+    if form == "recurrent":
+        return linattn_recurrent(phiq, phik, v, la, s_init, z_init)
+    raise ValueError(form)
+
+
+def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None):
+    """One decode step from state (S [B,H,F,dv], z [B,H,F]) with one token per
+    (b, h): q, k [B,H,d], v [B,H,dv], dt [B,H].  Returns (o [B,H,dv], S', z').
+    This is the recurrent form advanced by a single token  [LA part 5]."""
+    q = np.asarray(q, dtype=np.float64)[:, :, None, :]
+    k = np.asarray(k, dtype=np.float64)[:, :, None, :]
+    v = np.asarray(v, dtype=np.float64)[:, :, None, :]
+    dt3 = None if dt is None else np.asarray(dt, dtype=np.float64)[:, :, None]
+    o, S2, z2 = forward(q, k, v, w_q, w_k, dt3, a_log, S, z)
+    return o[:, :, 0, :], S2, z2
+
+
+# --------------------------------------------------------------------------
+# State buffer layout used at the library boundary: per (b, h) one contiguous
+# block of F*dv + F float32 values, the numerator S [F][dv] row-major followed
+# by the denominator state z [F].
+# --------------------------------------------------------------------------
+def pack_state(S, z):
+    B, H, F, dv = S.shape
+    return np.concatenate([S.reshape(B, H, F * dv), z.reshape(B, H, F)], axis=-1)
+
+
+def unpack_state(flat, F, dv):
+    flat = np.asarray(flat, dtype=np.float64)
+    B, H, _ = flat.shape
+    return flat[:, :, : F * dv].reshape(B, H, F, dv), flat[:, :, F * dv:]
