@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of causal, normalized Hedgehog linear attention on one MI355X.
+
+One step = one hm_linattn_fwd over the Pythia-1B-shaped layer (B=8, H=16,
+n=2048, d=128, f=64, dv=128, bf16 in, float32 accumulation, identity decay):
+featurize q and k, intra- and inter-chunk products, state passing, normalize.
+Prints ONE JSON line.  Beside the headline prefill number it reports:
+  * roofline: the prefill kernel against HBM bandwidth (it is HBM-bound:
+    ~96 flop/byte against a ridge of ~315), from HIP-event timing of the
+    launches on the stream they run on;
+  * mfma: executed and algorithmic bf16 MFMA rates against the dense peak;
+  * decode: the decode step at B=256, H=16 (state [128 x 129] float32 per head,
+    4096-token prefix, 512 steps) against HBM bandwidth;
+  * prefill_extra: the Mamba-decay workloads (n=8192 and n=131072);
+  * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extra]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+MFMA_FLOP = 16 * 16 * 32 * 2   # one v_mfma_f32_16x16x32_bf16
+METRIC = "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW (1 MI355X)"
+KERNEL_SOURCES = ["hm_device.hpp", "hm_prefill.hpp", "hm_step.hpp"]
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "selective_state_space_hm_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_bytes(B, H, n, d, f, dv, decay, elem=2):
+    """Algorithmic HBM bytes of one prefill: q, k, v read once, o written once,
+    dt read once (decay only), W_q and W_k read once."""
+    per_token_head = elem * (2 * d + 2 * dv) + (4 if decay else 0)
+    return B * H * n * per_token_head + 2 * d * f * elem + (H * 4 if decay else 0)
+
+
+def prefill_flops_algorithmic(B, H, n, d, f, dv):
+    """Chunk-independent work per token-head: featurize q and k (2 x 2df) and the
+    state update plus read-out with the denominator column (2 x 2F(dv+1))."""
+    F = 2 * f
+    return B * H * n * (4 * d * f + 4 * F * (dv + 1))
+
+
+def prefill_mfma_count(plan, B, H, n, d, f, dv):
+    """MFMA instructions the prefill kernels issue (16x16x32 bf16), from the loop
+    structure of the chunk kernel: per (b, h) chunk of 64 tokens and workgroup."""
+    chunk, segments, dsplit = plan
+    C = chunk
+    NCT, NFH, NFT = C // 16, f // 16, 2 * f // 16
+    KD, KF, KC = d // 32, NFT // 2, NCT // 2
+    NW = dv // dsplit // 16
+    intra_steps = sum(bt // 2 + 1 for bt in range(NCT))
+    full = (2 * NCT * NFH * KD            # featurize q and k
+            + NCT * NFT                   # phi(k) re-layout
+            + NW * NCT                    # v re-layout
+            + sum(NCT - a for a in range(NCT)) * KF   # score tiles
+            + NW * NCT * KF               # inter read-out
+            + NW * intra_steps            # intra read-out
+            + NW * NFT * KC)              # state update
+    local = NCT * NFH * KD + NCT * NFT + NW * NCT + NW * NFT * KC
+    chunks = (n + C - 1) // C
+    seg_len = -(-chunks // segments) * C
+    local_chunks = min(n, seg_len * (segments - 1))
+    local_chunks = (local_chunks + C - 1) // C
+    return B * H * dsplit * (full * chunks + local * local_chunks)
+
+
+def time_launches(fn, steps, warmup, torch):
+    """Average ms per call of fn(), HIP events on torch's current stream (the stream
+    the library launches on), bracketed by device synchronization."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return s.elapsed_time(e) / steps, wall
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The float64 oracle's recurrent form on the same inputs, all (b, h) at once,
+    token slices continued through the carried state until the time budget is used."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import hm_oracle as orc
+    from selective_state_space_hm_amd import inputs
+
+    f64 = inputs.to_f64
+    q, k, v = f64(case.q), f64(case.k), f64(case.v)
+    wq, wk = f64(case.w_q), f64(case.w_k)
+    S = z = None
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < case.n and time.perf_counter() - t0 < budget_s:
+            sl = slice(done, min(case.n, done + 64))
+            _, S, z = orc.forward(q[:, :, sl], k[:, :, sl], v[:, :, sl], wq, wk, None, None, S, z)
+            done = sl.stop
+    el = time.perf_counter() - t0
+    return {"value": case.B * done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"recurrent float64 oracle, all {case.B}x{case.H} (b,h) of the B=8 H=16 d=128 f=64 layer, "
+                      f"first {done} of {case.n} tokens in {el:.1f} s on 1 thread (BLAS limited to 1); "
+                      f"host has {len(os.sched_getaffinity(0))} cores"}
+
+
+def hbm_traffic(launch_bytes):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel sources; otherwise None."""
+    try:
+        with open(PROFILE_COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("prefill_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip decode and the decay workloads")
+    ap.add_argument("--segments", type=int, default=0)
+    ap.add_argument("--dsplit", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the workload is the single-GPU hot path and this build "
+              "has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_hm_amd import hm, inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("[bench] generating the B=8 H=16 n=2048 layer")
+    case = inputs.pythia1b()
+    g = {k: getattr(case, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k")}
+    o = torch.empty_like(g["v"])
+    plan = hm.hm_linattn_fwd_plan(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], segments=args.segments,
+                                  dsplit=args.dsplit)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def step():
+        hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], o=o, segments=args.segments,
+                          dsplit=args.dsplit, workspace=ws)
+
+    log(f"[bench] prefill plan (chunk, segments, dsplit) = {plan}; timing {args.steps} steps")
+    ms, wall = time_launches(step, args.steps, args.warmup, torch)
+    B, H, n, d, f, dv = case.B, case.H, case.n, case.d, case.f, case.dv
+    tokens = B * n
+    nbytes = prefill_bytes(B, H, n, d, f, dv, False)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    mfma = prefill_mfma_count(plan, B, H, n, d, f, dv) * MFMA_FLOP
+    algo = prefill_flops_algorithmic(B, H, n, d, f, dv)
+    traffic = hbm_traffic(nbytes)
+    result = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v; W ~ N(0, 1/d))",
+        "config": {"workload": "Pythia-1B-shaped layer prefill, identity decay", "B": B, "H": H, "seq_len": n,
+                   "d": d, "f": f, "dv": dv, "global_batch": B,
+                   "plan": {"chunk": plan[0], "segments": plan[1], "dsplit": plan[2]}},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "hm::fwd_kernel<bf16,128,64,DW,false,0>" + (" (+segment pass)" if plan[1] > 1 else ""),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "mfma": {"executed_tflops": mfma / (ms * 1e-3) / 1e12,
+                 "executed_frac": mfma / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "algorithmic_tflops": algo / (ms * 1e-3) / 1e12,
+                 "algorithmic_frac": algo / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                 "peak_tflops": BF16_PEAK_TFLOPS},
+        "wall_s_timed": wall,
+    }
+    del g, o
+
+    if not args.no_extra:
+        extra = []
+        for maker in (inputs.mamba_decay, inputs.long_context):
+            c = maker()
+            log(f"[bench] {c.name} n={c.n}")
+            gg = {k: getattr(c, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k", "dt", "a_log")}
+            oo = torch.empty_like(gg["v"])
+            pl = hm.hm_linattn_fwd_plan(gg["q"], gg["k"], gg["v"], gg["w_q"], gg["w_k"], gg["dt"], gg["a_log"])
+            steps = 20 if c.n <= 8192 else 5
+
+            def stepx():
+                hm.hm_linattn_fwd(gg["q"], gg["k"], gg["v"], gg["w_q"], gg["w_k"], gg["dt"], gg["a_log"], o=oo,
+                                  workspace=ws)
+
+            msx, _ = time_launches(stepx, steps, 2, torch)
+            bx = prefill_bytes(c.B, c.H, c.n, c.d, c.f, c.dv, True)
+            extra.append({"workload": f"{c.name} B={c.B} H={c.H} n={c.n} Mamba decay", "ms": msx,
+                          "tokens_per_s": c.B * c.n / (msx * 1e-3), "achieved_GBs": bx / (msx * 1e-3) / 1e9,
+                          "hbm_frac": bx / (msx * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "plan": {"chunk": pl[0], "segments": pl[1], "dsplit": pl[2]}})
+            del gg, oo
+        result["prefill_extra"] = extra
+        result["decode"] = bench_decode(torch, hm, inputs, dev, ws)
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+def bench_decode(torch, hm, inputs, dev, ws):
+    dc = inputs.decode_setup()
+    log(f"[bench] decode B={dc.B} H={dc.H}: prefix {dc.prefix} tokens, {dc.steps} steps")
+    wq, wk, a_log = dc.w_q.to(dev), dc.w_k.to(dev), dc.a_log.to(dev)
+    state = torch.empty((dc.B, dc.H, hm.state_numel(dc.f, dc.dv)), dtype=torch.float32, device=dev)
+    pk, pv, pdt = dc.prefix_k.to(dev), dc.prefix_v.to(dev), dc.prefix_dt.to(dev)
+    hm.hm_linattn_fwd(pk, pk, pv, wq, wk, pdt, a_log, s_final=state, workspace=ws)  # prefill -> decode handoff
+    del pk, pv, pdt
+    qs, ks, vs, dts = [], [], [], []
+    for t in range(dc.steps):
+        q, k, v, dt = inputs.decode_step_inputs(dc, t)
+        qs.append(q)
+        ks.append(k)
+        vs.append(v)
+        dts.append(dt)
+    Q = torch.stack(qs).to(dev)
+    K = torch.stack(ks).to(dev)
+    V = torch.stack(vs).to(dev)
+    DT = torch.stack(dts).to(dev)
+    O = torch.empty((dc.steps, dc.B, dc.H, dc.dv), dtype=torch.bfloat16, device=dev)
+    base = state.clone()
+
+    def run_all():
+        for t in range(dc.steps):
+            hm.hm_linattn_step(Q[t], K[t], V[t], wq, wk, state, DT[t], a_log, o=O[t])
+
+    state.copy_(base)
+    run_all()                       # warm-up pass over all steps
+    state.copy_(base)
+    torch.cuda.synchronize()
+    ms_all, _ = time_launches(run_all, 1, 0, torch)
+    ms = ms_all / dc.steps
+    F = 2 * dc.f
+    per_bh = 2 * (F * dc.dv + F) * 4 + 2 * (2 * dc.d + 2 * dc.dv) + 4
+    nbytes = dc.B * dc.H * per_bh + 2 * dc.d * dc.f * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"decode B={dc.B} H={dc.H} d={dc.d} f={dc.f} dv={dc.dv}, state [{F}x{dc.dv + 1}] fp32, "
+                        f"{dc.prefix}-token prefix, {dc.steps} steps, Mamba decay",
+            "tokens_per_s": dc.B / (ms * 1e-3), "ms_per_step": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "hm::step_kernel<bf16,128,64,128,true>", "algorithmic_bytes_per_launch": nbytes}}
+
+
+if __name__ == "__main__":
+    main()

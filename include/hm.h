@@ -1,0 +1,181 @@
+/*
+ * hm.h — C ABI of the MI355X (gfx950) library for causal, normalized Hedgehog
+ * linear attention, the hot path of the HedgeMamba mixer.
+ *
+ * Pages that define the operations:
+ *   [HM]  "HedgeMamba：融合线性注意力与状态空间模型的高效序列建模" (gsyq.cn):
+ *         §2.1 Hedgehog feature map, §2.3 state expansion with a numerator and
+ *         a denominator, §3.1 stage-1 identity init (a_t = 1), §5.2 the mixer's
+ *         [batch, seq_len, num_heads, head_dim] tensors, §5.3 HedgehogProjection.
+ *   [LA]  "线性注意力（Linear Attention）详解" (cnblogs): part 2 normalized kernel
+ *         attention, part 3 recurrent state S_i = S_{i-1} + phi(k_i) v_i^T,
+ *         part 4.3 scalar decay, part 5 chunk-parallel and recurrent modes,
+ *         "Q、K、V 的维度详解" (Q,K [b,h,n,d], V [b,h,n,d_v], S [b,h,d,d_v]).
+ *   [SSM] "状态空间模型：Mamba、S4 的线性复杂度路径" (quant67.com): §3.2 softplus on
+ *         the step size, §4.2 associative composition of affine maps.
+ *
+ * The computation, per batch b, head h and token t (F = 2f is the feature width):
+ *   phi(x)  = softmax([x W, -x W])                       (feature axis)
+ *   log a_t = -softplus(dt[b,h,t]) * exp(A_log[h])       (a_t = 1 when dt is NULL)
+ *   S_t = a_t S_{t-1} + phi(k_t) v_t^T   [F x dv]
+ *   z_t = a_t z_{t-1} + phi(k_t)         [F]
+ *   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library never
+ *     allocates, frees, copies to the host or synchronizes; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL means the default stream).
+ *   - Strides are in ELEMENTS; the last (feature) dimension is always contiguous.
+ *     Base pointers must be 16-byte aligned, and every stride times the element
+ *     size must be a multiple of 16 bytes.
+ *   - W is [d, f] row-major and applied as x @ W (no bias, no temperature).  One W
+ *     may serve all heads (sw_h = 0) or each head may have its own (sw_h = d*f).
+ *   - dt is float32 [B, H, n] (strides sdt_*), A_log float32 [H] contiguous.  Both
+ *     NULL selects the identity decay; exactly one NULL is HM_ERR_NULL.
+ *   - State buffers are float32, one contiguous block of F*dv + F values per
+ *     (b, h), blocks at stride (F*dv + F), [b][h] order: the numerator S [F][dv]
+ *     row-major followed by the denominator state z [F].
+ *   - All arguments are checked on the host before any HIP call.  A failed check
+ *     returns its code, launches nothing and sets hm_last_error_message().  A
+ *     launch failure returns HM_ERR_HIP.  Device faults surface at the caller's
+ *     next synchronization.  NaN/Inf in the inputs are not checked; they
+ *     propagate to the outputs.
+ *   - Supported sizes (anything else is HM_ERR_UNSUPPORTED):
+ *       bf16:  d in {32, 64, 128}, f in {16, 32, 64}, dv in {64, 128}
+ *              (hm_featurize: d in {32, 64, 128}, f in {16, 32, 64})
+ *       f32:   d in {16, 32, 64},  f in {16, 32},     dv in {16, 32, 64}
+ *              (hm_featurize: d in {16, 32, 64, 128}, f in {16, 32, 64})
+ *     B, H, n may be 0 (nothing to compute; s_final is still written).
+ */
+#ifndef HM_H
+#define HM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HM_ABI_VERSION 1
+
+typedef enum {
+  HM_OK = 0,
+  HM_ERR_NULL = 1,        /* a required pointer is NULL (or dt/A_log given alone) */
+  HM_ERR_SHAPE = 2,       /* negative size, or a stride that makes rows overlap   */
+  HM_ERR_DTYPE = 3,       /* unknown dtype code                                    */
+  HM_ERR_ALIGN = 4,       /* pointer or stride not 16-byte aligned                 */
+  HM_ERR_UNSUPPORTED = 5, /* valid but not built: see the size table above         */
+  HM_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required            */
+  HM_ERR_HIP = 7          /* a HIP launch failed                                   */
+} hm_status;
+
+typedef enum { HM_F32 = 0, HM_BF16 = 1 } hm_dtype;
+
+/*
+ * hm_featurize — the Hedgehog feature map alone ([HM] §2.1, §5.3):
+ *   phi[b,h,t,:] = softmax([x[b,h,t,:] W_h, -x[b,h,t,:] W_h]),  F = 2f entries,
+ *   the +xW half first.
+ * x: [B, H, n, d] in `dtype` (strides sx_*); w: [d, f] in `dtype` (head stride
+ * sw_h); phi: [B, H, n, 2f] in `phi_dtype` (strides sp_*).  The projection is
+ * accumulated in float32, the softmax is evaluated in float32.
+ */
+typedef struct {
+  const void *x;
+  const void *w;
+  void *phi;
+  int32_t dtype;      /* hm_dtype of x and w */
+  int32_t phi_dtype;  /* hm_dtype of phi     */
+  int64_t B, H, n, d, f;
+  int64_t sx_b, sx_h, sx_t;
+  int64_t sw_h;
+  int64_t sp_b, sp_h, sp_t;
+} hm_featurize_args;
+
+hm_status hm_featurize(const hm_featurize_args *args, void *stream);
+
+/*
+ * hm_linattn_fwd — causal prefill over n tokens (the chunk-parallel mode of
+ * [LA] part 5): featurize q and k, run the decayed state scan with the
+ * numerator/denominator split of [HM] §2.3, write o.
+ *   q, k: [B, H, n, d]; v: [B, H, n, dv]; o: [B, H, n, dv] — all in `dtype`
+ *   (strides s*_b, s*_h, s*_t; inner dimension contiguous).
+ *   w_q, w_k: [d, f] each (head stride sw_h).
+ *   s_init: optional initial state (NULL = zeros); s_final: optional, receives the
+ *   state after token n-1.  They may point to the same buffer.
+ *   chunk: 0 = automatic, else 64 (the only chunk length built).
+ *   segments: 0 = automatic, else the number of sequence segments scanned in
+ *   parallel (their start states are joined by the affine composition of
+ *   [SSM] §4.2).  dsplit: 0 = automatic, 1 or 2 = number of workgroups that
+ *   share one (b, h), each owning dv/dsplit value columns.
+ *   workspace: device scratch of at least hm_linattn_fwd_workspace_size() bytes
+ *   (it may be NULL when that size is 0).  Its size grows with B*H*segments,
+ *   never with n^2.
+ * Accumulation is float32 and the carried state is float32; bf16 operands of the
+ * matrix products (phi, the masked score tile, the state copy used for the
+ * read-out) are rounded to nearest even.
+ */
+typedef struct {
+  const void *q, *k, *v, *w_q, *w_k;
+  const float *dt, *a_log;
+  const float *s_init;
+  float *s_final;
+  void *o;
+  int32_t dtype;
+  int32_t chunk;
+  int32_t segments;
+  int32_t dsplit;
+  int64_t B, H, n, d, f, dv;
+  int64_t sq_b, sq_h, sq_t;
+  int64_t sk_b, sk_h, sk_t;
+  int64_t sv_b, sv_h, sv_t;
+  int64_t so_b, so_h, so_t;
+  int64_t sw_h;
+  int64_t sdt_b, sdt_h, sdt_t;
+  void *workspace;
+  size_t workspace_bytes;
+} hm_linattn_fwd_args;
+
+hm_status hm_linattn_fwd_workspace_size(const hm_linattn_fwd_args *args, size_t *bytes);
+
+/* The (chunk, segments, dsplit) that hm_linattn_fwd will use for these args. */
+hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *args, int32_t *chunk,
+                              int32_t *segments, int32_t *dsplit);
+
+hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
+
+/*
+ * hm_linattn_step — one decode token per (b, h) (the recurrent mode of [LA]
+ * part 5): featurize q_t, k_t, then S <- a_t S + phi(k_t) v_t^T,
+ * z <- a_t z + phi(k_t), o_t = phi(q_t)^T S / phi(q_t)^T z.  The state is read and
+ * written in place.
+ *   q, k: [B, H, d]; v, o: [B, H, dv] in `dtype` (strides s*_b, s*_h);
+ *   dt: [B, H] float32 (strides sdt_b, sdt_h) or NULL; state: see above.
+ */
+typedef struct {
+  const void *q, *k, *v, *w_q, *w_k;
+  const float *dt, *a_log;
+  float *state;
+  void *o;
+  int32_t dtype;
+  int32_t reserved;
+  int64_t B, H, d, f, dv;
+  int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h;
+  int64_t sw_h;
+  int64_t sdt_b, sdt_h;
+} hm_linattn_step_args;
+
+hm_status hm_linattn_step(const hm_linattn_step_args *args, void *stream);
+
+const char *hm_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *hm_last_error_message(void);
+int hm_abi_version(void);
+/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step), for bindings. */
+size_t hm_args_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HM_H */

@@ -1,0 +1,362 @@
+// Host side of the C ABI declared in include/hm.h: argument validation (before
+// any HIP call), plan selection, launch-table lookup and launches.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "hm.h"
+#include "hm_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+hm_status fail(hm_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+hm_status ok() {
+  g_err.clear();
+  return HM_OK;
+}
+
+size_t esize(int dt) { return dt == HM_BF16 ? 2 : 4; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
+
+struct Tables {
+  hm::Table parts[4];
+  Tables() {
+    parts[0] = hm::table_fwd_bf16();
+    parts[1] = hm::table_fwd_bf16_decay();
+    parts[2] = hm::table_fwd_f32();
+    parts[3] = hm::table_step_feat();
+  }
+};
+const Tables &tables() {
+  static Tables t;
+  return t;
+}
+
+const hm::FwdEntry *find_fwd(int dt, int64_t dk, int64_t fh, int64_t dw, int decay, int mode) {
+  for (const auto &part : tables().parts)
+    for (int i = 0; i < part.nfwd; ++i) {
+      const auto &e = part.fwd[i];
+      if (e.dtype == dt && e.dk == dk && e.fh == fh && e.dw == dw && e.decay == decay && e.mode == mode) return &e;
+    }
+  return nullptr;
+}
+const hm::StepEntry *find_step(int dt, int64_t dk, int64_t fh, int64_t dv, int decay) {
+  for (const auto &part : tables().parts)
+    for (int i = 0; i < part.nstep; ++i) {
+      const auto &e = part.step[i];
+      if (e.dtype == dt && e.dk == dk && e.fh == fh && e.dv == dv && e.decay == decay) return &e;
+    }
+  return nullptr;
+}
+const hm::FeatEntry *find_feat(int dt, int pdt, int64_t dk, int64_t fh) {
+  for (const auto &part : tables().parts)
+    for (int i = 0; i < part.nfeat; ++i) {
+      const auto &e = part.feat[i];
+      if (e.dtype == dt && e.phi_dtype == pdt && e.dk == dk && e.fh == fh) return &e;
+    }
+  return nullptr;
+}
+
+hm_status check_launch(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(HM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ------------------------------------------------------------------ prefill
+struct Plan {
+  int chunk, segments, dsplit;
+  int64_t seg_len;
+  bool alias;           // s_init and s_final overlap
+  bool init_copy;       // s_init is copied into the workspace first
+  size_t ws_state_floats, ws_lam_floats, ws_init_floats;
+  size_t bytes() const { return 4 * (ws_state_floats + ws_lam_floats + ws_init_floats); }
+};
+
+hm_status validate_fwd(const hm_linattn_fwd_args *a) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f, dv >= 1");
+  // with no token to process, q, k, v, w and o are never touched and may be NULL
+  if (a->B * a->H * a->n > 0 && (!a->q || !a->k || !a->v || !a->w_q || !a->w_k || !a->o))
+    return fail(HM_ERR_NULL, "q, k, v, w_q, w_k and o must be non-NULL");
+  if (a->B * a->H * a->n > 0 && (a->dt == nullptr) != (a->a_log == nullptr))
+    return fail(HM_ERR_NULL, "dt and a_log must be given together");
+  const int64_t strides[] = {a->sq_b, a->sq_h, a->sq_t, a->sk_b, a->sk_h, a->sk_t, a->sv_b,
+                             a->sv_h, a->sv_t, a->so_b, a->so_h, a->so_t, a->sw_h};
+  for (int64_t s : strides)
+    if (s < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->sdt_b < 0 || a->sdt_h < 0 || a->sdt_t < 0) return fail(HM_ERR_SHAPE, "dt strides must be non-negative");
+  if (a->n > 1 && (a->so_t < a->dv || a->sq_t < a->d || a->sk_t < a->d || a->sv_t < a->dv))
+    return fail(HM_ERR_SHAPE, "token stride smaller than the row length (rows overlap)");
+  const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->o};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(HM_ERR_ALIGN, "q, k, v, w_q, w_k, o must be 16-byte aligned");
+  if ((a->s_init && !aligned16(a->s_init)) || (a->s_final && !aligned16(a->s_final)))
+    return fail(HM_ERR_ALIGN, "state buffers must be 16-byte aligned");
+  for (int64_t s : strides)
+    if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  if (a->chunk != 0 && a->chunk != hm::CHUNK) return fail(HM_ERR_UNSUPPORTED, "chunk %d: only 0 (auto) or 64 are built", a->chunk);
+  if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0");
+  if (a->dsplit < 0 || a->dsplit > 2) return fail(HM_ERR_UNSUPPORTED, "dsplit must be 0, 1 or 2");
+  const int decay = a->dt != nullptr && a->a_log != nullptr;
+  // the full-pass kernel for dsplit 1 must exist for the size to count as supported
+  if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) &&
+      !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL))
+    return fail(HM_ERR_UNSUPPORTED, "no kernel built for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
+                (long long)a->f, (long long)a->dv);
+  if (a->dsplit == 2 && (a->dv % 2 || !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL)))
+    return fail(HM_ERR_UNSUPPORTED, "dsplit=2 is not built for dv=%lld", (long long)a->dv);
+  if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL))
+    return fail(HM_ERR_UNSUPPORTED, "dsplit=1 is not built for dv=%lld", (long long)a->dv);
+  return ok();
+}
+
+Plan make_plan(const hm_linattn_fwd_args *a) {
+  Plan p{};
+  const int decay = a->dt != nullptr && a->a_log != nullptr;
+  const int64_t BH = a->B * a->H;
+  const int64_t F = 2 * a->f;
+  const int64_t BLK = F * a->dv + F;
+  const int C = hm::CHUNK;
+  p.chunk = C;
+  // dsplit: split the value columns over two workgroups when (b, h) pairs alone
+  // cannot fill the 256 compute units
+  if (a->dsplit) {
+    p.dsplit = a->dsplit;
+  } else {
+    const bool can2 = a->dv % 2 == 0 && find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL);
+    const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) != nullptr;
+    p.dsplit = (!can1 || (can2 && BH < 256)) ? 2 : 1;
+  }
+  const int64_t nchunks = (a->n + C - 1) / C;
+  int64_t segs;
+  if (a->segments) {
+    segs = a->segments;
+  } else {
+    // enough (b, h, segment, half) workgroups for two waves of the chip, with
+    // segments of at least 16 chunks so the extra k, v pass stays small
+    const int64_t wg = BH * p.dsplit;
+    segs = wg >= 512 || wg == 0 ? 1 : (512 + wg - 1) / wg;
+    const int64_t cap = nchunks / 16 > 1 ? nchunks / 16 : 1;
+    if (segs > cap) segs = cap;
+  }
+  if (segs > nchunks) segs = nchunks > 0 ? nchunks : 1;
+  if (segs < 1) segs = 1;
+  const int64_t per = nchunks > 0 ? (nchunks + segs - 1) / segs : 1;
+  p.seg_len = per * C;
+  p.segments = nchunks > 0 ? (int)((nchunks + per - 1) / per) : 1;
+  // aliasing of s_init and s_final: several workgroups per (b, h) would race
+  p.alias = false;
+  if (a->s_init && a->s_final) {
+    const char *i0 = (const char *)a->s_init, *f0 = (const char *)a->s_final;
+    const size_t len = (size_t)BH * BLK * 4;
+    p.alias = i0 < f0 + len && f0 < i0 + len;
+  }
+  p.init_copy = p.alias && (p.segments > 1 || p.dsplit > 1);
+  p.ws_state_floats = p.segments > 1 ? (size_t)(p.segments - 1) * BH * BLK : 0;
+  p.ws_lam_floats = p.segments > 1 ? (size_t)(p.segments - 1) * BH : 0;
+  p.ws_lam_floats = (p.ws_lam_floats + 3) / 4 * 4;
+  p.ws_init_floats = p.init_copy ? (size_t)BH * BLK : 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+hm_status hm_linattn_fwd_workspace_size(const hm_linattn_fwd_args *a, size_t *bytes) {
+  if (!bytes) return fail(HM_ERR_NULL, "bytes is NULL");
+  hm_status st = validate_fwd(a);
+  if (st != HM_OK) return st;
+  *bytes = make_plan(a).bytes();
+  return ok();
+}
+
+hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *a, int32_t *chunk, int32_t *segments, int32_t *dsplit) {
+  hm_status st = validate_fwd(a);
+  if (st != HM_OK) return st;
+  Plan p = make_plan(a);
+  if (chunk) *chunk = p.chunk;
+  if (segments) *segments = p.segments;
+  if (dsplit) *dsplit = p.dsplit;
+  return ok();
+}
+
+hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
+  hm_status st = validate_fwd(a);
+  if (st != HM_OK) return st;
+  const Plan pl = make_plan(a);
+  if (pl.bytes() > 0) {
+    if (!a->workspace) return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.bytes());
+    if (a->workspace_bytes < pl.bytes())
+      return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.bytes(), a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(HM_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  const int64_t BH = a->B * a->H;
+  if (BH == 0) return ok();
+  if (a->n == 0 && !a->s_final) return ok();
+  const int decay = a->dt != nullptr && a->a_log != nullptr;
+  const int64_t dw = a->dv / pl.dsplit;
+  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_FULL);
+  const hm::FwdEntry *local = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_LOCAL);
+  if (!full || !local) return fail(HM_ERR_UNSUPPORTED, "no kernel for dv/dsplit=%lld", (long long)dw);
+  hipStream_t s = (hipStream_t)stream;
+
+  float *ws = (float *)a->workspace;
+  float *ws_state = ws;
+  float *ws_lam = ws ? ws + pl.ws_state_floats : nullptr;
+  float *ws_init = ws ? ws + pl.ws_state_floats + pl.ws_lam_floats : nullptr;
+  const int64_t F = 2 * a->f;
+  const int64_t BLK = F * a->dv + F;
+
+  hm::FwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
+  p.dt = a->dt; p.a_log = a->a_log;
+  p.s_start0 = pl.init_copy ? ws_init : a->s_init;
+  p.s_final = a->s_final;
+  p.o = a->o;
+  p.ws_state = ws_state; p.ws_lam = ws_lam;
+  p.B = a->B; p.H = a->H; p.n = a->n; p.dv = a->dv;
+  p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sq_t = a->sq_t;
+  p.sk_b = a->sk_b; p.sk_h = a->sk_h; p.sk_t = a->sk_t;
+  p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t;
+  p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
+  p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
+  p.seg_len = pl.seg_len;
+  p.nseg = pl.segments;
+  p.dsplit = pl.dsplit;
+
+  auto grid_for = [&](int64_t items) { return (unsigned)(((items + 7) / 8) * 8 * pl.dsplit); };
+  if (pl.segments > 1) {
+    hm::FwdParams pp = p;
+    pp.nseg_run = pl.segments - 1;
+    pp.nitems = BH * pp.nseg_run;
+    local->launch(pp, grid_for(pp.nitems), s);
+    if ((st = check_launch("segment pass")) != HM_OK) return st;
+  }
+  if (pl.segments > 1 || pl.init_copy) {
+    dim3 grid((unsigned)((BLK + 255) / 256), (unsigned)BH);
+    hipLaunchKernelGGL(hm::combine_kernel, grid, dim3(256), 0, s, ws_state, ws_lam, a->s_init,
+                       pl.init_copy ? ws_init : nullptr, BH, BLK, pl.segments);
+    if ((st = check_launch("segment combine")) != HM_OK) return st;
+  }
+  p.nseg_run = pl.segments;
+  p.nitems = BH * pl.segments;
+  full->launch(p, grid_for(p.nitems), s);
+  return check_launch("prefill");
+}
+
+// ------------------------------------------------------------------ decode
+hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H >= 0 and d, f, dv >= 1");
+  if (a->B * a->H > 0 && (!a->q || !a->k || !a->v || !a->w_q || !a->w_k || !a->o || !a->state))
+    return fail(HM_ERR_NULL, "q, k, v, w_q, w_k, state and o must be non-NULL");
+  if ((a->dt == nullptr) != (a->a_log == nullptr)) return fail(HM_ERR_NULL, "dt and a_log must be given together");
+  const int64_t strides[] = {a->sq_b, a->sq_h, a->sk_b, a->sk_h, a->sv_b, a->sv_h, a->so_b, a->so_h, a->sw_h};
+  for (int64_t s : strides)
+    if (s < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->sdt_b < 0 || a->sdt_h < 0) return fail(HM_ERR_SHAPE, "dt strides must be non-negative");
+  const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->o, a->state};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(HM_ERR_ALIGN, "q, k, v, w_q, w_k, o and state must be 16-byte aligned");
+  for (int64_t s : strides)
+    if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  const int decay = a->dt != nullptr;
+  const hm::StepEntry *e = find_step(a->dtype, a->d, a->f, a->dv, decay);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no decode kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
+                (long long)a->f, (long long)a->dv);
+  const int64_t BH = a->B * a->H;
+  if (BH == 0) return ok();
+  hm::StepParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
+  p.dt = a->dt; p.a_log = a->a_log; p.state = a->state; p.o = a->o;
+  p.B = a->B; p.H = a->H;
+  p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sk_b = a->sk_b; p.sk_h = a->sk_h;
+  p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.so_b = a->so_b; p.so_h = a->so_h;
+  p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h;
+  e->launch(p, (unsigned)BH, (hipStream_t)stream);
+  return check_launch("decode step");
+}
+
+// ------------------------------------------------------------------ featurize
+hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if ((a->dtype != HM_F32 && a->dtype != HM_BF16) || (a->phi_dtype != HM_F32 && a->phi_dtype != HM_BF16))
+    return fail(HM_ERR_DTYPE, "dtype %d / phi_dtype %d must be HM_F32 or HM_BF16", a->dtype, a->phi_dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f >= 1");
+  if (a->B * a->H * a->n > 0 && (!a->x || !a->w || !a->phi)) return fail(HM_ERR_NULL, "x, w and phi must be non-NULL");
+  if (a->sx_b < 0 || a->sx_h < 0 || a->sx_t < 0 || a->sw_h < 0 || a->sp_b < 0 || a->sp_h < 0 || a->sp_t < 0)
+    return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->n > 1 && (a->sx_t < a->d || a->sp_t < 2 * a->f))
+    return fail(HM_ERR_SHAPE, "token stride smaller than the row length (rows overlap)");
+  if (!aligned16(a->x) || !aligned16(a->w) || !aligned16(a->phi))
+    return fail(HM_ERR_ALIGN, "x, w and phi must be 16-byte aligned");
+  if (!stride_ok(a->sx_b, a->dtype) || !stride_ok(a->sx_h, a->dtype) || !stride_ok(a->sx_t, a->dtype) ||
+      !stride_ok(a->sw_h, a->dtype) || !stride_ok(a->sp_b, a->phi_dtype) || !stride_ok(a->sp_h, a->phi_dtype) ||
+      !stride_ok(a->sp_t, a->phi_dtype))
+    return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  const hm::FeatEntry *e = find_feat(a->dtype, a->phi_dtype, a->d, a->f);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no featurize kernel for dtype=%d phi_dtype=%d d=%lld f=%lld", a->dtype,
+                a->phi_dtype, (long long)a->d, (long long)a->f);
+  const int64_t BH = a->B * a->H;
+  if (BH == 0 || a->n == 0) return ok();
+  hm::FeatParams p{};
+  p.x = a->x; p.w = a->w; p.phi = a->phi;
+  p.B = a->B; p.H = a->H; p.n = a->n;
+  p.sx_b = a->sx_b; p.sx_h = a->sx_h; p.sx_t = a->sx_t; p.sw_h = a->sw_h;
+  p.sp_b = a->sp_b; p.sp_h = a->sp_h; p.sp_t = a->sp_t;
+  e->launch(p, dim3((unsigned)((a->n + 63) / 64), (unsigned)BH), (hipStream_t)stream);
+  return check_launch("featurize");
+}
+
+const char *hm_status_string(int s) {
+  switch (s) {
+    case HM_OK: return "HM_OK";
+    case HM_ERR_NULL: return "HM_ERR_NULL";
+    case HM_ERR_SHAPE: return "HM_ERR_SHAPE";
+    case HM_ERR_DTYPE: return "HM_ERR_DTYPE";
+    case HM_ERR_ALIGN: return "HM_ERR_ALIGN";
+    case HM_ERR_UNSUPPORTED: return "HM_ERR_UNSUPPORTED";
+    case HM_ERR_WORKSPACE: return "HM_ERR_WORKSPACE";
+    case HM_ERR_HIP: return "HM_ERR_HIP";
+    default: return "HM_ERR_UNKNOWN";
+  }
+}
+
+const char *hm_last_error_message(void) { return g_err.c_str(); }
+
+int hm_abi_version(void) { return HM_ABI_VERSION; }
+
+size_t hm_args_size(int which) {
+  switch (which) {
+    case 0: return sizeof(hm_featurize_args);
+    case 1: return sizeof(hm_linattn_fwd_args);
+    case 2: return sizeof(hm_linattn_step_args);
+    default: return 0;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Launch tables: each kernel translation unit exports the instantiations it
+// builds; the ABI layer looks a configuration up and launches it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "hm_prefill.hpp"
+#include "hm_step.hpp"
+
+namespace hm {
+
+struct FwdEntry {
+  int dtype, dk, fh, dw, decay, mode;
+  void (*launch)(const FwdParams &, unsigned grid, hipStream_t);
+};
+struct StepEntry {
+  int dtype, dk, fh, dv, decay;
+  void (*launch)(const StepParams &, unsigned grid, hipStream_t);
+};
+struct FeatEntry {
+  int dtype, phi_dtype, dk, fh;
+  void (*launch)(const FeatParams &, dim3 grid, hipStream_t);
+};
+struct Table {
+  const FwdEntry *fwd;
+  int nfwd;
+  const StepEntry *step;
+  int nstep;
+  const FeatEntry *feat;
+  int nfeat;
+};
+
+// one per kernel translation unit
+Table table_fwd_bf16();
+Table table_fwd_bf16_decay();
+Table table_fwd_f32();
+Table table_step_feat();
+
+template <typename T, int DK, int FH, int DW, bool DECAY, int MODE>
+void launch_fwd(const FwdParams &p, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_kernel<T, DK, FH, DW, DECAY, MODE>), dim3(grid), dim3(fwd_waves(DW) * 64), 0, s, p);
+}
+template <typename T, int DK, int FH, int DV, bool DECAY>
+void launch_step(const StepParams &p, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((step_kernel<T, DK, FH, DV, DECAY>), dim3(grid), dim3(256), 0, s, p);
+}
+template <typename T, typename TO, int DK, int FH>
+void launch_feat(const FeatParams &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((featurize_kernel<T, TO, DK, FH>), grid, dim3(256), 0, s, p);
+}
+
+}  // namespace hm
+
+// dtype codes as in hm.h
+#define HM_DT_F32 0
+#define HM_DT_BF16 1
+
+#define HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, MODE) \
+  {TC, DK, FH, DW, DEC, MODE, &hm::launch_fwd<T, DK, FH, DW, (DEC != 0), MODE>}
+// both modes of one configuration
+#define HM_FWD_PAIR(T, TC, DK, FH, DW, DEC) \
+  HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 0), HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 1)

@@ -1,0 +1,204 @@
+// Decode step and standalone featurizer.
+//
+// Decode (the recurrent mode of the cnblogs linear-attention tutorial, part 5;
+// per-step cost is the fixed-size state, quant67 SSM lecture §5.1): one
+// workgroup per (b, h).  The kernel is bound by HBM traffic on the state
+// (F*dv + F floats read and written once), so it is organised around that:
+// every thread issues all of its 16-byte state loads first, computes the two
+// Hedgehog features and the decay while they are in flight, then updates,
+// reads out and stores its slice with 16-byte accesses.
+#pragma once
+
+#include "hm_device.hpp"
+
+namespace hm {
+
+struct StepParams {
+  const void *q, *k, *v, *wq, *wk;
+  const float *dt, *a_log;
+  float *state;
+  void *o;
+  int64_t B, H;
+  int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h, sw_h, sdt_b, sdt_h;
+};
+
+template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
+
+template <typename T, int DK, int FH, int DV, bool DECAY>
+__global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
+  constexpr int NT = 256;
+  constexpr int F = 2 * FH;
+  constexpr int RV = DV / 4;                 // float4 per state row
+  constexpr int NS4 = F * RV;                // float4 in S
+  constexpr int PER = (NS4 + NT - 1) / NT;   // float4 per thread
+  constexpr int GROUPS = NT / RV;            // threads sharing one column group
+  constexpr int PARTS = NT / (2 * FH);       // threads per projection output
+  constexpr int DPART = DK / PARTS;
+  static_assert(NT % RV == 0 && NT % (2 * FH) == 0 && DK % PARTS == 0, "step mapping");
+
+  __shared__ float sx[2][DK];
+  __shared__ float su[PARTS][2 * FH];
+  __shared__ __align__(16) float sphi[2][F];  // [0] = phi(q), [1] = phi(k)
+  __shared__ __align__(16) float sred[GROUPS][DV];
+  __shared__ float sden[F / 4 > 0 ? F / 4 : 1];
+  __shared__ float sa;
+
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh % p.H;
+  constexpr int64_t BLK = (int64_t)F * DV + F;
+  float *st = p.state + bh * BLK;
+
+  // 1. issue the state loads
+  f32x4 sv[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + NT * m;
+    if (idx < NS4) sv[m] = reinterpret_cast<const f32x4 *>(st)[idx];
+  }
+  f32x4 zv = zero4();
+  if (tid < F / 4) zv = reinterpret_cast<const f32x4 *>(st + F * DV)[tid];
+
+  // 2. featurize q and k: u[j] = sum_i x[i] W[i][j], split over PARTS threads
+  const T *xq = (const T *)p.q + b * p.sq_b + h * p.sq_h;
+  const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
+  for (int i = tid; i < 2 * DK; i += NT) sx[i / DK][i % DK] = ldf(i < DK ? xq + i : xk + (i - DK));
+  if (tid == 0) {
+    float a = 1.f;
+    if constexpr (DECAY) a = __expf(-softplus_f32(p.dt[b * p.sdt_b + h * p.sdt_h]) * expf(p.a_log[h]));
+    sa = a;
+  }
+  __syncthreads();
+  {
+    const int o = tid % (2 * FH), part = tid / (2 * FH);
+    const int proj = o / FH, j = o % FH;
+    const T *W = (const T *)(proj == 0 ? p.wq : p.wk) + h * p.sw_h;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int i = part * DPART; i < (part + 1) * DPART; ++i) acc += sx[proj][i] * ldf(W + i * FH + j);
+    su[part][o] = acc;
+  }
+  __syncthreads();
+  // softmax over [u, -u]: wave 0 handles q, wave 1 handles k (FH <= 64 lanes)
+  {
+    const int w = tid >> 6, lane = tid & 63;
+    if (w < 2) {
+      float u = 0.f;
+      if (lane < FH) {
+#pragma unroll
+        for (int part = 0; part < PARTS; ++part) u += su[part][w * FH + lane];
+      }
+      float m = lane < FH ? fabsf(u) : 0.f;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float ep = lane < FH ? __expf(u - m) : 0.f, em = lane < FH ? __expf(-u - m) : 0.f;
+      float sum = ep + em;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      const float inv = 1.f / sum;
+      if (lane < FH) {
+        sphi[w][lane] = ep * inv;
+        sphi[w][FH + lane] = em * inv;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 3. update, read out, store.  Thread tid owns column group c4 = tid % RV and
+  //    rows f = tid / RV + GROUPS * m.
+  const float a = sa;
+  const int c4 = tid % RV;
+  const T *vp = (const T *)p.v + b * p.sv_b + h * p.sv_h + 4 * c4;
+  const f32x4 v4 = f32x4{ldf(vp), ldf(vp + 1), ldf(vp + 2), ldf(vp + 3)};
+  f32x4 num = zero4();
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + NT * m;
+    if (idx < NS4) {
+      const int f = idx / RV;
+      const f32x4 s = a * sv[m] + sphi[1][f] * v4;
+      num += sphi[0][f] * s;
+      reinterpret_cast<f32x4 *>(st)[idx] = s;
+    }
+  }
+  *reinterpret_cast<f32x4 *>(&sred[tid / RV][4 * c4]) = num;
+  if (tid < F / 4) {
+    const f32x4 pk = *reinterpret_cast<const f32x4 *>(&sphi[1][4 * tid]);
+    const f32x4 pq = *reinterpret_cast<const f32x4 *>(&sphi[0][4 * tid]);
+    const f32x4 z = a * zv + pk;
+    reinterpret_cast<f32x4 *>(st + F * DV)[tid] = z;
+    sden[tid] = pq[0] * z[0] + pq[1] * z[1] + pq[2] * z[2] + pq[3] * z[3];
+  }
+  __syncthreads();
+  if (tid < DV) {
+    float nsum = 0.f, den = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < GROUPS; ++gi) nsum += sred[gi][tid];
+#pragma unroll
+    for (int i = 0; i < F / 4; ++i) den += sden[i];
+    T *op = (T *)p.o + b * p.so_b + h * p.so_h;
+    op[tid] = to_elem<T>(nsum / den);
+  }
+}
+
+struct FeatParams {
+  const void *x, *w;
+  void *phi;
+  int64_t B, H, n;
+  int64_t sx_b, sx_h, sx_t, sw_h, sp_b, sp_h, sp_t;
+};
+
+// Standalone Hedgehog featurizer (gsyq.cn HedgeMamba explainer §2.1, §5.3):
+// phi = softmax([x W, -x W]).  One workgroup = 64 tokens of one (b, h); wave w
+// computes U^T = W^T X^T for token tile w on the MFMA, then the row softmax with
+// cross-lane reductions, and stores phi rows with 8/16-byte vector stores.
+template <typename T, typename TO, int DK, int FH>
+__global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int NFH = FH / 16, NFT = 2 * NFH, KD = DK / M::KS, LDW = DK + M::PAD;
+  __shared__ __align__(16) T sW[FH * LDW];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
+  const int64_t bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const T *W = (const T *)p.w + h * p.sw_h;
+  for (int i = tid; i < DK * FH; i += 256) sW[(i % FH) * LDW + i / FH] = W[i];
+  const int64_t c = (int64_t)blockIdx.x * 64 + 16 * wv + col;
+  const T *X = (const T *)p.x + b * p.sx_b + h * p.sx_h + c * p.sx_t;
+  frag xf[KD];
+#pragma unroll
+  for (int s = 0; s < KD; ++s) xf[s] = c < p.n ? M::ld_contig(X + s * M::KS, g) : frag{};
+  __syncthreads();
+  f32x4 u[NFH];
+#pragma unroll
+  for (int t = 0; t < NFH; ++t) {
+    u[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < KD; ++s) u[t] = M::mma(M::ld_contig(sW + (16 * t + col) * LDW + s * M::KS, g), xf[s], u[t]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int t = 0; t < NFH; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[t][r]));
+  m = group_max(m);
+  f32x4 ph[NFT];
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < NFH; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ep = __expf(u[t][r] - m), em = __expf(-u[t][r] - m);
+      ph[t][r] = ep;
+      ph[NFH + t][r] = em;
+      sum += ep + em;
+    }
+  sum = group_sum(sum);
+  const float inv = 1.f / sum;
+  if (c < p.n) {
+    TO *P = (TO *)p.phi + b * p.sp_b + h * p.sp_h + c * p.sp_t;
+#pragma unroll
+    for (int t = 0; t < NFT; ++t) store4(P + 16 * t + 4 * g, ph[t] * inv);
+  }
+}
+
+}  // namespace hm

@@ -1,0 +1,9 @@
+// Prefill instantiations: float32 (both decay variants).
+#include "hm_kernels.hpp"
+
+namespace hm {
+#define HM_SET(DK, DEC) \
+  HM_FWD_PAIR(float, HM_DT_F32, DK, 16, 16, DEC), HM_FWD_PAIR(float, HM_DT_F32, DK, 16, 32, DEC)
+static const FwdEntry kFwd[] = {HM_SET(16, 0), HM_SET(16, 1), HM_SET(32, 0), HM_SET(32, 1)};
+Table table_fwd_f32() { return Table{kFwd, (int)(sizeof(kFwd) / sizeof(kFwd[0])), nullptr, 0, nullptr, 0}; }
+}  // namespace hm

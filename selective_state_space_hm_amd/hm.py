@@ -1,0 +1,248 @@
+"""Thin ctypes binding of libhm.so (the C ABI declared in include/hm.h).
+
+Argument marshalling only: tensors are validated for device/dtype, their
+data_ptr() and element strides go into the argument structs, the current torch
+stream is passed as the HIP stream, and outputs / workspaces are allocated with
+torch.  Every step of the computation runs in the library's HIP kernels; there
+is no fallback.  If libhm.so is missing or cannot be loaded, every entry point
+raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhm.so")
+
+HM_OK, HM_ERR_NULL, HM_ERR_SHAPE, HM_ERR_DTYPE, HM_ERR_ALIGN, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(8)
+HM_F32, HM_BF16 = 0, 1
+CHUNK = 64
+
+p_void = C.c_void_p
+i64 = C.c_int64
+i32 = C.c_int32
+
+
+class FeaturizeArgs(C.Structure):
+    _fields_ = [("x", p_void), ("w", p_void), ("phi", p_void), ("dtype", i32), ("phi_dtype", i32),
+                ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64),
+                ("sx_b", i64), ("sx_h", i64), ("sx_t", i64), ("sw_h", i64),
+                ("sp_b", i64), ("sp_h", i64), ("sp_t", i64)]
+
+
+class FwdArgs(C.Structure):
+    _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
+                ("dt", p_void), ("a_log", p_void), ("s_init", p_void), ("s_final", p_void), ("o", p_void),
+                ("dtype", i32), ("chunk", i32), ("segments", i32), ("dsplit", i32),
+                ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64), ("dv", i64),
+                ("sq_b", i64), ("sq_h", i64), ("sq_t", i64), ("sk_b", i64), ("sk_h", i64), ("sk_t", i64),
+                ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
+                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
+                ("workspace", p_void), ("workspace_bytes", C.c_size_t)]
+
+
+class StepArgs(C.Structure):
+    _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
+                ("dt", p_void), ("a_log", p_void), ("state", p_void), ("o", p_void),
+                ("dtype", i32), ("reserved", i32),
+                ("B", i64), ("H", i64), ("d", i64), ("f", i64), ("dv", i64),
+                ("sq_b", i64), ("sq_h", i64), ("sk_b", i64), ("sk_h", i64), ("sv_b", i64), ("sv_h", i64),
+                ("so_b", i64), ("so_h", i64), ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64)]
+
+
+class HMError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
+           "hm_linattn_step", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
+
+
+def lib():
+    """Load libhm.so once; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = C.CDLL(LIB_PATH)
+        L.hm_featurize.argtypes = [C.POINTER(FeaturizeArgs), p_void]
+        L.hm_linattn_fwd_workspace_size.argtypes = [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]
+        L.hm_linattn_fwd_plan.argtypes = [C.POINTER(FwdArgs), C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)]
+        L.hm_linattn_fwd.argtypes = [C.POINTER(FwdArgs), p_void]
+        L.hm_linattn_step.argtypes = [C.POINTER(StepArgs), p_void]
+        for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
+                   "hm_linattn_step"):
+            getattr(L, fn).restype = C.c_int
+        L.hm_status_string.argtypes = [C.c_int]
+        L.hm_status_string.restype = C.c_char_p
+        L.hm_last_error_message.argtypes = []
+        L.hm_last_error_message.restype = C.c_char_p
+        L.hm_abi_version.restype = C.c_int
+        L.hm_args_size.argtypes = [C.c_int]
+        L.hm_args_size.restype = C.c_size_t
+        _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().hm_status_string(st).decode()
+
+
+def last_error() -> str:
+    return lib().hm_last_error_message().decode()
+
+
+def _check(st):
+    if st != HM_OK:
+        raise HMError(st, last_error())
+
+
+# ---------------------------------------------------------------- raw calls
+def call_featurize(args: FeaturizeArgs, stream=None) -> int:
+    return lib().hm_featurize(C.byref(args), stream)
+
+
+def call_fwd(args: FwdArgs, stream=None) -> int:
+    return lib().hm_linattn_fwd(C.byref(args), stream)
+
+
+def call_workspace_size(args: FwdArgs):
+    n = C.c_size_t(0)
+    st = lib().hm_linattn_fwd_workspace_size(C.byref(args), C.byref(n))
+    return st, n.value
+
+
+def call_plan(args: FwdArgs):
+    c, s, d = i32(0), i32(0), i32(0)
+    st = lib().hm_linattn_fwd_plan(C.byref(args), C.byref(c), C.byref(s), C.byref(d))
+    return st, (c.value, s.value, d.value)
+
+
+def call_step(args: StepArgs, stream=None) -> int:
+    return lib().hm_linattn_step(C.byref(args), stream)
+
+
+# ------------------------------------------------------------ torch-facing
+_DT = {torch.float32: HM_F32, torch.bfloat16: HM_BF16}
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _w_strides(w):
+    if w.dim() == 2:
+        return 0
+    return w.stride(0)
+
+
+def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Tensor | None = None):
+    """phi = softmax([x W, -x W]) for x [B, H, n, d], W [d, f] or [H, d, f]."""
+    _dev(x, w)
+    B, H, n, d = x.shape
+    f = w.shape[-1]
+    if phi is None:
+        phi = torch.empty((B, H, n, 2 * f), dtype=phi_dtype or x.dtype, device=x.device)
+    a = FeaturizeArgs(x=_ptr(x), w=_ptr(w), phi=_ptr(phi), dtype=_code(x), phi_dtype=_code(phi),
+                      B=B, H=H, n=n, d=d, f=f, sx_b=x.stride(0), sx_h=x.stride(1), sx_t=x.stride(2),
+                      sw_h=_w_strides(w), sp_b=phi.stride(0), sp_h=phi.stride(1), sp_t=phi.stride(2))
+    if x.stride(3) != 1 or phi.stride(3) != 1 or w.stride(-1) != 1:
+        raise ValueError("inner dimensions must be contiguous")
+    _check(call_featurize(a, _stream()))
+    return phi
+
+
+def fwd_args(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
+             chunk=0, segments=0, dsplit=0) -> FwdArgs:
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    f = w_q.shape[-1]
+    for t in (q, k, v, o):
+        if t is not None and t.stride(3) != 1:
+            raise ValueError("inner dimensions must be contiguous")
+    return FwdArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
+                   s_init=_ptr(s_init), s_final=_ptr(s_final), o=_ptr(o), dtype=_code(q), chunk=chunk,
+                   segments=segments, dsplit=dsplit, B=B, H=H, n=n, d=d, f=f, dv=dv,
+                   sq_b=q.stride(0), sq_h=q.stride(1), sq_t=q.stride(2),
+                   sk_b=k.stride(0), sk_h=k.stride(1), sk_t=k.stride(2),
+                   sv_b=v.stride(0), sv_h=v.stride(1), sv_t=v.stride(2),
+                   so_b=o.stride(0) if o is not None else 0, so_h=o.stride(1) if o is not None else 0,
+                   so_t=o.stride(2) if o is not None else 0, sw_h=_w_strides(w_q),
+                   sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0,
+                   sdt_t=dt.stride(2) if dt is not None else 0)
+
+
+def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segments=0, dsplit=0, o=None):
+    o = o if o is not None else v
+    a = fwd_args(q, k, v, w_q, w_k, dt, a_log, o=o, chunk=chunk, segments=segments, dsplit=dsplit)
+    st, plan = call_plan(a)
+    _check(st)
+    return plan
+
+
+def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
+                   chunk=0, segments=0, dsplit=0, workspace=None):
+    """Causal prefill.  Returns o [B, H, n, dv] (v's dtype).  s_final (if given) receives
+    the float32 state [B, H, F*dv + F] after the last token."""
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o)
+    if dt is not None and dt.dtype != torch.float32 or a_log is not None and a_log.dtype != torch.float32:
+        raise TypeError("dt and A_log are float32")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit)
+    st, nbytes = call_workspace_size(a)
+    _check(st)
+    if nbytes:
+        if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(call_fwd(a, _stream()))
+    return o
+
+
+def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None):
+    """One decode token per (b, h): q, k [B, H, d], v [B, H, dv]; state [B, H, F*dv+F]
+    float32 is updated in place.  Returns o [B, H, dv]."""
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o)
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    f = w_q.shape[-1]
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    if state.dtype != torch.float32:
+        raise TypeError("state is float32")
+    a = StepArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
+                 state=_ptr(state), o=_ptr(o), dtype=_code(q), B=B, H=H, d=d, f=f, dv=dv,
+                 sq_b=q.stride(0), sq_h=q.stride(1), sk_b=k.stride(0), sk_h=k.stride(1),
+                 sv_b=v.stride(0), sv_h=v.stride(1), so_b=o.stride(0), so_h=o.stride(1), sw_h=_w_strides(w_q),
+                 sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0)
+    _check(call_step(a, _stream()))
+    return o
+
+
+def state_numel(f: int, dv: int) -> int:
+    """float32 elements of one (b, h) state block: S [2f][dv] then z [2f]."""
+    return 2 * f * dv + 2 * f

@@ -1,0 +1,207 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point that
+include/hm.h declares, its struct layouts match the binding, and every invalid
+argument is rejected with the documented status before any HIP call (fake,
+never-dereferenced device addresses are used, so no GPU is needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from selective_state_space_hm_amd import hm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hm.h")
+
+A = 0x7f0000000000  # fake 16-byte aligned device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 9
+    L = hm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(hm.EXPORTS)
+
+
+def test_struct_layouts_match_binding():
+    L = hm.lib()
+    assert L.hm_args_size(0) == C.sizeof(hm.FeaturizeArgs)
+    assert L.hm_args_size(1) == C.sizeof(hm.FwdArgs)
+    assert L.hm_args_size(2) == C.sizeof(hm.StepArgs)
+    assert L.hm_args_size(3) == 0
+
+
+def test_version_and_status_strings():
+    assert hm.lib().hm_abi_version() == 1
+    for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
+                                 "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
+        assert hm.status_string(code) == name
+    assert hm.status_string(99) == "HM_ERR_UNKNOWN"
+
+
+def fwd(B=2, H=16, n=2048, d=128, f=64, dv=128, dtype=hm.HM_BF16, decay=False, **kw):
+    a = hm.FwdArgs(q=A, k=A + 0x1000000, v=A + 0x2000000, w_q=A + 0x3000000, w_k=A + 0x3100000,
+                   o=A + 0x4000000, dtype=dtype, B=B, H=H, n=n, d=d, f=f, dv=dv,
+                   sq_b=H * n * d, sq_h=n * d, sq_t=d, sk_b=H * n * d, sk_h=n * d, sk_t=d,
+                   sv_b=H * n * dv, sv_h=n * dv, sv_t=dv, so_b=H * n * dv, so_h=n * dv, so_t=dv)
+    if decay:
+        a.dt = A + 0x5000000
+        a.a_log = A + 0x6000000
+        a.sdt_b, a.sdt_h, a.sdt_t = H * n, n, 1
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def expect(st, code):
+    assert st == code, f"{hm.status_string(st)} ({hm.last_error()}) != {hm.status_string(code)}"
+    if code != hm.HM_OK:
+        assert hm.last_error() != ""
+
+
+def test_fwd_validation_errors():
+    expect(hm.lib().hm_linattn_fwd(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_fwd(fwd(q=None)), hm.HM_ERR_NULL)
+    expect(hm.call_fwd(fwd(o=None)), hm.HM_ERR_NULL)
+    a = fwd()
+    a.dt = A
+    expect(hm.call_fwd(a), hm.HM_ERR_NULL)            # dt without A_log
+    a = fwd(decay=True)
+    a.a_log = None
+    expect(hm.call_fwd(a), hm.HM_ERR_NULL)            # A_log without dt
+    expect(hm.call_fwd(fwd(dtype=7)), hm.HM_ERR_DTYPE)
+    expect(hm.call_fwd(fwd(n=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_fwd(fwd(d=0)), hm.HM_ERR_SHAPE)
+    expect(hm.call_fwd(fwd(sq_t=-128)), hm.HM_ERR_SHAPE)
+    expect(hm.call_fwd(fwd(so_t=64)), hm.HM_ERR_SHAPE)  # rows of o would overlap
+    expect(hm.call_fwd(fwd(q=A + 2)), hm.HM_ERR_ALIGN)
+    expect(hm.call_fwd(fwd(sq_t=132)), hm.HM_ERR_ALIGN)  # 264 bytes: not a multiple of 16
+    expect(hm.call_fwd(fwd(s_init=A + 4)), hm.HM_ERR_ALIGN)
+    expect(hm.call_fwd(fwd(d=96)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(f=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(dtype=hm.HM_F32)), hm.HM_ERR_UNSUPPORTED)  # f32 at d=128 not built
+    expect(hm.call_fwd(fwd(chunk=128)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(dsplit=3)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(segments=-2)), hm.HM_ERR_SHAPE)
+
+
+def test_fwd_workspace_required_when_segmented():
+    a = fwd(B=1, H=16, n=131072, decay=True)
+    st, nbytes = hm.call_workspace_size(a)
+    expect(st, hm.HM_OK)
+    assert nbytes > 0
+    expect(hm.call_fwd(a), hm.HM_ERR_WORKSPACE)        # NULL workspace
+    a.workspace = A + 0x7000000
+    a.workspace_bytes = nbytes - 16
+    expect(hm.call_fwd(a), hm.HM_ERR_WORKSPACE)        # too small
+    a.workspace_bytes = nbytes
+    a.workspace = A + 0x7000004
+    expect(hm.call_fwd(a), hm.HM_ERR_ALIGN)
+
+
+def test_workspace_is_linear_not_quadratic():
+    # explicit segment count: the workspace does not depend on n at all
+    sizes = [hm.call_workspace_size(fwd(B=1, H=16, n=n, segments=8))[1] for n in (4096, 65536, 1 << 20)]
+    assert sizes[0] == sizes[1] == sizes[2]
+    F, dv, BH = 128, 128, 16
+    assert sizes[0] == 7 * BH * (F * dv + F) * 4 + 4 * ((7 * BH + 3) // 4 * 4)
+    # automatic plans stay bounded by the segment cap as n grows
+    auto = [hm.call_workspace_size(fwd(B=1, H=16, n=n, decay=True))[1] for n in (8192, 131072, 1 << 21)]
+    assert max(auto) <= 512 * (F * dv + F) * 4 * 2
+    assert hm.call_workspace_size(fwd(B=8, H=16, n=2048, segments=1))[1] == 0
+
+
+def test_plans():
+    st, plan = hm.call_plan(fwd(B=8, H=16, n=2048))
+    expect(st, hm.HM_OK)
+    assert plan[0] == 64 and plan[2] in (1, 2)
+    st, plan = hm.call_plan(fwd(B=1, H=16, n=131072, decay=True))
+    expect(st, hm.HM_OK)
+    assert plan[1] > 1                                  # long context is segmented
+    st, plan = hm.call_plan(fwd(B=1, H=16, n=131072, decay=True, segments=4, dsplit=1))
+    assert plan == (64, 4, 1)
+    st, plan = hm.call_plan(fwd(B=1, H=16, n=100, segments=50))
+    assert plan[1] == 2                                 # at most one segment per chunk
+    st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=16, f=16, dv=16, dtype=hm.HM_F32))
+    expect(st, hm.HM_OK)
+    assert plan[2] == 1                                 # dv=16 cannot be split
+
+
+def test_alias_needs_init_copy_workspace():
+    a = fwd(B=1, H=16, n=4096, dsplit=2, segments=1)
+    st, base = hm.call_workspace_size(a)
+    a.s_init = A + 0x8000000
+    a.s_final = A + 0x8000000
+    st, aliased = hm.call_workspace_size(a)
+    expect(st, hm.HM_OK)
+    assert aliased - base == 16 * (128 * 128 + 128) * 4
+
+
+def test_zero_sizes_are_valid_without_launch():
+    # B*H == 0 and (n == 0 without s_final) return before any HIP call
+    expect(hm.call_fwd(fwd(B=0)), hm.HM_OK)
+    expect(hm.call_fwd(fwd(n=0)), hm.HM_OK)
+
+
+def step(B=256, H=16, d=128, f=64, dv=128, dtype=hm.HM_BF16, **kw):
+    a = hm.StepArgs(q=A, k=A + 0x100000, v=A + 0x200000, w_q=A + 0x300000, w_k=A + 0x310000,
+                    state=A + 0x400000, o=A + 0x9000000, dtype=dtype, B=B, H=H, d=d, f=f, dv=dv,
+                    sq_b=H * d, sq_h=d, sk_b=H * d, sk_h=d, sv_b=H * dv, sv_h=dv, so_b=H * dv, so_h=dv)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_step_validation_errors():
+    expect(hm.lib().hm_linattn_step(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_step(step(state=None)), hm.HM_ERR_NULL)
+    expect(hm.call_step(step(dt=A)), hm.HM_ERR_NULL)
+    expect(hm.call_step(step(dtype=5)), hm.HM_ERR_DTYPE)
+    expect(hm.call_step(step(B=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_step(step(state=A + 8)), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(sq_h=100)), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(d=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(B=0)), hm.HM_OK)
+
+
+def feat(B=2, H=16, n=2048, d=128, f=64, dtype=hm.HM_BF16, phi_dtype=hm.HM_BF16, **kw):
+    a = hm.FeaturizeArgs(x=A, w=A + 0x1000000, phi=A + 0x2000000, dtype=dtype, phi_dtype=phi_dtype,
+                         B=B, H=H, n=n, d=d, f=f, sx_b=H * n * d, sx_h=n * d, sx_t=d,
+                         sp_b=H * n * 2 * f, sp_h=n * 2 * f, sp_t=2 * f)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_featurize_validation_errors():
+    expect(hm.lib().hm_featurize(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_featurize(feat(phi=None)), hm.HM_ERR_NULL)
+    expect(hm.call_featurize(feat(phi_dtype=3)), hm.HM_ERR_DTYPE)
+    expect(hm.call_featurize(feat(f=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_featurize(feat(sp_t=64)), hm.HM_ERR_SHAPE)
+    expect(hm.call_featurize(feat(x=A + 6)), hm.HM_ERR_ALIGN)
+    expect(hm.call_featurize(feat(d=24)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_featurize(feat(n=0)), hm.HM_OK)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(hm, "_lib", None)
+    monkeypatch.setattr(hm, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        hm.lib()
+
+
+def test_null_pointers_allowed_when_nothing_to_compute():
+    a = fwd(n=0, q=None, k=None, v=None, o=None, w_q=None, w_k=None)
+    expect(hm.call_fwd(a), hm.HM_OK)
+    expect(hm.call_fwd(fwd(n=5, q=None)), hm.HM_ERR_NULL)
+    expect(hm.call_step(step(B=0, q=None, state=None)), hm.HM_OK)
+    expect(hm.call_featurize(feat(n=0, x=None, phi=None)), hm.HM_OK)

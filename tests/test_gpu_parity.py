@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU float64 oracle.
+
+Bars: rel-L2 <= 1e-5 for float32 inputs, <= 2e-2 for bf16 inputs with float32
+accumulation; max-abs is printed beside every rel-L2.  Small cases compare every
+output; the full-size workloads compare whole sampled (b, h) rows, which the
+oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hm_oracle as orc
+from selective_state_space_hm_amd import hm, inputs
+from parity_util import (BF16_TOL, FP32_TOL, oracle_heads, rel_l2, report, run_fwd, to_dev, tol_for)
+
+pytestmark = pytest.mark.gpu
+f64 = inputs.to_f64
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    hm.lib()
+
+
+def full_oracle(case, s_init=None, z_init=None, form="recurrent"):
+    return orc.forward(f64(case.q), f64(case.k), f64(case.v), f64(case.w_q), f64(case.w_k),
+                       f64(case.dt), f64(case.a_log), s_init, z_init, form=form)
+
+
+# ------------------------------------------------------------------ featurize
+@pytest.mark.parametrize("dtype,phi_dtype,d,f", [
+    (torch.float32, torch.float32, 16, 16), (torch.float32, torch.float32, 128, 64),
+    (torch.float32, torch.float32, 64, 32), (torch.bfloat16, torch.bfloat16, 128, 64),
+    (torch.bfloat16, torch.float32, 128, 64), (torch.bfloat16, torch.float32, 32, 16)])
+def test_featurize(dtype, phi_dtype, d, f):
+    c = inputs.make_prefill("feat", 2, 3, 77, d, f, 16, dtype, None, None, seed=3)
+    phi = hm.hm_featurize(c.q.cuda(), c.w_q.cuda(), phi_dtype=phi_dtype)
+    torch.cuda.synchronize()
+    ref = orc.hedgehog_features(f64(c.q), f64(c.w_q))
+    got = f64(phi)
+    r = report(f"featurize {dtype} -> {phi_dtype} d={d} f={f}", got, ref)
+    # float32 output: the float32 softmax itself; bf16 output adds one rounding (2^-9)
+    assert r <= (FP32_TOL if phi_dtype == torch.float32 else 4e-3)
+    np.testing.assert_allclose(got.sum(-1), 1.0, rtol=0, atol=1e-5 if phi_dtype == torch.float32 else 2e-2)
+    assert np.all(got >= 0)
+
+
+def test_featurize_per_head_weights_and_strides():
+    c = inputs.make_prefill("feat", 2, 3, 70, 64, 32, 16, torch.float32, None, None, seed=4)
+    wh = torch.randn((3, 64, 32), generator=torch.Generator().manual_seed(9)) / 8
+    x = c.q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)  # [B, H, n, d] view of [B, n, H, d]
+    phi = hm.hm_featurize(x.cuda(), wh.cuda())
+    torch.cuda.synchronize()
+    ref = orc.hedgehog_features(f64(c.q), f64(wh))
+    assert report("featurize per-head W, strided x", f64(phi), ref) <= FP32_TOL
+
+
+# ------------------------------------------------------------------ prefill
+def test_tiny_fp32_config():
+    """B=1, H=2, n=256, d=16, f=16, fp32, a_t = 1: against both oracle forms."""
+    c = inputs.tiny()
+    o = run_fwd(c)
+    torch.cuda.synchronize()
+    oq, _, _ = full_oracle(c, form="quadratic")
+    orr, _, _ = full_oracle(c)
+    assert report("tiny fp32 vs quadratic", f64(o), oq) <= FP32_TOL
+    assert report("tiny fp32 vs recurrent", f64(o), orr) <= FP32_TOL
+
+
+@pytest.mark.parametrize("n", [1, 5, 37, 64, 65, 200, 333])
+@pytest.mark.parametrize("decay", [None, "mamba", "mild"])
+def test_small_fp32_ragged(n, decay):
+    c = inputs.small(n=n, decay=decay, dtype=torch.float32, d=16, f=16, dv=16, B=2, H=3, seed=n)
+    s_final = torch.full((2, 3, hm.state_numel(16, 16)), float("nan"), device="cuda")
+    o = run_fwd(c, s_final=s_final)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c)
+    assert report(f"fp32 n={n} decay={decay}", f64(o), ref) <= FP32_TOL
+    Sg, zg = orc.unpack_state(f64(s_final), 32, 16)
+    assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
+
+
+@pytest.mark.parametrize("dv", [16, 32])
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (3, 1), (1, 2), (4, 2)])
+def test_fp32_plans_with_initial_state(dv, segments, dsplit):
+    if dsplit == 2 and dv == 16:
+        pytest.skip("dv=16 has one value tile")
+    c = inputs.small(n=300, decay="mild", dtype=torch.float32, d=32, f=16, dv=dv, B=2, H=2, seed=11)
+    r = np.random.default_rng(5)
+    kk = r.random((2, 2, 9, 32))
+    kk /= kk.sum(-1, keepdims=True)
+    S0 = np.einsum("bhjf,bhjd->bhfd", kk, r.normal(size=(2, 2, 9, dv)))
+    z0 = kk.sum(2)
+    s_init = torch.tensor(orc.pack_state(S0, z0), dtype=torch.float32, device="cuda")
+    s_final = torch.empty_like(s_init)
+    o = run_fwd(c, s_init=s_init, s_final=s_final, segments=segments, dsplit=dsplit)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c, S0, z0)
+    assert report(f"fp32 dv={dv} segs={segments} dsplit={dsplit} +S_init", f64(o), ref) <= FP32_TOL
+    Sg, zg = orc.unpack_state(f64(s_final), 32, dv)
+    assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
+
+
+@pytest.mark.parametrize("shape", [(64, 32, 64), (128, 64, 128), (128, 32, 64), (64, 64, 128)])
+@pytest.mark.parametrize("decay", [None, "mild", "mamba"])
+def test_bf16_shapes_ragged(shape, decay):
+    d, f, dv = shape
+    c = inputs.make_prefill("bf16", 2, 3, 333, d, f, dv, torch.bfloat16, None, decay, seed=d + f)
+    s_final = torch.empty((2, 3, hm.state_numel(f, dv)), device="cuda")
+    o = run_fwd(c, s_final=s_final)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c)
+    assert report(f"bf16 d={d} f={f} dv={dv} decay={decay}", f64(o), ref) <= BF16_TOL
+    Sg, zg = orc.unpack_state(f64(s_final), 2 * f, dv)
+    assert report("  state S", Sg, S) <= BF16_TOL
+    assert rel_l2(zg, z) <= BF16_TOL
+
+
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (1, 2), (2, 1), (5, 2), (16, 2)])
+def test_bf16_segment_and_split_invariance(segments, dsplit):
+    c = inputs.mild_decay(n=2000, B=1)
+    o = run_fwd(c, segments=segments, dsplit=dsplit)
+    o_ref = run_fwd(c, segments=1, dsplit=1)
+    torch.cuda.synchronize()
+    heads = [(0, 0), (0, 7), (0, 15)]
+    ref, _, _ = oracle_heads(c, heads)
+    got = f64(o)[[0, 0, 0], [0, 7, 15]]
+    assert report(f"mild n=2000 segs={segments} dsplit={dsplit}", got, ref) <= BF16_TOL
+    # different plans only reorder float32 sums
+    assert rel_l2(f64(o), f64(o_ref)) <= 5e-3
+
+
+def test_deterministic_bitwise():
+    c = inputs.mamba_decay(n=1000, B=1)
+    a = run_fwd(c, segments=3, dsplit=2)
+    b = run_fwd(c, segments=3, dsplit=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_outputs_are_convex_combinations():
+    c = inputs.make_prefill("cvx", 1, 4, 500, 128, 64, 128, torch.bfloat16, None, "mild", seed=2)
+    o = f64(run_fwd(c))
+    v = f64(c.v)
+    lo = np.minimum.accumulate(v, axis=2)
+    hi = np.maximum.accumulate(v, axis=2)
+    slack = 1e-2 * (hi - lo) + 1e-2
+    assert np.all(o >= lo - slack) and np.all(o <= hi + slack)
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=0, atol=1e-2)  # o_0 = v_0
+
+
+def test_per_head_weights_and_strided_layout():
+    B, H, n, d, f = 2, 4, 150, 64, 32
+    c = inputs.make_prefill("ph", B, H, n, d, f, 64, torch.bfloat16, None, "mild", seed=8)
+    gw = torch.Generator().manual_seed(3)
+    wq = (torch.randn((H, d, f), generator=gw) / 8).to(torch.bfloat16)
+    wk = (torch.randn((H, d, f), generator=gw) / 8).to(torch.bfloat16)
+    # q, k, v handed over as [B, n, H, d] memory (the mixer's layout), viewed as [B, H, n, d]
+    tr = lambda t: t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    o = hm.hm_linattn_fwd(tr(c.q), tr(c.k), tr(c.v), wq.cuda(), wk.cuda(), c.dt.cuda(), c.a_log.cuda())
+    torch.cuda.synchronize()
+    ref, _, _ = orc.forward(f64(c.q), f64(c.k), f64(c.v), f64(wq), f64(wk), f64(c.dt), f64(c.a_log))
+    assert report("per-head W, [B,n,H,d] layout", f64(o), ref) <= BF16_TOL
+
+
+def test_empty_sequence_copies_initial_state():
+    c = inputs.make_prefill("e", 1, 2, 0, 64, 32, 64, torch.bfloat16, None, "mamba", seed=1)
+    s_init = torch.randn((1, 2, hm.state_numel(32, 64)), device="cuda").abs()
+    s_final = torch.zeros_like(s_init)
+    o = run_fwd(c, s_init=s_init, s_final=s_final)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+    assert torch.equal(s_final, s_init)
+    s_final.zero_()
+    run_fwd(c, s_final=s_final)          # no initial state: zeros
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(s_final) == 0
+
+
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (1, 2), (3, 2)])
+def test_split_handoff_with_aliased_state(segments, dsplit):
+    """fwd[0,n) == fwd[0,m) -> state -> fwd[m,n), with s_init and s_final the same buffer."""
+    c = inputs.make_prefill("h", 1, 2, 700, 128, 64, 128, torch.bfloat16, None, "mild", seed=6)
+    m = 260
+    g = to_dev(c)
+    st = torch.empty((1, 2, hm.state_numel(64, 128)), device="cuda")
+    sl = lambda t, a, b: None if t is None else t[:, :, a:b]
+    o1 = hm.hm_linattn_fwd(sl(g["q"], 0, m), sl(g["k"], 0, m), sl(g["v"], 0, m), g["w_q"], g["w_k"],
+                           sl(g["dt"], 0, m), g["a_log"], s_final=st)
+    o2 = hm.hm_linattn_fwd(sl(g["q"], m, 700), sl(g["k"], m, 700), sl(g["v"], m, 700), g["w_q"], g["w_k"],
+                           sl(g["dt"], m, 700), g["a_log"], s_init=st, s_final=st, segments=segments, dsplit=dsplit)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c)
+    got = np.concatenate([f64(o1), f64(o2)], axis=2)
+    assert report(f"handoff aliased segs={segments} dsplit={dsplit}", got, ref) <= BF16_TOL
+    Sg, zg = orc.unpack_state(f64(st), 128, 128)
+    assert rel_l2(Sg, S) <= BF16_TOL and rel_l2(zg, z) <= BF16_TOL
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype,shape", [(torch.float32, (16, 16, 16)), (torch.float32, (32, 16, 32)),
+                                         (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64))])
+@pytest.mark.parametrize("decay", [True, False])
+def test_decode_steps(dtype, shape, decay):
+    d, f, dv = shape
+    B, H, steps = 3, 2, 40
+    dc = inputs.decode_setup(B, H, d, f, dv, prefix=50, steps=steps, decay=decay, dtype=dtype, seed=d)
+    pk = orc.hedgehog_features(f64(dc.prefix_k), f64(dc.w_k))
+    la = orc.log_decay(f64(dc.prefix_dt), f64(dc.a_log)) if decay else None
+    S, z = orc.prefix_state(pk, f64(dc.prefix_v), la)
+    state = torch.tensor(orc.pack_state(S, z), dtype=torch.float32, device="cuda")
+    wq, wk = dc.w_q.cuda(), dc.w_k.cuda()
+    a_log = dc.a_log.cuda() if decay else None
+    worst = 0.0
+    for t in range(steps):
+        q, k, v, dt = inputs.decode_step_inputs(dc, t, dtype)
+        o = hm.hm_linattn_step(q.cuda(), k.cuda(), v.cuda(), wq, wk, state, dt.cuda() if decay else None, a_log)
+        torch.cuda.synchronize()
+        ot, S, z = orc.step(S, z, f64(q), f64(k), f64(v), f64(dc.w_q), f64(dc.w_k),
+                            f64(dt) if decay else None, f64(dc.a_log) if decay else None)
+        worst = max(worst, rel_l2(f64(o), ot))
+    Sg, zg = orc.unpack_state(f64(state), 2 * f, dv)
+    print(f"[parity] decode {dtype} {shape} decay={decay}: worst step rel-L2 {worst:.3e}, "
+          f"state rel-L2 {rel_l2(Sg, S):.3e}", flush=True)
+    assert worst <= tol_for(dtype)
+    assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)
+
+
+def test_prefill_then_decode_handoff():
+    c = inputs.make_prefill("pd", 2, 2, 300, 128, 64, 128, torch.bfloat16, None, "mamba", seed=12)
+    st = torch.empty((2, 2, hm.state_numel(64, 128)), device="cuda")
+    run_fwd(c, s_final=st)
+    _, S, z = full_oracle(c)
+    g = torch.Generator().manual_seed(2)
+    for t in range(5):
+        q, k, v = (torch.randn((2, 2, 128), generator=g).to(torch.bfloat16) for _ in range(3))
+        dt = torch.randn((2, 2), generator=g)
+        o = hm.hm_linattn_step(q.cuda(), k.cuda(), v.cuda(), c.w_q.cuda(), c.w_k.cuda(), st, dt.cuda(), c.a_log.cuda())
+        torch.cuda.synchronize()
+        ot, S, z = orc.step(S, z, f64(q), f64(k), f64(v), f64(c.w_q), f64(c.w_k), f64(dt), f64(c.a_log))
+        assert report(f"prefill->decode step {t}", f64(o), ot) <= BF16_TOL
