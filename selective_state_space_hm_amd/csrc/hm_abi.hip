@@ -136,25 +136,24 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
   const int64_t BLK = F * a->dv + F;
   const int C = hm::CHUNK;
   p.chunk = C;
-  // dsplit: split the value columns over two workgroups when (b, h) pairs alone
-  // cannot fill the 256 compute units
+  // dsplit: one workgroup owns all value columns of a (b, h) whenever that
+  // kernel is built (splitting duplicates the featurization and measured slower)
   if (a->dsplit) {
     p.dsplit = a->dsplit;
   } else {
-    const bool can2 = a->dv % 2 == 0 && find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL);
     const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) != nullptr;
-    p.dsplit = (!can1 || (can2 && BH < 256)) ? 2 : 1;
+    p.dsplit = can1 ? 1 : 2;
   }
   const int64_t nchunks = (a->n + C - 1) / C;
   int64_t segs;
   if (a->segments) {
     segs = a->segments;
   } else {
-    // enough (b, h, segment, half) workgroups for two waves of the chip, with
-    // segments of at least 16 chunks so the extra k, v pass stays small
+    // one workgroup per compute unit (256 on MI355X): split each sequence into
+    // enough segments, each at least 4 chunks long
     const int64_t wg = BH * p.dsplit;
-    segs = wg >= 512 || wg == 0 ? 1 : (512 + wg - 1) / wg;
-    const int64_t cap = nchunks / 16 > 1 ? nchunks / 16 : 1;
+    segs = wg >= 256 || wg == 0 ? 1 : (256 + wg - 1) / wg;
+    const int64_t cap = nchunks / 4 > 1 ? nchunks / 4 : 1;
     if (segs > cap) segs = cap;
   }
   if (segs > nchunks) segs = nchunks > 0 ? nchunks : 1;

@@ -58,20 +58,23 @@ struct FwdParams {
 
 template <typename F> __device__ __forceinline__ F zfrag() { return F{}; }
 
-// Waves per workgroup for a value-column slice of width DW: each wave owns two
-// 16-column value tiles (one when DW == 16).
-constexpr int fwd_ntw(int DW) { return DW >= 32 ? 2 : 1; }
-constexpr int fwd_waves(int DW) { return DW / (16 * fwd_ntw(DW)); }
+// One wave per 16-column value tile.
+constexpr int fwd_waves(int DW) { return DW / 16; }
+
+// Element pointer `base` (wave-uniform) plus a per-lane 32-bit byte offset: lets
+// the compiler address global memory as scalar base + vector offset.
+template <typename T>
+__device__ __forceinline__ const T *at(const T *base, uint32_t byte_off) {
+  return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
 
 template <typename T, int DK, int FH, int DW, bool DECAY, int MODE>
-__global__ __launch_bounds__(fwd_waves(DW) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int C = CHUNK;
   constexpr int F = 2 * FH;
-  constexpr int NTW = fwd_ntw(DW);    // value tiles per wave
-  constexpr int NW = fwd_waves(DW);   // waves
+  constexpr int NW = fwd_waves(DW);   // waves; wave w owns value tile w
   constexpr int NT = NW * 64;
   constexpr int NCT = C / 16;         // token tiles per chunk
   constexpr int NFH = FH / 16;        // feature tiles per half of phi
@@ -79,23 +82,25 @@ void fwd_kernel(const FwdParams p) {
   constexpr int KD = DK / M::KS;      // featurize K-steps (contiguous order)
   constexpr int KF = M::steps(NFT);   // K-steps over F (tile order)
   constexpr int KC = M::steps(NCT);   // K-steps over the chunk (tile order)
+  constexpr int EPL = M::EPL;         // operand elements per lane
   constexpr int PAD = M::PAD;
   constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD;
   constexpr bool FULL = MODE == MODE_FULL;
   constexpr int NTASK = FULL ? 2 * NCT : NCT;  // featurize tasks: (q|k, token tile)
   constexpr int TPW = (NTASK + NW - 1) / NW;   // consecutive tasks per wave
-  constexpr int KVL = M::EPL == 8 ? 1 : 4;     // K-steps of the v re-layout per tile
+  constexpr int KVL = EPL == 8 ? 1 : 4;        // K-steps of the v re-layout per tile
   constexpr int TPF = NT >= F ? NT / F : 1;    // threads per feature row in the z update
-  static_assert(DW % 16 == 0 && NW >= 1 && NW <= 4, "value tile split");
+  constexpr float L2E = 1.4426950408889634f;
+  static_assert(DW % 16 == 0 && NW >= 1 && NW <= 8, "value tile split");
   static_assert(DK % M::KS == 0 && F % M::KS == 0, "K multiples");
   static_assert(C % TPF == 0, "z update mapping");
 
   __shared__ __align__(16) T sWq[FULL ? FH * LDW : 8];  // W^T: sW[f][d] = W[d][f]
   __shared__ __align__(16) T sWk[FH * LDW];
   __shared__ __align__(16) T sKt[F * LDC];                // decay-weighted phi(k)^T, tile order
-  __shared__ __align__(16) T sQ[FULL ? C * LDQ : 8];      // phi(q), tile order
+  __shared__ __align__(16) T sQ[FULL ? C * LDQ : 8];      // phi(q) (unnormalized), tile order
   __shared__ __align__(16) T sP[FULL ? C * LDC : 8];      // masked decayed scores, tile order
-  __shared__ __align__(16) double sL[2][C];   // inclusive log-decay prefix, float64
+  __shared__ __align__(16) double sL[2][C];               // inclusive log-decay prefix, float64
   __shared__ __align__(16) float seL[2][C];
   __shared__ __align__(16) float seK[2][C];
   __shared__ float sLast[2];
@@ -120,7 +125,7 @@ void fwd_kernel(const FwdParams p) {
   const int64_t b = bh / p.H, h = bh % p.H;
   const int64_t t0 = (int64_t)seg * p.seg_len;
   const int64_t t1 = t0 + p.seg_len < p.n ? t0 + p.seg_len : p.n;
-  const int ncol0 = half * DW + 16 * NTW * wv;  // first value column of this wave
+  const int ncol = half * DW + 16 * wv;  // first value column of this wave
   const int64_t BLK = (int64_t)F * p.dv + F;
 
   const T *Q = (const T *)p.q + b * p.sq_b + h * p.sq_h;
@@ -144,12 +149,9 @@ void fwd_kernel(const FwdParams p) {
       for (int i = tid; i < DK * FH; i += NT) sWq[(i % FH) * LDW + i / FH] = wq[i];
     }
   }
-  // the projections this wave featurizes: its first task's, and the other one
-  // when its tasks span both (only with a single wave)
-  constexpr int NWP = (FULL && NW == 1) ? 2 : 1;
 
   // Start state.
-  f32x4 S[NTW][NFT];
+  f32x4 S[NFT];
   {
     const float *st = nullptr;
     if constexpr (FULL) {
@@ -157,41 +159,46 @@ void fwd_kernel(const FwdParams p) {
       else st = p.ws_state + ((int64_t)(seg - 1) * BH + bh) * BLK;
     }
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int t = 0; t < NFT; ++t)
 #pragma unroll
-      for (int t = 0; t < NFT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          S[j][t][r] = st ? st[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol0 + 16 * j + col] : 0.f;
+      for (int r = 0; r < 4; ++r)
+        S[t][r] = st ? st[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + col] : 0.f;
     for (int i = tid; i < F; i += NT) sZ[i] = st ? st[(int64_t)F * p.dv + i] : 0.f;
   }
 
+  // Per-lane byte offsets of the global rows this lane reads (32-bit; the chunk
+  // and tile bases are wave-uniform).
+  uint32_t xoff[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+    xoff[i] = (uint32_t)(((int64_t)(16 * task_tile(i) + col) * (task_isq(i) ? p.sq_t : p.sk_t) + EPL * g) * sizeof(T));
+  const uint32_t voff = (uint32_t)(((int64_t)col * p.sv_t + ncol + (EPL == 8 ? 8 * g : g)) * sizeof(T));
+  const int64_t vtile = 16 * p.sv_t;  // elements between token tiles of v
+
   // Prefetch registers for one chunk.
   frag xf[TPW][KD];
-  frag vf[NTW][NCT][KVL];
+  frag vf[NCT][KVL];
   float dtn = 0.f;
   auto load_chunk = [&](int64_t tc) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       if (!task_ok(i)) continue;
       const bool isq = task_isq(i);
-      const int64_t c = tc + 16 * task_tile(i) + col;
-      const T *xr = (isq ? Q : K) + c * (isq ? p.sq_t : p.sk_t);
+      const T *base = (isq ? Q : K) + tc * (isq ? p.sq_t : p.sk_t);
+      const bool ok = tc + 16 * task_tile(i) + col < t1;
 #pragma unroll
-      for (int s = 0; s < KD; ++s) xf[i][s] = c < t1 ? M::ld_contig(xr + s * M::KS, g) : zfrag<frag>();
+      for (int s = 0; s < KD; ++s)
+        xf[i][s] = ok ? M::ld_contig(at(base, xoff[i]) + s * M::KS, 0) : zfrag<frag>();
     }
 #pragma unroll
     for (int bt = 0; bt < NCT; ++bt) {
-      const int64_t c = tc + 16 * bt + col;
-      const T *vr = V + c * p.sv_t + ncol0;
+      const T *base = V + (tc * p.sv_t + bt * vtile);
+      const bool ok = tc + 16 * bt + col < t1;
+      if constexpr (EPL == 8) {
+        vf[bt][0] = (ok && g < 2) ? M::ld_contig(at(base, voff), 0) : zfrag<frag>();
+      } else {
 #pragma unroll
-      for (int j = 0; j < NTW; ++j) {
-        if constexpr (M::EPL == 8) {
-          vf[j][bt][0] = (c < t1 && g < 2) ? M::ld_contig(vr + 16 * j, g) : zfrag<frag>();
-        } else {
-#pragma unroll
-          for (int s = 0; s < KVL; ++s) vf[j][bt][s] = c < t1 ? vr[16 * j + 4 * s + g] : 0.f;
-        }
+        for (int s = 0; s < KVL; ++s) vf[bt][s] = ok ? at(base, voff)[4 * s] : 0.f;
       }
     }
     if constexpr (DECAY) {
@@ -214,25 +221,29 @@ void fwd_kernel(const FwdParams p) {
       if (lane == 0) sLast[bufi] = __expf((float)Ll);
       lam += Ll;
     } else {
-      sL[bufi][lane] = 0.0;
-      seL[bufi][lane] = 1.f;
-      seK[bufi][lane] = valid ? 1.f : 0.f;
       if (lane == 0) sLast[bufi] = 1.f;
     }
   };
+
+  // Loop-invariant selector operands of the re-layout products.
+  frag vsel[KVL];
+#pragma unroll
+  for (int s = 0; s < KVL; ++s) {
+    if constexpr (EPL == 8) vsel[s] = M::select([&](int e) { return 8 * g + e == col; });
+    else vsel[s] = M::select([&](int) { return 4 * s + g == col; });
+  }
+  constexpr int NKS = EPL == 8 ? 2 : 4;
+  frag ksel[NKS];
+#pragma unroll
+  for (int x = 0; x < NKS; ++x) {
+    if constexpr (EPL == 8) ksel[x] = M::select([&](int e) { return 16 * (e >> 2) + 4 * g + (e & 3) == 16 * x + col; });
+    else ksel[x] = M::select([&](int) { return 4 * g + x == col; });
+  }
 
   const int64_t nch = t1 > t0 ? (t1 - t0 + C - 1) / C : 0;
   if (nch > 0) {
     load_chunk(t0);
     if (wv == 0) decay(t0, 0);
-  }
-
-  // Selectors that move a contiguous-order v row slice into accumulator layout.
-  frag vsel[KVL];
-#pragma unroll
-  for (int s = 0; s < KVL; ++s) {
-    if constexpr (M::EPL == 8) vsel[s] = M::select([&](int e) { return 8 * g + e == col; });
-    else vsel[s] = M::select([&](int) { return 4 * s + g == col; });
   }
 
   for (int64_t ci = 0; ci < nch; ++ci) {
@@ -241,44 +252,36 @@ void fwd_kernel(const FwdParams p) {
     __syncthreads();  // decay[buf] visible; previous chunk's LDS readers done
 
     // v tile rows -> accumulator layout: lane (g, col n) holds v[16bt + 4g + r][n]
-    frag vfr[NTW][KC];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
+    frag vfr[KC];
+    {
       f32x4 vacc[NCT];
 #pragma unroll
       for (int bt = 0; bt < NCT; ++bt) {
         vacc[bt] = zero4();
 #pragma unroll
-        for (int s = 0; s < KVL; ++s) vacc[bt] = M::mma(vf[j][bt][s], vsel[s], vacc[bt]);
+        for (int s = 0; s < KVL; ++s) vacc[bt] = M::mma(vf[bt][s], vsel[s], vacc[bt]);
       }
 #pragma unroll
-      for (int s = 0; s < KC; ++s) vfr[j][s] = M::from_acc(vacc, s);
+      for (int s = 0; s < KC; ++s) vfr[s] = M::from_acc(vacc, s);
     }
 
     // ---- phase A: featurize (q tasks -> sQ, den_inter; k tasks -> kf, sKt)
     f32x4 u[TPW][NFH];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-      for (int t = 0; t < NFH; ++t) u[i][t] = zero4();
-#pragma unroll
-    for (int pi = 0; pi < NWP; ++pi) {
-      const bool useq = NWP == 2 ? pi == 0 : task_isq(0);
-      const T *sW = useq ? sWq : sWk;
+    for (int i = 0; i < TPW; ++i) {
+      if (!task_ok(i)) continue;
+      const T *sW = task_isq(i) ? sWq : sWk;
 #pragma unroll
       for (int t = 0; t < NFH; ++t) {
-        frag wa[KD];  // W^T fragments of feature tile t, shared by the wave's tasks
+        frag wa[KD];
 #pragma unroll
         for (int s = 0; s < KD; ++s) wa[s] = M::ld_contig(sW + (16 * t + col) * LDW + s * M::KS, g);
+        u[i][t] = zero4();
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          if (!task_ok(i) || task_isq(i) != useq) continue;
-#pragma unroll
-          for (int s = 0; s < KD; ++s) u[i][t] = M::mma(wa[s], xf[i][s], u[i][t]);
-        }
+        for (int s = 0; s < KD; ++s) u[i][t] = M::mma(wa[s], xf[i][s], u[i][t]);
       }
     }
-    if (ci + 1 < nch) load_chunk(tc + C);  // X, V, dt of the next chunk (registers now free)
+    if (ci + 1 < nch) load_chunk(tc + C);  // next chunk's q, k, v, dt (registers now free)
 
     frag kf[TPW][KF];
 #pragma unroll
@@ -291,51 +294,57 @@ void fwd_kernel(const FwdParams p) {
       for (int t = 0; t < NFH; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[i][t][r]));
-      m = group_max(m);
+      const float ml = group_max(m) * L2E;
       f32x4 ph[NFT];
       float sum = 0.f;
 #pragma unroll
       for (int t = 0; t < NFH; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float ep = __expf(u[i][t][r] - m), em = __expf(-u[i][t][r] - m);
+          const float x = u[i][t][r];
+          const float ep = __builtin_amdgcn_exp2f(__builtin_fmaf(x, L2E, -ml));
+          const float em = __builtin_amdgcn_exp2f(__builtin_fmaf(-x, L2E, -ml));
           ph[t][r] = ep;
           ph[NFH + t][r] = em;
           sum += ep + em;
         }
-      sum = group_sum(sum);
-      const float inv = 1.f / sum;
-#pragma unroll
-      for (int t = 0; t < NFT; ++t) ph[t] = round4(ph[t] * inv, T{});
-
       if (task_isq(i)) {
+        // phi(q) is used unnormalized: a positive per-query factor multiplies both
+        // o's numerator and denominator and cancels exactly.
         const int cr = 16 * bt + col;
         float dz = 0.f;
 #pragma unroll
         for (int t = 0; t < NFT; ++t) {
+          ph[t] = round4(ph[t], T{});
           store4(&sQ[cr * LDQ + M::tpos(16 * t + 4 * g)], ph[t]);
           const f32x4 z4 = *reinterpret_cast<const f32x4 *>(&sZ[16 * t + 4 * g]);
           dz += ph[t][0] * z4[0] + ph[t][1] * z4[1] + ph[t][2] * z4[2] + ph[t][3] * z4[3];
         }
         dz = group_sum(dz);
-        if (g == 0) sDenInter[cr] = dz * seL[buf][cr];
+        if (g == 0) sDenInter[cr] = DECAY ? dz * seL[buf][cr] : dz;
       } else {
+        float inv = 1.f / group_sum(sum);
+        if constexpr (!DECAY) {
+          if (tc + 16 * bt + col >= t1) inv = 0.f;  // rows past the end contribute nothing
+        }
+#pragma unroll
+        for (int t = 0; t < NFT; ++t) ph[t] *= inv;
 #pragma unroll
         for (int s = 0; s < KF; ++s) kf[i][s] = M::from_acc(ph, s);
-        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&seK[buf][16 * bt + 4 * g]);
-        // phiK^T tile uo, decay-weighted: lane (g, col f') gets phiK[16bt+4g+r][16uo+f']
+        f32x4 w4;
+        if constexpr (DECAY) w4 = *reinterpret_cast<const f32x4 *>(&seK[buf][16 * bt + 4 * g]);
+        // phiK^T tile uo (decay-weighted): lane (g, col f') gets phiK[16bt+4g+r][16uo+f']
 #pragma unroll
         for (int uo = 0; uo < NFT; ++uo) {
           f32x4 acc = zero4();
-          if constexpr (M::EPL == 8) {
-            const frag sel = M::select([&](int e) { return 16 * (e >> 2) + 4 * g + (e & 3) == 16 * (uo & 1) + col; });
-            acc = M::mma(kf[i][uo >> 1], sel, acc);
+          if constexpr (EPL == 8) {
+            acc = M::mma(kf[i][uo >> 1], ksel[uo & 1], acc);
           } else {
 #pragma unroll
-            for (int s = 4 * uo; s < 4 * uo + 4; ++s)
-              acc = M::mma(kf[i][s], M::select([&](int) { return 4 * g + (s & 3) == col; }), acc);
+            for (int s = 4 * uo; s < 4 * uo + 4; ++s) acc = M::mma(kf[i][s], ksel[s & 3], acc);
           }
-          store4(&sKt[(16 * uo + col) * LDC + M::tpos(16 * bt + 4 * g)], acc * w4);
+          if constexpr (DECAY) acc *= w4;
+          store4(&sKt[(16 * uo + col) * LDC + M::tpos(16 * bt + 4 * g)], acc);
         }
       }
     }
@@ -343,33 +352,20 @@ void fwd_kernel(const FwdParams p) {
 
     // ---- phase B: score tiles (k-task owners), z update, inter read-out, state update
     if constexpr (FULL) {
-      // rows a of this wave's k tasks; the phiQ fragments of column tile bt are
-      // loaded once for all of them
-      int amin = NCT;
 #pragma unroll
-      for (int i = 0; i < TPW; ++i)
-        if (task_ok(i) && !task_isq(i) && task_tile(i) < amin) amin = task_tile(i);
+      for (int i = 0; i < TPW; ++i) {
+        if (!task_ok(i) || task_isq(i)) continue;
+        const int a = task_tile(i);  // rows c' of this wave's tiles
 #pragma unroll
-      for (int bt = 0; bt < NCT; ++bt) {
-        const int cc = 16 * bt + col;
-        if (bt < amin) {
-#pragma unroll
-          for (int i = 0; i < TPW; ++i)
-            if (task_ok(i) && !task_isq(i))
-              store4(&sP[cc * LDC + M::tpos(16 * task_tile(i) + 4 * g)], zero4());
-          continue;
-        }
-        frag bq[KF];
-#pragma unroll
-        for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[cc * LDQ], s, g);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          if (!task_ok(i) || task_isq(i)) continue;
-          const int a = task_tile(i);
+        for (int bt = 0; bt < NCT; ++bt) {
+          const int cc = 16 * bt + col;
           if (bt < a) {
             store4(&sP[cc * LDC + M::tpos(16 * a + 4 * g)], zero4());
             continue;
           }
+          frag bq[KF];
+#pragma unroll
+          for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[cc * LDQ], s, g);
           f32x4 acc = zero4();
 #pragma unroll
           for (int s = 0; s < KF; ++s) acc = M::mma(kf[i][s], bq[s], acc);
@@ -379,10 +375,9 @@ void fwd_kernel(const FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int cp = 16 * a + 4 * g + r;
-            float x = 0.f;
-            if (cp <= cc) {
-              x = acc[r];
-              if constexpr (DECAY) x *= __expf((float)(lc - sL[buf][cp]));
+            float x = cp <= cc ? acc[r] : 0.f;
+            if constexpr (DECAY) {
+              if (cp <= cc) x *= __expf((float)(lc - sL[buf][cp]));
             }
             w[r] = x;
           }
@@ -403,74 +398,63 @@ void fwd_kernel(const FwdParams p) {
         for (int c = 0; c < C / TPF; ++c) zs += (float)row[c];
 #pragma unroll
         for (int off = 1; off < TPF; off <<= 1) zs += __shfl_xor(zs, off);
-        if (part == 0) sZ[f] = el * sZ[f] + zs;
+        if (part == 0) sZ[f] = DECAY ? el * sZ[f] + zs : sZ[f] + zs;
       }
     }
-    f32x4 oacc[NTW][NCT];
+    f32x4 oacc[NCT];
     if constexpr (FULL) {
-      frag sfr[NTW][KF];
+      frag sfr[KF];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
+      for (int s = 0; s < KF; ++s) sfr[s] = M::from_acc(S, s);
+      frag bq[NCT][KF];
 #pragma unroll
-        for (int s = 0; s < KF; ++s) sfr[j][s] = M::from_acc(S[j], s);
+      for (int bt = 0; bt < NCT; ++bt)
+#pragma unroll
+        for (int s = 0; s < KF; ++s) bq[bt][s] = M::ld_tile(&sQ[(16 * bt + col) * LDQ], s, g);
 #pragma unroll
       for (int bt = 0; bt < NCT; ++bt) {
-        const int cc = 16 * bt + col;
-        frag bq[KF];
+        oacc[bt] = zero4();
 #pragma unroll
-        for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[cc * LDQ], s, g);
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) {
-          oacc[j][bt] = zero4();
-#pragma unroll
-          for (int s = 0; s < KF; ++s) oacc[j][bt] = M::mma(sfr[j][s], bq[s], oacc[j][bt]);
-        }
-        if constexpr (DECAY) {
-          const float el = seL[buf][cc];
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) oacc[j][bt] *= el;
-        }
+        for (int s = 0; s < KF; ++s) oacc[bt] = M::mma(sfr[s], bq[bt][s], oacc[bt]);
+        if constexpr (DECAY) oacc[bt] *= seL[buf][16 * bt + col];
       }
     }
     if constexpr (DECAY) {
       const float el = sLast[buf];
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
-#pragma unroll
-        for (int t = 0; t < NFT; ++t) S[j][t] *= el;
+      for (int t = 0; t < NFT; ++t) S[t] *= el;
     }
+    {
+      frag ak[NFT][KC];
 #pragma unroll
-    for (int t = 0; t < NFT; ++t) {
-      frag ak[KC];
+      for (int t = 0; t < NFT; ++t)
 #pragma unroll
-      for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[(16 * t + col) * LDC], s, g);
+        for (int s = 0; s < KC; ++s) ak[t][s] = M::ld_tile(&sKt[(16 * t + col) * LDC], s, g);
 #pragma unroll
-      for (int j = 0; j < NTW; ++j)
+      for (int t = 0; t < NFT; ++t)
 #pragma unroll
-        for (int s = 0; s < KC; ++s) S[j][t] = M::mma(ak[s], vfr[j][s], S[j][t]);
+        for (int s = 0; s < KC; ++s) S[t] = M::mma(ak[t][s], vfr[s], S[t]);
     }
     __syncthreads();
 
     // ---- phase C: intra-chunk read-out, normalize, store; next chunk's decay
     if constexpr (FULL) {
+      frag bp[NCT][M::steps_upto(NCT - 1)];
+#pragma unroll
+      for (int bt = 0; bt < NCT; ++bt)
+#pragma unroll
+        for (int s = 0; s < M::steps_upto(bt); ++s) bp[bt][s] = M::ld_tile(&sP[(16 * bt + col) * LDC], s, g);
 #pragma unroll
       for (int bt = 0; bt < NCT; ++bt) {
         const int cc = 16 * bt + col;
-        frag bp[M::steps_upto(NCT - 1)];
 #pragma unroll
-        for (int s = 0; s < M::steps_upto(bt); ++s) bp[s] = M::ld_tile(&sP[cc * LDC], s, g);
-#pragma unroll
-        for (int j = 0; j < NTW; ++j)
-#pragma unroll
-          for (int s = 0; s < M::steps_upto(bt); ++s) oacc[j][bt] = M::mma(vfr[j][s], bp[s], oacc[j][bt]);
+        for (int s = 0; s < M::steps_upto(bt); ++s) oacc[bt] = M::mma(vfr[s], bp[bt][s], oacc[bt]);
         const int64_t c = tc + cc;
         if (c < t1) {
           float den = sDenInter[cc];
 #pragma unroll
           for (int a = 0; a <= bt; ++a) den += sDenPart[a][cc];
-          const float inv = 1.f / den;
-#pragma unroll
-          for (int j = 0; j < NTW; ++j) store4(O + c * p.so_t + ncol0 + 16 * j + 4 * g, oacc[j][bt] * inv);
+          store4(O + c * p.so_t + ncol + 4 * g, oacc[bt] * (1.f / den));
         }
       }
     }
@@ -488,11 +472,9 @@ void fwd_kernel(const FwdParams p) {
   }
   if (dst) {
 #pragma unroll
-    for (int j = 0; j < NTW; ++j)
+    for (int t = 0; t < NFT; ++t)
 #pragma unroll
-      for (int t = 0; t < NFT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol0 + 16 * j + col] = S[j][t][r];
+      for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + col] = S[t][r];
     if (half == 0)
       for (int i = tid; i < F; i += NT) dst[(int64_t)F * p.dv + i] = sZ[i];
   }
