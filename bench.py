@@ -63,26 +63,24 @@ def prefill_flops_algorithmic(B, H, n, d, f, dv):
 
 
 def prefill_mfma_count(plan, B, H, n, d, f, dv):
-    """MFMA instructions the prefill kernels issue (16x16x32 bf16), from the loop
-    structure of the chunk kernel: per (b, h) chunk of 64 tokens and workgroup."""
+    """MFMA instructions (16x16x32 bf16) the prefill kernels issue, from the loop
+    structure of the chunk kernel, per 64-token chunk and workgroup:
+      feature waves: featurize q and k, phi(k)^T re-layout, score tiles (causal
+      half), den_inter and the z update (ones-column products);
+      state waves: v re-layout, inter read-out, state update, intra read-out."""
     chunk, segments, dsplit = plan
     C = chunk
     NCT, NFH, NFT = C // 16, f // 16, 2 * f // 16
     KD, KF, KC = d // 32, NFT // 2, NCT // 2
-    NW = dv // dsplit // 16
+    vt = dv // dsplit // 16                        # value tiles per workgroup
     intra_steps = sum(bt // 2 + 1 for bt in range(NCT))
-    full = (2 * NCT * NFH * KD            # featurize q and k
-            + NCT * NFT                   # phi(k) re-layout
-            + NW * NCT                    # v re-layout
-            + sum(NCT - a for a in range(NCT)) * KF   # score tiles
-            + NW * NCT * KF               # inter read-out
-            + NW * intra_steps            # intra read-out
-            + NW * NFT * KC)              # state update
-    local = NCT * NFH * KD + NCT * NFT + NW * NCT + NW * NFT * KC
+    full = (2 * NCT * NFH * KD + NCT * NFT + sum(NCT - a for a in range(NCT)) * KF + NCT * KF + NFT * KC
+            + vt * NCT + vt * NCT * KF + vt * NFT * KC + vt * intra_steps)
+    local = NCT * NFH * KD + NCT * NFT + NFT * KC + vt * NCT + vt * NFT * KC
     chunks = (n + C - 1) // C
-    seg_len = -(-chunks // segments) * C
-    local_chunks = min(n, seg_len * (segments - 1))
-    local_chunks = (local_chunks + C - 1) // C
+    per = -(-chunks // segments)
+    nseg = -(-chunks // per)
+    local_chunks = per * (nseg - 1)
     return B * H * dsplit * (full * chunks + local * local_chunks)
 
 
@@ -130,9 +128,9 @@ def cpu_baseline(case, budget_s=12.0):
                       f"host has {len(os.sched_getaffinity(0))} cores"}
 
 
-def hbm_traffic(launch_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
-    on the current kernel sources; otherwise None."""
+def hbm_traffic(key):
+    """HBM bytes per launch from committed rocprofv3 counter runs (profiles/), if
+    they were taken on the current kernel sources; otherwise None."""
     try:
         with open(PROFILE_COUNTERS) as fh:
             rec = json.load(fh)
@@ -140,7 +138,7 @@ def hbm_traffic(launch_bytes):
         return None
     if rec.get("kernel_hash") != kernel_hash():
         return None
-    return rec.get("prefill_bytes_per_launch")
+    return rec.get(key)
 
 
 def main():
@@ -150,6 +148,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the decay workloads")
+    ap.add_argument("--part", choices=["all", "decode", "copy"], default="all",
+                    help="decode: only the decode benchmark; copy: one 256 MiB device copy, the "
+                         "reference run that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--dsplit", type=int, default=0)
     args = ap.parse_args()
@@ -164,6 +165,18 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.part == "copy":
+        a = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copied 3 x 256 MiB")
+        return
+    if args.part == "decode":
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+        print(json.dumps({"decode": bench_decode(torch, hm, inputs, dev, ws)}), flush=True)
+        return
     log("[bench] generating the B=8 H=16 n=2048 layer")
     case = inputs.pythia1b()
     g = {k: getattr(case, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k")}
@@ -184,7 +197,7 @@ def main():
     achieved = nbytes / (ms * 1e-3) / 1e9
     mfma = prefill_mfma_count(plan, B, H, n, d, f, dv) * MFMA_FLOP
     algo = prefill_flops_algorithmic(B, H, n, d, f, dv)
-    traffic = hbm_traffic(nbytes)
+    traffic = hbm_traffic("prefill_bytes_per_launch")
     result = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -203,7 +216,8 @@ def main():
                    "plan": {"chunk": plan[0], "segments": plan[1], "dsplit": plan[2]}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "hm::fwd_kernel<bf16,128,64,DW,false,0>" + (" (+segment pass)" if plan[1] > 1 else ""),
+                     "kernel": "hm_linattn_fwd: fwd_kernel<bf16,128,64,128,false,FULL>"
+                               + (" + segment pass + combine_kernel" if plan[1] > 1 else ""),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"executed_tflops": mfma / (ms * 1e-3) / 1e12,
                  "executed_frac": mfma / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
@@ -284,7 +298,7 @@ def bench_decode(torch, hm, inputs, dev, ws):
                         f"{dc.prefix}-token prefix, {dc.steps} steps, Mamba decay",
             "tokens_per_s": dc.B / (ms * 1e-3), "ms_per_step": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": hbm_traffic("decode_bytes_per_launch"),
                          "kernel": "hm::step_kernel<bf16,128,64,128,true>", "algorithmic_bytes_per_launch": nbytes}}
 
 
