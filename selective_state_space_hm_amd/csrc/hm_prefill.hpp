@@ -88,7 +88,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   constexpr int KC = M::steps(NCT);        // K-steps over the chunk (tile order)
   constexpr int EPL = M::EPL;              // operand elements per lane
   constexpr int PAD = M::PAD;
-  constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD;
+  constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD, LDO = DW + 32 / (int)sizeof(T);
   constexpr bool FULL = MODE == MODE_FULL;
   constexpr int TPF_ = FULL ? 2 : 1;       // featurize tasks per feature wave
   constexpr int KVL = EPL == 8 ? 1 : 4;    // K-steps of the v re-layout per tile
@@ -100,16 +100,20 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   __shared__ __align__(16) T sWq[FULL ? FH * LDW : 8];    // W^T: sW[f][d] = W[d][f]
   __shared__ __align__(16) T sWk[FH * LDW];
   __shared__ __align__(16) T sKt[2][F * LDC];               // decay-weighted phi(k)^T, tile order
-  __shared__ __align__(16) T sQ[FULL ? 2 : 1][FULL ? C * LDQ : 8];  // phi(q) (unnormalized)
-  __shared__ __align__(16) T sP[FULL ? 2 : 1][FULL ? C * LDC : 8];  // masked decayed scores
+  __shared__ __align__(16) T sQ[FULL ? 2 : 1][FULL ? C * LDQ : 8];  // phi(q) (unnormalized), tile order
+  __shared__ __align__(16) T sK0[FULL ? 16 * LDQ : 8];              // phi(k) of token tile 0, tile order
+  __shared__ __align__(16) T sP[FULL ? C * LDC : 8];                 // masked decayed scores
+  __shared__ __align__(16) T sO[FULL ? C * LDO : 8];                 // normalized output rows
   __shared__ __align__(16) double sL[3][C];                 // inclusive log-decay prefix, float64
   __shared__ __align__(16) float seL[3][C];
   __shared__ __align__(16) float seK[3][C];
   __shared__ float sLast[3];
-  __shared__ __align__(16) float sDenPart[2][NCT][C];
+  __shared__ __align__(16) float sDenPart[NCT][C];
   __shared__ __align__(16) float sDenInter[2][C];
+  __shared__ __align__(16) float sZ[2][F];                  // z after each chunk (by chunk parity)
 
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets the compiler keep it scalar
   const bool fwave = wv < 4;
   const int sw = wv - 4;  // state wave index
 
@@ -138,13 +142,35 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   const float *DT = DECAY ? p.dt + b * p.sdt_b + h * p.sdt_h : nullptr;
   const float expA = DECAY ? expf(p.a_log[h]) : 1.f;
 
-  // W^T into LDS: sW[f][d] = W[d][f]
+  // W^T into LDS: sW[f][d] = W[d][f].  W is read as 16-byte vectors, all of them
+  // issued before the first LDS write.
   {
+    constexpr int EP = 16 / (int)sizeof(T);
+    constexpr int NV = DK * FH / EP;                 // vectors per matrix
+    constexpr int VPT = (NV + NT - 1) / NT;          // vectors per thread
+    typedef T tvec __attribute__((ext_vector_type(16 / sizeof(T))));
     const T *wk = (const T *)p.wk + h * p.sw_h;
-    for (int i = tid; i < DK * FH; i += NT) sWk[(i % FH) * LDW + i / FH] = wk[i];
-    if constexpr (FULL) {
-      const T *wq = (const T *)p.wq + h * p.sw_h;
-      for (int i = tid; i < DK * FH; i += NT) sWq[(i % FH) * LDW + i / FH] = wq[i];
+    const T *wq = (const T *)p.wq + h * p.sw_h;
+    tvec vk[VPT], vq[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = tid + i * NT;
+      if (v < NV) {
+        vk[i] = *reinterpret_cast<const tvec *>(wk + v * EP);
+        if constexpr (FULL) vq[i] = *reinterpret_cast<const tvec *>(wq + v * EP);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = tid + i * NT;
+      if (v < NV) {
+        const int d = v * EP / FH, f0 = v * EP % FH;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) {
+          sWk[(f0 + e) * LDW + d] = vk[i][e];
+          if constexpr (FULL) sWq[(f0 + e) * LDW + d] = vq[i][e];
+        }
+      }
     }
   }
 
@@ -161,44 +187,52 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     dst = p.ws_state + ((int64_t)seg * BH + bh) * BLK;
   }
 
-  // The two roles run separate loops with the same two barriers per iteration:
-  // iteration j, half A: feature waves featurize chunk j while state waves read
-  // out and advance the state over chunk j-1; half B: feature waves form chunk
-  // j's score tiles and denominators while state waves finish chunk j-1.
+  // The two roles run separate loops with the same two barriers per iteration j:
+  //   half A: feature waves featurize chunk j (phiQ, phiK, phiK^T, den_inter);
+  //           state waves read out chunk j-1 (inter and intra parts), normalize, store;
+  //   half B: feature waves form chunk j's score tiles and advance z;
+  //           state waves advance S over chunk j-1.
+  // Wave w of each role runs on SIMD w % 4, so every SIMD pairs the softmax VALU
+  // work of one feature wave with the MFMA work of one state wave.
   if (fwave) {
     // ---------------------------------------------------------------- feature waves
-    // Feature-wave tasks.  FULL: waves 0, 1 featurize q tiles {0,1}, {2,3}; waves
-    // 2, 3 featurize k tiles {0,3}, {1,2} (their score-tile rows balance: 4+1, 3+2).
-    // LOCAL: wave w featurizes k tile w.
-    const bool isq = FULL && wv < 2;
-    int tile[TPF_];
-#pragma unroll
-    for (int i = 0; i < TPF_; ++i) {
-      if constexpr (!FULL) tile[i] = wv;
-      else tile[i] = wv < 2 ? 2 * wv + i : (wv == 2 ? (i == 0 ? 0 : 3) : (i == 0 ? 1 : 2));
-    }
+    // Wave w featurizes token tile w of the chunk: q (FULL only) and k.
+    constexpr int XQ = 0, XK = TPF_ - 1;  // xf slots of the q and k rows
     uint32_t xoff[TPF_];
 #pragma unroll
     for (int i = 0; i < TPF_; ++i)
-      xoff[i] = (uint32_t)(((int64_t)(16 * tile[i] + col) * (isq ? p.sq_t : p.sk_t) + EPL * g) * sizeof(T));
+      xoff[i] = (uint32_t)(((int64_t)(16 * wv + col) * (FULL && i == XQ ? p.sq_t : p.sk_t) + EPL * g) * sizeof(T));
 
-    // z (feature wave 0): first column of an [F x 16] accumulator block
-    f32x4 Z[NFT];
+    // z: column 0 of an [F x 16] accumulator block, feature tiles dealt to the
+    // feature waves (wave w owns tiles ZT*w .. ZT*w + ZT-1); a copy of each chunk's
+    // end value goes to sZ for the inter-chunk denominators.
+    constexpr int ZT = (NFT + 3) / 4;
+    f32x4 Z[ZT];
 #pragma unroll
-    for (int t = 0; t < NFT; ++t) Z[t] = zero4();
-    if (st && wv == 0 && col == 0) {
+    for (int i = 0; i < ZT; ++i) {
+      Z[i] = zero4();
+      const int t = ZT * wv + i;
+      if (t < NFT && st && col == 0) {
 #pragma unroll
-      for (int t = 0; t < NFT; ++t)
+        for (int r = 0; r < 4; ++r) Z[i][r] = st[(int64_t)F * p.dv + 16 * t + 4 * g + r];
+      }
+    }
+    for (int i = tid; i < F; i += 4 * 64) sZ[1][i] = st ? st[(int64_t)F * p.dv + i] : 0.f;
+    if constexpr (FULL && EPL == 8) {
+      // The intra read-out of token tile b (b even) takes K-steps over tiles b and
+      // b+1; score tile (b+1, b) lies above the diagonal and stays zero.
+      if (wv == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Z[t][r] = st[(int64_t)F * p.dv + 16 * t + 4 * g + r];
+        for (int b2 = 0; b2 < NCT; b2 += 2) store4(&sP[(16 * b2 + col) * LDC + M::tpos(16 * (b2 + 1) + 4 * g)], zero4());
+      }
     }
 
     frag xf[TPF_][KD];
     auto load_x = [&](int64_t tc) {
-      const T *base = (isq ? Q : K) + tc * (isq ? p.sq_t : p.sk_t);
+      const bool ok = tc + 16 * wv + col < t1;
 #pragma unroll
       for (int i = 0; i < TPF_; ++i) {
-        const bool ok = tc + 16 * tile[i] + col < t1;
+        const T *base = FULL && i == XQ ? Q + tc * p.sq_t : K + tc * p.sk_t;
 #pragma unroll
         for (int s = 0; s < KD; ++s) xf[i][s] = ok ? M::ld_contig(at(base, xoff[i]) + s * M::KS, 0) : zfrag<frag>();
       }
@@ -244,148 +278,200 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     }
     __syncthreads();
 
-    frag kf[TPF_][KF];  // phi(k) of the current chunk, tile order
+    // W_k^T fragments stay in registers for the whole segment (A operands); W_q^T
+    // is read from LDS per chunk.
+    frag wk[NFH][KD];
+#pragma unroll
+    for (int t = 0; t < NFH; ++t)
+#pragma unroll
+      for (int s = 0; s < KD; ++s) wk[t][s] = M::ld_contig(sWk + (16 * t + col) * LDW + s * M::KS, g);
+
+    // One token's features into a tile-order LDS row: the bf16 operand fragments
+    // are already in that order (one 16-byte write each); f32 rows take the
+    // accumulator tiles.
+    auto store_frags = [&](T *row, const frag *fr, const f32x4 *ph) {
+      if constexpr (EPL == 8) {
+#pragma unroll
+        for (int s = 0; s < KF; ++s) *reinterpret_cast<frag *>(row + 32 * s + 8 * g) = fr[s];
+      } else {
+#pragma unroll
+        for (int t = 0; t < NFT; ++t) store4(row + M::tpos(16 * t + 4 * g), ph[t]);
+      }
+    };
+
+    // softmax([u, -u]) of one token per lane column, shifted by max|u|: ph[t] for
+    // t < NFH holds e^{u}, ph[NFH + t] holds e^{-u}; returns the row sum.
+    auto features = [&](const f32x4 *u, f32x4 *ph) {
+      float m = 0.f;
+#pragma unroll
+      for (int t = 0; t < NFH; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[t][r]));
+      const float ml = group_max(m) * L2E;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < NFH; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = u[t][r];
+          const float ep = __builtin_amdgcn_exp2f(__builtin_fmaf(x, L2E, -ml));
+          const float em = __builtin_amdgcn_exp2f(__builtin_fmaf(-x, L2E, -ml));
+          ph[t][r] = ep;
+          ph[NFH + t][r] = em;
+          sum += ep + em;
+        }
+      return group_sum(sum);
+    };
+
+    // score tile (a, bt) of the chunk in buffers bf / df: Pt[c'][c] for c' in tile
+    // a (A operand rows), c in tile bt (B operand columns), masked to c' <= c and
+    // decay-weighted, into sP (row c, tile order over c'); row sums into sDenPart.
+    auto score_tile = [&](int a, int bt, const frag *fa, const frag *fb, int df) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < KF; ++s) acc = M::mma(fa[s], fb[s], acc);
+      const int cc = 16 * bt + col;
+      double lc = 0.0;
+      if constexpr (DECAY) lc = sL[df][cc];
+      f32x4 w;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cp = 16 * a + 4 * g + r;
+        float xv = cp <= cc ? acc[r] : 0.f;
+        if constexpr (DECAY) {
+          if (cp <= cc) xv *= __expf((float)(lc - sL[df][cp]));
+        }
+        w[r] = xv;
+      }
+      w = round4(w, T{});
+      store4(&sP[cc * LDC + M::tpos(16 * a + 4 * g)], w);
+      const float dsum = group_sum(w[0] + w[1] + w[2] + w[3]);
+      if (g == 0) sDenPart[a][cc] = dsum;
+    };
+
     for (int64_t j = 0; j <= nch; ++j) {
       const int64_t tf = t0 + j * C;
       const int bf = (int)(j & 1);
       const int df = (int)(j % 3);
-      // ---- half A: featurize chunk j
+      const int cr = 16 * wv + col;  // this lane's token row in the chunk
+      frag qf[FULL ? KF : 1], kf[KF];  // phiQ, phiK of token tile wv (tile order)
+      // ---- half A: featurize token tile wv of chunk j
       if (j < nch) {
-        f32x4 u[TPF_][NFH];
-        const T *sW = isq ? sWq : sWk;
+        f32x4 uq[NFH], uk[NFH];
 #pragma unroll
         for (int t = 0; t < NFH; ++t) {
-          frag wa[KD];  // W^T fragments of feature tile t, shared by the wave's tiles
+          uk[t] = zero4();
 #pragma unroll
-          for (int s = 0; s < KD; ++s) wa[s] = M::ld_contig(sW + (16 * t + col) * LDW + s * M::KS, g);
+          for (int s = 0; s < KD; ++s) uk[t] = M::mma(wk[t][s], xf[XK][s], uk[t]);
+          if constexpr (FULL) {
+            frag wq[KD];
 #pragma unroll
-          for (int i = 0; i < TPF_; ++i) {
-            u[i][t] = zero4();
+            for (int s = 0; s < KD; ++s) wq[s] = M::ld_contig(sWq + (16 * t + col) * LDW + s * M::KS, g);
+            uq[t] = zero4();
 #pragma unroll
-            for (int s = 0; s < KD; ++s) u[i][t] = M::mma(wa[s], xf[i][s], u[i][t]);
+            for (int s = 0; s < KD; ++s) uq[t] = M::mma(wq[s], xf[XQ][s], uq[t]);
           }
         }
         if (j + 1 < nch) load_x(tf + C);
+        f32x4 ph[NFT];
+        if constexpr (FULL) {
+          // phi(q) unnormalized: a positive per-query factor cancels in o's ratio.
+          // den_inter = e^{L_c} phiQ_c . z, with z at the end of the previous chunk.
+          features(uq, ph);
 #pragma unroll
-        for (int i = 0; i < TPF_; ++i) {
-          const int bt = tile[i];
-          float m = 0.f;
+          for (int s = 0; s < KF; ++s) qf[s] = M::from_acc(ph, s);
+          store_frags(&sQ[bf][cr * LDQ], qf, ph);
+          const float *zp = sZ[(j + 1) & 1];
+          float dz = 0.f;
 #pragma unroll
-          for (int t = 0; t < NFH; ++t)
+          for (int t = 0; t < NFT; ++t) {
+            const f32x4 z4 = *reinterpret_cast<const f32x4 *>(zp + 16 * t + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[i][t][r]));
-          const float ml = group_max(m) * L2E;
-          f32x4 ph[NFT];
-          float sum = 0.f;
+            for (int r = 0; r < 4; ++r) dz = __builtin_fmaf(ph[t][r], z4[r], dz);
+          }
+          dz = group_sum(dz);
+          if (g == 0) sDenInter[bf][cr] = DECAY ? dz * seL[df][cr] : dz;
+        }
+        {
+          float inv = __builtin_amdgcn_rcpf(features(uk, ph));
+          if constexpr (!DECAY) {
+            if (tf + cr >= t1) inv = 0.f;  // rows past the end contribute nothing
+          }
 #pragma unroll
-          for (int t = 0; t < NFH; ++t)
+          for (int t = 0; t < NFT; ++t) ph[t] *= inv;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float x = u[i][t][r];
-              const float ep = __builtin_amdgcn_exp2f(__builtin_fmaf(x, L2E, -ml));
-              const float em = __builtin_amdgcn_exp2f(__builtin_fmaf(-x, L2E, -ml));
-              ph[t][r] = ep;
-              ph[NFH + t][r] = em;
-              sum += ep + em;
-            }
-          if (isq) {
-            // phi(q) unnormalized: a positive per-query factor cancels in o's ratio
-            const int cr = 16 * bt + col;
+          for (int s = 0; s < KF; ++s) kf[s] = M::from_acc(ph, s);
+          if constexpr (FULL) {
+            // phiK rows of token tile 0, for the one score tile formed from phiQ's side
+            if (wv == 0) store_frags(&sK0[col * LDQ], kf, ph);
+          }
+          f32x4 w4;
+          if constexpr (DECAY) w4 = *reinterpret_cast<const f32x4 *>(&seK[df][16 * wv + 4 * g]);
+          // phiK^T tile uo (decay-weighted): lane (g, col f') gets phiK[16wv+4g+r][16uo+f'],
+          // in groups of four tiles
 #pragma unroll
-            for (int t = 0; t < NFT; ++t) store4(&sQ[bf][cr * LDQ + M::tpos(16 * t + 4 * g)], ph[t]);
-          } else {
-            float inv = 1.f / group_sum(sum);
-            if constexpr (!DECAY) {
-              if (tf + 16 * bt + col >= t1) inv = 0.f;  // rows past the end contribute nothing
-            }
+          for (int u0 = 0; u0 < NFT; u0 += 4) {
+            f32x4 tr[4];
 #pragma unroll
-            for (int t = 0; t < NFT; ++t) ph[t] *= inv;
-#pragma unroll
-            for (int s = 0; s < KF; ++s) kf[i][s] = M::from_acc(ph, s);
-            f32x4 w4;
-            if constexpr (DECAY) w4 = *reinterpret_cast<const f32x4 *>(&seK[df][16 * bt + 4 * g]);
-            // phiK^T tile uo (decay-weighted): lane (g, col f') gets phiK[16bt+4g+r][16uo+f']
-#pragma unroll
-            for (int uo = 0; uo < NFT; ++uo) {
-              f32x4 acc = zero4();
+            for (int uo = u0; uo < u0 + 4 && uo < NFT; ++uo) {
+              tr[uo - u0] = zero4();
               if constexpr (EPL == 8) {
-                acc = M::mma(kf[i][uo >> 1], ksel[uo & 1], acc);
+                tr[uo - u0] = M::mma(kf[uo >> 1], ksel[uo & 1], tr[uo - u0]);
               } else {
 #pragma unroll
-                for (int s = 4 * uo; s < 4 * uo + 4; ++s) acc = M::mma(kf[i][s], ksel[s & 3], acc);
+                for (int s = 4 * uo; s < 4 * uo + 4; ++s) tr[uo - u0] = M::mma(kf[s], ksel[s & 3], tr[uo - u0]);
               }
-              if constexpr (DECAY) acc *= w4;
-              store4(&sKt[bf][(16 * uo + col) * LDC + M::tpos(16 * bt + 4 * g)], acc);
+            }
+#pragma unroll
+            for (int uo = u0; uo < u0 + 4 && uo < NFT; ++uo) {
+              if constexpr (DECAY) tr[uo - u0] *= w4;
+              store4(&sKt[bf][(16 * uo + col) * LDC + M::tpos(16 * wv + 4 * g)], tr[uo - u0]);
             }
           }
         }
       }
       __syncthreads();
-      // ---- half B: score tiles, denominators and z for chunk j; decay of chunk j+1
+      // ---- half B: score tiles and z over chunk j, decay of chunk j+1 (wave 1)
       if (j < nch) {
         if constexpr (FULL) {
-          if (wv >= 2) {
-            // score tiles of rows a (this wave's k tiles) -> sP, row sums -> sDenPart
+          // Ten causal tiles (a <= b): wave w forms (w, w) from its own phiK and
+          // phiQ, wave w < 3 also (w, b) for b = w+1 .. min(w+2, 3) with phiQ of
+          // tile b read back, and wave 3 forms (0, 3) with phiK of tile 0 read back.
+          if (wv < 3) {
+            const int nb = wv < 2 ? 2 : 1;
+            frag bq[2][KF];
 #pragma unroll
-            for (int i = 0; i < TPF_; ++i) {
-              const int a = tile[i];
+            for (int i = 0; i < 2; ++i)
+              if (i < nb) {
 #pragma unroll
-              for (int bt = 0; bt < NCT; ++bt) {
-                const int cc = 16 * bt + col;
-                if (bt < a) {
-                  store4(&sP[bf][cc * LDC + M::tpos(16 * a + 4 * g)], zero4());
-                  continue;
-                }
-                frag bq[KF];
-#pragma unroll
-                for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[bf][cc * LDQ], s, g);
-                f32x4 acc = zero4();
-#pragma unroll
-                for (int s = 0; s < KF; ++s) acc = M::mma(kf[i][s], bq[s], acc);
-                f32x4 w;
-                double lc = 0.0;
-                if constexpr (DECAY) lc = sL[df][cc];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                  const int cp = 16 * a + 4 * g + r;
-                  float x = cp <= cc ? acc[r] : 0.f;
-                  if constexpr (DECAY) {
-                    if (cp <= cc) x *= __expf((float)(lc - sL[df][cp]));
-                  }
-                  w[r] = x;
-                }
-                w = round4(w, T{});
-                store4(&sP[bf][cc * LDC + M::tpos(16 * a + 4 * g)], w);
-                const float dsum = group_sum(w[0] + w[1] + w[2] + w[3]);
-                if (g == 0) sDenPart[bf][a][cc] = dsum;
+                for (int s = 0; s < KF; ++s) bq[i][s] = M::ld_tile(&sQ[bf][(16 * (wv + 1 + i) + col) * LDQ], s, g);
               }
-            }
-          } else if (wv == 0) {
-            // den_inter = e^{L_c} z . phi(q_c): z as row 0 of the A operand
-            frag zf[KF];
+            score_tile(wv, wv, kf, qf, df);
 #pragma unroll
-            for (int s = 0; s < KF; ++s) zf[s] = M::from_acc(Z, s);
+            for (int i = 0; i < 2; ++i)
+              if (i < nb) score_tile(wv, wv + 1 + i, kf, bq[i], df);
+          } else {
+            frag ak[KF];
 #pragma unroll
-            for (int bt = 0; bt < NCT; ++bt) {
-              const int cc = 16 * bt + col;
-              f32x4 acc = zero4();
-#pragma unroll
-              for (int s = 0; s < KF; ++s) acc = M::mma(zf[s], M::ld_tile(&sQ[bf][cc * LDQ], s, g), acc);
-              if (g == 0) sDenInter[bf][cc] = DECAY ? acc[0] * seL[df][cc] : acc[0];
-            }
+            for (int s = 0; s < KF; ++s) ak[s] = M::ld_tile(&sK0[col * LDQ], s, g);
+            score_tile(wv, wv, kf, qf, df);
+            score_tile(0, wv, ak, qf, df);
           }
         }
-        if (wv == 0) {
-          // z <- e^{L_last} z + sum_c' phi~(k_c'): phi~(k)^T times a ones column
-          if constexpr (DECAY) {
-            const float el = sLast[df];
+        // z <- e^{L_last} z + sum_c' phi~(k_c'): phi~(k)^T times a ones column
+        const float el = DECAY ? sLast[df] : 1.f;
 #pragma unroll
-            for (int t = 0; t < NFT; ++t) Z[t] *= el;
+        for (int i = 0; i < ZT; ++i) {
+          const int t = ZT * wv + i;
+          if (t < NFT) {
+            frag ak[KC];
+#pragma unroll
+            for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[bf][(16 * t + col) * LDC], s, g);
+            if constexpr (DECAY) Z[i] *= el;
+#pragma unroll
+            for (int s = 0; s < KC; ++s) Z[i] = M::mma(ak[s], ones, Z[i]);
+            if (col == 0) *reinterpret_cast<f32x4 *>(&sZ[bf][16 * t + 4 * g]) = Z[i];
           }
-#pragma unroll
-          for (int t = 0; t < NFT; ++t)
-#pragma unroll
-            for (int s = 0; s < KC; ++s) Z[t] = M::mma(M::ld_tile(&sKt[bf][(16 * t + col) * LDC], s, g), ones, Z[t]);
         }
         if (wv == 1 && j + 1 < nch) {
           decay(tf + C, (int)((j + 1) % 3));
@@ -395,11 +481,15 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       __syncthreads();
     }
     if (!FULL && half == 0 && wv == 1 && lane == 0) p.ws_lam[(int64_t)seg * BH + bh] = (float)lam;
-    if (dst && wv == 0 && col == 0 && half == 0) {
+    if (dst && col == 0 && half == 0) {
 #pragma unroll
-      for (int t = 0; t < NFT; ++t)
+      for (int i = 0; i < ZT; ++i) {
+        const int t = ZT * wv + i;
+        if (t < NFT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[(int64_t)F * p.dv + 16 * t + 4 * g + r] = Z[t][r];
+          for (int r = 0; r < 4; ++r) dst[(int64_t)F * p.dv + 16 * t + 4 * g + r] = Z[i][r];
+        }
+      }
     }
   } else {
     // ---------------------------------------------------------------- state waves
@@ -411,44 +501,49 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           S[jj][t][r] = st ? st[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + 16 * jj + col] : 0.f;
-    uint32_t voff[NTW];
+    // v rows of the chunk, in registers.  bf16: lane (g, col) holds
+    // v[token col][8g .. 8g+7] of the wave's 16*NTW columns (one 16-byte load; lanes
+    // g >= 2*NTW idle), turned into each value tile's accumulator layout by a
+    // selector product.  f32: lane (g, col) holds v[token col][16jj + g + 4s].
+    constexpr int VJ = EPL == 8 ? 1 : NTW;
+    uint32_t voff[VJ];
 #pragma unroll
-    for (int jj = 0; jj < NTW; ++jj)
+    for (int jj = 0; jj < VJ; ++jj)
       voff[jj] = (uint32_t)(((int64_t)col * p.sv_t + ncol + 16 * jj + (EPL == 8 ? 8 * g : g)) * sizeof(T));
-    frag vf[NTW][NCT][KVL];
+    frag vf[VJ][NCT][KVL];
     auto load_v = [&](int64_t tc) {
 #pragma unroll
       for (int bt = 0; bt < NCT; ++bt) {
         const T *base = V + (tc + 16 * bt) * p.sv_t;
         const bool ok = tc + 16 * bt + col < t1;
+        if constexpr (EPL == 8) {
+          vf[0][bt][0] = (ok && g < 2 * NTW) ? M::ld_contig(at(base, voff[0]), 0) : zfrag<frag>();
+        } else {
 #pragma unroll
-        for (int jj = 0; jj < NTW; ++jj) {
-          if constexpr (EPL == 8) {
-            vf[jj][bt][0] = (ok && g < 2) ? M::ld_contig(at(base, voff[jj]), 0) : zfrag<frag>();
-          } else {
+          for (int jj = 0; jj < NTW; ++jj)
 #pragma unroll
             for (int s = 0; s < KVL; ++s) vf[jj][bt][s] = ok ? at(base, voff[jj])[4 * s] : 0.f;
-          }
         }
       }
     };
-    frag vsel[KVL];
+    frag vsel[NTW][KVL];
 #pragma unroll
-    for (int s = 0; s < KVL; ++s) {
-      if constexpr (EPL == 8) vsel[s] = M::select([&](int e) { return 8 * g + e == col; });
-      else vsel[s] = M::select([&](int) { return 4 * s + g == col; });
-    }
+    for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+      for (int s = 0; s < KVL; ++s) {
+        if constexpr (EPL == 8) vsel[jj][s] = M::select([&](int e) { return 8 * g + e == 16 * jj + col; });
+        else vsel[jj][s] = M::select([&](int) { return 4 * s + g == col; });
+      }
 
     if (nch > 0) load_v(t0);
     __syncthreads();
 
     frag vfr[NTW][KC];  // v of the chunk being read out, tile order
-    f32x4 oacc[NTW][NCT];
     for (int64_t j = 0; j <= nch; ++j) {
-      const int64_t ts = t0 + (j - 1) * C;  // chunk read out in this iteration (j >= 1)
+      const int64_t ts = t0 + (j - 1) * C;  // chunk handled in this iteration (j >= 1)
       const int bs = (int)((j + 1) & 1);
       const int ds = (int)((j + 2) % 3);
-      // ---- half A: inter read-out and state update over chunk j-1
+      // ---- half A: read-out of chunk j-1
       if (j >= 1) {
         // v of chunk ts -> accumulator layout: lane (g, col n) holds v[16bt + 4g + r][n]
 #pragma unroll
@@ -458,7 +553,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           for (int bt = 0; bt < NCT; ++bt) {
             vacc[bt] = zero4();
 #pragma unroll
-            for (int s = 0; s < KVL; ++s) vacc[bt] = M::mma(vf[jj][bt][s], vsel[s], vacc[bt]);
+            for (int s = 0; s < KVL; ++s) vacc[bt] = M::mma(vf[EPL == 8 ? 0 : jj][bt][s], vsel[jj][s], vacc[bt]);
           }
 #pragma unroll
           for (int s = 0; s < KC; ++s) vfr[jj][s] = M::from_acc(vacc, s);
@@ -470,19 +565,63 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           for (int jj = 0; jj < NTW; ++jj)
 #pragma unroll
             for (int s = 0; s < KF; ++s) sfr[jj][s] = M::from_acc(S[jj], s);
+          float den[NCT];
+#pragma unroll
+          for (int bt = 0; bt < NCT; ++bt) {
+            const int cc = 16 * bt + col;
+            den[bt] = sDenInter[bs][cc];
+#pragma unroll
+            for (int a = 0; a <= bt; ++a) den[bt] += sDenPart[a][cc];
+          }
+          f32x4 oacc[NTW][NCT];
 #pragma unroll
           for (int bt = 0; bt < NCT; ++bt) {
             const int cc = 16 * bt + col;
             frag bq[KF];
 #pragma unroll
             for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[bs][cc * LDQ], s, g);
+            frag bp[M::steps_upto(NCT - 1)];
+#pragma unroll
+            for (int s = 0; s < M::steps_upto(bt); ++s) bp[s] = M::ld_tile(&sP[cc * LDC], s, g);
 #pragma unroll
             for (int jj = 0; jj < NTW; ++jj) {
-              oacc[jj][bt] = zero4();
+              // inter: S^T phiQ^T e^{L_c};  intra: V^T Pt
+              f32x4 acc = zero4();
 #pragma unroll
-              for (int s = 0; s < KF; ++s) oacc[jj][bt] = M::mma(sfr[jj][s], bq[s], oacc[jj][bt]);
-              if constexpr (DECAY) oacc[jj][bt] *= seL[ds][cc];
+              for (int s = 0; s < KF; ++s) acc = M::mma(sfr[jj][s], bq[s], acc);
+              if constexpr (DECAY) acc *= seL[ds][cc];
+#pragma unroll
+              for (int s = 0; s < M::steps_upto(bt); ++s) acc = M::mma(vfr[jj][s], bp[s], acc);
+              oacc[jj][bt] = acc;
             }
+          }
+#pragma unroll
+          for (int bt = 0; bt < NCT; ++bt) {
+            const float inv = __builtin_amdgcn_rcpf(den[bt]);
+#pragma unroll
+            for (int jj = 0; jj < NTW; ++jj) oacc[jj][bt] *= inv;
+          }
+          // output rows to LDS; they leave for HBM as whole rows in half B
+          T *orow = &sO[col * LDO + 16 * NTW * sw + 4 * g];
+#pragma unroll
+          for (int bt = 0; bt < NCT; ++bt)
+#pragma unroll
+            for (int jj = 0; jj < NTW; ++jj) store4(orow + 16 * bt * LDO + 16 * jj, oacc[jj][bt]);
+        }
+      }
+      __syncthreads();
+      // ---- half B: output rows of chunk j-1 to HBM, state update over chunk j-1
+      if (j >= 1) {
+        if constexpr (FULL) {
+          constexpr int EP = 16 / (int)sizeof(T);          // elements per 16-byte piece
+          constexpr int PPR = DW / EP;                      // pieces per row
+          T *ob = O + ts * p.so_t + half * DW;
+#pragma unroll
+          for (int i = sw * 64 + lane; i < C * PPR; i += NS * 64) {
+            const int row = i / PPR, pc = i % PPR;
+            if (ts + row < t1)
+              *reinterpret_cast<f32x4 *>(ob + row * p.so_t + pc * EP) =
+                  *reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]);
           }
         }
         if constexpr (DECAY) {
@@ -501,32 +640,6 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           for (int jj = 0; jj < NTW; ++jj)
 #pragma unroll
             for (int s = 0; s < KC; ++s) S[jj][t] = M::mma(ak[s], vfr[jj][s], S[jj][t]);
-        }
-      }
-      __syncthreads();
-      // ---- half B: intra read-out of chunk j-1, normalize, store
-      if constexpr (FULL) {
-        if (j >= 1) {
-#pragma unroll
-          for (int bt = 0; bt < NCT; ++bt) {
-            const int cc = 16 * bt + col;
-            frag bp[M::steps_upto(NCT - 1)];
-#pragma unroll
-            for (int s = 0; s < M::steps_upto(bt); ++s) bp[s] = M::ld_tile(&sP[bs][cc * LDC], s, g);
-#pragma unroll
-            for (int jj = 0; jj < NTW; ++jj)
-#pragma unroll
-              for (int s = 0; s < M::steps_upto(bt); ++s) oacc[jj][bt] = M::mma(vfr[jj][s], bp[s], oacc[jj][bt]);
-            const int64_t c = ts + cc;
-            if (c < t1) {
-              float den = sDenInter[bs][cc];
-#pragma unroll
-              for (int a = 0; a <= bt; ++a) den += sDenPart[bs][a][cc];
-              const float inv = 1.f / den;
-#pragma unroll
-              for (int jj = 0; jj < NTW; ++jj) store4(O + c * p.so_t + ncol + 16 * jj + 4 * g, oacc[jj][bt] * inv);
-            }
-          }
         }
       }
       __syncthreads();
