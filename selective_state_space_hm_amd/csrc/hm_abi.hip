@@ -242,15 +242,32 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.nseg = pl.segments;
   p.dsplit = pl.dsplit;
 
-  auto grid_for = [&](int64_t items) { return (unsigned)(((items + 7) / 8) * 8 * pl.dsplit); };
+  auto grid_for = [&](int64_t items, int ds) { return (unsigned)(((items + 7) / 8) * 8 * ds); };
   if (pl.segments > 1) {
+    // Segment pass: end state of every segment but the last, segment 0 starting
+    // from s_init (read before anything writes s_final) and the others from zero.
+    // It owns fewer value columns per workgroup when that fills more of the chip.
+    const hm::FwdEntry *loc = local;
+    int lds = pl.dsplit;
+    for (int cand = 4; cand > pl.dsplit; cand /= 2) {
+      const hm::FwdEntry *e = a->dv % cand ? nullptr : find_fwd(a->dtype, a->d, a->f, a->dv / cand, decay, hm::MODE_LOCAL);
+      if (e && BH * (pl.segments - 1) * cand <= 256) {
+        loc = e;
+        lds = cand;
+        break;
+      }
+    }
     hm::FwdParams pp = p;
+    pp.s_start0 = a->s_init;
+    pp.dsplit = lds;
     pp.nseg_run = pl.segments - 1;
     pp.nitems = BH * pp.nseg_run;
-    local->launch(pp, grid_for(pp.nitems), s);
+    loc->launch(pp, grid_for(pp.nitems, lds), s);
     if ((st = check_launch("segment pass")) != HM_OK) return st;
   }
-  if (pl.segments > 1 || pl.init_copy) {
+  // Start states of segments 2.. (segment 1 starts from the segment pass's
+  // state directly); the copy of s_init when it aliases s_final.
+  if (pl.segments > 2 || pl.init_copy) {
     dim3 grid((unsigned)((BLK + 255) / 256), (unsigned)BH);
     hipLaunchKernelGGL(hm::combine_kernel, grid, dim3(256), 0, s, ws_state, ws_lam, a->s_init,
                        pl.init_copy ? ws_init : nullptr, BH, BLK, pl.segments);
@@ -258,7 +275,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   }
   p.nseg_run = pl.segments;
   p.nitems = BH * pl.segments;
-  full->launch(p, grid_for(p.nitems), s);
+  full->launch(p, grid_for(p.nitems, pl.dsplit), s);
   return check_launch("prefill");
 }
 

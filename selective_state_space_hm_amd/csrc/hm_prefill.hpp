@@ -174,11 +174,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     }
   }
 
+  // start state: s_start0 for segment 0 (both passes); the full pass takes the
+  // start states of later segments from the workspace, the segment pass zeros
   const float *st = nullptr;
-  if constexpr (FULL) {
-    if (seg == 0) st = p.s_start0 ? p.s_start0 + bh * BLK : nullptr;
-    else st = p.ws_state + ((int64_t)(seg - 1) * BH + bh) * BLK;
-  }
+  if (seg == 0) st = p.s_start0 ? p.s_start0 + bh * BLK : nullptr;
+  else if constexpr (FULL) st = p.ws_state + ((int64_t)(seg - 1) * BH + bh) * BLK;
   const int64_t nch = t1 > t0 ? (t1 - t0 + C - 1) / C : 0;
   float *dst = nullptr;  // end state destination
   if constexpr (FULL) {
@@ -615,13 +615,19 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         if constexpr (FULL) {
           constexpr int EP = 16 / (int)sizeof(T);          // elements per 16-byte piece
           constexpr int PPR = DW / EP;                      // pieces per row
+          constexpr int NIT = C * PPR / (NS * 64);         // pieces per lane
+          static_assert(NIT * NS * 64 == C * PPR, "whole rows per pass");
           T *ob = O + ts * p.so_t + half * DW;
+          f32x4 piece[NIT];
 #pragma unroll
-          for (int i = sw * 64 + lane; i < C * PPR; i += NS * 64) {
-            const int row = i / PPR, pc = i % PPR;
-            if (ts + row < t1)
-              *reinterpret_cast<f32x4 *>(ob + row * p.so_t + pc * EP) =
-                  *reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]);
+          for (int it = 0; it < NIT; ++it) {
+            const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+            piece[it] = *reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]);
+          }
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+            if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[it];
           }
         }
         if constexpr (DECAY) {
@@ -655,8 +661,9 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   }
 }
 
-// Start states of segments 1..nseg-1 from the local end states (in place):
-//   start(s) = e^{lam(s-1)} start(s-1) + local(s-1),  start(0) = s_init,
+// Start states of segments 2..nseg-1 from the segment pass's end states (in
+// place): start(1) = end(0), which already began from s_init, and
+//   start(s) = e^{lam(s-1)} start(s-1) + local(s-1),
 // the composition of affine maps of [SSM] §4.2 with a scalar decay.  Optionally
 // copies s_init to `init_copy` first (used when s_init aliases s_final).
 static __global__ __launch_bounds__(256) void combine_kernel(float *ws_state, const float *ws_lam, const float *s_init,
@@ -664,12 +671,12 @@ static __global__ __launch_bounds__(256) void combine_kernel(float *ws_state, co
   const int64_t bh = blockIdx.y;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= BLK) return;
-  float cur = s_init ? s_init[bh * BLK + e] : 0.f;
-  if (init_copy) init_copy[bh * BLK + e] = cur;
-  for (int s = 1; s < nseg; ++s) {
+  if (init_copy) init_copy[bh * BLK + e] = s_init ? s_init[bh * BLK + e] : 0.f;
+  if (nseg < 3) return;
+  float cur = ws_state[bh * BLK + e];
+  for (int s = 2; s < nseg; ++s) {
     const int64_t slot = (int64_t)(s - 1) * BH + bh;
-    const float loc = ws_state[slot * BLK + e];
-    cur = expf(ws_lam[slot]) * cur + loc;
+    cur = expf(ws_lam[slot]) * cur + ws_state[slot * BLK + e];
     ws_state[slot * BLK + e] = cur;
   }
 }

@@ -83,7 +83,7 @@ def test_small_fp32_ragged(n, decay):
 
 
 @pytest.mark.parametrize("dv", [16, 32])
-@pytest.mark.parametrize("segments,dsplit", [(1, 1), (3, 1), (1, 2), (4, 2)])
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (2, 1), (3, 1), (1, 2), (2, 2), (4, 2)])
 def test_fp32_plans_with_initial_state(dv, segments, dsplit):
     if dsplit == 2 and dv == 16:
         pytest.skip("dv=16 has one value tile")
@@ -179,7 +179,7 @@ def test_empty_sequence_copies_initial_state():
     assert torch.count_nonzero(s_final) == 0
 
 
-@pytest.mark.parametrize("segments,dsplit", [(1, 1), (1, 2), (3, 2)])
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (1, 2), (2, 1), (3, 2)])
 def test_split_handoff_with_aliased_state(segments, dsplit):
     """fwd[0,n) == fwd[0,m) -> state -> fwd[m,n), with s_init and s_final the same buffer."""
     c = inputs.make_prefill("h", 1, 2, 700, 128, 64, 128, torch.bfloat16, None, "mild", seed=6)
