@@ -144,8 +144,10 @@ def hbm_traffic(key):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU raises its clocks over the first ~20 ms of sustained work; the default
+    # warm-up (about 30 ms of launches) times the steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip decode and the decay workloads")
     ap.add_argument("--part", choices=["all", "decode", "copy"], default="all",
@@ -236,13 +238,13 @@ def main():
             gg = {k: getattr(c, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k", "dt", "a_log")}
             oo = torch.empty_like(gg["v"])
             pl = hm.hm_linattn_fwd_plan(gg["q"], gg["k"], gg["v"], gg["w_q"], gg["w_k"], gg["dt"], gg["a_log"])
-            steps = 20 if c.n <= 8192 else 5
+            steps = 50 if c.n <= 8192 else 10
 
             def stepx():
                 hm.hm_linattn_fwd(gg["q"], gg["k"], gg["v"], gg["w_q"], gg["w_k"], gg["dt"], gg["a_log"], o=oo,
                                   workspace=ws)
 
-            msx, _ = time_launches(stepx, steps, 2, torch)
+            msx, _ = time_launches(stepx, steps, 4 * steps, torch)
             bx = prefill_bytes(c.B, c.H, c.n, c.d, c.f, c.dv, True)
             extra.append({"workload": f"{c.name} B={c.B} H={c.H} n={c.n} Mamba decay", "ms": msx,
                           "tokens_per_s": c.B * c.n / (msx * 1e-3), "achieved_GBs": bx / (msx * 1e-3) / 1e9,

@@ -334,16 +334,24 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       double lc = 0.0;
       if constexpr (DECAY) lc = sL[df][cc];
       f32x4 w;
+      if (a == bt) {  // diagonal tile: causal mask
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int cp = 16 * a + 4 * g + r;
-        float xv = cp <= cc ? acc[r] : 0.f;
-        if constexpr (DECAY) {
-          if (cp <= cc) xv *= __expf((float)(lc - sL[df][cp]));
+        for (int r = 0; r < 4; ++r) {
+          const int cp = 16 * a + 4 * g + r;
+          float xv = cp <= cc ? acc[r] : 0.f;
+          if constexpr (DECAY) {
+            if (cp <= cc) xv *= __expf((float)(lc - sL[df][cp]));
+          }
+          w[r] = xv;
         }
-        w[r] = xv;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float xv = acc[r];
+          if constexpr (DECAY) xv *= __expf((float)(lc - sL[df][16 * a + 4 * g + r]));
+          w[r] = xv;
+        }
       }
-      w = round4(w, T{});
       store4(&sP[cc * LDC + M::tpos(16 * a + 4 * g)], w);
       const float dsum = group_sum(w[0] + w[1] + w[2] + w[3]);
       if (g == 0) sDenPart[a][cc] = dsum;
