@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 MFMA_FLOP = 16 * 16 * 32 * 2   # one v_mfma_f32_16x16x32_bf16
 METRIC = "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW (1 MI355X)"
-KERNEL_SOURCES = ["hm_device.hpp", "hm_prefill.hpp", "hm_step.hpp"]
+KERNEL_SOURCES = ["hm_device.hpp", "hm_prefill.hpp", "hm_step.hpp", "hm_abi.hip"]  # kernels and launch plans
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 
 
@@ -62,26 +62,38 @@ def prefill_flops_algorithmic(B, H, n, d, f, dv):
     return B * H * n * (4 * d * f + 4 * F * (dv + 1))
 
 
+def segment_pass_split(B, H, nseg, dv, dsplit):
+    """Column split of the segment pass, as the library chooses it: the widest of 4
+    or 2 (32 columns at least) that keeps the pass within 256 workgroups."""
+    for cand in (4, 2):
+        if cand > dsplit and dv % cand == 0 and dv // cand >= 32 and B * H * (nseg - 1) * cand <= 256:
+            return cand
+    return dsplit
+
+
 def prefill_mfma_count(plan, B, H, n, d, f, dv):
     """MFMA instructions (16x16x32 bf16) the prefill kernels issue, from the loop
     structure of the chunk kernel, per 64-token chunk and workgroup:
-      feature waves: featurize q and k, phi(k)^T re-layout, score tiles (causal
-      half), den_inter and the z update (ones-column products);
-      state waves: v re-layout, inter read-out, state update, intra read-out."""
+      feature waves: featurize q and k, phi(k)^T re-layout, the ten causal score
+      tiles, the z update (ones-column products);
+      state waves: v re-layout, inter read-out, intra read-out, state update.
+    The segment pass featurizes k only and updates the state only."""
     chunk, segments, dsplit = plan
     C = chunk
     NCT, NFH, NFT = C // 16, f // 16, 2 * f // 16
     KD, KF, KC = d // 32, NFT // 2, NCT // 2
     vt = dv // dsplit // 16                        # value tiles per workgroup
     intra_steps = sum(bt // 2 + 1 for bt in range(NCT))
-    full = (2 * NCT * NFH * KD + NCT * NFT + sum(NCT - a for a in range(NCT)) * KF + NCT * KF + NFT * KC
+    full = (2 * NCT * NFH * KD + NCT * NFT + sum(NCT - a for a in range(NCT)) * KF + NFT * KC
             + vt * NCT + vt * NCT * KF + vt * NFT * KC + vt * intra_steps)
-    local = NCT * NFH * KD + NCT * NFT + NFT * KC + vt * NCT + vt * NFT * KC
     chunks = (n + C - 1) // C
     per = -(-chunks // segments)
     nseg = -(-chunks // per)
+    ls = segment_pass_split(B, H, nseg, dv, dsplit)
+    vtl = dv // ls // 16
+    local = NCT * NFH * KD + NCT * NFT + NFT * KC + vtl * NCT + vtl * NFT * KC
     local_chunks = per * (nseg - 1)
-    return B * H * dsplit * (full * chunks + local * local_chunks)
+    return B * H * (dsplit * full * chunks + ls * local * local_chunks)
 
 
 def time_launches(fn, steps, warmup, torch):
@@ -219,7 +231,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "hm_linattn_fwd: fwd_kernel<bf16,128,64,128,false,FULL>"
-                               + (" + segment pass + combine_kernel" if plan[1] > 1 else ""),
+                               + (" + segment pass" if plan[1] > 1 else "")
+                               + (" + combine_kernel" if plan[1] > 2 else ""),
                      "algorithmic_bytes_per_launch": nbytes},
         "mfma": {"executed_tflops": mfma / (ms * 1e-3) / 1e12,
                  "executed_frac": mfma / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,

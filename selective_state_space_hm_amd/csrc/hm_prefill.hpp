@@ -17,16 +17,20 @@
 // This is the chunk-parallel mode of [LA] part 5; chunking only reorders the sums
 // of the recurrent definition.
 //
-// Layout choices (all matrix products are 16x16 MFMA tiles, wave w owns value
-// tile w, i.e. columns n0 + 16w .. n0 + 16w + 15):
-//   * q and k rows are read from HBM straight into B-operand fragments (no LDS);
-//   * v rows are read into A-operand fragments and turned into the
-//     accumulator layout by one MFMA against a 0/1 selector, which is the
-//     tile-order operand layout both V products need: v never touches LDS;
-//   * phiK is likewise re-laid out by selector MFMAs into phiK^T for the state
-//     update; all LDS traffic is 8- or 16-byte vectors;
-//   * the state S stays in accumulators and is fed back as the A operand of the
-//     read-out in tile order (see hm_device.hpp);
+// Work split (all matrix products are 16x16 MFMA tiles): four feature waves and
+// NS state waves; feature wave w and state wave w run on the same SIMD, so each SIMD
+// interleaves softmax VALU work with MFMA work.
+//   * feature wave w featurizes token tile w of the chunk for q and k, stores
+//     phiQ, phiK^T (and phiK of tile 0) in LDS, then forms its share of the score
+//     tiles and of z; feature waves run one chunk ahead of the state waves;
+//   * state wave s owns value columns [32s, 32s + 32) of S in accumulators: the
+//     read-out, the output rows and the state update for those columns.
+// Layout choices:
+//   * q, k and v rows are read from HBM straight into operand fragments; v is
+//     turned into the accumulator layout by one MFMA against a 0/1 selector, and
+//     phiK into phiK^T the same way;
+//   * S is fed back as the A operand of the read-out in tile order (hm_device.hpp);
+//   * output rows are staged in LDS and leave as whole rows;
 //   * the next chunk's q, k, v, dt are loaded into registers while the current
 //     chunk computes.
 #pragma once
