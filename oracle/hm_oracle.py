@@ -21,6 +21,7 @@ What is computed, per (batch b, head h), for tokens t = 0..n-1:
   log a_t = -softplus(dt_t) * exp(A_log[h]);  a_t = 1 without dt [SSM §3.2; HM §3.1]
   S_t = a_t S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t)
   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t                          [LA parts 2-3, 4.3; HM §2.3]
+  optionally o_t <- o_t * SiLU(g_t) with the gate branch's g    [HM §5.2 step 6]
 S_{-1}, z_{-1} are the given initial state (zeros when absent); a_t scales the
 carried state only, never the current token (the RetNet form, [LA] 4.3).
 
@@ -186,32 +187,55 @@ def prefix_state(phik, v, log_a=None):
 
 
 # --------------------------------------------------------------------------
+# Gate branch of the mixer  [HM §1 (Mamba's gate branch), §3.1, §5.2 step 6]
+# --------------------------------------------------------------------------
+def silu(x):
+    """SiLU(x) = x * sigmoid(x), the gate branch's activation.  Evaluated as
+    x / (1 + e^-x) for x >= 0 and x e^x / (1 + e^x) for x < 0, so that no
+    exponential overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, x / (1.0 + e), x * e / (1.0 + e))
+
+
+def apply_gate(o, gate):
+    """The normalized output multiplied element-wise by the gate branch's output
+    SiLU(g) ([HM] §5.2 step 6); gate None leaves o unchanged."""
+    if gate is None:
+        return o
+    return o * silu(gate)
+
+
+# --------------------------------------------------------------------------
 # Whole path and decode step
 # --------------------------------------------------------------------------
-def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, form="recurrent"):
-    """Featurize q and k, then run the chosen form.  Returns (o, S_final, z_final);
-    the quadratic form returns None for the state."""
+def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, form="recurrent", gate=None):
+    """Featurize q and k, then run the chosen form; a gate [B,H,n,dv] (pre-activation)
+    multiplies the output by SiLU(gate).  Returns (o, S_final, z_final); the
+    quadratic form returns None for the state."""
     phiq = hedgehog_features(q, w_q)
     phik = hedgehog_features(k, w_k)
     v = np.asarray(v, dtype=np.float64)
     la = log_decay(dt, a_log)
     if form == "quadratic":
-        return linattn_quadratic(phiq, phik, v, la, s_init, z_init), None, None
+        return apply_gate(linattn_quadratic(phiq, phik, v, la, s_init, z_init), gate), None, None
     if form == "recurrent":
-        return linattn_recurrent(phiq, phik, v, la, s_init, z_init)
+        o, S, z = linattn_recurrent(phiq, phik, v, la, s_init, z_init)
+        return apply_gate(o, gate), S, z
     raise ValueError(form)
 
 
-def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None):
+def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None, gate=None):
     """One decode step from state (S [B,H,F,dv], z [B,H,F]) with one token per
-    (b, h): q, k [B,H,d], v [B,H,dv], dt [B,H].  Returns (o [B,H,dv], S', z').
-    This is the recurrent form advanced by a single token  [LA part 5]."""
+    (b, h): q, k [B,H,d], v [B,H,dv], dt [B,H], gate [B,H,dv] or None.
+    Returns (o [B,H,dv], S', z').  This is the recurrent form advanced by a single
+    token  [LA part 5]."""
     q = np.asarray(q, dtype=np.float64)[:, :, None, :]
     k = np.asarray(k, dtype=np.float64)[:, :, None, :]
     v = np.asarray(v, dtype=np.float64)[:, :, None, :]
     dt3 = None if dt is None else np.asarray(dt, dtype=np.float64)[:, :, None]
     o, S2, z2 = forward(q, k, v, w_q, w_k, dt3, a_log, S, z)
-    return o[:, :, 0, :], S2, z2
+    return apply_gate(o[:, :, 0, :], gate), S2, z2
 
 
 # --------------------------------------------------------------------------

@@ -345,6 +345,47 @@ def test_state_pack_roundtrip():
     np.testing.assert_array_equal(z2, z)
 
 
+# ------------------------------------------------------------------ gate
+def test_silu_against_library_sigmoid():
+    x = np.concatenate([np.linspace(-40, 40, 801), [-750.0, -80.0, 80.0, 750.0]])
+    ref = x * scipy.special.expit(x)
+    np.testing.assert_allclose(orc.silu(x), ref, rtol=1e-14, atol=1e-300)
+    assert np.all(np.isfinite(orc.silu(x)))
+    assert orc.silu(np.array([0.0]))[0] == 0.0
+
+
+def test_gate_at_identity_init_leaves_output_unchanged():
+    # stage-1 init: gate weights 0 and bias SiLU^-1(1), so the gate branch outputs 1
+    import scipy.optimize
+    c = scipy.optimize.brentq(lambda x: x * scipy.special.expit(x) - 1.0, 0.0, 4.0, xtol=1e-15)
+    q, k, v, wq, wk, dt, a_log, s0, z0 = random_case(31, state=True)
+    o, S, z = orc.forward(q, k, v, wq, wk, dt, a_log, s0, z0)
+    og, Sg, zg = orc.forward(q, k, v, wq, wk, dt, a_log, s0, z0, gate=np.full(v.shape, c))
+    assert rel_l2(og, o) < 1e-13
+    np.testing.assert_array_equal(Sg, S)       # the gate never touches the state
+    np.testing.assert_array_equal(zg, z)
+
+
+def test_gate_is_elementwise_on_the_output():
+    q, k, v, wq, wk, dt, a_log, _, _ = random_case(32)
+    g = rng(33).normal(size=v.shape) * 3
+    o, _, _ = orc.forward(q, k, v, wq, wk, dt, a_log)
+    for form in ("quadratic", "recurrent"):
+        og, _, _ = orc.forward(q, k, v, wq, wk, dt, a_log, form=form, gate=g)
+        np.testing.assert_allclose(og, o * g * scipy.special.expit(g), rtol=1e-11, atol=1e-14)
+    og, _, _ = orc.forward(q, k, v, wq, wk, dt, a_log, gate=np.zeros(v.shape))
+    assert np.all(og == 0.0)
+
+
+def test_gated_step_equals_gated_forward_last_token():
+    q, k, v, wq, wk, dt, a_log, _, _ = random_case(34, n=12)
+    g = rng(35).normal(size=v.shape)
+    o, _, _ = orc.forward(q, k, v, wq, wk, dt, a_log, gate=g)
+    _, S, z = orc.forward(q[:, :, :11], k[:, :, :11], v[:, :, :11], wq, wk, dt[:, :, :11], a_log)
+    o1, _, _ = orc.step(S, z, q[:, :, 11], k[:, :, 11], v[:, :, 11], wq, wk, dt[:, :, 11], a_log, gate=g[:, :, 11])
+    assert rel_l2(o1, o[:, :, 11]) < 1e-12
+
+
 def test_planted_mistakes_are_caught():
     # Each of these plausible mistakes, planted in a copy of the oracle's
     # arithmetic, must break one of the pins above.
