@@ -48,10 +48,10 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def prefill_bytes(B, H, n, d, f, dv, decay, elem=2):
+def prefill_bytes(B, H, n, d, f, dv, decay, elem=2, gate=False):
     """Algorithmic HBM bytes of one prefill: q, k, v read once, o written once,
-    dt read once (decay only), W_q and W_k read once."""
-    per_token_head = elem * (2 * d + 2 * dv) + (4 if decay else 0)
+    dt read once (decay only), the gate read once (gated only), W_q and W_k read once."""
+    per_token_head = elem * (2 * d + 2 * dv + (dv if gate else 0)) + (4 if decay else 0)
     return B * H * n * per_token_head + 2 * d * f * elem + (H * 4 if decay else 0)
 
 
@@ -241,10 +241,25 @@ def main():
                  "peak_tflops": BF16_PEAK_TFLOPS},
         "wall_s_timed": wall,
     }
+    if not args.no_extra:
+        extra = []
+        # the same layer with the mixer's gate branch fused into the output store
+        gate = inputs.gate(case.v.shape, torch.bfloat16).to(dev)
+        log("[bench] gated prefill, same layer")
+
+        def stepg():
+            hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], o=o, workspace=ws, gate=gate)
+
+        msg, _ = time_launches(stepg, 50, 200, torch)
+        bg = prefill_bytes(B, H, n, d, f, dv, False, gate=True)
+        extra.append({"workload": f"{case.name} B={B} H={H} n={n}, identity decay, o * SiLU(gate)", "ms": msg,
+                      "tokens_per_s": tokens / (msg * 1e-3), "achieved_GBs": bg / (msg * 1e-3) / 1e9,
+                      "hbm_frac": bg / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "plan": {"chunk": plan[0], "segments": plan[1], "dsplit": plan[2]}})
+        del gate
     del g, o
 
     if not args.no_extra:
-        extra = []
         for maker in (inputs.mamba_decay, inputs.long_context):
             c = maker()
             log(f"[bench] {c.name} n={c.n}")

@@ -20,6 +20,8 @@
  *   S_t = a_t S_{t-1} + phi(k_t) v_t^T   [F x dv]
  *   z_t = a_t z_{t-1} + phi(k_t)         [F]
  *   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t
+ *   o_t <- o_t * SiLU(g_t)  when a gate g is given (the mixer's gate branch,
+ *                           [HM] §5.2 step 6; SiLU(x) = x / (1 + e^-x))
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library never
@@ -41,10 +43,12 @@
  *     next synchronization.  NaN/Inf in the inputs are not checked; they
  *     propagate to the outputs.
  *   - Supported sizes (anything else is HM_ERR_UNSUPPORTED):
- *       bf16:  d in {32, 64, 128}, f in {16, 32, 64}, dv in {64, 128}
- *              (hm_featurize: d in {32, 64, 128}, f in {16, 32, 64})
- *       f32:   d in {16, 32, 64},  f in {16, 32},     dv in {16, 32, 64}
- *              (hm_featurize: d in {16, 32, 64, 128}, f in {16, 32, 64})
+ *       hm_linattn_fwd, hm_linattn_step:
+ *         bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}
+ *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}
+ *       hm_featurize:
+ *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
+ *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}
  *     B, H, n may be 0 (nothing to compute; s_final is still written).
  */
 #ifndef HM_H
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 1
+#define HM_ABI_VERSION 2
 
 typedef enum {
   HM_OK = 0,
@@ -111,6 +115,10 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   workspace: device scratch of at least hm_linattn_fwd_workspace_size() bytes
  *   (it may be NULL when that size is 0).  Its size grows with B*H*segments,
  *   never with n^2.
+ *   gate: optional [B, H, n, dv] in `dtype` (strides sg_*), the pre-activation of
+ *   the mixer's gate branch; when given, o = (normalized output) * SiLU(gate),
+ *   rounded once to `dtype` after the normalized output was rounded (NULL = no
+ *   gate).
  * Accumulation is float32 and the carried state is float32; bf16 operands of the
  * matrix products (phi, the masked score tile, the state copy used for the
  * read-out) are rounded to nearest even.
@@ -134,6 +142,8 @@ typedef struct {
   int64_t sdt_b, sdt_h, sdt_t;
   void *workspace;
   size_t workspace_bytes;
+  const void *gate;
+  int64_t sg_b, sg_h, sg_t;
 } hm_linattn_fwd_args;
 
 hm_status hm_linattn_fwd_workspace_size(const hm_linattn_fwd_args *args, size_t *bytes);
@@ -151,6 +161,8 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
  * written in place.
  *   q, k: [B, H, d]; v, o: [B, H, dv] in `dtype` (strides s*_b, s*_h);
  *   dt: [B, H] float32 (strides sdt_b, sdt_h) or NULL; state: see above.
+ *   gate: optional [B, H, dv] in `dtype` (strides sg_b, sg_h): o_t is multiplied
+ *   by SiLU(gate) (NULL = no gate).
  */
 typedef struct {
   const void *q, *k, *v, *w_q, *w_k;
@@ -163,6 +175,8 @@ typedef struct {
   int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h;
   int64_t sw_h;
   int64_t sdt_b, sdt_h;
+  const void *gate;
+  int64_t sg_b, sg_h;
 } hm_linattn_step_args;
 
 hm_status hm_linattn_step(const hm_linattn_step_args *args, void *stream);

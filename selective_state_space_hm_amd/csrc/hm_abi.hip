@@ -108,6 +108,12 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
   const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->o};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(HM_ERR_ALIGN, "q, k, v, w_q, w_k, o must be 16-byte aligned");
+  if (a->gate) {
+    if (a->sg_b < 0 || a->sg_h < 0 || a->sg_t < 0) return fail(HM_ERR_SHAPE, "gate strides must be non-negative");
+    if (!aligned16(a->gate)) return fail(HM_ERR_ALIGN, "gate must be 16-byte aligned");
+    if (!stride_ok(a->sg_b, a->dtype) || !stride_ok(a->sg_h, a->dtype) || !stride_ok(a->sg_t, a->dtype))
+      return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  }
   if ((a->s_init && !aligned16(a->s_init)) || (a->s_final && !aligned16(a->s_final)))
     return fail(HM_ERR_ALIGN, "state buffers must be 16-byte aligned");
   for (int64_t s : strides)
@@ -238,6 +244,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t;
   p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
   p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
+  p.gate = a->gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h; p.sg_t = a->sg_t;
   p.seg_len = pl.seg_len;
   p.nseg = pl.segments;
   p.dsplit = pl.dsplit;
@@ -295,6 +302,12 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->o, a->state};
   for (const void *p : ptrs)
     if (!aligned16(p)) return fail(HM_ERR_ALIGN, "q, k, v, w_q, w_k, o and state must be 16-byte aligned");
+  if (a->gate) {
+    if (a->sg_b < 0 || a->sg_h < 0) return fail(HM_ERR_SHAPE, "gate strides must be non-negative");
+    if (!aligned16(a->gate)) return fail(HM_ERR_ALIGN, "gate must be 16-byte aligned");
+    if (!stride_ok(a->sg_b, a->dtype) || !stride_ok(a->sg_h, a->dtype))
+      return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  }
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
   const int decay = a->dt != nullptr;
@@ -311,6 +324,7 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sk_b = a->sk_b; p.sk_h = a->sk_h;
   p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.so_b = a->so_b; p.so_h = a->so_h;
   p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h;
+  p.gate = a->gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h;
   e->launch(p, (unsigned)BH, (hipStream_t)stream);
   return check_launch("decode step");
 }

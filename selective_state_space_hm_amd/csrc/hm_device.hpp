@@ -143,6 +143,12 @@ __device__ __forceinline__ float softplus_f32(float x) {
   return x > 20.f ? x : log1pf(expf(x));
 }
 
+// x * sigmoid(x) in float32 (the reciprocal to ~1 ulp); for x < -88 the exponential
+// overflows to +inf and the result is -0, the correct limit.
+__device__ __forceinline__ float silu_f32(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 template <typename T> __device__ __forceinline__ T to_elem(float x) { return (T)x; }
 
 // Four consecutive elements as one vector store / load.

@@ -53,6 +53,8 @@ struct FwdParams {
   int64_t B, H, n, dv;
   int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
+  const void *gate;       // optional gate pre-activation, o's shape (NULL = none)
+  int64_t sg_b, sg_h, sg_t;
   int64_t seg_len;        // tokens per segment, a multiple of CHUNK
   int64_t nitems;         // (b,h,segment) items in this launch
   int nseg;               // segments of the whole sequence
@@ -61,6 +63,22 @@ struct FwdParams {
 };
 
 template <typename F> __device__ __forceinline__ F zfrag() { return F{}; }
+
+// One 16-byte piece of output row times SiLU of the matching gate piece: eight
+// bf16 or four float values, held as the raw 16 bytes.
+__device__ __forceinline__ f32x4 gate_piece(f32x4 o, f32x4 g, bf16) {
+  const bf16x8 ov = __builtin_bit_cast(bf16x8, o), gv = __builtin_bit_cast(bf16x8, g);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)((float)ov[e] * silu_f32((float)gv[e]));
+  return __builtin_bit_cast(f32x4, r);
+}
+__device__ __forceinline__ f32x4 gate_piece(f32x4 o, f32x4 g, float) {
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = o[e] * silu_f32(g[e]);
+  return r;
+}
 
 // Workgroup layout: 4 feature waves (featurize, score tiles, denominators, decay)
 // and NS state waves (value columns, state, read-out), the two roles one chunk
@@ -108,6 +126,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   __shared__ __align__(16) T sK0[FULL ? 16 * LDQ : 8];              // phi(k) of token tile 0, tile order
   __shared__ __align__(16) T sP[FULL ? C * LDC : 8];                 // masked decayed scores
   __shared__ __align__(16) T sO[FULL ? C * LDO : 8];                 // normalized output rows
+  __shared__ __align__(16) T sG[FULL ? C * DW : 8];                  // gate rows, in store-piece order
   __shared__ __align__(16) double sL[3][C];                 // inclusive log-decay prefix, float64
   __shared__ __align__(16) float seL[3][C];
   __shared__ __align__(16) float seK[3][C];
@@ -557,6 +576,22 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       const int ds = (int)((j + 2) % 3);
       // ---- half A: read-out of chunk j-1
       if (j >= 1) {
+        if constexpr (FULL) {
+          if (p.gate) {
+            // gate rows of chunk j-1 go straight to LDS (no registers held while the
+            // read-out runs); each lane later reads back the 16 bytes it brought in
+            constexpr int EP = 16 / (int)sizeof(T), PPR = DW / EP, NIT = C * PPR / (NS * 64);
+            const T *gb = (const T *)p.gate + b * p.sg_b + h * p.sg_h + ts * p.sg_t + half * DW;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+              const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+              if (ts + row < t1)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(gb + (int64_t)row * p.sg_t + pc * EP),
+                    (__attribute__((address_space(3))) void *)&sG[(it * NS + sw) * 64 * EP], 16, 0, 0);
+            }
+          }
+        }
         // v of chunk ts -> accumulator layout: lane (g, col n) holds v[16bt + 4g + r][n]
 #pragma unroll
         for (int jj = 0; jj < NTW; ++jj) {
@@ -630,16 +665,38 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           constexpr int NIT = C * PPR / (NS * 64);         // pieces per lane
           static_assert(NIT * NS * 64 == C * PPR, "whole rows per pass");
           T *ob = O + ts * p.so_t + half * DW;
-          f32x4 piece[NIT];
+          if (p.gate) {
+            // mixer gate: o * SiLU(g) on the rounded output, the gate rows from LDS;
+            // two pieces at a time so that the gate adds few live registers
+            constexpr int GB = NIT < 2 ? NIT : 2;
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
-            piece[it] = *reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]);
-          }
+            for (int i0 = 0; i0 < NIT; i0 += GB) {
+              f32x4 piece[GB];
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
-            if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[it];
+              for (int u = 0; u < GB; ++u) {
+                const int i = ((i0 + u) * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+                piece[u] = gate_piece(*reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]),
+                                      *reinterpret_cast<const f32x4 *>(&sG[i * EP]), T{});
+              }
+#pragma unroll
+              for (int u = 0; u < GB; ++u) {
+                const int i = ((i0 + u) * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+                if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[u];
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+            f32x4 piece[NIT];
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+              const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+              piece[it] = *reinterpret_cast<const f32x4 *>(&sO[row * LDO + pc * EP]);
+            }
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+              const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+              if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[it];
+            }
           }
         }
         if constexpr (DECAY) {

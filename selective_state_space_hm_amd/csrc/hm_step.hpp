@@ -20,6 +20,8 @@ struct StepParams {
   void *o;
   int64_t B, H;
   int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h, sw_h, sdt_b, sdt_h;
+  const void *gate;  // optional gate pre-activation [B, H, dv] (NULL = none)
+  int64_t sg_b, sg_h;
 };
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
@@ -137,7 +139,9 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
 #pragma unroll
     for (int i = 0; i < F / 4; ++i) den += sden[i];
     T *op = (T *)p.o + b * p.so_b + h * p.so_h;
-    op[tid] = to_elem<T>(nsum / den);
+    float o = nsum / den;
+    if (p.gate) o = (float)to_elem<T>(o) * silu_f32(ldf((const T *)p.gate + b * p.sg_b + h * p.sg_h + tid));
+    op[tid] = to_elem<T>(o);
   }
 }
 

@@ -41,7 +41,8 @@ class FwdArgs(C.Structure):
                 ("sq_b", i64), ("sq_h", i64), ("sq_t", i64), ("sk_b", i64), ("sk_h", i64), ("sk_t", i64),
                 ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
                 ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
-                ("workspace", p_void), ("workspace_bytes", C.c_size_t)]
+                ("workspace", p_void), ("workspace_bytes", C.c_size_t),
+                ("gate", p_void), ("sg_b", i64), ("sg_h", i64), ("sg_t", i64)]
 
 
 class StepArgs(C.Structure):
@@ -50,7 +51,8 @@ class StepArgs(C.Structure):
                 ("dtype", i32), ("reserved", i32),
                 ("B", i64), ("H", i64), ("d", i64), ("f", i64), ("dv", i64),
                 ("sq_b", i64), ("sq_h", i64), ("sk_b", i64), ("sk_h", i64), ("sv_b", i64), ("sv_h", i64),
-                ("so_b", i64), ("so_h", i64), ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64)]
+                ("so_b", i64), ("so_h", i64), ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64),
+                ("gate", p_void), ("sg_b", i64), ("sg_h", i64)]
 
 
 class HMError(RuntimeError):
@@ -175,11 +177,11 @@ def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Te
 
 
 def fwd_args(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
-             chunk=0, segments=0, dsplit=0) -> FwdArgs:
+             chunk=0, segments=0, dsplit=0, gate=None) -> FwdArgs:
     B, H, n, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
-    for t in (q, k, v, o):
+    for t in (q, k, v, o, gate):
         if t is not None and t.stride(3) != 1:
             raise ValueError("inner dimensions must be contiguous")
     return FwdArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
@@ -191,7 +193,9 @@ def fwd_args(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, 
                    so_b=o.stride(0) if o is not None else 0, so_h=o.stride(1) if o is not None else 0,
                    so_t=o.stride(2) if o is not None else 0, sw_h=_w_strides(w_q),
                    sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0,
-                   sdt_t=dt.stride(2) if dt is not None else 0)
+                   sdt_t=dt.stride(2) if dt is not None else 0, gate=_ptr(gate),
+                   sg_b=gate.stride(0) if gate is not None else 0, sg_h=gate.stride(1) if gate is not None else 0,
+                   sg_t=gate.stride(2) if gate is not None else 0)
 
 
 def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segments=0, dsplit=0, o=None):
@@ -202,16 +206,23 @@ def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segment
     return plan
 
 
+def _gate_shape(gate, v):
+    if gate is not None and (gate.shape != v.shape or gate.dtype != v.dtype):
+        raise ValueError("gate must have v's shape and dtype")
+
+
 def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
-                   chunk=0, segments=0, dsplit=0, workspace=None):
-    """Causal prefill.  Returns o [B, H, n, dv] (v's dtype).  s_final (if given) receives
-    the float32 state [B, H, F*dv + F] after the last token."""
-    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o)
+                   chunk=0, segments=0, dsplit=0, workspace=None, gate=None):
+    """Causal prefill.  Returns o [B, H, n, dv] (v's dtype), times SiLU(gate) when a
+    gate [B, H, n, dv] is given.  s_final (if given) receives the float32 state
+    [B, H, F*dv + F] after the last token."""
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
+    _gate_shape(gate, v)
     if dt is not None and dt.dtype != torch.float32 or a_log is not None and a_log.dtype != torch.float32:
         raise TypeError("dt and A_log are float32")
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
-    a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit)
+    a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit, gate)
     st, nbytes = call_workspace_size(a)
     _check(st)
     if nbytes:
@@ -223,10 +234,12 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     return o
 
 
-def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None):
+def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=None):
     """One decode token per (b, h): q, k [B, H, d], v [B, H, dv]; state [B, H, F*dv+F]
-    float32 is updated in place.  Returns o [B, H, dv]."""
-    _dev(q, k, v, w_q, w_k, state, dt, a_log, o)
+    float32 is updated in place.  Returns o [B, H, dv], times SiLU(gate) when a gate
+    [B, H, dv] is given."""
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate)
+    _gate_shape(gate, v)
     B, H, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
@@ -238,7 +251,11 @@ def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None):
                  state=_ptr(state), o=_ptr(o), dtype=_code(q), B=B, H=H, d=d, f=f, dv=dv,
                  sq_b=q.stride(0), sq_h=q.stride(1), sk_b=k.stride(0), sk_h=k.stride(1),
                  sv_b=v.stride(0), sv_h=v.stride(1), so_b=o.stride(0), so_h=o.stride(1), sw_h=_w_strides(w_q),
-                 sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0)
+                 sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0,
+                 gate=_ptr(gate), sg_b=gate.stride(0) if gate is not None else 0,
+                 sg_h=gate.stride(1) if gate is not None else 0)
+    if gate is not None and gate.stride(2) != 1:
+        raise ValueError("inner dimensions must be contiguous")
     _check(call_step(a, _stream()))
     return o
 

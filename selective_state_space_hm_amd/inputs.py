@@ -14,7 +14,10 @@ Recipe (every case):
     N(0, w_std^2) (w_std = 1 for the tiny case, 1/sqrt(d) otherwise);
   * dt ~ N(0, 1) float32 [B, H, n];
   * A_log float32 [H], uniform on [lo, hi]: [0, ln 16] for the Mamba-style
-    decay, [ln 2^-9, ln 2^-3] for the mild decay that keeps a_t near 0.99.
+    decay, [ln 2^-9, ln 2^-3] for the mild decay that keeps a_t near 0.99;
+  * the gate branch's pre-activation (when a case has one) comes from its own
+    generator, seeded with 7919 * (seed + 1), ~ N(0, 2^2) in o's shape, so that
+    both signs and the saturated ends of SiLU are exercised.
 
 The shapes follow the HedgeMamba mixer as the gsyq.cn explainer describes it
 (section 5.2: heads of width head_dim; Pythia-1B width H*d = 2048) and the
@@ -167,6 +170,12 @@ def decode_step_inputs(dc: DecodeCase, step: int, dtype=torch.bfloat16):
     v = _normal(g, (dc.B, dc.H, dc.dv)).to(dtype)
     dt = _normal(g, (dc.B, dc.H)) if dc.a_log is not None else None
     return q, k, v, dt
+
+
+def gate(shape, dtype=torch.bfloat16, seed=0, std=2.0):
+    """Gate pre-activation in o's shape (prefill [B, H, n, dv], decode [B, H, dv])."""
+    g = torch.Generator().manual_seed(7919 * (seed + 1))
+    return _normal(g, tuple(shape), std).to(dtype)
 
 
 def to_f64(t):

@@ -40,7 +40,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 1
+    assert hm.lib().hm_abi_version() == 2
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -91,6 +91,13 @@ def test_fwd_validation_errors():
     expect(hm.call_fwd(fwd(chunk=128)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(dsplit=3)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(segments=-2)), hm.HM_ERR_SHAPE)
+    G = A + 0xa000000
+    g = dict(sg_b=16 * 2048 * 128, sg_h=2048 * 128, sg_t=128)
+    expect(hm.call_fwd(fwd(gate=G + 8, **g)), hm.HM_ERR_ALIGN)
+    expect(hm.call_fwd(fwd(gate=G, **{**g, "sg_t": 132})), hm.HM_ERR_ALIGN)
+    expect(hm.call_fwd(fwd(gate=G, **{**g, "sg_h": -128})), hm.HM_ERR_SHAPE)
+    expect(hm.call_fwd(fwd(gate=G, B=0, **g)), hm.HM_OK)     # a read-only input: stride 0 (broadcast) is fine
+    expect(hm.call_fwd(fwd(gate=G, B=0, sg_b=0, sg_h=0, sg_t=0)), hm.HM_OK)
 
 
 def test_fwd_workspace_required_when_segmented():
@@ -169,6 +176,9 @@ def test_step_validation_errors():
     expect(hm.call_step(step(state=A + 8)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(sq_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(d=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(gate=A + 0xa000008, sg_b=16 * 128, sg_h=128)), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(gate=A + 0xa000000, sg_b=16 * 128, sg_h=100)), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(gate=A + 0xa000000, sg_b=-1, sg_h=128)), hm.HM_ERR_SHAPE)
     expect(hm.call_step(step(B=0)), hm.HM_OK)
 
 

@@ -241,3 +241,75 @@ def test_prefill_then_decode_handoff():
         torch.cuda.synchronize()
         ot, S, z = orc.step(S, z, f64(q), f64(k), f64(v), f64(c.w_q), f64(c.w_k), f64(dt), f64(c.a_log))
         assert report(f"prefill->decode step {t}", f64(o), ot) <= BF16_TOL
+
+
+# ------------------------------------------------------------------ gate branch
+def gated_oracle(case, gate, s_init=None, z_init=None):
+    return orc.forward(f64(case.q), f64(case.k), f64(case.v), f64(case.w_q), f64(case.w_k),
+                       f64(case.dt), f64(case.a_log), s_init, z_init, gate=f64(gate))
+
+
+@pytest.mark.parametrize("n", [1, 63, 200])
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (3, 1), (2, 2)])
+def test_gate_fp32(n, segments, dsplit):
+    c = inputs.small(n=n, decay="mild", dtype=torch.float32, d=32, f=16, dv=32, B=2, H=3, seed=n + 1)
+    gt = inputs.gate(c.v.shape, torch.float32, seed=n)
+    s_final = torch.empty((2, 3, hm.state_numel(16, 32)), device="cuda")
+    o = run_fwd(c, s_final=s_final, gate=gt.cuda(), segments=segments, dsplit=dsplit)
+    o_plain = run_fwd(c, segments=segments, dsplit=dsplit)
+    torch.cuda.synchronize()
+    ref, S, z = gated_oracle(c, gt)
+    assert report(f"gate fp32 n={n} segs={segments} dsplit={dsplit}", f64(o), ref) <= FP32_TOL
+    # the gate touches only the output: the state is the ungated one
+    Sg, zg = orc.unpack_state(f64(s_final), 32, 32)
+    assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
+    # and the gated output is the ungated one times SiLU(g), element by element
+    np.testing.assert_allclose(f64(o), f64(o_plain) * orc.silu(f64(gt)), rtol=2e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("shape", [(128, 64, 128), (64, 32, 64)])
+@pytest.mark.parametrize("decay", [None, "mamba"])
+def test_gate_bf16_ragged(shape, decay):
+    d, f, dv = shape
+    c = inputs.make_prefill("gb", 2, 3, 333, d, f, dv, torch.bfloat16, None, decay, seed=d + 3)
+    gt = inputs.gate(c.v.shape, torch.bfloat16, seed=d)
+    o = run_fwd(c, gate=gt.cuda())
+    torch.cuda.synchronize()
+    ref, _, _ = gated_oracle(c, gt)
+    assert report(f"gate bf16 d={d} f={f} dv={dv} decay={decay}", f64(o), ref) <= BF16_TOL
+
+
+def test_gate_strided_and_extreme():
+    """A gate handed over in [B, n, H, dv] memory, with saturating values (|g| up to 60)."""
+    c = inputs.make_prefill("gs", 2, 4, 150, 128, 64, 128, torch.bfloat16, None, "mild", seed=21)
+    gt = inputs.gate(c.v.shape, torch.float32, seed=5, std=20.0).to(torch.bfloat16)
+    gdev = gt.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    o = run_fwd(c, gate=gdev, segments=2, dsplit=2)
+    torch.cuda.synchronize()
+    ref, _, _ = gated_oracle(c, gt)
+    assert np.all(np.isfinite(f64(o)))
+    assert report("gate bf16 strided, std 20", f64(o), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype,shape", [(torch.float32, (32, 16, 32)), (torch.bfloat16, (128, 64, 128))])
+def test_gate_decode_steps(dtype, shape):
+    d, f, dv = shape
+    B, H, steps = 3, 2, 12
+    dc = inputs.decode_setup(B, H, d, f, dv, prefix=40, steps=steps, decay=True, dtype=dtype, seed=d + 1)
+    pk = orc.hedgehog_features(f64(dc.prefix_k), f64(dc.w_k))
+    S, z = orc.prefix_state(pk, f64(dc.prefix_v), orc.log_decay(f64(dc.prefix_dt), f64(dc.a_log)))
+    state = torch.tensor(orc.pack_state(S, z), dtype=torch.float32, device="cuda")
+    wq, wk, a_log = dc.w_q.cuda(), dc.w_k.cuda(), dc.a_log.cuda()
+    worst = 0.0
+    for t in range(steps):
+        q, k, v, dt = inputs.decode_step_inputs(dc, t, dtype)
+        gt = inputs.gate(v.shape, dtype, seed=100 + t)
+        o = hm.hm_linattn_step(q.cuda(), k.cuda(), v.cuda(), wq, wk, state, dt.cuda(), a_log, gate=gt.cuda())
+        torch.cuda.synchronize()
+        ot, S, z = orc.step(S, z, f64(q), f64(k), f64(v), f64(dc.w_q), f64(dc.w_k), f64(dt), f64(dc.a_log),
+                            gate=f64(gt))
+        worst = max(worst, rel_l2(f64(o), ot))
+    print(f"[parity] gated decode {dtype} {shape}: worst step rel-L2 {worst:.3e}", flush=True)
+    assert worst <= tol_for(dtype)
+    Sg, _ = orc.unpack_state(f64(state), 2 * f, dv)
+    assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)
