@@ -22,6 +22,9 @@ What is computed, per (batch b, head h), for tokens t = 0..n-1:
   S_t = a_t S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t)
   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t                          [LA parts 2-3, 4.3; HM §2.3]
   optionally o_t <- o_t * SiLU(g_t) with the gate branch's g    [HM §5.2 step 6]
+and, as a separate step ahead of the featurizer, Mamba's short causal conv
+(depthwise over time, K taps per channel, identity at the stage-1 init)
+[HM §2.2, §2.3 item 4, §3.1].
 S_{-1}, z_{-1} are the given initial state (zeros when absent); a_t scales the
 carried state only, never the current token (the RetNet form, [LA] 4.3).
 
@@ -204,6 +207,39 @@ def apply_gate(o, gate):
     if gate is None:
         return o
     return o * silu(gate)
+
+
+# --------------------------------------------------------------------------
+# Short causal conv of the mixer  [HM §2.2 (local mixing by a light conv),
+# §2.3 item 4 (kept in HedgeMamba), §3.1 (init: taps [0, ..., 0, 1], bias 0)]
+# --------------------------------------------------------------------------
+def causal_conv(x, w, bias=None, prev=None):
+    """Depthwise causal convolution over the token axis.
+
+    x [B,H,n,d]; w [d,K] (one set of K taps per channel, shared by the heads) or
+    [H,d,K]; bias [d] or [H,d] or None; prev [B,H,K-1,d] = the K-1 input rows that
+    precede token 0 (None = zeros).  Tap K-1 multiplies the current token, tap j
+    the token K-1-j steps earlier:
+        y_t[c] = bias[c] + sum_j w[c, j] * x_{t-K+1+j}[c].
+    Returns (y [B,H,n,d], final [B,H,K-1,d]) where final holds the last K-1 rows
+    of the stream prev ++ x, i.e. the prev of a call that continues the sequence.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, H, n, d = x.shape
+    K = w.shape[-1]
+    wh = np.broadcast_to(w if w.ndim == 3 else w[None], (H, d, K))
+    if prev is None:
+        prev = np.zeros((B, H, K - 1, d))
+    stream = np.concatenate([np.asarray(prev, dtype=np.float64), x], axis=2)  # row K-1+t is token t
+    y = np.zeros((B, H, n, d))
+    if bias is not None:
+        bh = np.asarray(bias, dtype=np.float64)
+        y += (bh if bh.ndim == 2 else bh[None])[None, :, None, :]
+    for j in range(K):
+        # stream rows j .. j+n-1 are tokens t-K+1+j for t = 0..n-1
+        y += wh[None, :, None, :, j] * stream[:, :, j:j + n, :]
+    return y, stream[:, :, n:n + K - 1, :].copy()
 
 
 # --------------------------------------------------------------------------

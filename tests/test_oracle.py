@@ -410,3 +410,63 @@ def test_planted_mistakes_are_caught():
     u = x @ w
     bad = scipy.special.softmax(np.concatenate([u, u], -1), axis=-1)
     assert not np.allclose(bad[0], golden()["features_rational"]["phi"])
+
+
+# ------------------------------------------------------------ short causal conv
+def test_conv_identity_init_is_the_identity():
+    """[HM] §3.1: taps [0, ..., 0, 1] with zero bias pass the input through."""
+    x = np.random.default_rng(0).normal(size=(2, 3, 11, 8))
+    for K in (1, 2, 3, 4):
+        w = np.zeros((8, K))
+        w[:, -1] = 1.0
+        y, fin = orc.causal_conv(x, w, np.zeros(8))
+        assert np.array_equal(y, x)
+        if K > 1:
+            assert np.array_equal(fin, x[:, :, -(K - 1):])
+
+
+def test_conv_matches_numpy_convolve_per_channel():
+    r = np.random.default_rng(1)
+    x = r.normal(size=(1, 2, 13, 5))
+    w = r.normal(size=(2, 5, 4))          # per-head taps
+    b = r.normal(size=(2, 5))
+    y, _ = orc.causal_conv(x, w, b)
+    for h in range(2):
+        for c in range(5):
+            ref = np.convolve(x[0, h, :, c], w[h, c, ::-1])[:13] + b[h, c]
+            np.testing.assert_allclose(y[0, h, :, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_single_tap_delays():
+    """A single tap at position K-1-s delays the stream by s tokens, prev first."""
+    r = np.random.default_rng(2)
+    x = r.normal(size=(2, 1, 9, 4))
+    prev = r.normal(size=(2, 1, 3, 4))
+    for s_ in range(4):
+        w = np.zeros((4, 4))
+        w[:, 3 - s_] = 1.0
+        y, _ = orc.causal_conv(x, w, None, prev)
+        stream = np.concatenate([prev, x], axis=2)
+        np.testing.assert_array_equal(y, stream[:, :, 3 - s_:3 - s_ + 9])
+
+
+def test_conv_is_causal_and_splits():
+    r = np.random.default_rng(3)
+    x = r.normal(size=(1, 2, 30, 6))
+    w = r.normal(size=(6, 4))
+    b = r.normal(size=6)
+    prev = r.normal(size=(1, 2, 3, 6))
+    y, fin = orc.causal_conv(x, w, b, prev)
+    x2 = x.copy()
+    x2[:, :, 17] += 5.0
+    y2, _ = orc.causal_conv(x2, w, b, prev)
+    np.testing.assert_array_equal(y2[:, :, :17], y[:, :, :17])
+    assert np.all(y2[:, :, 17:21] != y[:, :, 17:21]) and np.array_equal(y2[:, :, 21:], y[:, :, 21:])
+    for m in (0, 1, 2, 5, 29):
+        ya, fa = orc.causal_conv(x[:, :, :m], w, b, prev)
+        yb, fb = orc.causal_conv(x[:, :, m:], w, b, fa)
+        np.testing.assert_allclose(np.concatenate([ya, yb], axis=2), y, rtol=1e-14, atol=1e-14)
+        np.testing.assert_array_equal(fb, fin)
+    # a stream shorter than the window: final mixes prev and x
+    _, f1 = orc.causal_conv(x[:, :, :1], w, b, prev)
+    np.testing.assert_array_equal(f1, np.concatenate([prev[:, :, 1:], x[:, :, :1]], axis=2))
