@@ -256,7 +256,29 @@ def main():
                       "tokens_per_s": tokens / (msg * 1e-3), "achieved_GBs": bg / (msg * 1e-3) / 1e9,
                       "hbm_frac": bg / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "plan": {"chunk": plan[0], "segments": plan[1], "dsplit": plan[2]}})
-        del gate
+        # the mixer's short causal conv (K = 4) on q, alone and as part of the
+        # stage-2 chain conv(q), conv(k) -> gated prefill
+        cw = (torch.randn((d, 4), generator=torch.Generator().manual_seed(1)) / 2).to(dev)
+        qc, kc = torch.empty_like(g["q"]), torch.empty_like(g["k"])
+
+        def stepc():
+            hm.hm_causal_conv(g["q"], cw, y=qc)
+
+        msc, _ = time_launches(stepc, 50, 200, torch)
+        bc = 2 * B * H * n * d * 2 + d * 4 * 4
+        extra.append({"workload": f"short causal conv K=4 over q, B={B} H={H} n={n} d={d} bf16", "ms": msc,
+                      "achieved_GBs": bc / (msc * 1e-3) / 1e9, "hbm_frac": bc / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "kernel": "hm::conv_kernel<bf16,4>", "algorithmic_bytes_per_launch": bc})
+
+        def stepm():
+            hm.hm_causal_conv(g["q"], cw, y=qc)
+            hm.hm_causal_conv(g["k"], cw, y=kc)
+            hm.hm_linattn_fwd(qc, kc, g["v"], g["w_q"], g["w_k"], o=o, workspace=ws, gate=gate)
+
+        msm, _ = time_launches(stepm, 50, 200, torch)
+        extra.append({"workload": f"stage-2 mixer chain: conv(q), conv(k), gated prefill, B={B} H={H} n={n}",
+                      "ms": msm, "tokens_per_s": tokens / (msm * 1e-3)})
+        del gate, qc, kc
     del g, o
 
     if not args.no_extra:

@@ -181,11 +181,50 @@ typedef struct {
 
 hm_status hm_linattn_step(const hm_linattn_step_args *args, void *stream);
 
+/*
+ * hm_causal_conv — the mixer's short causal convolution ([HM] §2.2: Mamba's light
+ * conv mixes neighbouring tokens; §2.3 item 4: HedgeMamba keeps it; §3.1: taps
+ * [0, ..., 0, 1] and zero bias make it the identity at the stage-1 init).  Applied
+ * to q and to k ahead of hm_linattn_fwd / hm_linattn_step, one call per tensor.
+ * Depthwise over the token axis, K = width taps per channel:
+ *   y[b,h,t,c] = bias[c] + sum_{j<K} w[c][j] * x[b,h,t-K+1+j,c]
+ * where rows t < 0 come from `prev` (the K-1 rows before token 0; NULL = zeros).
+ *   x, y: [B, H, n, d] in `dtype` (strides s*_b, s*_h, s*_t); y must not overlap x,
+ *   prev or final_rows.
+ *   w: float32 [d][K] (each channel's K taps, tap K-1 on the current token), head
+ *   stride sw_h (0 = shared by the heads); bias: float32 [d] (head stride sb_h) or
+ *   NULL.
+ *   prev, final_rows: [B, H, K-1, d] in `dtype`, contiguous, optional.  final_rows
+ *   receives the last K-1 rows of the stream prev ++ x (the prev of a call that
+ *   continues the sequence); it may be the same buffer as prev, so a decode step
+ *   (n = 1) keeps its conv state in place.  With n = 0 only final_rows is written
+ *   and x, y, w may be NULL.
+ * Products and sums in float32, y rounded to `dtype` to nearest even.
+ * Built: width 1..4; d times the element size a multiple of 16 bytes; one thread
+ * per 8 tokens and 16 bytes of channels, fewer than 2^31 threads (B*H*n*d below
+ * about 2^37 elements for bf16, 2^36 for f32).
+ */
+typedef struct {
+  const void *x;
+  void *y;
+  const float *w, *bias;
+  const void *prev;
+  void *final_rows;
+  int32_t dtype;
+  int32_t width;
+  int64_t B, H, n, d;
+  int64_t sx_b, sx_h, sx_t;
+  int64_t sy_b, sy_h, sy_t;
+  int64_t sw_h, sb_h;
+} hm_causal_conv_args;
+
+hm_status hm_causal_conv(const hm_causal_conv_args *args, void *stream);
+
 const char *hm_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char *hm_last_error_message(void);
 int hm_abi_version(void);
-/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step), for bindings. */
+/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step, 3: causal conv), for bindings. */
 size_t hm_args_size(int which);
 
 #ifdef __cplusplus

@@ -2,6 +2,8 @@
 // any HIP call), plan selection, launch-table lookup and launches.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -329,6 +331,69 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   return check_launch("decode step");
 }
 
+// ------------------------------------------------------------------ short conv
+hm_status hm_causal_conv(const hm_causal_conv_args *a, void *stream) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->width <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, width >= 1");
+  if (a->width > 4) return fail(HM_ERR_UNSUPPORTED, "width %d: 1 to 4 taps are built", a->width);
+  const int64_t BH = a->B * a->H;
+  const size_t es = esize(a->dtype);
+  if (BH > 0 && a->n > 0 && (!a->x || !a->y || !a->w)) return fail(HM_ERR_NULL, "x, y and w must be non-NULL");
+  const int64_t strides[] = {a->sx_b, a->sx_h, a->sx_t, a->sy_b, a->sy_h, a->sy_t, a->sw_h, a->sb_h};
+  for (int64_t s : strides)
+    if (s < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->n > 1 && a->sy_t < a->d) return fail(HM_ERR_SHAPE, "token stride of y smaller than the row length (rows overlap)");
+  if (((size_t)a->d * es) % 16) return fail(HM_ERR_UNSUPPORTED, "d times the element size must be a multiple of 16 bytes");
+  if (!aligned16(a->x) || !aligned16(a->y) || !aligned16(a->w) || !aligned16(a->prev) || !aligned16(a->final_rows))
+    return fail(HM_ERR_ALIGN, "x, y, w, prev and final_rows must be 16-byte aligned");
+  if (((uintptr_t)a->bias & 3) != 0) return fail(HM_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (!stride_ok(a->sx_b, a->dtype) || !stride_ok(a->sx_h, a->dtype) || !stride_ok(a->sx_t, a->dtype) ||
+      !stride_ok(a->sy_b, a->dtype) || !stride_ok(a->sy_h, a->dtype) || !stride_ok(a->sy_t, a->dtype) ||
+      ((size_t)a->sw_h * 4) % 16)
+    return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  if (BH == 0) return ok();
+  // byte ranges: y must not overlap an input; final_rows is prev itself or apart from it
+  auto span = [&](const void *p, int64_t sb, int64_t sh, int64_t st, int64_t rows) {
+    const char *lo = (const char *)p;
+    const int64_t last = (a->B - 1) * sb + (a->H - 1) * sh + (rows - 1) * st + a->d;
+    return std::make_pair(lo, lo + (size_t)last * es);
+  };
+  auto apart = [](std::pair<const char *, const char *> u, std::pair<const char *, const char *> v) {
+    return u.second <= v.first || v.second <= u.first;
+  };
+  const int64_t R = a->width - 1, blk = R * a->d;
+  if (a->n > 0) {
+    const auto ys = span(a->y, a->sy_b, a->sy_h, a->sy_t, a->n);
+    if (!apart(ys, span(a->x, a->sx_b, a->sx_h, a->sx_t, a->n))) return fail(HM_ERR_SHAPE, "y overlaps x");
+    if (R > 0 && a->prev && !apart(ys, span(a->prev, a->H * blk, blk, a->d, R))) return fail(HM_ERR_SHAPE, "y overlaps prev");
+    if (R > 0 && a->final_rows && !apart(ys, span(a->final_rows, a->H * blk, blk, a->d, R)))
+      return fail(HM_ERR_SHAPE, "y overlaps final_rows");
+  }
+  if (R > 0 && a->prev && a->final_rows && a->prev != a->final_rows &&
+      !apart(span(a->prev, a->H * blk, blk, a->d, R), span(a->final_rows, a->H * blk, blk, a->d, R)))
+    return fail(HM_ERR_SHAPE, "final_rows overlaps prev without being the same buffer");
+  const hm::ConvTable ct = hm::table_conv();
+  const hm::ConvEntry *e = nullptr;
+  for (int i = 0; i < ct.nconv; ++i)
+    if (ct.conv[i].dtype == a->dtype && ct.conv[i].width == a->width) e = &ct.conv[i];
+  if (!e) return fail(HM_ERR_UNSUPPORTED, "no conv kernel for dtype=%d width=%d", a->dtype, a->width);
+  if (a->n == 0 && (R == 0 || !a->final_rows)) return ok();
+  hm::ConvParams p{};
+  p.x = a->x; p.y = a->y; p.w = a->w; p.bias = a->bias; p.prev = R > 0 ? a->prev : nullptr;
+  p.fin = R > 0 ? a->final_rows : nullptr;
+  p.B = a->B; p.H = a->H; p.n = a->n; p.d = a->d;
+  p.sx_b = a->sx_b; p.sx_h = a->sx_h; p.sx_t = a->sx_t;
+  p.sy_b = a->sy_b; p.sy_h = a->sy_h; p.sy_t = a->sy_t; p.sw_h = a->sw_h; p.sb_h = a->sb_h;
+  p.runs = a->n > 0 ? (a->n + hm::CONV_RUN - 1) / hm::CONV_RUN : 1;
+  p.groups = (int64_t)((size_t)a->d * es / 16);
+  const int64_t threads = BH * p.runs * p.groups;
+  if (threads >= (int64_t)1 << 31) return fail(HM_ERR_UNSUPPORTED, "B*H*n*d too large: more than 2^31 conv threads");
+  e->launch(p, dim3((unsigned)((threads + 255) / 256)), (hipStream_t)stream);
+  return check_launch("causal conv");
+}
+
 // ------------------------------------------------------------------ featurize
 hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
   if (!a) return fail(HM_ERR_NULL, "args is NULL");
@@ -385,6 +450,7 @@ size_t hm_args_size(int which) {
     case 0: return sizeof(hm_featurize_args);
     case 1: return sizeof(hm_linattn_fwd_args);
     case 2: return sizeof(hm_linattn_step_args);
+    case 3: return sizeof(hm_causal_conv_args);
     default: return 0;
   }
 }

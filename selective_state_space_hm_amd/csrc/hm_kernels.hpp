@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "hm_conv.hpp"
 #include "hm_prefill.hpp"
 #include "hm_step.hpp"
 
@@ -30,7 +31,17 @@ struct Table {
   int nfeat;
 };
 
+struct ConvEntry {
+  int dtype, width;
+  void (*launch)(const ConvParams &, dim3 grid, hipStream_t);
+};
+struct ConvTable {
+  const ConvEntry *conv;
+  int nconv;
+};
+
 // one per kernel translation unit
+ConvTable table_conv();
 Table table_fwd_bf16();
 Table table_fwd_bf16_decay();
 Table table_fwd_f32();
@@ -43,6 +54,10 @@ void launch_fwd(const FwdParams &p, unsigned grid, hipStream_t s) {
 template <typename T, int DK, int FH, int DV, bool DECAY>
 void launch_step(const StepParams &p, unsigned grid, hipStream_t s) {
   hipLaunchKernelGGL((step_kernel<T, DK, FH, DV, DECAY>), dim3(grid), dim3(256), 0, s, p);
+}
+template <typename T, int K>
+void launch_conv(const ConvParams &p, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((conv_kernel<T, K>), grid, dim3(256), 0, s, p);
 }
 template <typename T, typename TO, int DK, int FH>
 void launch_feat(const FeatParams &p, dim3 grid, hipStream_t s) {

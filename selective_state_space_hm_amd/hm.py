@@ -55,6 +55,14 @@ class StepArgs(C.Structure):
                 ("gate", p_void), ("sg_b", i64), ("sg_h", i64)]
 
 
+class ConvArgs(C.Structure):
+    _fields_ = [("x", p_void), ("y", p_void), ("w", p_void), ("bias", p_void), ("prev", p_void),
+                ("final_rows", p_void), ("dtype", i32), ("width", i32),
+                ("B", i64), ("H", i64), ("n", i64), ("d", i64),
+                ("sx_b", i64), ("sx_h", i64), ("sx_t", i64), ("sy_b", i64), ("sy_h", i64), ("sy_t", i64),
+                ("sw_h", i64), ("sb_h", i64)]
+
+
 class HMError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{status_string(status)}: {message}")
@@ -63,7 +71,7 @@ class HMError(RuntimeError):
 
 _lib = None
 EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
-           "hm_linattn_step", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
+           "hm_linattn_step", "hm_causal_conv", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
 
 
 def lib():
@@ -78,8 +86,9 @@ def lib():
         L.hm_linattn_fwd_plan.argtypes = [C.POINTER(FwdArgs), C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)]
         L.hm_linattn_fwd.argtypes = [C.POINTER(FwdArgs), p_void]
         L.hm_linattn_step.argtypes = [C.POINTER(StepArgs), p_void]
+        L.hm_causal_conv.argtypes = [C.POINTER(ConvArgs), p_void]
         for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
-                   "hm_linattn_step"):
+                   "hm_linattn_step", "hm_causal_conv"):
             getattr(L, fn).restype = C.c_int
         L.hm_status_string.argtypes = [C.c_int]
         L.hm_status_string.restype = C.c_char_p
@@ -128,6 +137,10 @@ def call_plan(args: FwdArgs):
 
 def call_step(args: StepArgs, stream=None) -> int:
     return lib().hm_linattn_step(C.byref(args), stream)
+
+
+def call_conv(args: ConvArgs, stream=None) -> int:
+    return lib().hm_causal_conv(C.byref(args), stream)
 
 
 # ------------------------------------------------------------ torch-facing
@@ -258,6 +271,36 @@ def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=
         raise ValueError("inner dimensions must be contiguous")
     _check(call_step(a, _stream()))
     return o
+
+
+def hm_causal_conv(x, w, bias=None, prev=None, final_rows=None, y=None):
+    """Short causal conv over the token axis of x [B, H, n, d]: w float32 [d, K]
+    (or [H, d, K]), bias float32 [d] (or [H, d]) or None; prev [B, H, K-1, d] the rows
+    before token 0 (None = zeros); final_rows [B, H, K-1, d] (optional, may be prev)
+    receives the last K-1 rows of prev ++ x.  Returns y (x's shape and dtype)."""
+    _dev(x, w, bias, prev, final_rows, y)
+    B, H, n, d = x.shape
+    K = w.shape[-1]
+    if w.dtype != torch.float32 or (bias is not None and bias.dtype != torch.float32):
+        raise TypeError("conv taps and bias are float32")
+    if w.shape[-2] != d or w.stride(-1) != 1 or w.stride(-2) != K:
+        raise ValueError("w must be [d, K] (or [H, d, K]) with contiguous rows")
+    for t in (prev, final_rows):
+        if t is not None and (tuple(t.shape) != (B, H, K - 1, d) or not t.is_contiguous() or t.dtype != x.dtype):
+            raise ValueError("prev and final_rows are contiguous [B, H, K-1, d] in x's dtype")
+    if bias is not None and bias.stride(-1) != 1:
+        raise ValueError("bias must be contiguous along d")
+    if y is None:
+        y = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    if x.stride(3) != 1 or y.stride(3) != 1:
+        raise ValueError("inner dimensions must be contiguous")
+    a = ConvArgs(x=_ptr(x), y=_ptr(y), w=_ptr(w), bias=_ptr(bias), prev=_ptr(prev), final_rows=_ptr(final_rows),
+                 dtype=_code(x), width=K, B=B, H=H, n=n, d=d,
+                 sx_b=x.stride(0), sx_h=x.stride(1), sx_t=x.stride(2), sy_b=y.stride(0), sy_h=y.stride(1),
+                 sy_t=y.stride(2), sw_h=w.stride(0) if w.dim() == 3 else 0,
+                 sb_h=bias.stride(0) if bias is not None and bias.dim() == 2 else 0)
+    _check(call_conv(a, _stream()))
+    return y
 
 
 def state_numel(f: int, dv: int) -> int:

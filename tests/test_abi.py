@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     L = hm.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -36,7 +36,8 @@ def test_struct_layouts_match_binding():
     assert L.hm_args_size(0) == C.sizeof(hm.FeaturizeArgs)
     assert L.hm_args_size(1) == C.sizeof(hm.FwdArgs)
     assert L.hm_args_size(2) == C.sizeof(hm.StepArgs)
-    assert L.hm_args_size(3) == 0
+    assert L.hm_args_size(3) == C.sizeof(hm.ConvArgs)
+    assert L.hm_args_size(4) == 0
 
 
 def test_version_and_status_strings():
@@ -200,6 +201,37 @@ def test_featurize_validation_errors():
     expect(hm.call_featurize(feat(x=A + 6)), hm.HM_ERR_ALIGN)
     expect(hm.call_featurize(feat(d=24)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_featurize(feat(n=0)), hm.HM_OK)
+
+
+def conv(B=2, H=16, n=2048, d=128, width=4, dtype=hm.HM_BF16, **kw):
+    a = hm.ConvArgs(x=A, y=A + 0x1000000, w=A + 0x2000000, bias=A + 0x2100000, dtype=dtype, width=width,
+                    B=B, H=H, n=n, d=d, sx_b=H * n * d, sx_h=n * d, sx_t=d, sy_b=H * n * d, sy_h=n * d, sy_t=d)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_conv_validation_errors():
+    L = hm.lib()
+    expect(L.hm_causal_conv(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_conv(conv(w=None)), hm.HM_ERR_NULL)
+    expect(hm.call_conv(conv(dtype=4)), hm.HM_ERR_DTYPE)
+    expect(hm.call_conv(conv(width=0)), hm.HM_ERR_SHAPE)
+    expect(hm.call_conv(conv(width=5)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_conv(conv(n=-3)), hm.HM_ERR_SHAPE)
+    expect(hm.call_conv(conv(sy_t=64)), hm.HM_ERR_SHAPE)               # rows of y overlap
+    expect(hm.call_conv(conv(d=12)), hm.HM_ERR_UNSUPPORTED)            # 24 bytes per row
+    expect(hm.call_conv(conv(x=A + 8)), hm.HM_ERR_ALIGN)
+    expect(hm.call_conv(conv(bias=A + 2)), hm.HM_ERR_ALIGN)
+    expect(hm.call_conv(conv(sw_h=127)), hm.HM_ERR_ALIGN)
+    expect(hm.call_conv(conv(sx_t=132)), hm.HM_ERR_ALIGN)
+    expect(hm.call_conv(conv(y=A + 0x100)), hm.HM_ERR_SHAPE)           # y overlaps x
+    expect(hm.call_conv(conv(prev=A + 0x3000000, final_rows=A + 0x3000100)), hm.HM_ERR_SHAPE)
+    expect(hm.call_conv(conv(B=0)), hm.HM_OK)
+    expect(hm.call_conv(conv(n=0)), hm.HM_OK)                           # nothing to write
+    expect(hm.call_conv(conv(n=0, width=1, final_rows=A + 0x3000000)), hm.HM_OK)
+    expect(hm.call_conv(conv(n=0, x=None, y=None, w=None)), hm.HM_OK)  # nothing is read
+    expect(hm.call_conv(conv(n=1, y=None)), hm.HM_ERR_NULL)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

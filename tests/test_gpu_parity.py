@@ -313,3 +313,101 @@ def test_gate_decode_steps(dtype, shape):
     assert worst <= tol_for(dtype)
     Sg, _ = orc.unpack_state(f64(state), 2 * f, dv)
     assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)
+
+
+# ------------------------------------------------------------------ short causal conv
+def conv_inputs(B, H, n, d, K, dtype, seed, per_head=False, with_prev=True):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((B, H, n, d), generator=g).to(dtype)
+    w = torch.randn(((H, d, K) if per_head else (d, K)), generator=g) / K
+    bias = torch.randn(((H, d) if per_head else (d,)), generator=g) / 4
+    prev = torch.randn((B, H, K - 1, d), generator=g).to(dtype) if with_prev and K > 1 else None
+    return x, w, bias, prev
+
+
+def check_conv(got, ref, dtype, name):
+    r = report(name, got, ref)
+    if dtype == torch.float32:
+        assert r <= FP32_TOL
+    else:
+        # one rounding of a float32 sum to bf16: within 2^-8 relative of the exact value
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 100])
+def test_conv_against_oracle(dtype, K, n):
+    x, w, bias, prev = conv_inputs(2, 3, n, 64, K, dtype, seed=10 * K + n, per_head=(n % 2 == 1))
+    fin = torch.full((2, 3, K - 1, 64), float("nan"), dtype=dtype, device="cuda") if K > 1 else None
+    y = hm.hm_causal_conv(x.cuda(), w.cuda(), bias.cuda(), None if prev is None else prev.cuda(), fin)
+    torch.cuda.synchronize()
+    ref, rfin = orc.causal_conv(f64(x), f64(w), f64(bias), f64(prev))
+    check_conv(f64(y), ref, dtype, f"conv {dtype} K={K} n={n}")
+    if K > 1:
+        assert np.array_equal(f64(fin), rfin)          # rows are copied, bit for bit
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_conv_identity_init_is_exact(dtype):
+    x, _, _, _ = conv_inputs(2, 4, 70, 128, 4, dtype, seed=3)
+    w = torch.zeros((128, 4))
+    w[:, 3] = 1.0
+    y = hm.hm_causal_conv(x.cuda(), w.cuda(), torch.zeros(128).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(y.cpu(), x)
+
+
+def test_conv_decode_in_place_matches_prefill():
+    """n=1 steps with prev and final_rows the same buffer reproduce one long call."""
+    B, H, n, d, K = 3, 2, 40, 128, 4
+    x, w, bias, prev = conv_inputs(B, H, n, d, K, torch.bfloat16, seed=8)
+    xd, wd, bd = x.cuda(), w.cuda(), bias.cuda()
+    y_all = hm.hm_causal_conv(xd, wd, bd, prev.cuda())
+    state = prev.cuda().clone()
+    ys = []
+    for t in range(n):
+        ys.append(hm.hm_causal_conv(xd[:, :, t:t + 1], wd, bd, state, state))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(ys, dim=2), y_all)
+    assert torch.equal(state.cpu(), x[:, :, n - 3:])
+    # split handoff through a separate final buffer, n = 0 call included
+    fin = torch.empty_like(state)
+    y1 = hm.hm_causal_conv(xd[:, :, :23], wd, bd, prev.cuda(), fin)
+    fin0 = torch.empty_like(state)
+    hm.hm_causal_conv(xd[:, :, 23:23], wd, bd, fin, fin0)
+    y2 = hm.hm_causal_conv(xd[:, :, 23:], wd, bd, fin0)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([y1, y2], dim=2), y_all)
+
+
+def test_conv_full_size_strided():
+    """q of the B=8 H=16 n=2048 d=128 layer in [B, n, H, d] memory, per-head taps."""
+    c = inputs.pythia1b()
+    g = torch.Generator().manual_seed(4)
+    w = torch.randn((16, 128, 4), generator=g) / 2
+    bias = torch.randn((16, 128), generator=g) / 4
+    xs = c.q.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    fin = torch.empty((8, 16, 3, 128), dtype=torch.bfloat16, device="cuda")
+    y = hm.hm_causal_conv(xs, w.cuda(), bias.cuda(), None, fin)
+    torch.cuda.synchronize()
+    ref, rfin = orc.causal_conv(f64(c.q), f64(w), f64(bias))
+    check_conv(f64(y), ref, torch.bfloat16, "conv full size, [B,n,H,d] layout")
+    assert np.array_equal(f64(fin), rfin)
+
+
+def test_mixer_path_conv_then_gated_attention():
+    """conv(q), conv(k) -> prefill with the gate, against the oracle's same chain."""
+    c = inputs.make_prefill("mx", 2, 3, 200, 128, 64, 128, torch.bfloat16, None, "mamba", seed=31)
+    g = torch.Generator().manual_seed(6)
+    wq, wk = torch.randn((128, 4), generator=g) / 2, torch.randn((128, 4), generator=g) / 2
+    gt = inputs.gate(c.v.shape, torch.bfloat16, seed=31)
+    d = to_dev(c)
+    qc = hm.hm_causal_conv(d["q"], wq.cuda())
+    kc = hm.hm_causal_conv(d["k"], wk.cuda())
+    o = hm.hm_linattn_fwd(qc, kc, d["v"], d["w_q"], d["w_k"], d["dt"], d["a_log"], gate=gt.cuda())
+    torch.cuda.synchronize()
+    qr, _ = orc.causal_conv(f64(c.q), f64(wq))
+    kr, _ = orc.causal_conv(f64(c.k), f64(wk))
+    ref, _, _ = orc.forward(qr, kr, f64(c.v), f64(c.w_q), f64(c.w_k), f64(c.dt), f64(c.a_log), gate=f64(gt))
+    assert report("mixer path: conv + gated attention", f64(o), ref) <= BF16_TOL
