@@ -342,6 +342,22 @@ def bench_decode(torch, hm, inputs, dev, ws):
     torch.cuda.synchronize()
     ms_all, _ = time_launches(run_all, 1, 0, torch)
     ms = ms_all / dc.steps
+    # the stage-2 step: q, k through the fused short conv (K = 4), output gated
+    g2 = torch.Generator().manual_seed(3)
+    cw = [(torch.randn((dc.d, 4), generator=g2) / 2).to(dev) for _ in range(2)]
+    cst = [torch.zeros((dc.B, dc.H, 3, dc.d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    G = (torch.randn((dc.steps, dc.B, dc.H, dc.dv), generator=g2)).to(torch.bfloat16).to(dev)
+
+    def run_all2():
+        for t in range(dc.steps):
+            hm.hm_linattn_step(Q[t], K[t], V[t], wq, wk, state, DT[t], a_log, o=O[t], gate=G[t],
+                               conv=(cw[0], cw[1], None, None, cst[0], cst[1]))
+
+    state.copy_(base)
+    run_all2()
+    state.copy_(base)
+    torch.cuda.synchronize()
+    ms2 = time_launches(run_all2, 1, 0, torch)[0] / dc.steps
     F = 2 * dc.f
     per_bh = 2 * (F * dc.dv + F) * 4 + 2 * (2 * dc.d + 2 * dc.dv) + 4
     nbytes = dc.B * dc.H * per_bh + 2 * dc.d * dc.f * 2
@@ -351,7 +367,10 @@ def bench_decode(torch, hm, inputs, dev, ws):
             "tokens_per_s": dc.B / (ms * 1e-3), "ms_per_step": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": hbm_traffic("decode_bytes_per_launch"),
-                         "kernel": "hm::step_kernel<bf16,128,64,128,true>", "algorithmic_bytes_per_launch": nbytes}}
+                         "kernel": "hm::step_kernel<bf16,128,64,128,true>", "algorithmic_bytes_per_launch": nbytes},
+            "stage2_step": {"workload": "same steps with q, k through the fused short conv (K=4, state in place) "
+                                        "and the output gated", "ms_per_step": ms2,
+                            "tokens_per_s": dc.B / (ms2 * 1e-3)}}
 
 
 if __name__ == "__main__":

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 2
+#define HM_ABI_VERSION 3
 
 typedef enum {
   HM_OK = 0,
@@ -163,6 +163,13 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
  *   dt: [B, H] float32 (strides sdt_b, sdt_h) or NULL; state: see above.
  *   gate: optional [B, H, dv] in `dtype` (strides sg_b, sg_h): o_t is multiplied
  *   by SiLU(gate) (NULL = no gate).
+ *   conv_width: 0 = no conv; 1..4 = q_t and k_t first pass through the mixer's
+ *   short causal conv, exactly as hm_causal_conv with n = 1 would compute it (same
+ *   order of operations, result rounded to `dtype`), with taps conv_wq / conv_wk
+ *   float32 [d][K] (head stride scw_h), bias conv_bq / conv_bk float32 [d] (head
+ *   stride scb_h) or NULL, and conv states conv_sq / conv_sk [B, H, K-1, d] in
+ *   `dtype`, contiguous: the K-1 previous input rows, read and shifted in place
+ *   (hm_causal_conv's final_rows after a prefill is this state).
  */
 typedef struct {
   const void *q, *k, *v, *w_q, *w_k;
@@ -170,13 +177,16 @@ typedef struct {
   float *state;
   void *o;
   int32_t dtype;
-  int32_t reserved;
+  int32_t conv_width;
   int64_t B, H, d, f, dv;
   int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h;
   int64_t sw_h;
   int64_t sdt_b, sdt_h;
   const void *gate;
   int64_t sg_b, sg_h;
+  const float *conv_wq, *conv_wk, *conv_bq, *conv_bk;
+  void *conv_sq, *conv_sk;
+  int64_t scw_h, scb_h;
 } hm_linattn_step_args;
 
 hm_status hm_linattn_step(const hm_linattn_step_args *args, void *stream);

@@ -312,6 +312,17 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   }
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  if (a->conv_width < 0) return fail(HM_ERR_SHAPE, "conv_width must be >= 0");
+  if (a->conv_width > 4) return fail(HM_ERR_UNSUPPORTED, "conv_width %d: 1 to 4 taps are built", a->conv_width);
+  if (a->conv_width > 0) {
+    if (a->B * a->H > 0 && (!a->conv_wq || !a->conv_wk || (a->conv_width > 1 && (!a->conv_sq || !a->conv_sk))))
+      return fail(HM_ERR_NULL, "conv taps and conv states must be non-NULL when conv_width > 0");
+    if (a->scw_h < 0 || a->scb_h < 0) return fail(HM_ERR_SHAPE, "conv strides must be non-negative");
+    const uintptr_t ea = (uintptr_t)esize(a->dtype) - 1;
+    if (((uintptr_t)a->conv_wq | (uintptr_t)a->conv_wk | (uintptr_t)a->conv_bq | (uintptr_t)a->conv_bk) & 3 ||
+        ((uintptr_t)a->conv_sq | (uintptr_t)a->conv_sk) & ea)
+      return fail(HM_ERR_ALIGN, "conv taps, bias and states must be aligned to their element size");
+  }
   const int decay = a->dt != nullptr;
   const hm::StepEntry *e = find_step(a->dtype, a->d, a->f, a->dv, decay);
   if (!e)
@@ -327,6 +338,9 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.so_b = a->so_b; p.so_h = a->so_h;
   p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h;
   p.gate = a->gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h;
+  p.cwidth = a->conv_width;
+  p.cwq = a->conv_wq; p.cwk = a->conv_wk; p.cbq = a->conv_bq; p.cbk = a->conv_bk;
+  p.csq = a->conv_sq; p.csk = a->conv_sk; p.scw_h = a->scw_h; p.scb_h = a->scb_h;
   e->launch(p, (unsigned)BH, (hipStream_t)stream);
   return check_launch("decode step");
 }

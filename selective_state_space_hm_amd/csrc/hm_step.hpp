@@ -22,6 +22,12 @@ struct StepParams {
   int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h, sw_h, sdt_b, sdt_h;
   const void *gate;  // optional gate pre-activation [B, H, dv] (NULL = none)
   int64_t sg_b, sg_h;
+  // optional short causal conv on q and k (width 0 = none): taps [d][K], bias [d]
+  // (head strides scw_h, scb_h), conv states [B, H, K-1, d] in the input dtype
+  const float *cwq, *cwk, *cbq, *cbk;
+  void *csq, *csk;
+  int cwidth;
+  int64_t scw_h, scb_h;
 };
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
@@ -64,7 +70,29 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
   // 2. featurize q and k: u[j] = sum_i x[i] W[i][j], split over PARTS threads
   const T *xq = (const T *)p.q + b * p.sq_b + h * p.sq_h;
   const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
-  for (int i = tid; i < 2 * DK; i += NT) sx[i / DK][i % DK] = ldf(i < DK ? xq + i : xk + (i - DK));
+  for (int i = tid; i < 2 * DK; i += NT) {
+    const int proj = i / DK, c = i % DK;
+    const T xt = (proj == 0 ? xq : xk)[c];
+    float xv = (float)xt;
+    if (p.cwidth > 0) {
+      // the mixer's short causal conv on this channel, in the order of the
+      // standalone conv (bias, then taps oldest first), rounded to the input type;
+      // the conv state shifts by one row in place
+      const int K = p.cwidth;
+      const float *w = (proj == 0 ? p.cwq : p.cwk) + h * p.scw_h + (int64_t)c * K;
+      const float *bias = proj == 0 ? p.cbq : p.cbk;
+      T *cs = (T *)(proj == 0 ? p.csq : p.csk) + bh * (int64_t)(K - 1) * DK + c;
+      T prev[3];
+      for (int r = 0; r < K - 1; ++r) prev[r] = cs[r * DK];
+      float acc = bias ? bias[h * p.scb_h + c] : 0.f;
+      for (int r = 0; r < K - 1; ++r) acc = __builtin_fmaf(w[r], (float)prev[r], acc);
+      acc = __builtin_fmaf(w[K - 1], xv, acc);
+      for (int r = 0; r + 1 < K - 1; ++r) cs[r * DK] = prev[r + 1];
+      if (K > 1) cs[(K - 2) * DK] = xt;
+      xv = (float)to_elem<T>(acc);
+    }
+    sx[proj][c] = xv;
+  }
   if (tid == 0) {
     float a = 1.f;
     if constexpr (DECAY) a = __expf(-softplus_f32(p.dt[b * p.sdt_b + h * p.sdt_h]) * expf(p.a_log[h]));

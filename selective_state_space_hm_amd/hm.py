@@ -48,11 +48,13 @@ class FwdArgs(C.Structure):
 class StepArgs(C.Structure):
     _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
                 ("dt", p_void), ("a_log", p_void), ("state", p_void), ("o", p_void),
-                ("dtype", i32), ("reserved", i32),
+                ("dtype", i32), ("conv_width", i32),
                 ("B", i64), ("H", i64), ("d", i64), ("f", i64), ("dv", i64),
                 ("sq_b", i64), ("sq_h", i64), ("sk_b", i64), ("sk_h", i64), ("sv_b", i64), ("sv_h", i64),
                 ("so_b", i64), ("so_h", i64), ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64),
-                ("gate", p_void), ("sg_b", i64), ("sg_h", i64)]
+                ("gate", p_void), ("sg_b", i64), ("sg_h", i64),
+                ("conv_wq", p_void), ("conv_wk", p_void), ("conv_bq", p_void), ("conv_bk", p_void),
+                ("conv_sq", p_void), ("conv_sk", p_void), ("scw_h", i64), ("scb_h", i64)]
 
 
 class ConvArgs(C.Structure):
@@ -247,11 +249,13 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     return o
 
 
-def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=None):
+def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=None, conv=None):
     """One decode token per (b, h): q, k [B, H, d], v [B, H, dv]; state [B, H, F*dv+F]
     float32 is updated in place.  Returns o [B, H, dv], times SiLU(gate) when a gate
-    [B, H, dv] is given."""
-    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate)
+    [B, H, dv] is given.  conv = (w_q, w_k, b_q, b_k, state_q, state_k) runs q and k
+    through the short causal conv first (taps float32 [d, K] or [H, d, K], bias
+    float32 [d] / [H, d] or None, states [B, H, K-1, d] updated in place)."""
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
     _gate_shape(gate, v)
     B, H, d = q.shape
     dv = v.shape[-1]
@@ -269,6 +273,26 @@ def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=
                  sg_h=gate.stride(1) if gate is not None else 0)
     if gate is not None and gate.stride(2) != 1:
         raise ValueError("inner dimensions must be contiguous")
+    if conv is not None:
+        cwq, cwk, cbq, cbk, csq, csk = conv
+        K = cwq.shape[-1]
+        for t in (cwq, cwk):
+            if t.dtype != torch.float32 or t.shape[-2:] != (d, K) or t.stride(-1) != 1 or t.stride(-2) != K:
+                raise ValueError("conv taps are float32 [d, K] (or [H, d, K]) with contiguous rows")
+        for t in (cbq, cbk):
+            if t is not None and (t.dtype != torch.float32 or t.stride(-1) != 1):
+                raise ValueError("conv bias is float32, contiguous along d")
+        for t in (csq, csk):
+            if t is not None and (tuple(t.shape) != (B, H, K - 1, d) or not t.is_contiguous() or t.dtype != q.dtype):
+                raise ValueError("conv states are contiguous [B, H, K-1, d] in q's dtype")
+        a.conv_width = K
+        a.conv_wq, a.conv_wk, a.conv_bq, a.conv_bk = _ptr(cwq), _ptr(cwk), _ptr(cbq), _ptr(cbk)
+        a.conv_sq, a.conv_sk = _ptr(csq), _ptr(csk)
+        a.scw_h = cwq.stride(0) if cwq.dim() == 3 else 0
+        a.scb_h = cbq.stride(0) if cbq is not None and cbq.dim() == 2 else 0
+        if (cwk.dim() == 3) != (cwq.dim() == 3) or (cbq is None) != (cbk is None) or \
+                (cbk is not None and cbk.dim() != cbq.dim()):
+            raise ValueError("conv taps and biases of q and k must have the same layout")
     _check(call_step(a, _stream()))
     return o
 

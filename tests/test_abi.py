@@ -41,7 +41,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 2
+    assert hm.lib().hm_abi_version() == 3
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -180,6 +180,15 @@ def test_step_validation_errors():
     expect(hm.call_step(step(gate=A + 0xa000008, sg_b=16 * 128, sg_h=128)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=16 * 128, sg_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=-1, sg_h=128)), hm.HM_ERR_SHAPE)
+    cv = dict(conv_wq=A + 0xb000000, conv_wk=A + 0xb100000, conv_sq=A + 0xb200000, conv_sk=A + 0xb300000)
+    expect(hm.call_step(step(conv_width=5, **cv)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(conv_width=-1, **cv)), hm.HM_ERR_SHAPE)
+    expect(hm.call_step(step(conv_width=4, **{**cv, "conv_sk": None})), hm.HM_ERR_NULL)
+    # one tap needs no state: the conv checks pass and the size check comes next
+    expect(hm.call_step(step(conv_width=1, d=48, **{**cv, "conv_sk": None, "conv_sq": None})), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(conv_width=4, B=0, **cv)), hm.HM_OK)
+    expect(hm.call_step(step(conv_width=4, **{**cv, "conv_sq": A + 0xb200001})), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(conv_width=4, **{**cv, "conv_wq": A + 0xb000002})), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(B=0)), hm.HM_OK)
 
 

@@ -411,3 +411,44 @@ def test_mixer_path_conv_then_gated_attention():
     kr, _ = orc.causal_conv(f64(c.k), f64(wk))
     ref, _, _ = orc.forward(qr, kr, f64(c.v), f64(c.w_q), f64(c.w_k), f64(c.dt), f64(c.a_log), gate=f64(gt))
     assert report("mixer path: conv + gated attention", f64(o), ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype,shape", [(torch.float32, (32, 16, 32)), (torch.bfloat16, (128, 64, 128))])
+@pytest.mark.parametrize("K", [2, 4])
+def test_decode_step_with_fused_conv(dtype, shape, K):
+    """The step's fused conv equals hm_causal_conv (n = 1) followed by a plain step,
+    bit for bit, and both follow the oracle's conv -> step chain."""
+    d, f, dv = shape
+    B, H, steps = 3, 2, 6
+    dc = inputs.decode_setup(B, H, d, f, dv, prefix=30, steps=steps, decay=True, dtype=dtype, seed=K + d)
+    pk = orc.hedgehog_features(f64(dc.prefix_k), f64(dc.w_k))
+    S, z = orc.prefix_state(pk, f64(dc.prefix_v), orc.log_decay(f64(dc.prefix_dt), f64(dc.a_log)))
+    st_a = torch.tensor(orc.pack_state(S, z), dtype=torch.float32, device="cuda")
+    st_b = st_a.clone()
+    g = torch.Generator().manual_seed(K)
+    cwq, cwk = torch.randn((H, d, K), generator=g) / 2, torch.randn((H, d, K), generator=g) / 2
+    cbq, cbk = torch.randn((H, d), generator=g) / 4, torch.randn((H, d), generator=g) / 4
+    sq = torch.randn((B, H, K - 1, d), generator=g).to(dtype)
+    sk = torch.randn((B, H, K - 1, d), generator=g).to(dtype)
+    dev = [t.cuda() for t in (cwq, cwk, cbq, cbk)]
+    sq_a, sk_a, sq_b, sk_b = sq.cuda(), sk.cuda(), sq.cuda(), sk.cuda()
+    wq, wk, a_log = dc.w_q.cuda(), dc.w_k.cuda(), dc.a_log.cuda()
+    prev_q, prev_k = f64(sq), f64(sk)
+    worst = 0.0
+    for t in range(steps):
+        q, k, v, dt = inputs.decode_step_inputs(dc, t, dtype)
+        qd, kd, vd, dtd = q.cuda(), k.cuda(), v.cuda(), dt.cuda()
+        oa = hm.hm_linattn_step(qd, kd, vd, wq, wk, st_a, dtd, a_log, conv=(*dev, sq_a, sk_a))
+        qc = hm.hm_causal_conv(qd[:, :, None], dev[0], dev[2], sq_b, sq_b)[:, :, 0]
+        kc = hm.hm_causal_conv(kd[:, :, None], dev[1], dev[3], sk_b, sk_b)[:, :, 0]
+        ob = hm.hm_linattn_step(qc, kc, vd, wq, wk, st_b, dtd, a_log)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(st_a, st_b)
+        assert torch.equal(sq_a, sq_b) and torch.equal(sk_a, sk_b)
+        qr, prev_q = orc.causal_conv(f64(q)[:, :, None], f64(cwq), f64(cbq), prev_q)
+        kr, prev_k = orc.causal_conv(f64(k)[:, :, None], f64(cwk), f64(cbk), prev_k)
+        ot, S, z = orc.step(S, z, qr[:, :, 0], kr[:, :, 0], f64(v), f64(dc.w_q), f64(dc.w_k), f64(dt), f64(dc.a_log))
+        worst = max(worst, rel_l2(f64(oa), ot))
+    print(f"[parity] decode + fused conv {dtype} {shape} K={K}: worst step rel-L2 {worst:.3e}", flush=True)
+    assert worst <= tol_for(dtype)
+    assert np.array_equal(f64(sq_a), prev_q) and np.array_equal(f64(sk_a), prev_k)
