@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 3
+#define HM_ABI_VERSION 4
 
 typedef enum {
   HM_OK = 0,
@@ -115,6 +115,9 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   workspace: device scratch of at least hm_linattn_fwd_workspace_size() bytes
  *   (it may be NULL when that size is 0).  Its size grows with B*H*segments,
  *   never with n^2.
+ *   save: optional (NULL = inference), hm_linattn_save_size() bytes: the forward
+ *   also keeps what hm_linattn_bwd reads (chunk-start states, denominators); it
+ *   then runs with dsplit 1.  Built for the sizes hm_linattn_bwd lists.
  *   gate: optional [B, H, n, dv] in `dtype` (strides sg_*), the pre-activation of
  *   the mixer's gate branch; when given, o = (normalized output) * SiLU(gate),
  *   rounded once to `dtype` after the normalized output was rounded (NULL = no
@@ -144,6 +147,8 @@ typedef struct {
   size_t workspace_bytes;
   const void *gate;
   int64_t sg_b, sg_h, sg_t;
+  void *save;
+  size_t save_bytes;
 } hm_linattn_fwd_args;
 
 hm_status hm_linattn_fwd_workspace_size(const hm_linattn_fwd_args *args, size_t *bytes);
@@ -153,6 +158,58 @@ hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *args, int32_t *chunk,
                               int32_t *segments, int32_t *dsplit);
 
 hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
+
+/* Bytes of the `save` buffer a training forward needs (only B, H, n, f, dv and
+ * dtype of args are read). */
+hm_status hm_linattn_save_size(const hm_linattn_fwd_args *args, size_t *bytes);
+
+/*
+ * hm_linattn_bwd — gradients of the prefill (training: [HM] §3 trains the mixer;
+ * the chunk-wise form of [LA] part 5 run backwards).  For a scalar loss with
+ * d_o = dloss/do (and optionally d_s_final = dloss/ds_final) it writes
+ *   d_q, d_k: [B, H, n, d] in `dtype`, strides of q / k;  d_v: like v;
+ *   d_wq, d_wk: float32 [d][f] (one W) or [H][d][f] (sw_h = d*f), overwritten;
+ *   d_dt: float32 with dt's strides and d_a_log: float32 [H], when dt is given;
+ *   d_s_init: optional float32 state-layout gradient of s_init.
+ * Inputs: the forward's q, k, v, w_q, w_k, dt, a_log (same strides), d_o (strides
+ * so_*), and `save`: the buffer the forward filled when it was called with a
+ * non-NULL `save` (hm_linattn_save_size bytes; that forward runs with dsplit 1;
+ * it holds the float32 output before the gate, so o itself is not an input).
+ * gate: the forward's gate or NULL; with it, d_gate (strides sg_*, like gate)
+ * receives d_o * o * SiLU'(g) and the core sees d_o * SiLU(g).  d_s_final: optional
+ * dloss/ds_final (float32, state layout).  Outputs must not overlap inputs.
+ * Math: with dnum_t = dO_t / den_t and dden_t = -(dO_t . o_t) / den_t, the gradient
+ * of the state at each chunk end, G <- e^{Lam} G + sum_t e^{L_t} phi(q_t) dnum_t^T,
+ * runs from the last chunk back (chunk-start states come from `save`, nothing is
+ * recomputed sequentially in the forward direction); d log a_t is the sum, over
+ * the (query, key) pairs whose decay product contains a_t, of their weight times
+ * its loss gradient, taken per chunk without differences of nearly equal terms.
+ * Products in the dtype on MFMA with float32 accumulation; the decay gradient's
+ * per-chunk sums in float64.
+ * Built: bf16 (d, f, dv) = (64, 32, 64), (128, 64, 128); f32 (16, 16, 16), (32, 16, 32).
+ * workspace: hm_linattn_bwd_workspace_size() bytes (O(B*H*n*(2F+dv))).
+ */
+typedef struct {
+  const void *q, *k, *v, *w_q, *w_k;
+  const float *dt, *a_log;
+  const void *d_o;
+  const void *gate;
+  const float *d_s_final;
+  const void *save;
+  size_t save_bytes;
+  void *d_q, *d_k, *d_v, *d_gate;
+  float *d_wq, *d_wk, *d_dt, *d_a_log, *d_s_init;
+  int32_t dtype;
+  int32_t reserved;
+  int64_t B, H, n, d, f, dv;
+  int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t, sg_b, sg_h, sg_t;
+  int64_t sw_h, sdt_b, sdt_h, sdt_t;
+  void *workspace;
+  size_t workspace_bytes;
+} hm_linattn_bwd_args;
+
+hm_status hm_linattn_bwd_workspace_size(const hm_linattn_bwd_args *args, size_t *bytes);
+hm_status hm_linattn_bwd(const hm_linattn_bwd_args *args, void *stream);
 
 /*
  * hm_linattn_step — one decode token per (b, h) (the recurrent mode of [LA]
@@ -234,7 +291,7 @@ const char *hm_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char *hm_last_error_message(void);
 int hm_abi_version(void);
-/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step, 3: causal conv), for bindings. */
+/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step, 3: causal conv, 4: bwd), for bindings. */
 size_t hm_args_size(int which);
 
 #ifdef __cplusplus

@@ -42,7 +42,7 @@ def features(x, w):
     return torch.softmax(torch.cat([u, -u], dim=-1), dim=-1)
 
 
-def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None):
+def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, gate=None):
     """Differentiable forward: returns (o [B,H,n,dv], S_final [B,H,F,dv], z_final [B,H,F]).
 
     L_t = sum_{s<=t} log a_s with log a_s = -softplus(dt_s) exp(A_log) ([SSM] §3.2);
@@ -67,6 +67,8 @@ def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=No
         num = num + eL[..., None] * (phiq @ s_init)
         den = den + eL * (phiq @ z_init[..., None])[..., 0]
     o = num / den[..., None]
+    if gate is not None:
+        o = o * (gate * torch.sigmoid(gate))        # the mixer's gate branch, [HM] §5.2 step 6
     if n > 0:
         tail = torch.exp(L[..., -1:] - L)                             # e^{L_{n-1} - L_j}
         S = (phik * tail[..., None]).transpose(-1, -2) @ v
@@ -83,15 +85,17 @@ def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=No
 
 
 def grads(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, d_o=None, ds_final=None,
-          dz_final=None):
+          dz_final=None, gate=None):
     """Gradients of loss = <o, dO> + <S_final, dS_final> + <z_final, dz_final>.
 
     Returns a dict with keys q, k, v, w_q, w_k and, when given, dt, a_log,
-    s_init, z_init (float64 numpy arrays), plus "o" the forward output.
+    s_init, z_init, gate (float64 numpy arrays), plus "o" the forward output
+    (after the gate, when there is one).
     """
     args = dict(q=_t(q, True), k=_t(k, True), v=_t(v, True), w_q=_t(w_q, True), w_k=_t(w_k, True),
                 dt=_t(dt, dt is not None), a_log=_t(a_log, a_log is not None),
-                s_init=_t(s_init, s_init is not None), z_init=_t(z_init, z_init is not None))
+                s_init=_t(s_init, s_init is not None), z_init=_t(z_init, z_init is not None),
+                gate=_t(gate, gate is not None))
     o, S, z = forward_torch(**args)
     loss = (o * _t(d_o)).sum()
     if ds_final is not None:

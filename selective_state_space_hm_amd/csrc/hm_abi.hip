@@ -10,6 +10,7 @@
 #include <string>
 
 #include "hm.h"
+#include "hm_bwd_params.hpp"
 #include "hm_kernels.hpp"
 
 namespace {
@@ -36,12 +37,13 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
 
 struct Tables {
-  hm::Table parts[4];
+  hm::Table parts[5];
   Tables() {
     parts[0] = hm::table_fwd_bf16();
     parts[1] = hm::table_fwd_bf16_decay();
     parts[2] = hm::table_fwd_f32();
     parts[3] = hm::table_step_feat();
+    parts[4] = hm::table_train();
   }
 };
 const Tables &tables() {
@@ -133,7 +135,32 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
     return fail(HM_ERR_UNSUPPORTED, "dsplit=2 is not built for dv=%lld", (long long)a->dv);
   if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL))
     return fail(HM_ERR_UNSUPPORTED, "dsplit=1 is not built for dv=%lld", (long long)a->dv);
+  if (a->save) {
+    if (a->dsplit > 1) return fail(HM_ERR_UNSUPPORTED, "saving for the backward pass runs with dsplit 1");
+    if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_TRAIN))
+      return fail(HM_ERR_UNSUPPORTED, "no training kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                  (long long)a->d, (long long)a->f, (long long)a->dv);
+    if (!aligned16(a->save)) return fail(HM_ERR_ALIGN, "save must be 16-byte aligned");
+  }
   return ok();
+}
+
+// What the training forward saves, per (b, h): the state at every chunk start in
+// the dtype [nch][F][dv], z there in float32 [nch][F], and the per-token
+// denominator in float32 [n]; regions 256-byte aligned.
+struct SaveLayout {
+  size_t off_S, off_z, off_den, off_o, bytes;
+};
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+SaveLayout save_layout(int dtype, int64_t BH, int64_t n, int64_t f, int64_t dv) {
+  const int64_t nch = (n + hm::CHUNK - 1) / hm::CHUNK, F = 2 * f;
+  SaveLayout l{};
+  l.off_S = 0;
+  l.off_z = align256((size_t)(BH * nch * F * dv) * esize(dtype));
+  l.off_den = l.off_z + align256((size_t)(BH * nch * F) * 4);
+  l.off_o = l.off_den + align256((size_t)(BH * n) * 4);
+  l.bytes = l.off_o + align256((size_t)(BH * n * dv) * 4);
+  return l;
 }
 
 Plan make_plan(const hm_linattn_fwd_args *a) {
@@ -146,7 +173,9 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
   p.chunk = C;
   // dsplit: one workgroup owns all value columns of a (b, h) whenever that
   // kernel is built (splitting duplicates the featurization and measured slower)
-  if (a->dsplit) {
+  if (a->save) {
+    p.dsplit = 1;
+  } else if (a->dsplit) {
     p.dsplit = a->dsplit;
   } else {
     const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) != nullptr;
@@ -221,7 +250,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   if (a->n == 0 && !a->s_final) return ok();
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int64_t dw = a->dv / pl.dsplit;
-  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_FULL);
+  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, a->save ? hm::MODE_TRAIN : hm::MODE_FULL);
   const hm::FwdEntry *local = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_LOCAL);
   if (!full || !local) return fail(HM_ERR_UNSUPPORTED, "no kernel for dv/dsplit=%lld", (long long)dw);
   hipStream_t s = (hipStream_t)stream;
@@ -250,6 +279,16 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.seg_len = pl.seg_len;
   p.nseg = pl.segments;
   p.dsplit = pl.dsplit;
+  p.nchunks = (a->n + hm::CHUNK - 1) / hm::CHUNK;
+  if (a->save) {
+    const SaveLayout sl = save_layout(a->dtype, BH, a->n, a->f, a->dv);
+    if (a->save_bytes < sl.bytes)
+      return fail(HM_ERR_WORKSPACE, "save buffer of %zu bytes required, got %zu", sl.bytes, a->save_bytes);
+    p.save_S = (char *)a->save + sl.off_S;
+    p.save_z = (float *)((char *)a->save + sl.off_z);
+    p.save_den = (float *)((char *)a->save + sl.off_den);
+    p.save_o = (float *)((char *)a->save + sl.off_o);
+  }
 
   auto grid_for = [&](int64_t items, int ds) { return (unsigned)(((items + 7) / 8) * 8 * ds); };
   if (pl.segments > 1) {
@@ -286,6 +325,138 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.nitems = BH * pl.segments;
   full->launch(p, grid_for(p.nitems, pl.dsplit), s);
   return check_launch("prefill");
+}
+
+hm_status hm_linattn_save_size(const hm_linattn_fwd_args *a, size_t *bytes) {
+  if (!bytes) return fail(HM_ERR_NULL, "bytes is NULL");
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and f, dv >= 1");
+  *bytes = save_layout(a->dtype, a->B * a->H, a->n, a->f, a->dv).bytes;
+  return ok();
+}
+
+// ------------------------------------------------------------------ backward
+namespace {
+struct BwdLayout {
+  size_t phq, phk, dnum, dden, Lc, eQ, eK, eW, Xc, gS, gz, dwq, dwk, da, bytes;
+  int ngrp;
+};
+BwdLayout bwd_layout(const hm_linattn_bwd_args *a) {
+  BwdLayout l{};
+  const int64_t BH = a->B * a->H, n = a->n, F = 2 * a->f, nch = (n + hm::CHUNK - 1) / hm::CHUNK;
+  const size_t es = esize(a->dtype);
+  // enough (b, h, chunk range) workgroups to fill the 256 compute units
+  int64_t ng = BH > 0 ? (256 + BH - 1) / BH : 1;
+  if (ng > nch) ng = nch;
+  if (ng < 1) ng = 1;
+  l.ngrp = (int)ng;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
+  l.phq = take((size_t)(BH * n * F) * es);
+  l.phk = take((size_t)(BH * n * F) * es);
+  l.dnum = take((size_t)(BH * n * a->dv) * es);
+  l.dden = take((size_t)(BH * n) * 4);
+  l.Lc = take((size_t)(BH * n) * 4);
+  l.eQ = take((size_t)(BH * n) * 4);
+  l.eK = take((size_t)(BH * n) * 4);
+  l.eW = take((size_t)(BH * n) * 4);
+  l.Xc = take((size_t)(BH * nch) * 4);
+  l.gS = take((size_t)(BH * nch * F * a->dv) * es);
+  l.gz = take((size_t)(BH * nch * F) * 4);
+  l.dwq = take((size_t)(BH * ng * a->d * a->f) * 4);
+  l.dwk = take((size_t)(BH * ng * a->d * a->f) * 4);
+  l.da = take((size_t)BH * 4);
+  l.bytes = o;
+  return l;
+}
+const hm::BwdEntry *find_bwd(int dt, int64_t dk, int64_t fh, int64_t dv) {
+  const hm::BwdTable t = hm::table_bwd();
+  for (int i = 0; i < t.nbwd; ++i)
+    if (t.bwd[i].dtype == dt && t.bwd[i].dk == dk && t.bwd[i].fh == fh && t.bwd[i].dv == dv) return &t.bwd[i];
+  return nullptr;
+}
+hm_status validate_bwd(const hm_linattn_bwd_args *a) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f, dv >= 1");
+  if (a->B * a->H > 0) {
+    if (!a->w_q || !a->w_k || !a->d_wq || !a->d_wk)
+      return fail(HM_ERR_NULL, "w_q, w_k, d_wq and d_wk must be non-NULL");
+    if (a->n > 0 && (!a->q || !a->k || !a->v || !a->d_o || !a->d_q || !a->d_k || !a->d_v || !a->save))
+      return fail(HM_ERR_NULL, "q, k, v, d_o, save, d_q, d_k and d_v must be non-NULL");
+    if (a->gate && a->n > 0 && !a->d_gate) return fail(HM_ERR_NULL, "d_gate is required with a gate");
+  }
+  // with no token dt may be NULL beside A_log (an empty tensor); d_a_log is then zero
+  if (a->n > 0 && (a->dt == nullptr) != (a->a_log == nullptr)) return fail(HM_ERR_NULL, "dt and a_log must be given together");
+  if (a->a_log && a->B * a->H > 0 && (!a->d_a_log || (a->n > 0 && !a->d_dt)))
+    return fail(HM_ERR_NULL, "d_dt and d_a_log are required with dt");
+  const int64_t strides[] = {a->sq_b, a->sq_h, a->sq_t, a->sk_b, a->sk_h, a->sk_t, a->sv_b, a->sv_h,
+                             a->sv_t, a->so_b, a->so_h, a->so_t, a->sg_b, a->sg_h, a->sg_t, a->sw_h};
+  for (int64_t s : strides)
+    if (s < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->sdt_b < 0 || a->sdt_h < 0 || a->sdt_t < 0) return fail(HM_ERR_SHAPE, "dt strides must be non-negative");
+  if (a->n > 1 && (a->so_t < a->dv || a->sq_t < a->d || a->sk_t < a->d || a->sv_t < a->dv ||
+                   (a->gate && a->sg_t < a->dv)))
+    return fail(HM_ERR_SHAPE, "token stride smaller than the row length (rows overlap)");
+  if (a->sw_h != 0 && a->sw_h != a->d * a->f)
+    return fail(HM_ERR_SHAPE, "sw_h must be 0 (one W) or d*f (contiguous per-head W)");
+  const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->d_o, a->gate, a->d_gate, a->d_q, a->d_k, a->d_v,
+                        a->save, a->workspace, a->d_s_final, a->d_s_init};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(HM_ERR_ALIGN, "tensors, save and workspace must be 16-byte aligned");
+  for (int64_t s : strides)
+    if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  if (!find_bwd(a->dtype, a->d, a->f, a->dv))
+    return fail(HM_ERR_UNSUPPORTED, "no backward kernels for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv);
+  return ok();
+}
+}  // namespace
+
+hm_status hm_linattn_bwd_workspace_size(const hm_linattn_bwd_args *a, size_t *bytes) {
+  if (!bytes) return fail(HM_ERR_NULL, "bytes is NULL");
+  hm_status st = validate_bwd(a);
+  if (st != HM_OK) return st;
+  *bytes = bwd_layout(a).bytes;
+  return ok();
+}
+
+hm_status hm_linattn_bwd(const hm_linattn_bwd_args *a, void *stream) {
+  hm_status st = validate_bwd(a);
+  if (st != HM_OK) return st;
+  const int64_t BH = a->B * a->H;
+  if (BH == 0) return ok();
+  const SaveLayout sl = save_layout(a->dtype, BH, a->n, a->f, a->dv);
+  if (a->save_bytes < sl.bytes) return fail(HM_ERR_WORKSPACE, "save buffer of %zu bytes expected, got %zu", sl.bytes, a->save_bytes);
+  const BwdLayout wl = bwd_layout(a);
+  if (!a->workspace || a->workspace_bytes < wl.bytes)
+    return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", wl.bytes, a->workspace ? a->workspace_bytes : 0);
+  char *ws = (char *)a->workspace;
+  const char *sv = (const char *)a->save;
+  hm::BwdParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
+  p.dt = a->n > 0 ? a->dt : nullptr; p.a_log = a->a_log; p.d_o = a->d_o; p.ds_final = a->d_s_final;
+  p.gate = a->gate; p.d_gate = a->d_gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h; p.sg_t = a->sg_t;
+  p.sS = sv + sl.off_S; p.sz = (const float *)(sv + sl.off_z); p.sden = (const float *)(sv + sl.off_den);
+  p.so32 = (const float *)(sv + sl.off_o);
+  p.phq = ws + wl.phq; p.phk = ws + wl.phk; p.dnum = ws + wl.dnum;
+  p.dden = (float *)(ws + wl.dden); p.Lc = (float *)(ws + wl.Lc);
+  p.eQ = (float *)(ws + wl.eQ); p.eK = (float *)(ws + wl.eK); p.eW = (float *)(ws + wl.eW);
+  p.Xc = (float *)(ws + wl.Xc);
+  p.gS = ws + wl.gS; p.gz = (float *)(ws + wl.gz);
+  p.dwq_part = (float *)(ws + wl.dwq); p.dwk_part = (float *)(ws + wl.dwk); p.da_part = (float *)(ws + wl.da);
+  p.dq = a->d_q; p.dk = a->d_k; p.dv = a->d_v;
+  p.dwq = a->d_wq; p.dwk = a->d_wk; p.ddt = a->d_dt; p.da_log = a->a_log ? a->d_a_log : nullptr; p.ds_init = a->d_s_init;
+  p.B = a->B; p.H = a->H; p.n = a->n; p.nch = (a->n + hm::CHUNK - 1) / hm::CHUNK;
+  p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sq_t = a->sq_t; p.sk_b = a->sk_b; p.sk_h = a->sk_h; p.sk_t = a->sk_t;
+  p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t; p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
+  p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
+  p.ngrp = wl.ngrp;
+  find_bwd(a->dtype, a->d, a->f, a->dv)->launch(p, (hipStream_t)stream);
+  return check_launch("backward");
 }
 
 // ------------------------------------------------------------------ decode
@@ -465,6 +636,7 @@ size_t hm_args_size(int which) {
     case 1: return sizeof(hm_linattn_fwd_args);
     case 2: return sizeof(hm_linattn_step_args);
     case 3: return sizeof(hm_causal_conv_args);
+    case 4: return sizeof(hm_linattn_bwd_args);
     default: return 0;
   }
 }

@@ -1,0 +1,757 @@
+// Backward pass of causal, normalized Hedgehog linear attention.
+//
+// Pages: "线性注意力（Linear Attention）详解" (cnblogs) parts 2-5 (the causal kernel
+// form, the recurrent state and its chunk-wise evaluation), "HedgeMamba：融合线性
+// 注意力与状态空间模型的高效序列建模" §2.1 (Hedgehog map), §2.3 (numerator and
+// denominator), §3 (the model is trained, so the mixer needs gradients), and the
+// quant67 SSM lecture §3.2 (softplus step size).
+//
+// Notation per (b, h) and chunk of C tokens, L_t the chunk-local inclusive sum of
+// log a, Lam its value at the chunk's last token, phiq the unnormalized feature
+// row exp([u, -u] - max|u|) the forward used (o does not depend on its scale),
+// phik the softmax feature row, S_c / z_c the state at the chunk's start:
+//   dnum_t = dO_t / den_t,  dden_t = -(dO_t . o_t) / den_t
+//   A[t][j] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t)
+//   dphiq_t = sum_j A[t][j] phik_j + e^{L_t} (S_c dnum_t + dden_t z_c)
+//   G (gradient of the state at a chunk's end, carried from the last chunk back):
+//     G <- e^{Lam} G + sum_t e^{L_t} phiq_t dnum_t^T,   g likewise with dden
+//   dphik_j = sum_t A[t][j] phiq_t + e^{Lam - L_j} (G v_j + g)
+//   dv_j = sum_t [j <= t] e^{L_t - L_j} (phiq_t . phik_j) dnum_t + e^{Lam - L_j} G^T phik_j
+//   d log a_t = sum over the (query s, key j) pairs with j < t <= s of
+//     W_sj = [j <= s] e^{L_s - L_j} (phiq_s . phik_j)(dnum_s . v_j + dden_s): per chunk,
+//     the in-chunk pairs strictly below the diagonal, Q_s = e^{L_s} phiq_s . (S_c dnum_s
+//     + dden_s z_c) for keys before the chunk, K_j = e^{Lam - L_j} phik_j . (G v_j + g)
+//     for queries after it, and X_c = e^{Lam} (<G, S_c> + <g, z_c>) for pairs spanning
+//     it.  No term is a difference of the diagonal's nearly equal parts (v_t against
+//     o_t under a fast decay), so the result keeps its relative accuracy.
+//   through the maps: du'_q = phiq * dphiq (the max shift is a scale);
+//     du'_k = phik * (dphik - phik . dphik) (softmax); du = du'[:f] - du'[f:];
+//     dx = du W^T, dW = sum_t x_t^T du_t.
+// Kernels, launched in this order on one stream:
+//   bwd_prep   (per chunk)  features, dnum, dden, L
+//   bwd_gstate (per (b,h), chunks last to first)  G, g at every chunk end; dS_init
+//   bwd_dq     (per (b,h), a range of chunks)  dq, partial dW_q, Q_s
+//   bwd_dk     (same)  dk, partial dW_k, K_j
+//   bwd_dv     (same)  dv, the in-chunk pair sums, X_c
+//   bwd_decay  (per (b,h))  d dt, partial dA_log
+//   bwd_reduce (per weight element)  dW_q, dW_k, dA_log
+// Every matrix product runs on MFMA from LDS rows that are contiguous along K;
+// operands needed the other way round are written to LDS transposed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "hm_bwd_params.hpp"
+#include "hm_device.hpp"
+
+namespace hm {
+
+namespace bw {
+
+constexpr int C = 64;  // chunk length (the forward's)
+
+template <typename T> constexpr int ep() { return 16 / (int)sizeof(T); }
+
+// acc += A[16 rows][K] * B[16 rows][K]^T, both row-major in LDS with K contiguous:
+// A row (lane % 16) starts at A + row * la, B row (lane % 16) at B + row * lb.
+// acc[r] is element (4g + r, lane % 16) of the 16x16 product.
+// The operand registers stay allocated until the chain's result has been read:
+// measured on gfx950, a VALU write (here an accumulator read into a VGPR that had
+// just been freed) to a source register of an MFMA still waiting on the previous
+// MFMA of its chain changed that MFMA's operand; the empty asm below keeps every
+// fragment live past the point where the result is available.
+template <typename T, int K>
+__device__ __forceinline__ f32x4 mm(const T *A, int la, const T *B, int lb, f32x4 acc) {
+  using M = Mma<T>;
+  constexpr int NK = K / M::KS;
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  typename M::frag a[NK], b[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    a[s] = M::ld_contig(A + i * la + s * M::KS, g);
+    b[s] = M::ld_contig(B + i * lb + s * M::KS, g);
+  }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) acc = M::mma(a[s], b[s], acc);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a[s]), "v"(b[s]), "v"(acc));
+  return acc;
+}
+
+template <typename T> struct Vec { typedef T type __attribute__((ext_vector_type(16 / sizeof(T)))); };
+
+// rows x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
+// beyond `valid` zeroed; one 16-byte piece per thread per step.
+template <typename T, int COLS>
+__device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, int rows, int valid) {
+  constexpr int E = ep<T>(), PPR = COLS / E;
+  typedef typename Vec<T>::type V;
+  for (int idx = threadIdx.x; idx < rows * PPR; idx += blockDim.x) {
+    const int r = idx / PPR, pc = idx % PPR;
+    const V x = r < valid ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+    *reinterpret_cast<V *>(dst + r * ld + pc * E) = x;
+  }
+}
+// the same rows written transposed: dst[c * ld + r] = scale_r * src[r][c]
+template <typename T, int COLS, bool SCALE = false>
+__device__ __forceinline__ void stage_t(T *dst, int ld, const T *src, int64_t gs, int rows, int valid,
+                                        const float *rscale = nullptr) {
+  constexpr int E = ep<T>(), PPR = COLS / E;
+  typedef typename Vec<T>::type V;
+  for (int idx = threadIdx.x; idx < rows * PPR; idx += blockDim.x) {
+    const int r = idx / PPR, pc = idx % PPR;
+    const V x = r < valid ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+    const float s = SCALE ? rscale[r] : 1.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dst[(pc * E + e) * ld + r] = SCALE ? (T)((float)x[e] * s) : x[e];
+  }
+}
+
+// accumulator tile -> LDS, row-major (row 4g + r, column lane % 16) or transposed
+template <typename T>
+__device__ __forceinline__ void put(T *dst, int ld, f32x4 a) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[(4 * g + r) * ld + i] = (T)a[r];
+}
+template <typename T>
+__device__ __forceinline__ void put_t(T *dst, int ld, f32x4 a) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dst[i * ld + 4 * g + r] = (T)a[r];
+}
+
+// W [d][f] (head h) into LDS, as stored (ld = f + pad) or transposed (ld = d + pad)
+template <typename T, int DK, int FH>
+__device__ __forceinline__ void load_w(T *dst, int ld, const T *w, bool transposed) {
+  for (int idx = threadIdx.x; idx < DK * FH; idx += blockDim.x) {
+    const int i = idx / FH, f = idx % FH;
+    if (transposed) dst[f * ld + i] = w[idx];
+    else dst[i * ld + f] = w[idx];
+  }
+}
+
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+}  // namespace bw
+
+// ---------------------------------------------------------------- bwd_prep
+// One workgroup per (b, h, chunk): phiq (unnormalized, as the forward computed
+// it), phik (softmax), dnum, dden and L for the chunk's tokens.
+template <typename T, int DK, int FH, int DV>
+__global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDW = DK + PAD, E = ep<T>();
+  constexpr float L2E = 1.4426950408889634f;
+  __shared__ __align__(16) T sW[2][FH * LDW];
+  __shared__ __align__(16) T sX[C * LDW];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
+  const int64_t b = bh / p.H, h = bh % p.H, t0 = c * C;
+  const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+  load_w<T, DK, FH>(sW[0], LDW, (const T *)p.wq + h * p.sw_h, true);
+  load_w<T, DK, FH>(sW[1], LDW, (const T *)p.wk + h * p.sw_h, true);
+  for (int proj = 0; proj < 2; ++proj) {
+    const T *X = proj == 0 ? (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t
+                           : (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
+    stage<T, DK>(sX, LDW, X, proj == 0 ? p.sq_t : p.sk_t, C, nv);
+    __syncthreads();
+    // u^T tiles: rows f, columns the wave's 16 tokens
+    f32x4 u[FH / 16];
+    float m = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < FH / 16; ++rt) {
+      u[rt] = mm<T, DK>(sW[proj] + 16 * rt * LDW, LDW, sX + 16 * w * LDW, LDW, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[rt][r]));
+    }
+    const float ml = group_max(m) * L2E;
+    float sum = 0.f;
+    f32x4 ep_[FH / 16], em_[FH / 16];
+#pragma unroll
+    for (int rt = 0; rt < FH / 16; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ep_[rt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(u[rt][r], L2E, -ml));
+        em_[rt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(-u[rt][r], L2E, -ml));
+        sum += ep_[rt][r] + em_[rt][r];
+      }
+    const float inv = proj == 1 ? __builtin_amdgcn_rcpf(group_sum(sum)) : 1.f;
+    const int t = 16 * w + i;
+    if (t < nv) {
+      T *ph = (T *)(proj == 0 ? p.phq : p.phk) + (bh * p.n + t0 + t) * F;
+#pragma unroll
+      for (int rt = 0; rt < FH / 16; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ph[16 * rt + 4 * g + r] = (T)(ep_[rt][r] * inv);
+          ph[FH + 16 * rt + 4 * g + r] = (T)(em_[rt][r] * inv);
+        }
+    }
+    __syncthreads();
+  }
+  // chunk-local log-decay prefix, float64 sums as in the forward
+  if (p.dt && w == 0) {
+    const bool valid = lane < nv;
+    const float dtv = valid ? p.dt[b * p.sdt_b + h * p.sdt_h + (t0 + lane) * p.sdt_t] : 0.f;
+    const float la = valid ? -softplus_f32(dtv) * expf(p.a_log[h]) : 0.f;
+    const double L = wave_inclusive_scan((double)la);
+    if (valid) p.Lc[bh * p.n + t0 + lane] = (float)L;
+  }
+  // dnum = dO / den, dden = -(dO . o) / den with o the float32 output the training
+  // forward saved (before any gate); with a gate g, dO here is d_o * SiLU(g) and
+  // d_gate = d_o * o * SiLU'(g).  PPR threads per row.
+  constexpr int PPR = DV / E, RPP = 256 / PPR;
+  typedef typename Vec<T>::type V;
+  const T *DO = (const T *)p.d_o + b * p.so_b + h * p.so_h + t0 * p.so_t;
+  const float *O = p.so32 + (bh * p.n + t0) * DV;
+  for (int r0 = 0; r0 < C; r0 += RPP) {
+    const int r = r0 + tid / PPR, pc = tid % PPR;
+    const bool valid = r < nv;
+    float dv_[E], ov[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) dv_[e] = ov[e] = 0.f;
+    if (valid) {
+      const V x = *reinterpret_cast<const V *>(DO + r * p.so_t + pc * E);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dv_[e] = (float)x[e];
+        ov[e] = O[r * DV + pc * E + e];
+      }
+      if (p.gate) {
+        const V gv = *reinterpret_cast<const V *>((const T *)p.gate + b * p.sg_b + h * p.sg_h + (t0 + r) * p.sg_t + pc * E);
+        V dg;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float x2 = (float)gv[e], sg = 1.f / (1.f + expf(-x2));
+          dg[e] = (T)(dv_[e] * ov[e] * sg * (1.f + x2 * (1.f - sg)));
+          dv_[e] *= x2 * sg;
+        }
+        *reinterpret_cast<V *>((T *)p.d_gate + b * p.sg_b + h * p.sg_h + (t0 + r) * p.sg_t + pc * E) = dg;
+      }
+    }
+    // dden from the same rounded dnum the products use: with a fast decay
+    // dnum_t . v_t + dden_t = dnum_t . (v_t - o_t) nearly cancels, and the two
+    // terms must carry the same rounding of dnum for the difference to survive
+    const float rden = valid ? 1.f / p.sden[bh * p.n + t0 + r] : 0.f;
+    V nv_;
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      nv_[e] = (T)(dv_[e] * rden);
+      part += (float)nv_[e] * ov[e];
+    }
+    for (int off = 1; off < PPR; off <<= 1) part += __shfl_xor(part, off);
+    if (valid) {
+      *reinterpret_cast<V *>((T *)p.dnum + (bh * p.n + t0 + r) * DV + pc * E) = nv_;
+      if (pc == 0) p.dden[bh * p.n + t0 + r] = -part;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_gstate
+// One workgroup per (b, h), chunks from last to first: G and g at every chunk's
+// end go to the workspace; after chunk 0 they are the gradient of the initial
+// state.  G [F][DV] lives in accumulators, tile tt = wave + 4m.
+template <typename T, int DK, int FH, int DV>
+__global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD;
+  constexpr int CT = DV / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
+  __shared__ __align__(16) T sA[F * LDC_];   // (e^{L_t} phiq_t)^T: [f][t]
+  __shared__ __align__(16) T sB[DV * LDC_];  // dnum^T: [c][t]
+  __shared__ float sdd[C], seL[C];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x;
+  const int64_t BLK = (int64_t)F * DV + F;
+  f32x4 G[NTT];
+  float gz = 0.f;
+#pragma unroll
+  for (int m = 0; m < NTT; ++m) {
+    G[m] = zero4();
+    const int tt = w + 4 * m;
+    if (tt < TILES && p.ds_final) {
+      const int rt = tt / CT, ct = tt % CT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) G[m][r] = p.ds_final[bh * BLK + (16 * rt + 4 * g + r) * DV + 16 * ct + i];
+    }
+  }
+  if (tid < F && p.ds_final) gz = p.ds_final[bh * BLK + (int64_t)F * DV + tid];
+  for (int64_t c = p.nch - 1; c >= 0; --c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    // G, g at the end of chunk c
+    T *gs = (T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TILES) {
+        const int rt = tt / CT, ct = tt % CT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gs[(16 * rt + 4 * g + r) * DV + 16 * ct + i] = (T)G[m][r];
+      }
+    }
+    if (tid < F) p.gz[(bh * p.nch + c) * F + tid] = gz;
+    if (tid < C) {
+      const bool valid = tid < nv;
+      seL[tid] = valid ? (p.dt ? __expf(p.Lc[bh * p.n + t0 + tid]) : 1.f) : 0.f;
+      sdd[tid] = valid ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    __syncthreads();
+    stage_t<T, F, true>(sA, LDC_, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv, seL);
+    stage_t<T, DV>(sB, LDC_, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    const float eLam = p.dt ? __expf(p.Lc[bh * p.n + t0 + nv - 1]) : 1.f;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TILES) {
+        const int rt = tt / CT, ct = tt % CT;
+        G[m] = mm<T, C>(sA + 16 * rt * LDC_, LDC_, sB + 16 * ct * LDC_, LDC_, G[m] * eLam);
+      }
+    }
+    if (tid < F) {
+      float acc = 0.f;
+      for (int t = 0; t < C; ++t) acc += (float)sA[tid * LDC_ + t] * sdd[t];
+      gz = eLam * gz + acc;
+    }
+    __syncthreads();
+  }
+  if (p.ds_init) {
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TILES) {
+        const int rt = tt / CT, ct = tt % CT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p.ds_init[bh * BLK + (16 * rt + 4 * g + r) * DV + 16 * ct + i] = G[m][r];
+      }
+    }
+    if (tid < F) p.ds_init[bh * BLK + (int64_t)F * DV + tid] = gz;
+  }
+}
+
+// The chunk range [c0, c1) of workgroup `grp` of a (b, h) in the per-chunk kernels.
+__device__ __forceinline__ void chunk_range(const BwdParams &p, int grp, int64_t &c0, int64_t &c1) {
+  const int64_t per = (p.nch + p.ngrp - 1) / p.ngrp;
+  c0 = grp * per;
+  c1 = c0 + per < p.nch ? c0 + per : p.nch;
+}
+
+// ---------------------------------------------------------------- bwd_dq
+// dphiq -> du_q -> dq = du_q W_q^T, and this workgroup's share of dW_q.
+template <typename T, int DK, int FH, int DV>
+__global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int LW = FH + PAD, LN = DV + PAD, LVQ = (DV > F ? DV : F) + PAD, LC = C + PAD, LS = DV + PAD;
+  constexpr int OW = 0, ON = OW + DK * LW, OVQ = ON + C * LN, OA = OVQ + C * LVQ, OKT = OA + C * LC,
+                OS = OKT + F * LC, ODU = OS + F * LS, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
+  __shared__ __align__(16) T sm[TOT];
+  __shared__ float sL[C], sdd[C], sz[F];
+  T *sW = sm + OW, *sDN = sm + ON, *sVQ = sm + OVQ, *sA = sm + OA, *sKT = sm + OKT, *sS = sm + OS, *sDu = sm + ODU,
+    *sDuT = sm + ODUT, *sXT = sm + OXT;
+  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = blockIdx.x % p.ngrp;
+  const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
+  int64_t c0, c1;
+  chunk_range(p, grp, c0, c1);
+  load_w<T, DK, FH>(sW, LW, (const T *)p.wq + h * p.sw_h, false);
+  f32x4 dW[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) dW[m] = zero4();
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    stage<T, DV>(sDN, LN, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    stage<T, DV>(sVQ, LVQ, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
+    stage_t<T, DK>(sXT, LC, (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, C, nv);
+    stage_t<T, F>(sKT, LC, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
+    stage<T, DV>(sS, LS, (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    if (tid < C) {
+      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    if (tid < F) sz[tid] = p.sz[(bh * p.nch + c) * F + tid];
+    __syncthreads();
+    // A[t][j] = [j <= t] e^{L_t - L_j} (dnum_t . v_j + dden_t); rows t of this wave
+#pragma unroll
+    for (int jt = 0; jt < C / 16; ++jt) {
+      const f32x4 d1 = mm<T, DV>(sDN + 16 * w * LN, LN, sVQ + 16 * jt * LVQ, LVQ, zero4());
+      f32x4 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r, j = 16 * jt + i;
+        a[r] = j <= t ? __expf(sL[t] - sL[j]) * (d1[r] + sdd[t]) : 0.f;
+      }
+      put<T>(sA + 16 * w * LC + 16 * jt, LC, a);
+    }
+    __syncthreads();
+    stage<T, F>(sVQ, LVQ, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
+    __syncthreads();
+    // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F]
+    f32x4 dph[F / 16];
+    float qs[4] = {0.f, 0.f, 0.f, 0.f};  // Q_t partial: phiq_t . (inter part of dphiq_t)
+#pragma unroll
+    for (int ft = 0; ft < F / 16; ++ft) {
+      const f32x4 a1 = mm<T, C>(sA + 16 * w * LC, LC, sKT + 16 * ft * LC, LC, zero4());
+      const f32x4 a2 = mm<T, DV>(sDN + 16 * w * LN, LN, sS + 16 * ft * LS, LS, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r;
+        const float eL = t < nv ? (p.dt ? __expf(sL[t]) : 1.f) : 0.f;
+        const float inter = eL * (a2[r] + sdd[t] * sz[16 * ft + i]);
+        dph[ft][r] = a1[r] + inter;
+        qs[r] += (float)sVQ[t * LVQ + 16 * ft + i] * inter;
+      }
+    }
+    if (p.a_log) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r;
+        const float q4 = sum16(qs[r]);
+        if (i == 0 && t < nv) p.eQ[bh * p.n + t0 + t] = q4;
+      }
+    }
+    // du_q = phiq * dphiq over [u, -u]: du[f] = du'[f] - du'[f + FH]
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      f32x4 du;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r, f = 16 * ft + i;
+        du[r] = (float)sVQ[t * LVQ + f] * dph[ft][r] - (float)sVQ[t * LVQ + FH + f] * dph[ft + FT][r];
+      }
+      put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
+      put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
+    }
+    __syncthreads();
+    // dq = du_q W_q^T
+    T *DQ = (T *)p.dq + b * p.sq_b + h * p.sq_h + t0 * p.sq_t;
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+      const f32x4 a = mm<T, FH>(sDu + 16 * w * LW, LW, sW + 16 * it * LW, LW, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r;
+        if (t < nv) DQ[t * p.sq_t + 16 * it + i] = (T)a[r];
+      }
+    }
+    // dW_q += X_q^T du_q
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TW) dW[m] = mm<T, C>(sXT + 16 * (tt / FT) * LC, LC, sDuT + 16 * (tt % FT) * LC, LC, dW[m]);
+    }
+    __syncthreads();
+  }
+  float *part = p.dwq_part + (bh * p.ngrp + grp) * (int64_t)(DK * FH);
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int tt = w + 4 * m;
+    if (tt < TW) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(16 * (tt / FT) + 4 * g + r) * FH + 16 * (tt % FT) + i] = dW[m][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_dk
+// dphik -> dL_t and du_k (softmax) -> dk = du_k W_k^T, and the share of dW_k.
+template <typename T, int DK, int FH, int DV>
+__global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int LW = FH + PAD, LV = DV + PAD, LNK = (DV > F ? DV : F) + PAD, LC = C + PAD, LG = DV + PAD;
+  constexpr int OW = 0, OV = OW + DK * LW, ONK = OV + C * LV, OA = ONK + C * LNK, OQT = OA + C * LC,
+                OG = OQT + F * LC, ODU = OG + F * LG, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
+  __shared__ __align__(16) T sm[TOT];
+  __shared__ float sL[C], sdd[C], sg[F];
+  T *sW = sm + OW, *sV = sm + OV, *sNK = sm + ONK, *sAT = sm + OA, *sQT = sm + OQT, *sG = sm + OG, *sDu = sm + ODU,
+    *sDuT = sm + ODUT, *sXT = sm + OXT;
+  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = blockIdx.x % p.ngrp;
+  const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
+  int64_t c0, c1;
+  chunk_range(p, grp, c0, c1);
+  load_w<T, DK, FH>(sW, LW, (const T *)p.wk + h * p.sw_h, false);
+  f32x4 dW[NTW];
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) dW[m] = zero4();
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    stage<T, DV>(sNK, LNK, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    stage<T, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
+    stage_t<T, DK>(sXT, LC, (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, C, nv);
+    stage_t<T, F>(sQT, LC, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
+    stage<T, DV>(sG, LG, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    if (tid < C) {
+      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    if (tid < F) sg[tid] = p.gz[(bh * p.nch + c) * F + tid];
+    __syncthreads();
+    // A^T[j][t] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t); rows j of this wave
+#pragma unroll
+    for (int tt = 0; tt < C / 16; ++tt) {
+      const f32x4 d1 = mm<T, DV>(sV + 16 * w * LV, LV, sNK + 16 * tt * LNK, LNK, zero4());
+      f32x4 a;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r, t = 16 * tt + i;
+        a[r] = j <= t ? __expf(sL[t] - sL[j]) * (d1[r] + sdd[t]) : 0.f;
+      }
+      put<T>(sAT + 16 * w * LC + 16 * tt, LC, a);
+    }
+    __syncthreads();
+    stage<T, F>(sNK, LNK, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
+    __syncthreads();
+    // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F]
+    const float Lam = sL[nv - 1];
+    f32x4 dph[F / 16];
+    float ks[4] = {0.f, 0.f, 0.f, 0.f};  // K_j partial: phik_j . (inter part of dphik_j)
+#pragma unroll
+    for (int ft = 0; ft < F / 16; ++ft) {
+      const f32x4 a1 = mm<T, C>(sAT + 16 * w * LC, LC, sQT + 16 * ft * LC, LC, zero4());
+      const f32x4 a2 = mm<T, DV>(sV + 16 * w * LV, LV, sG + 16 * ft * LG, LG, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r;
+        const float e = j < nv ? (p.dt ? __expf(Lam - sL[j]) : 1.f) : 0.f;
+        const float inter = e * (a2[r] + sg[16 * ft + i]);
+        dph[ft][r] = a1[r] + inter;
+        ks[r] += (float)sNK[j * LNK + 16 * ft + i] * inter;
+      }
+    }
+    // phik . dphik per token for the softmax backward
+    float dot[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * w + 4 * g + r;
+      float s = 0.f;
+#pragma unroll
+      for (int ft = 0; ft < F / 16; ++ft) s += (float)sNK[j * LNK + 16 * ft + i] * dph[ft][r];
+      dot[r] = sum16(s);
+      const float k4 = sum16(ks[r]);
+      if (p.a_log && i == 0 && j < nv) p.eK[bh * p.n + t0 + j] = k4;
+    }
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      f32x4 du;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r, f = 16 * ft + i;
+        du[r] = (float)sNK[j * LNK + f] * (dph[ft][r] - dot[r]) - (float)sNK[j * LNK + FH + f] * (dph[ft + FT][r] - dot[r]);
+      }
+      put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
+      put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
+    }
+    __syncthreads();
+    T *DK_ = (T *)p.dk + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
+#pragma unroll
+    for (int it = 0; it < DK / 16; ++it) {
+      const f32x4 a = mm<T, FH>(sDu + 16 * w * LW, LW, sW + 16 * it * LW, LW, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r;
+        if (j < nv) DK_[j * p.sk_t + 16 * it + i] = (T)a[r];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NTW; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TW) dW[m] = mm<T, C>(sXT + 16 * (tt / FT) * LC, LC, sDuT + 16 * (tt % FT) * LC, LC, dW[m]);
+    }
+    __syncthreads();
+  }
+  float *part = p.dwk_part + (bh * p.ngrp + grp) * (int64_t)(DK * FH);
+#pragma unroll
+  for (int m = 0; m < NTW; ++m) {
+    const int tt = w + 4 * m;
+    if (tt < TW) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(16 * (tt / FT) + 4 * g + r) * FH + 16 * (tt % FT) + i] = dW[m][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bwd_dv
+// dv[j] = sum_t [j <= t] e^{L_t - L_j} (phiq_t . phik_j) dnum_t + e^{Lam - L_j} G^T phik_j
+template <typename T, int DK, int FH, int DV>
+__global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int LF = F + PAD, LC = C + PAD, LV = DV + PAD;
+  constexpr int OK_ = 0, OQ = OK_ + C * LF, OP = OQ + C * LF, ONT = OP + C * LC, OGT = ONT + DV * LC,
+                OV = OGT + DV * LF, ON = OV + C * LV, TOT = ON + C * LV;
+  __shared__ __align__(16) T sm[TOT];
+  __shared__ float sL[C], sdd[C], sCol[4][C];
+  __shared__ double sX[4];
+  T *sK = sm + OK_, *sQ = sm + OQ, *sP = sm + OP, *sNT = sm + ONT, *sGT = sm + OGT, *sV = sm + OV, *sN = sm + ON;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = blockIdx.x % p.ngrp;
+  const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
+  int64_t c0, c1;
+  chunk_range(p, grp, c0, c1);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    stage<T, F>(sK, LF, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
+    stage<T, F>(sQ, LF, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
+    stage_t<T, DV>(sNT, LC, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    stage_t<T, DV>(sGT, LF, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    if (p.a_log) {
+      stage<T, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
+      stage<T, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    }
+    if (tid < C) {
+      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    __syncthreads();
+    // Pt[j][t] = [j <= t] e^{L_t - L_j} phik_j . phiq_t, and for the decay gradient the
+    // pair weights W^T[j][t] = [j < t] Pt[j][t] (v_j . dnum_t + dden_t): their sums
+    // along t (pairs with key j) and along j (pairs with query t)
+    float rowsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tt = 0; tt < C / 16; ++tt) {
+      const f32x4 s = mm<T, F>(sK + 16 * w * LF, LF, sQ + 16 * tt * LF, LF, zero4());
+      f32x4 a, d1 = zero4();
+      if (p.a_log) d1 = mm<T, DV>(sV + 16 * w * LV, LV, sN + 16 * tt * LV, LV, zero4());
+      float colsum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r, t = 16 * tt + i;
+        a[r] = j <= t ? __expf(sL[t] - sL[j]) * s[r] : 0.f;
+        const float wt = j < t ? a[r] * (d1[r] + sdd[t]) : 0.f;
+        rowsum[r] += wt;
+        colsum += wt;
+      }
+      if (p.a_log) {
+        colsum += __shfl_xor(colsum, 16);
+        colsum += __shfl_xor(colsum, 32);
+        if (g == 0) sCol[w][16 * tt + i] = colsum;
+      }
+      put<T>(sP + 16 * w * LC + 16 * tt, LC, a);
+    }
+    if (p.a_log) {
+      // X_c = e^{Lam} (<G_end, S_c> + <g_end, z_c>): pairs spanning the whole chunk
+      const T *Sc = (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV);
+      const T *Gc = (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
+      double x = 0.0;
+      for (int e2 = tid; e2 < F * DV; e2 += 256) x += (double)((float)Sc[e2] * (float)Gc[e2]);
+      if (tid < F) x += (double)p.sz[(bh * p.nch + c) * F + tid] * p.gz[(bh * p.nch + c) * F + tid];
+      for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+      if (lane == 0) sX[w] = x;
+    }
+    __syncthreads();
+    if (p.a_log) {
+      // per token: (pairs with key u, query later in the chunk) - (pairs with query u,
+      // key earlier in the chunk); the chunk-level constant X_c
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r;
+        const float rs = sum16(rowsum[r]);
+        if (i == 0 && j < nv) p.eW[bh * p.n + t0 + j] = rs - (sCol[0][j] + sCol[1][j] + sCol[2][j] + sCol[3][j]);
+      }
+      if (tid == 0) {
+        const float eLam = p.dt ? __expf(sL[nv - 1]) : 1.f;
+        p.Xc[bh * p.nch + c] = (float)((sX[0] + sX[1] + sX[2] + sX[3]) * eLam);
+      }
+    }
+    const float Lam = sL[nv - 1];
+    T *DV_ = (T *)p.dv + b * p.sv_b + h * p.sv_h + t0 * p.sv_t;
+#pragma unroll
+    for (int ct = 0; ct < DV / 16; ++ct) {
+      const f32x4 a1 = mm<T, C>(sP + 16 * w * LC, LC, sNT + 16 * ct * LC, LC, zero4());
+      const f32x4 a2 = mm<T, F>(sK + 16 * w * LF, LF, sGT + 16 * ct * LF, LF, zero4());
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * w + 4 * g + r;
+        const float e = p.dt ? __expf(Lam - sL[j]) : 1.f;
+        if (j < nv) DV_[j * p.sv_t + 16 * ct + i] = (T)(a1[r] + e * a2[r]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- bwd_decay
+// Per (b, h): d log a_t = X_c + sum_{s >= t} Q_s + sum_{u < t} (K_u + eW_u), with
+// the chunk-local sums taken by one wave per chunk (float64); then d dt_t =
+// d log a_t (-sigmoid(dt_t) e^{A_log}) and the (b, h) share of dA_log = sum_t
+// d log a_t log a_t.
+__global__ __launch_bounds__(256) void bwd_decay(const BwdParams p) {
+  __shared__ double sRed[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
+  const float expA = expf(p.a_log[h]);
+  double da = 0.0;
+  for (int64_t c = w; c < p.nch; c += 4) {
+    const int64_t t = c * 64 + lane;
+    const bool valid = t < p.n;
+    const double q = valid ? p.eQ[bh * p.n + t] : 0.0;
+    const double e = valid ? (double)p.eK[bh * p.n + t] + p.eW[bh * p.n + t] : 0.0;
+    double qsum = q;
+    for (int off = 32; off > 0; off >>= 1) qsum += __shfl_xor(qsum, off);
+    const double excl = wave_inclusive_scan(e - q) - (e - q);  // sum_{u < t} (e_u - q_u)
+    const double dla = (double)p.Xc[bh * p.nch + c] + qsum + excl;
+    if (valid) {
+      const int64_t off = b * p.sdt_b + h * p.sdt_h + t * p.sdt_t;
+      const float x = p.dt[off];
+      const float sig = 1.f / (1.f + expf(-x));
+      p.ddt[off] = (float)(dla * (double)(-sig * expA));
+      da += dla * (double)(-softplus_f32(x) * expA);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) da += __shfl_xor(da, off);
+  if (lane == 0) sRed[w] = da;
+  __syncthreads();
+  if (tid == 0) p.da_part[bh] = (float)(sRed[0] + sRed[1] + sRed[2] + sRed[3]);
+}
+
+// ---------------------------------------------------------------- bwd_reduce
+// dW = sum of the workgroup shares (over every (b, h) for a shared W, over b for
+// per-head W); dA_log[h] = sum_b of the (b, h) shares.
+template <int DK, int FH>
+__global__ __launch_bounds__(256) void bwd_reduce(const BwdParams p, int per_head) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nh = per_head ? p.H : 1;
+  constexpr int64_t W = (int64_t)DK * FH;
+  if (e < nh * W) {
+    const int64_t h = e / W, x = e % W;
+    float sq = 0.f, sk = 0.f;
+    for (int64_t bb = 0; bb < p.B; ++bb)
+      for (int64_t hh = per_head ? h : 0; hh < (per_head ? h + 1 : p.H); ++hh)
+        for (int gI = 0; gI < p.ngrp; ++gI) {
+          const int64_t slot = ((bb * p.H + hh) * p.ngrp + gI) * W + x;
+          sq += p.dwq_part[slot];
+          sk += p.dwk_part[slot];
+        }
+    p.dwq[e] = sq;
+    p.dwk[e] = sk;
+  }
+  if (p.da_log && blockIdx.x == 0) {
+    for (int64_t hh = threadIdx.x; hh < p.H; hh += 256) {
+      float s = 0.f;
+      for (int64_t bb = 0; bb < p.B; ++bb) s += p.da_part[bb * p.H + hh];
+      p.da_log[hh] = s;
+    }
+  }
+}
+
+}  // namespace hm

@@ -40,8 +40,20 @@ struct ConvTable {
   int nconv;
 };
 
+struct BwdParams;
+struct BwdEntry {
+  int dtype, dk, fh, dv;
+  void (*launch)(const BwdParams &, hipStream_t);
+};
+struct BwdTable {
+  const BwdEntry *bwd;
+  int nbwd;
+};
+
 // one per kernel translation unit
 ConvTable table_conv();
+BwdTable table_bwd();
+Table table_train();
 Table table_fwd_bf16();
 Table table_fwd_bf16_decay();
 Table table_fwd_f32();

@@ -40,7 +40,8 @@
 namespace hm {
 
 constexpr int CHUNK = 64;
-enum { MODE_FULL = 0, MODE_LOCAL = 1 };
+// MODE_TRAIN is the full pass that also saves what the backward pass reads.
+enum { MODE_FULL = 0, MODE_LOCAL = 1, MODE_TRAIN = 2 };
 
 struct FwdParams {
   const void *q, *k, *v, *wq, *wk;
@@ -55,6 +56,12 @@ struct FwdParams {
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
   const void *gate;       // optional gate pre-activation, o's shape (NULL = none)
   int64_t sg_b, sg_h, sg_t;
+  // MODE_TRAIN only: the state at the start of every
+  // chunk [B*H][nchunks][F][dv] in the dtype, z there [B*H][nchunks][F] and the
+  // per-token denominator [B*H][n] (unnormalized phi(q), as used for o)
+  void *save_S;
+  float *save_z, *save_den, *save_o;  // save_o: the output before any gate, [B*H][n][dv]
+  int64_t nchunks;
   int64_t seg_len;        // tokens per segment, a multiple of CHUNK
   int64_t nitems;         // (b,h,segment) items in this launch
   int nseg;               // segments of the whole sequence
@@ -111,7 +118,8 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   constexpr int EPL = M::EPL;              // operand elements per lane
   constexpr int PAD = M::PAD;
   constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD, LDO = DW + 32 / (int)sizeof(T);
-  constexpr bool FULL = MODE == MODE_FULL;
+  constexpr bool FULL = MODE != MODE_LOCAL;
+  constexpr bool SAVE = MODE == MODE_TRAIN;
   constexpr int TPF_ = FULL ? 2 : 1;       // featurize tasks per feature wave
   constexpr int KVL = EPL == 8 ? 1 : 4;    // K-steps of the v re-layout per tile
   constexpr float L2E = 1.4426950408889634f;
@@ -376,7 +384,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         }
       }
       store4(&sP[cc * LDC + M::tpos(16 * a + 4 * g)], w);
-      const float dsum = group_sum(w[0] + w[1] + w[2] + w[3]);
+      // row sums of the weights as rounded for the product with V, so that each output
+      // is an exact convex combination under one set of weights: o_t - v_t then keeps
+      // its relative accuracy when a fast decay makes it small (the backward pass
+      // differentiates through it)
+      const float dsum = group_sum((float)(T)w[0] + (float)(T)w[1] + (float)(T)w[2] + (float)(T)w[3]);
       if (g == 0) sDenPart[a][cc] = dsum;
     };
 
@@ -387,6 +399,13 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       const int cr = 16 * wv + col;  // this lane's token row in the chunk
       frag qf[FULL ? KF : 1], kf[KF];  // phiQ, phiK of token tile wv (tile order)
       // ---- half A: featurize token tile wv of chunk j
+      if constexpr (SAVE) {
+        if (j < nch && wv == 2 && half == 0) {
+          const float *zp = sZ[(j + 1) & 1];  // z at the start of chunk j
+          float *zs = p.save_z + (bh * p.nchunks + tf / C) * F;
+          for (int i = lane; i < F; i += 64) zs[i] = zp[i];
+        }
+      }
       if (j < nch) {
         f32x4 uq[NFH], uk[NFH];
 #pragma unroll
@@ -592,6 +611,18 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             }
           }
         }
+        if constexpr (SAVE) {
+          {
+            // the state at the start of chunk j-1 (this iteration's read-out state)
+            T *sv = (T *)p.save_S + (bh * p.nchunks + ts / C) * ((int64_t)F * p.dv) + ncol + col;
+#pragma unroll
+            for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+              for (int t = 0; t < NFT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sv[(int64_t)(16 * t + 4 * g + r) * p.dv + 16 * jj] = (T)S[jj][t][r];
+          }
+        }
         // v of chunk ts -> accumulator layout: lane (g, col n) holds v[16bt + 4g + r][n]
 #pragma unroll
         for (int jj = 0; jj < NTW; ++jj) {
@@ -620,6 +651,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
             for (int a = 0; a <= bt; ++a) den[bt] += sDenPart[a][cc];
           }
+          if (SAVE && sw == 0 && g == 0 && half == 0) {
+#pragma unroll
+            for (int bt = 0; bt < NCT; ++bt)
+              if (ts + 16 * bt + col < t1) p.save_den[bh * p.n + ts + 16 * bt + col] = den[bt];
+          }
           f32x4 oacc[NTW][NCT];
 #pragma unroll
           for (int bt = 0; bt < NCT; ++bt) {
@@ -647,6 +683,17 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             const float inv = __builtin_amdgcn_rcpf(den[bt]);
 #pragma unroll
             for (int jj = 0; jj < NTW; ++jj) oacc[jj][bt] *= inv;
+          }
+          if constexpr (SAVE) {
+            // float32 output rows for the backward pass: lane (g, col) holds token
+            // 16bt + col, columns 16 NTW sw + 16 jj + 4g .. +3
+#pragma unroll
+            for (int bt = 0; bt < NCT; ++bt)
+              if (ts + 16 * bt + col < t1) {
+                float *os = p.save_o + (bh * p.n + ts + 16 * bt + col) * p.dv + 16 * NTW * sw + 4 * g;
+#pragma unroll
+                for (int jj = 0; jj < NTW; ++jj) *reinterpret_cast<f32x4 *>(os + 16 * jj) = oacc[jj][bt];
+              }
           }
           // output rows to LDS; they leave for HBM as whole rows in half B
           T *orow = &sO[col * LDO + 16 * NTW * sw + 4 * g];

@@ -42,7 +42,8 @@ class FwdArgs(C.Structure):
                 ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
                 ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
                 ("workspace", p_void), ("workspace_bytes", C.c_size_t),
-                ("gate", p_void), ("sg_b", i64), ("sg_h", i64), ("sg_t", i64)]
+                ("gate", p_void), ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
+                ("save", p_void), ("save_bytes", C.c_size_t)]
 
 
 class StepArgs(C.Structure):
@@ -65,6 +66,21 @@ class ConvArgs(C.Structure):
                 ("sw_h", i64), ("sb_h", i64)]
 
 
+class BwdArgs(C.Structure):
+    _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
+                ("dt", p_void), ("a_log", p_void), ("d_o", p_void), ("gate", p_void),
+                ("d_s_final", p_void), ("save", p_void), ("save_bytes", C.c_size_t),
+                ("d_q", p_void), ("d_k", p_void), ("d_v", p_void), ("d_gate", p_void), ("d_wq", p_void),
+                ("d_wk", p_void), ("d_dt", p_void), ("d_a_log", p_void), ("d_s_init", p_void),
+                ("dtype", i32), ("reserved", i32),
+                ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64), ("dv", i64),
+                ("sq_b", i64), ("sq_h", i64), ("sq_t", i64), ("sk_b", i64), ("sk_h", i64), ("sk_t", i64),
+                ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
+                ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
+                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
+                ("workspace", p_void), ("workspace_bytes", C.c_size_t)]
+
+
 class HMError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{status_string(status)}: {message}")
@@ -73,7 +89,8 @@ class HMError(RuntimeError):
 
 _lib = None
 EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
-           "hm_linattn_step", "hm_causal_conv", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
+           "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
+           "hm_linattn_bwd", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
 
 
 def lib():
@@ -89,8 +106,12 @@ def lib():
         L.hm_linattn_fwd.argtypes = [C.POINTER(FwdArgs), p_void]
         L.hm_linattn_step.argtypes = [C.POINTER(StepArgs), p_void]
         L.hm_causal_conv.argtypes = [C.POINTER(ConvArgs), p_void]
+        L.hm_linattn_save_size.argtypes = [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]
+        L.hm_linattn_bwd_workspace_size.argtypes = [C.POINTER(BwdArgs), C.POINTER(C.c_size_t)]
+        L.hm_linattn_bwd.argtypes = [C.POINTER(BwdArgs), p_void]
         for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
-                   "hm_linattn_step", "hm_causal_conv"):
+                   "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
+                   "hm_linattn_bwd"):
             getattr(L, fn).restype = C.c_int
         L.hm_status_string.argtypes = [C.c_int]
         L.hm_status_string.restype = C.c_char_p
@@ -143,6 +164,22 @@ def call_step(args: StepArgs, stream=None) -> int:
 
 def call_conv(args: ConvArgs, stream=None) -> int:
     return lib().hm_causal_conv(C.byref(args), stream)
+
+
+def call_save_size(args: FwdArgs):
+    n = C.c_size_t(0)
+    st = lib().hm_linattn_save_size(C.byref(args), C.byref(n))
+    return st, n.value
+
+
+def call_bwd_workspace_size(args: BwdArgs):
+    n = C.c_size_t(0)
+    st = lib().hm_linattn_bwd_workspace_size(C.byref(args), C.byref(n))
+    return st, n.value
+
+
+def call_bwd(args: BwdArgs, stream=None) -> int:
+    return lib().hm_linattn_bwd(C.byref(args), stream)
 
 
 # ------------------------------------------------------------ torch-facing
@@ -227,7 +264,7 @@ def _gate_shape(gate, v):
 
 
 def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
-                   chunk=0, segments=0, dsplit=0, workspace=None, gate=None):
+                   chunk=0, segments=0, dsplit=0, workspace=None, gate=None, save=None):
     """Causal prefill.  Returns o [B, H, n, dv] (v's dtype), times SiLU(gate) when a
     gate [B, H, n, dv] is given.  s_final (if given) receives the float32 state
     [B, H, F*dv + F] after the last token."""
@@ -238,6 +275,11 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit, gate)
+    if save is not None:
+        if save.numel() * save.element_size() < save_size(q, v, w_q):
+            raise ValueError("save buffer too small (see save_size)")
+        a.save = save.data_ptr()
+        a.save_bytes = save.numel() * save.element_size()
     st, nbytes = call_workspace_size(a)
     _check(st)
     if nbytes:
@@ -325,6 +367,70 @@ def hm_causal_conv(x, w, bias=None, prev=None, final_rows=None, y=None):
                  sb_h=bias.stride(0) if bias is not None and bias.dim() == 2 else 0)
     _check(call_conv(a, _stream()))
     return y
+
+
+def save_size(q, v, w_q) -> int:
+    """Bytes of the buffer a training forward fills for hm_linattn_bwd."""
+    B, H, n, d = q.shape
+    a = FwdArgs(dtype=_code(q), B=B, H=H, n=n, d=d, f=w_q.shape[-1], dv=v.shape[-1])
+    st, nb = call_save_size(a)
+    _check(st)
+    return nb
+
+
+def hm_linattn_bwd(q, k, v, w_q, w_k, d_o, save, dt=None, a_log=None, gate=None, d_s_final=None,
+                   want_d_s_init=False, workspace=None):
+    """Gradients of the prefill from d_o = dloss/do (save: what the training forward
+    saved; gate: the forward's gate; d_s_final: dloss/ds_final).  Returns a dict: q,
+    k, v (dtype of q), w_q, w_k (float32, [d, f] or [H, d, f]), and gate, dt, a_log,
+    s_init when applicable."""
+    _dev(q, k, v, w_q, w_k, d_o, save, dt, a_log, gate, d_s_final)
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    f = w_q.shape[-1]
+    for t in (q, k, v, d_o, gate):
+        if t is not None and t.stride(3) != 1:
+            raise ValueError("inner dimensions must be contiguous")
+    _gate_shape(gate, v)
+    if w_q.dim() == 3 and not w_q.is_contiguous():
+        raise ValueError("per-head W must be contiguous [H, d, f]")
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dvv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    dwq = torch.empty(w_q.shape, dtype=torch.float32, device=q.device)
+    dwk = torch.empty(w_k.shape, dtype=torch.float32, device=q.device)
+    ddt = torch.empty_strided(dt.shape, dt.stride(), dtype=torch.float32, device=q.device) if dt is not None else None
+    dal = torch.empty_like(a_log) if a_log is not None else None
+    F = 2 * f
+    dsi = torch.empty((B, H, F * dv + F), dtype=torch.float32, device=q.device) if want_d_s_init else None
+    dg = torch.empty_strided(gate.shape, gate.stride(), dtype=gate.dtype, device=q.device) if gate is not None else None
+    a = BwdArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
+                d_o=_ptr(d_o), gate=_ptr(gate), d_s_final=_ptr(d_s_final), save=_ptr(save),
+                save_bytes=save.numel() * save.element_size(), d_q=_ptr(dq), d_k=_ptr(dk), d_v=_ptr(dvv),
+                d_gate=_ptr(dg), d_wq=_ptr(dwq), d_wk=_ptr(dwk), d_dt=_ptr(ddt), d_a_log=_ptr(dal),
+                d_s_init=_ptr(dsi), dtype=_code(q), B=B, H=H, n=n, d=d, f=f, dv=dv,
+                sq_b=q.stride(0), sq_h=q.stride(1), sq_t=q.stride(2), sk_b=k.stride(0), sk_h=k.stride(1),
+                sk_t=k.stride(2), sv_b=v.stride(0), sv_h=v.stride(1), sv_t=v.stride(2),
+                so_b=d_o.stride(0), so_h=d_o.stride(1), so_t=d_o.stride(2),
+                sg_b=gate.stride(0) if gate is not None else 0, sg_h=gate.stride(1) if gate is not None else 0,
+                sg_t=gate.stride(2) if gate is not None else 0, sw_h=_w_strides(w_q),
+                sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0,
+                sdt_t=dt.stride(2) if dt is not None else 0)
+    st, nbytes = call_bwd_workspace_size(a)
+    _check(st)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(call_bwd(a, _stream()))
+    out = {"q": dq, "k": dk, "v": dvv, "w_q": dwq, "w_k": dwk}
+    if dg is not None:
+        out["gate"] = dg
+    if dt is not None:
+        out["dt"], out["a_log"] = ddt, dal
+    if dsi is not None:
+        out["s_init"] = dsi
+    return out
 
 
 def state_numel(f: int, dv: int) -> int:

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 13
     L = hm.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -37,11 +37,12 @@ def test_struct_layouts_match_binding():
     assert L.hm_args_size(1) == C.sizeof(hm.FwdArgs)
     assert L.hm_args_size(2) == C.sizeof(hm.StepArgs)
     assert L.hm_args_size(3) == C.sizeof(hm.ConvArgs)
-    assert L.hm_args_size(4) == 0
+    assert L.hm_args_size(4) == C.sizeof(hm.BwdArgs)
+    assert L.hm_args_size(5) == 0
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 3
+    assert hm.lib().hm_abi_version() == 4
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -256,3 +257,48 @@ def test_null_pointers_allowed_when_nothing_to_compute():
     expect(hm.call_fwd(fwd(n=5, q=None)), hm.HM_ERR_NULL)
     expect(hm.call_step(step(B=0, q=None, state=None)), hm.HM_OK)
     expect(hm.call_featurize(feat(n=0, x=None, phi=None)), hm.HM_OK)
+
+
+def bwd(B=2, H=16, n=2048, d=128, f=64, dv=128, dtype=hm.HM_BF16, decay=False, **kw):
+    a = hm.BwdArgs(q=A, k=A + 0x1000000, v=A + 0x2000000, w_q=A + 0x3000000, w_k=A + 0x3100000,
+                   d_o=A + 0x4800000, save=A + 0x5000000, save_bytes=1 << 40,
+                   d_q=A + 0x6000000, d_k=A + 0x7000000, d_v=A + 0x8000000, d_wq=A + 0x9000000,
+                   d_wk=A + 0x9100000, dtype=dtype, B=B, H=H, n=n, d=d, f=f, dv=dv,
+                   sq_b=H * n * d, sq_h=n * d, sq_t=d, sk_b=H * n * d, sk_h=n * d, sk_t=d,
+                   sv_b=H * n * dv, sv_h=n * dv, sv_t=dv, so_b=H * n * dv, so_h=n * dv, so_t=dv)
+    if decay:
+        a.dt, a.a_log, a.d_dt, a.d_a_log = A + 0xa000000, A + 0xa100000, A + 0xa200000, A + 0xa300000
+        a.sdt_b, a.sdt_h, a.sdt_t = H * n, n, 1
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_backward_validation_and_sizes():
+    L = hm.lib()
+    expect(L.hm_linattn_bwd(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_bwd(bwd(d_o=None)), hm.HM_ERR_NULL)
+    expect(hm.call_bwd(bwd(save=None)), hm.HM_ERR_NULL)
+    expect(hm.call_bwd(bwd(decay=True, d_dt=None)), hm.HM_ERR_NULL)
+    expect(hm.call_bwd(bwd(gate=A + 0xb000000, sg_b=16 * 2048 * 128, sg_h=2048 * 128, sg_t=128)), hm.HM_ERR_NULL)
+    expect(hm.call_bwd(bwd(dtype=9)), hm.HM_ERR_DTYPE)
+    expect(hm.call_bwd(bwd(n=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_bwd(bwd(sw_h=7)), hm.HM_ERR_SHAPE)                  # per-head W must be contiguous
+    expect(hm.call_bwd(bwd(d_q=A + 0x6000008)), hm.HM_ERR_ALIGN)
+    expect(hm.call_bwd(bwd(d=96)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_bwd(bwd(f=32)), hm.HM_ERR_UNSUPPORTED)              # (128, 32, 128) has no backward build
+    expect(hm.call_bwd(bwd()), hm.HM_ERR_WORKSPACE)                     # no workspace
+    expect(hm.call_bwd(bwd(B=0)), hm.HM_OK)
+    st, nb = hm.call_bwd_workspace_size(bwd(B=8, H=16, n=2048))
+    expect(st, hm.HM_OK)
+    F, BH, n = 128, 128, 2048
+    # features, dnum and the chunk-end gradient states dominate: O(B*H*n*(2F + dv)), no n^2 term
+    assert 2 * (BH * n * (2 * F + 128)) < nb < 2 * (BH * n * (2 * F + 128)) * 2 + 64 << 20
+    a = hm.FwdArgs(dtype=hm.HM_BF16, B=8, H=16, n=2048, d=128, f=64, dv=128)
+    st, sb = hm.call_save_size(a)
+    expect(st, hm.HM_OK)
+    assert sb == BH * 32 * F * 128 * 2 + BH * 32 * F * 4 + BH * n * 4 + BH * n * 128 * 4
+    expect(hm.call_fwd(fwd(B=8, segments=1, save=A + 0xc000000, save_bytes=sb - 1)), hm.HM_ERR_WORKSPACE)
+    assert "save" in hm.last_error()
+    expect(hm.call_fwd(fwd(save=A + 0xc000000, save_bytes=sb, dsplit=2)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(save=A + 0xc000004, save_bytes=sb)), hm.HM_ERR_ALIGN)

@@ -24,13 +24,15 @@ def case(seed, B=1, H=2, n=9, d=6, f=4, dv=5, decay=True, init=True):
 
 def loss_np(c, d_o, ds, dz):
     o, S, z = orc.forward(c["q"], c["k"], c["v"], c["w_q"], c["w_k"], c.get("dt"), c.get("a_log"),
-                          c.get("s_init"), c.get("z_init"))
+                          c.get("s_init"), c.get("z_init"), gate=c.get("gate"))
     return float((o * d_o).sum() + (S * ds).sum() + (z * dz).sum())
 
 
-@pytest.mark.parametrize("decay,init", [(True, True), (False, False), (True, False)])
-def test_gradients_match_finite_differences(decay, init):
+@pytest.mark.parametrize("decay,init,gated", [(True, True, False), (False, False, False), (True, False, True)])
+def test_gradients_match_finite_differences(decay, init, gated):
     c = case(1, decay=decay, init=init)
+    if gated:
+        c["gate"] = np.random.default_rng(11).normal(size=c["v"].shape) * 2
     r = np.random.default_rng(7)
     B, H, n, _ = c["q"].shape
     F, dv = 2 * c["w_q"].shape[1], c["v"].shape[-1]
@@ -40,7 +42,7 @@ def test_gradients_match_finite_differences(decay, init):
     g = hm_grad.grads(**c, d_o=d_o, ds_final=ds, dz_final=dz)
     # the oracle's own forward agrees with the numpy oracle
     o_np = orc.forward(c["q"], c["k"], c["v"], c["w_q"], c["w_k"], c.get("dt"), c.get("a_log"),
-                       c.get("s_init"), c.get("z_init"))[0]
+                       c.get("s_init"), c.get("z_init"), gate=c.get("gate"))[0]
     np.testing.assert_allclose(g["o"], o_np, rtol=1e-12, atol=1e-12)
     eps = 1e-6
     for name in c:
