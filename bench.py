@@ -279,6 +279,29 @@ def main():
         extra.append({"workload": f"stage-2 mixer chain: conv(q), conv(k), gated prefill, B={B} H={H} n={n}",
                       "ms": msm, "tokens_per_s": tokens / (msm * 1e-3)})
         del gate, qc, kc
+        # training step of the same layer: forward that saves, then the backward pass
+        d_o = torch.randn(case.v.shape, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(dev)
+        save = torch.empty(hm.save_size(g["q"], g["v"], g["w_q"]), dtype=torch.uint8, device=dev)
+        bws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+        def stept():
+            hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], o=o, workspace=ws, save=save)
+
+        def stepb():
+            hm.hm_linattn_bwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], d_o, save, workspace=bws)
+
+        def steptb():
+            stept()
+            stepb()
+
+        log("[bench] training forward + backward, same layer")
+        msf, _ = time_launches(stept, 50, 100, torch)
+        msb, _ = time_launches(stepb, 50, 100, torch)
+        mst, _ = time_launches(steptb, 50, 100, torch)
+        extra.append({"workload": f"training step (forward saving for the backward, then hm_linattn_bwd), "
+                                  f"B={B} H={H} n={n}, identity decay", "ms": mst, "tokens_per_s": tokens / (mst * 1e-3),
+                      "forward_ms": msf, "backward_ms": msb})
+        del d_o, save, bws
     del g, o
 
     if not args.no_extra:

@@ -80,30 +80,74 @@ __device__ __forceinline__ f32x4 mm(const T *A, int la, const T *B, int lb, f32x
 
 template <typename T> struct Vec { typedef T type __attribute__((ext_vector_type(16 / sizeof(T)))); };
 
-// rows x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
-// beyond `valid` zeroed; one 16-byte piece per thread per step.
-template <typename T, int COLS>
-__device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, int rows, int valid) {
-  constexpr int E = ep<T>(), PPR = COLS / E;
+// ROWS x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
+// beyond `valid` zeroed; 16-byte pieces, every load of a thread issued before its
+// first LDS write (compile-time trip counts, fully unrolled).
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, int valid) {
+  constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + 255) / 256;
   typedef typename Vec<T>::type V;
-  for (int idx = threadIdx.x; idx < rows * PPR; idx += blockDim.x) {
-    const int r = idx / PPR, pc = idx % PPR;
-    const V x = r < valid ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
-    *reinterpret_cast<V *>(dst + r * ld + pc * E) = x;
+  V x[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+    x[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+    if (idx < N) *reinterpret_cast<V *>(dst + r * ld + pc * E) = x[m];
   }
 }
-// the same rows written transposed: dst[c * ld + r] = scale_r * src[r][c]
-template <typename T, int COLS, bool SCALE = false>
-__device__ __forceinline__ void stage_t(T *dst, int ld, const T *src, int64_t gs, int rows, int valid,
+// the same rows written transposed: dst[c * ld + r] = scale_r * src[r][c].
+// Consecutive lanes take consecutive source rows (two rows per lane for bf16,
+// packed into one 4-byte write), so the LDS writes of a wave are contiguous.
+template <typename T, int ROWS, int COLS, bool SCALE = false>
+__device__ __forceinline__ void stage_t(T *dst, int ld, const T *src, int64_t gs, int valid,
                                         const float *rscale = nullptr) {
   constexpr int E = ep<T>(), PPR = COLS / E;
   typedef typename Vec<T>::type V;
-  for (int idx = threadIdx.x; idx < rows * PPR; idx += blockDim.x) {
-    const int r = idx / PPR, pc = idx % PPR;
-    const V x = r < valid ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
-    const float s = SCALE ? rscale[r] : 1.f;
+  if constexpr (sizeof(T) == 2) {
+    constexpr int NP = ROWS / 2, N = NP * PPR, PER = (N + 255) / 256;
+    V x0[PER], x1[PER];
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[(pc * E + e) * ld + r] = SCALE ? (T)((float)x[e] * s) : x[e];
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = 2 * (idx % NP), pc = idx / NP;
+      x0[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+      x1[m] = (idx < N && r + 1 < valid) ? *reinterpret_cast<const V *>(src + (r + 1) * gs + pc * E) : V{};
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = 2 * (idx % NP), pc = idx / NP;
+      if (idx < N) {
+        const float s0 = SCALE ? rscale[r] : 1.f, s1 = SCALE ? rscale[r + 1] : 1.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const T a = SCALE ? (T)((float)x0[m][e] * s0) : x0[m][e];
+          const T b2 = SCALE ? (T)((float)x1[m][e] * s1) : x1[m][e];
+          const uint32_t packed =
+              (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b2) << 16);
+          *reinterpret_cast<uint32_t *>(dst + (pc * E + e) * ld + r) = packed;
+        }
+      }
+    }
+  } else {
+    constexpr int N = ROWS * PPR, PER = (N + 255) / 256;
+    V x[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = idx % ROWS, pc = idx / ROWS;
+      x[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = idx % ROWS, pc = idx / ROWS;
+      if (idx < N) {
+        const float s0 = SCALE ? rscale[r] : 1.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[(pc * E + e) * ld + r] = SCALE ? (T)((float)x[m][e] * s0) : x[m][e];
+      }
+    }
   }
 }
 
@@ -141,6 +185,13 @@ __device__ __forceinline__ float sum16(float v) {
 
 }  // namespace bw
 
+// The chunk range [c0, c1) of workgroup `grp` of a (b, h) in the per-chunk kernels.
+__device__ __forceinline__ void chunk_range(const BwdParams &p, int grp, int64_t &c0, int64_t &c1) {
+  const int64_t per = (p.nch + p.ngrp - 1) / p.ngrp;
+  c0 = grp * per;
+  c1 = c0 + per < p.nch ? c0 + per : p.nch;
+}
+
 // ---------------------------------------------------------------- bwd_prep
 // One workgroup per (b, h, chunk): phiq (unnormalized, as the forward computed
 // it), phik (softmax), dnum, dden and L for the chunk's tokens.
@@ -153,15 +204,18 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   __shared__ __align__(16) T sX[C * LDW];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / p.nch, c = blockIdx.x % p.nch;
-  const int64_t b = bh / p.H, h = bh % p.H, t0 = c * C;
-  const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+  // one chunk per workgroup: many small workgroups hide the latency best here
+  const int64_t bh = blockIdx.x / p.nch, b = bh / p.H, h = bh % p.H;
+  const int64_t c0 = blockIdx.x % p.nch, c1 = c0 + 1;
   load_w<T, DK, FH>(sW[0], LDW, (const T *)p.wq + h * p.sw_h, true);
   load_w<T, DK, FH>(sW[1], LDW, (const T *)p.wk + h * p.sw_h, true);
+  for (int64_t c = c0; c < c1; ++c) {
+  const int64_t t0 = c * C;
+  const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
   for (int proj = 0; proj < 2; ++proj) {
     const T *X = proj == 0 ? (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t
                            : (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
-    stage<T, DK>(sX, LDW, X, proj == 0 ? p.sq_t : p.sk_t, C, nv);
+    stage<T, C, DK>(sX, LDW, X, proj == 0 ? p.sq_t : p.sk_t, nv);
     __syncthreads();
     // u^T tiles: rows f, columns the wave's 16 tokens
     f32x4 u[FH / 16];
@@ -188,12 +242,10 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
     if (t < nv) {
       T *ph = (T *)(proj == 0 ? p.phq : p.phk) + (bh * p.n + t0 + t) * F;
 #pragma unroll
-      for (int rt = 0; rt < FH / 16; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          ph[16 * rt + 4 * g + r] = (T)(ep_[rt][r] * inv);
-          ph[FH + 16 * rt + 4 * g + r] = (T)(em_[rt][r] * inv);
-        }
+      for (int rt = 0; rt < FH / 16; ++rt) {
+        store4(ph + 16 * rt + 4 * g, ep_[rt] * inv);       // four consecutive features per lane
+        store4(ph + FH + 16 * rt + 4 * g, em_[rt] * inv);
+      }
     }
     __syncthreads();
   }
@@ -254,6 +306,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
       if (pc == 0) p.dden[bh * p.n + t0 + r] = -part;
     }
   }
+  }
 }
 
 // ---------------------------------------------------------------- bwd_gstate
@@ -306,8 +359,8 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
       sdd[tid] = valid ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
     __syncthreads();
-    stage_t<T, F, true>(sA, LDC_, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv, seL);
-    stage_t<T, DV>(sB, LDC_, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+    stage_t<T, C, F, true>(sA, LDC_, (const T *)p.phq + (bh * p.n + t0) * F, F, nv, seL);
+    stage_t<T, C, DV>(sB, LDC_, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     const float eLam = p.dt ? __expf(p.Lc[bh * p.n + t0 + nv - 1]) : 1.f;
     __syncthreads();
 #pragma unroll
@@ -339,12 +392,6 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   }
 }
 
-// The chunk range [c0, c1) of workgroup `grp` of a (b, h) in the per-chunk kernels.
-__device__ __forceinline__ void chunk_range(const BwdParams &p, int grp, int64_t &c0, int64_t &c1) {
-  const int64_t per = (p.nch + p.ngrp - 1) / p.ngrp;
-  c0 = grp * per;
-  c1 = c0 + per < p.nch ? c0 + per : p.nch;
-}
 
 // ---------------------------------------------------------------- bwd_dq
 // dphiq -> du_q -> dq = du_q W_q^T, and this workgroup's share of dW_q.
@@ -373,11 +420,11 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    stage<T, DV>(sDN, LN, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
-    stage<T, DV>(sVQ, LVQ, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
-    stage_t<T, DK>(sXT, LC, (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, C, nv);
-    stage_t<T, F>(sKT, LC, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
-    stage<T, DV>(sS, LS, (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    stage<T, C, DV>(sDN, LN, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    stage<T, C, DV>(sVQ, LVQ, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+    stage_t<T, C, DK>(sXT, LC, (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
+    stage_t<T, C, F>(sKT, LC, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    stage<T, F, DV>(sS, LS, (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     if (tid < C) {
       sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
@@ -397,7 +444,7 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
       put<T>(sA + 16 * w * LC + 16 * jt, LC, a);
     }
     __syncthreads();
-    stage<T, F>(sVQ, LVQ, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
+    stage<T, C, F>(sVQ, LVQ, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
     __syncthreads();
     // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F]
     f32x4 dph[F / 16];
@@ -493,11 +540,11 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    stage<T, DV>(sNK, LNK, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
-    stage<T, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
-    stage_t<T, DK>(sXT, LC, (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, C, nv);
-    stage_t<T, F>(sQT, LC, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
-    stage<T, DV>(sG, LG, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    stage<T, C, DV>(sNK, LNK, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+    stage_t<T, C, DK>(sXT, LC, (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
+    stage_t<T, C, F>(sQT, LC, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    stage<T, F, DV>(sG, LG, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     if (tid < C) {
       sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
@@ -517,7 +564,7 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
       put<T>(sAT + 16 * w * LC + 16 * tt, LC, a);
     }
     __syncthreads();
-    stage<T, F>(sNK, LNK, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
+    stage<T, C, F>(sNK, LNK, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
     __syncthreads();
     // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F]
     const float Lam = sL[nv - 1];
@@ -610,13 +657,13 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    stage<T, F>(sK, LF, (const T *)p.phk + (bh * p.n + t0) * F, F, C, nv);
-    stage<T, F>(sQ, LF, (const T *)p.phq + (bh * p.n + t0) * F, F, C, nv);
-    stage_t<T, DV>(sNT, LC, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
-    stage_t<T, DV>(sGT, LF, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F, F);
+    stage<T, C, F>(sK, LF, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    stage<T, C, F>(sQ, LF, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    stage_t<T, C, DV>(sNT, LC, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    stage_t<T, F, DV>(sGT, LF, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     if (p.a_log) {
-      stage<T, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, C, nv);
-      stage<T, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, C, nv);
+      stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+      stage<T, C, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     }
     if (tid < C) {
       sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
@@ -726,30 +773,44 @@ __global__ __launch_bounds__(256) void bwd_decay(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_reduce
 // dW = sum of the workgroup shares (over every (b, h) for a shared W, over b for
-// per-head W); dA_log[h] = sum_b of the (b, h) shares.
+// per-head W): 64 consecutive weight elements per workgroup, the shares split over
+// four thread groups; dA_log[h] = sum_b of the (b, h) shares.
 template <int DK, int FH>
 __global__ __launch_bounds__(256) void bwd_reduce(const BwdParams p, int per_head) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t nh = per_head ? p.H : 1;
+  __shared__ float sq[4][64], sk[4][64];
   constexpr int64_t W = (int64_t)DK * FH;
+  const int tid = threadIdx.x, el = tid & 63, pg = tid >> 6;
+  const int64_t e = (int64_t)blockIdx.x * 64 + el;  // over nh * W
+  const int64_t nh = per_head ? p.H : 1;
+  float aq = 0.f, ak = 0.f;
   if (e < nh * W) {
     const int64_t h = e / W, x = e % W;
-    float sq = 0.f, sk = 0.f;
-    for (int64_t bb = 0; bb < p.B; ++bb)
-      for (int64_t hh = per_head ? h : 0; hh < (per_head ? h + 1 : p.H); ++hh)
-        for (int gI = 0; gI < p.ngrp; ++gI) {
-          const int64_t slot = ((bb * p.H + hh) * p.ngrp + gI) * W + x;
-          sq += p.dwq_part[slot];
-          sk += p.dwk_part[slot];
-        }
-    p.dwq[e] = sq;
-    p.dwk[e] = sk;
+    // the shares of head h (per-head W) or of every head, slot = (bh * ngrp + grp)
+    const int64_t nslot = per_head ? p.B * p.ngrp : p.B * p.H * p.ngrp;
+    for (int64_t k2 = pg; k2 < nslot; k2 += 4) {
+      int64_t slot;
+      if (per_head) {
+        const int64_t bb = k2 / p.ngrp, gI = k2 % p.ngrp;
+        slot = (bb * p.H + h) * p.ngrp + gI;
+      } else {
+        slot = k2;
+      }
+      aq += p.dwq_part[slot * W + x];
+      ak += p.dwk_part[slot * W + x];
+    }
+  }
+  sq[pg][el] = aq;
+  sk[pg][el] = ak;
+  __syncthreads();
+  if (pg == 0 && e < nh * W) {
+    p.dwq[e] = sq[0][el] + sq[1][el] + sq[2][el] + sq[3][el];
+    p.dwk[e] = sk[0][el] + sk[1][el] + sk[2][el] + sk[3][el];
   }
   if (p.da_log && blockIdx.x == 0) {
-    for (int64_t hh = threadIdx.x; hh < p.H; hh += 256) {
-      float s = 0.f;
-      for (int64_t bb = 0; bb < p.B; ++bb) s += p.da_part[bb * p.H + hh];
-      p.da_log[hh] = s;
+    for (int64_t hh = tid; hh < p.H; hh += 256) {
+      float s2 = 0.f;
+      for (int64_t bb = 0; bb < p.B; ++bb) s2 += p.da_part[bb * p.H + hh];
+      p.da_log[hh] = s2;
     }
   }
 }

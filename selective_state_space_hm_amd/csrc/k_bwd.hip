@@ -16,7 +16,7 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
   if (p.a_log) hipLaunchKernelGGL(bwd_decay, dim3(BH), dim3(256), 0, s, p);  // dt may be NULL only when n = 0
   const int per_head = p.sw_h != 0;
   const int64_t nw = (per_head ? p.H : 1) * (int64_t)DK * FH;
-  hipLaunchKernelGGL((bwd_reduce<DK, FH>), dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, s, p, per_head);
+  hipLaunchKernelGGL((bwd_reduce<DK, FH>), dim3((unsigned)((nw + 63) / 64)), dim3(256), 0, s, p, per_head);
 }
 
 #define HM_TRAIN(T, TC, DK, FH, DV) HM_FWD_ENTRY(T, TC, DK, FH, DV, 0, 2), HM_FWD_ENTRY(T, TC, DK, FH, DV, 1, 2)

@@ -43,6 +43,21 @@ def check(name, got, ref, tol):
     assert r <= tol, name
 
 
+def check_a_log(name, got, ref, c, tol):
+    """dA_log[h] sums d log a_t * log a_t over every (b, t) of head h; bound its error
+    by tol times the sum of the terms' magnitudes (the bound for a sum of mixed-sign
+    terms), the terms taken from the oracle: d log a_t = d dt_t / (-sigmoid(dt_t) e^{A_log})."""
+    dt = f64(c.dt)
+    e_a = np.exp(f64(c.a_log))[None, :, None]
+    la = -orc.softplus(dt) * e_a
+    dla = ref["dt"] / (-(1.0 / (1.0 + np.exp(-dt))) * e_a)
+    scale = np.abs(dla * la).sum(axis=(0, 2))
+    err = np.abs(f64(got) - ref["a_log"])
+    print(f"[parity] {name}: |err| {err.max():.3e}  bound {(tol * scale).min():.3e}  "
+          f"rel {np.linalg.norm(err) / np.linalg.norm(ref['a_log']):.3e}", flush=True)
+    assert np.all(err <= tol * scale), name
+
+
 def oracle_grads(c, d_o, s_init=None, d_s_final=None, w=None, gate=None):
     F, dv = 2 * c.f, c.dv
     S0 = z0 = dS = dz = None
@@ -67,8 +82,10 @@ def test_backward_fp32(n, decay, shape):
     gr = hm.hm_linattn_bwd(g["q"], g["k"], g["v"], wq, wk, d_o.cuda(), save, g["dt"], g["a_log"])
     torch.cuda.synchronize()
     ref = oracle_grads(c, d_o)
-    for name in ("q", "k", "v", "w_q", "w_k") + (("dt", "a_log") if decay else ()):
+    for name in ("q", "k", "v", "w_q", "w_k") + (("dt",) if decay else ()):
         check(f"bwd fp32 {shape} n={n} decay={decay} d{name}", gr[name], ref[name], FP32_TOL)
+    if decay:
+        check_a_log(f"bwd fp32 {shape} n={n} decay={decay} da_log", gr["a_log"], ref, c, FP32_TOL)
 
 
 @pytest.mark.parametrize("shape", [(128, 64, 128), (64, 32, 64)])
@@ -81,8 +98,10 @@ def test_backward_bf16_ragged(shape, decay):
     gr = hm.hm_linattn_bwd(g["q"], g["k"], g["v"], wq, wk, d_o.cuda(), save, g["dt"], g["a_log"])
     torch.cuda.synchronize()
     ref = oracle_grads(c, d_o)
-    for name in ("q", "k", "v", "w_q", "w_k") + (("dt", "a_log") if decay else ()):
+    for name in ("q", "k", "v", "w_q", "w_k") + (("dt",) if decay else ()):
         check(f"bwd bf16 {shape} decay={decay} d{name}", gr[name], ref[name], BF16_TOL)
+    if decay:
+        check_a_log(f"bwd bf16 {shape} decay={decay} da_log", gr["a_log"], ref, c, BF16_TOL)
 
 
 @pytest.mark.parametrize("segments", [1, 3])
@@ -104,8 +123,9 @@ def test_backward_state_gradients_fp32(segments):
     got_S, got_z = orc.unpack_state(f64(gr["s_init"]), 32, 32)
     check(f"bwd segs={segments} d s_init (S)", got_S, ref["s_init"], FP32_TOL)
     check(f"bwd segs={segments} d s_init (z)", got_z, ref["z_init"], FP32_TOL)
-    for name in ("q", "k", "v", "w_q", "w_k", "dt", "a_log"):
+    for name in ("q", "k", "v", "w_q", "w_k", "dt"):
         check(f"bwd segs={segments} d{name}", gr[name], ref[name], FP32_TOL)
+    check_a_log(f"bwd segs={segments} da_log", gr["a_log"], ref, c, FP32_TOL)
 
 
 def test_backward_per_head_weights_bf16():
@@ -119,8 +139,9 @@ def test_backward_per_head_weights_bf16():
     torch.cuda.synchronize()
     ref = oracle_grads(c, d_o, w=w)
     assert gr["w_q"].shape == (3, 64, 32)
-    for name in ("q", "k", "v", "w_q", "w_k", "dt", "a_log"):
+    for name in ("q", "k", "v", "w_q", "w_k", "dt"):
         check(f"bwd per-head W d{name}", gr[name], ref[name], BF16_TOL)
+    check_a_log("bwd per-head W da_log", gr["a_log"], ref, c, BF16_TOL)
 
 
 def test_backward_empty_sequence():
@@ -145,5 +166,6 @@ def test_backward_with_gate(dtype, shape):
     gr = hm.hm_linattn_bwd(g["q"], g["k"], g["v"], wq, wk, d_o.cuda(), save, g["dt"], g["a_log"], gate=gt.cuda())
     torch.cuda.synchronize()
     ref = oracle_grads(c, d_o, gate=gt)
-    for name in ("gate", "q", "k", "v", "w_q", "w_k", "dt", "a_log"):
+    for name in ("gate", "q", "k", "v", "w_q", "w_k", "dt"):
         check(f"bwd gated {dtype} d{name}", gr[name], ref[name], tol_for(dtype))
+    check_a_log(f"bwd gated {dtype} da_log", gr["a_log"], ref, c, tol_for(dtype))
