@@ -42,15 +42,33 @@ def features(x, w):
     return torch.softmax(torch.cat([u, -u], dim=-1), dim=-1)
 
 
-def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, gate=None):
+def rotate(phi, pos, dims, base):
+    """Rotary encoding of the features ([HM] §5.2 step 3) in the GPT-NeoX rotate-half
+    form: pair (i, i + dims/2) turns by pos * base^(-2i/dims); pos [B, n]."""
+    h = dims // 2
+    inv_freq = torch.pow(torch.tensor(float(base), dtype=_F64), -2.0 * torch.arange(h, dtype=_F64) / dims)
+    ang = torch.as_tensor(pos, dtype=_F64)[:, None, :, None] * inv_freq
+    c, s = torch.cos(ang), torch.sin(ang)
+    x1, x2 = phi[..., :h], phi[..., h:dims]
+    return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s, phi[..., dims:]], dim=-1)
+
+
+def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, gate=None,
+                  rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """Differentiable forward: returns (o [B,H,n,dv], S_final [B,H,F,dv], z_final [B,H,F]).
 
     L_t = sum_{s<=t} log a_s with log a_s = -softplus(dt_s) exp(A_log) ([SSM] §3.2);
     o_t = (sum_{j<=t} e^{L_t-L_j} (phiq_t.phik_j) v_j + e^{L_t} phiq_t S_init)
-          / (sum_{j<=t} e^{L_t-L_j} (phiq_t.phik_j) + e^{L_t} phiq_t.z_init).
+          / (sum_{j<=t} e^{L_t-L_j} (phiq_t.phik_j) + e^{L_t} phiq_t.z_init),
+    with phiq, phik rotated at positions rope_pos0[b] + t when rope_dims > 0.
     """
     phiq, phik = features(q, w_q), features(k, w_k)
     B, H, n, F = phiq.shape
+    if rope_dims:
+        p0 = torch.zeros(B, dtype=_F64) if rope_pos0 is None else torch.as_tensor(
+            np.asarray(rope_pos0, dtype=np.float64).reshape(B))
+        pos = p0[:, None] + torch.arange(n, dtype=_F64)[None, :]
+        phiq, phik = rotate(phiq, pos, rope_dims, rope_base), rotate(phik, pos, rope_dims, rope_base)
     dv = v.shape[-1]
     if dt is None:
         L = torch.zeros((B, H, n), dtype=_F64)
@@ -85,7 +103,7 @@ def forward_torch(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=No
 
 
 def grads(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, d_o=None, ds_final=None,
-          dz_final=None, gate=None):
+          dz_final=None, gate=None, rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """Gradients of loss = <o, dO> + <S_final, dS_final> + <z_final, dz_final>.
 
     Returns a dict with keys q, k, v, w_q, w_k and, when given, dt, a_log,
@@ -96,7 +114,7 @@ def grads(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, d_o=
                 dt=_t(dt, dt is not None), a_log=_t(a_log, a_log is not None),
                 s_init=_t(s_init, s_init is not None), z_init=_t(z_init, z_init is not None),
                 gate=_t(gate, gate is not None))
-    o, S, z = forward_torch(**args)
+    o, S, z = forward_torch(**args, rope_dims=rope_dims, rope_base=rope_base, rope_pos0=rope_pos0)
     loss = (o * _t(d_o)).sum()
     if ds_final is not None:
         loss = loss + (S * _t(ds_final)).sum()

@@ -22,6 +22,9 @@ What is computed, per (batch b, head h), for tokens t = 0..n-1:
   S_t = a_t S_{t-1} + phi(k_t) v_t^T,  z_t = a_t z_{t-1} + phi(k_t)
   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t                          [LA parts 2-3, 4.3; HM §2.3]
   optionally o_t <- o_t * SiLU(g_t) with the gate branch's g    [HM §5.2 step 6]
+  optionally phi(q_t), phi(k_t) turned by rotary position encoding before
+  both sums, so numerator and denominator see the rotated features
+                                                                 [HM §5.2 step 3]
 and, as a separate step ahead of the featurizer, Mamba's short causal conv
 (depthwise over time, K taps per channel, identity at the stage-1 init)
 [HM §2.2, §2.3 item 4, §3.1].
@@ -32,11 +35,14 @@ Readings where the pages are silent (listed with reasons in the design notes):
 one shared W per projection applied as x @ W with no bias or temperature;
 separate W_q, W_k; the u half precedes the -u half; no epsilon in the
 denominator; the denominator state is one F-vector because the decay is a
-per-head scalar.
+per-head scalar.  Rotary encoding follows GPT-NeoX (the architecture Pythia
+uses, which [HM §5.2] names): feature i of the leading `dims` pairs with feature
+i + dims/2 and turns by pos * base^(-2i/dims); features past `dims` pass
+through; positions count from a start offset per sequence.
 
-Every function here is pinned by tests/test_oracle.py against closed forms,
-library routines, brute force and invariants; there is no parity-unpinned
-function in this module.
+Every function here is pinned by tests/test_oracle.py (and the rotary
+encoding by tests/test_oracle_rope.py) against closed forms, library routines,
+brute force and invariants; there is no parity-unpinned function in this module.
 """
 from __future__ import annotations
 
@@ -243,14 +249,58 @@ def causal_conv(x, w, bias=None, prev=None):
 
 
 # --------------------------------------------------------------------------
+# Rotary position encoding of the features  [HM §5.2 step 3: RoPE on phi(Q)
+# and phi(K), as in the original Transformer and Pythia]
+# --------------------------------------------------------------------------
+def rope_angles(pos, dims, base=10000.0):
+    """theta[..., i] = pos * base^(-2i/dims) for the dims/2 rotation pairs (float64)."""
+    i = np.arange(dims // 2, dtype=np.float64)
+    inv_freq = np.power(float(base), -2.0 * i / dims)
+    return np.asarray(pos, dtype=np.float64)[..., None] * inv_freq
+
+
+def rope(phi, pos, dims, base=10000.0):
+    """Turn each pair (phi_i, phi_{i+dims/2}), i < dims/2, by the angle
+    pos * base^(-2i/dims):  (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin)
+    (the rotate-half form of GPT-NeoX); features at index >= dims are unchanged.
+
+    phi [..., n, F]; pos broadcasts against phi's [..., n] (e.g. [n] or [B, 1, n]);
+    dims is even and at most F; dims = 0 returns phi unchanged.
+    """
+    phi = np.asarray(phi, dtype=np.float64)
+    if dims == 0:
+        return phi.copy()
+    h = dims // 2
+    ang = rope_angles(pos, dims, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = phi[..., :h], phi[..., h:dims]
+    out = phi.copy()
+    out[..., :h] = x1 * c - x2 * s
+    out[..., h:dims] = x2 * c + x1 * s
+    return out
+
+
+def rope_positions(B, n, pos0=None):
+    """Positions [B, 1, n] of a prefill: pos0[b] + t (pos0 None = 0)."""
+    p0 = np.zeros(B) if pos0 is None else np.asarray(pos0, dtype=np.float64).reshape(B)
+    return (p0[:, None] + np.arange(n, dtype=np.float64)[None, :])[:, None, :]
+
+
+# --------------------------------------------------------------------------
 # Whole path and decode step
 # --------------------------------------------------------------------------
-def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, form="recurrent", gate=None):
+def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, form="recurrent", gate=None,
+            rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """Featurize q and k, then run the chosen form; a gate [B,H,n,dv] (pre-activation)
-    multiplies the output by SiLU(gate).  Returns (o, S_final, z_final); the
-    quadratic form returns None for the state."""
+    multiplies the output by SiLU(gate).  With rope_dims > 0 both feature maps are
+    rotated at positions rope_pos0[b] + t before the sums.  Returns (o, S_final,
+    z_final); the quadratic form returns None for the state."""
     phiq = hedgehog_features(q, w_q)
     phik = hedgehog_features(k, w_k)
+    if rope_dims:
+        pos = rope_positions(phiq.shape[0], phiq.shape[2], rope_pos0)
+        phiq = rope(phiq, pos, rope_dims, rope_base)
+        phik = rope(phik, pos, rope_dims, rope_base)
     v = np.asarray(v, dtype=np.float64)
     la = log_decay(dt, a_log)
     if form == "quadratic":
@@ -261,16 +311,19 @@ def forward(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, z_init=None, fo
     raise ValueError(form)
 
 
-def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None, gate=None):
+def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None, gate=None, rope_dims=0, rope_base=10000.0,
+         rope_pos=None):
     """One decode step from state (S [B,H,F,dv], z [B,H,F]) with one token per
-    (b, h): q, k [B,H,d], v [B,H,dv], dt [B,H], gate [B,H,dv] or None.
+    (b, h): q, k [B,H,d], v [B,H,dv], dt [B,H], gate [B,H,dv] or None, and with
+    rope_dims > 0 the token's position rope_pos [B].
     Returns (o [B,H,dv], S', z').  This is the recurrent form advanced by a single
     token  [LA part 5]."""
     q = np.asarray(q, dtype=np.float64)[:, :, None, :]
     k = np.asarray(k, dtype=np.float64)[:, :, None, :]
     v = np.asarray(v, dtype=np.float64)[:, :, None, :]
     dt3 = None if dt is None else np.asarray(dt, dtype=np.float64)[:, :, None]
-    o, S2, z2 = forward(q, k, v, w_q, w_k, dt3, a_log, S, z)
+    o, S2, z2 = forward(q, k, v, w_q, w_k, dt3, a_log, S, z, rope_dims=rope_dims, rope_base=rope_base,
+                        rope_pos0=rope_pos)
     return apply_gate(o[:, :, 0, :], gate), S2, z2
 
 
