@@ -11,7 +11,9 @@ Prints ONE JSON line.  Beside the headline prefill number it reports:
   * mfma: executed and algorithmic bf16 MFMA rates against the dense peak;
   * decode: the decode step at B=256, H=16 (state [128 x 129] float32 per head,
     4096-token prefix, 512 steps) against HBM bandwidth;
-  * prefill_extra: the Mamba-decay workloads (n=8192 and n=131072);
+  * prefill_extra: the gated layer, the rotary encoding of 32 and of all 128
+    features, the short conv and the stage-2 chain, a training step (forward
+    that saves + backward), the Mamba-decay workloads (n=8192 and n=131072);
   * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extra]
@@ -256,6 +258,21 @@ def main():
                       "tokens_per_s": tokens / (msg * 1e-3), "achieved_GBs": bg / (msg * 1e-3) / 1e9,
                       "hbm_frac": bg / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "plan": {"chunk": plan[0], "segments": plan[1], "dsplit": plan[2]}})
+        # the rotary encoding of the features on the same layer: a quarter of the
+        # features turned (Pythia's rotary share) and all of them
+        pos0 = torch.zeros(B, dtype=torch.int64, device=dev)
+        for dims in (32, 128):
+            log(f"[bench] rotary prefill dims={dims}, same layer")
+
+            def stepr():
+                hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], o=o, workspace=ws, rope_dims=dims,
+                                  rope_pos0=pos0)
+
+            msr, _ = time_launches(stepr, 50, 200, torch)
+            br = prefill_bytes(B, H, n, d, f, dv, False)
+            extra.append({"workload": f"{case.name} B={B} H={H} n={n}, identity decay, rotary encoding of "
+                                      f"{dims} of {2 * f} features", "ms": msr, "tokens_per_s": tokens / (msr * 1e-3),
+                          "achieved_GBs": br / (msr * 1e-3) / 1e9, "hbm_frac": br / (msr * 1e-3) / 1e9 / HBM_PEAK_GBS})
         # the mixer's short causal conv (K = 4) on q, alone and as part of the
         # stage-2 chain conv(q), conv(k) -> gated prefill
         cw = (torch.randn((d, 4), generator=torch.Generator().manual_seed(1)) / 2).to(dev)
@@ -381,6 +398,20 @@ def bench_decode(torch, hm, inputs, dev, ws):
     state.copy_(base)
     torch.cuda.synchronize()
     ms2 = time_launches(run_all2, 1, 0, torch)[0] / dc.steps
+    # the same steps with the rotary encoding of all features at each row's position
+    P0 = torch.full((dc.B,), dc.prefix, dtype=torch.int64, device=dev)
+    POS = P0[None, :] + torch.arange(dc.steps, dtype=torch.int64, device=dev)[:, None]
+
+    def run_all3():
+        for t in range(dc.steps):
+            hm.hm_linattn_step(Q[t], K[t], V[t], wq, wk, state, DT[t], a_log, o=O[t], rope_dims=2 * dc.f,
+                               rope_pos=POS[t])
+
+    state.copy_(base)
+    run_all3()
+    state.copy_(base)
+    torch.cuda.synchronize()
+    ms3 = time_launches(run_all3, 1, 0, torch)[0] / dc.steps
     F = 2 * dc.f
     per_bh = 2 * (F * dc.dv + F) * 4 + 2 * (2 * dc.d + 2 * dc.dv) + 4
     nbytes = dc.B * dc.H * per_bh + 2 * dc.d * dc.f * 2
@@ -393,7 +424,9 @@ def bench_decode(torch, hm, inputs, dev, ws):
                          "kernel": "hm::step_kernel<bf16,128,64,128,true>", "algorithmic_bytes_per_launch": nbytes},
             "stage2_step": {"workload": "same steps with q, k through the fused short conv (K=4, state in place) "
                                         "and the output gated", "ms_per_step": ms2,
-                            "tokens_per_s": dc.B / (ms2 * 1e-3)}}
+                            "tokens_per_s": dc.B / (ms2 * 1e-3)},
+            "rotary_step": {"workload": f"same steps with the rotary encoding of all {F} features",
+                            "ms_per_step": ms3, "tokens_per_s": dc.B / (ms3 * 1e-3)}}
 
 
 if __name__ == "__main__":

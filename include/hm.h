@@ -22,6 +22,26 @@
  *   o_t = phi(q_t)^T S_t / phi(q_t)^T z_t
  *   o_t <- o_t * SiLU(g_t)  when a gate g is given (the mixer's gate branch,
  *                           [HM] §5.2 step 6; SiLU(x) = x / (1 + e^-x))
+ * and, when rope_dims > 0, phi(q_t) and phi(k_t) are first turned by the rotary
+ * position encoding ([HM] §5.2 step 3, in the GPT-NeoX rotate-half form, the
+ * architecture of the Pythia models the page builds on): for i < rope_dims/2 the
+ * pair (phi_i, phi_{i + rope_dims/2}) becomes
+ *   (phi_i cos(p w_i) - phi_{i+r/2} sin(p w_i),  phi_{i+r/2} cos(p w_i) + phi_i sin(p w_i))
+ * with w_i = rope_base^(-2i/rope_dims) and p the token's position; entries from
+ * rope_dims on are unchanged.  Numerator and denominator both use the turned
+ * features.  They are signed, so the denominator is no longer positive by
+ * construction; no epsilon is added (o = num / den as defined).
+ *
+ * Rotary fields, shared by hm_featurize, hm_linattn_fwd, hm_linattn_bwd and
+ * hm_linattn_step: rope_dims 0 = off, else a multiple of 32, at most 2f
+ * (HM_ERR_SHAPE if negative, above 2f or odd; HM_ERR_UNSUPPORTED if even but not a
+ * multiple of 32); rope_base > 0 and finite (HM_ERR_SHAPE otherwise; 10000 in
+ * GPT-NeoX); positions: device int64, one per batch row, 8-byte aligned
+ * (HM_ERR_ALIGN): rope_pos0[b] is the position of token 0 of a prefill (NULL =
+ * 0 for every row), rope_pos[b] the position of a decode step's token (required).
+ * Each angle is formed and reduced to one turn in float64, then a float32 sine and
+ * cosine are taken: the angle's error is about p * 2^-52 radians (below 1e-6 for
+ * positions under 2^32).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library never
@@ -49,6 +69,9 @@
  *       hm_featurize:
  *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
  *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}
+ *       with rope_dims > 0, hm_linattn_fwd is built for bf16 (d, f) in
+ *       {(128, 64), (64, 32)} and f32 (d, f) in {(16, 16), (32, 16)}; the step and
+ *       the featurizer for every size above.
  *     B, H, n may be 0 (nothing to compute; s_final is still written).
  */
 #ifndef HM_H
@@ -61,7 +84,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 4
+#define HM_ABI_VERSION 5
 
 typedef enum {
   HM_OK = 0,
@@ -94,6 +117,9 @@ typedef struct {
   int64_t sx_b, sx_h, sx_t;
   int64_t sw_h;
   int64_t sp_b, sp_h, sp_t;
+  int32_t rope_dims;        /* 0 = off (see the rotary fields above) */
+  float rope_base;
+  const int64_t *rope_pos0; /* [B] position of token 0 of each row, or NULL */
 } hm_featurize_args;
 
 hm_status hm_featurize(const hm_featurize_args *args, void *stream);
@@ -149,6 +175,9 @@ typedef struct {
   int64_t sg_b, sg_h, sg_t;
   void *save;
   size_t save_bytes;
+  int32_t rope_dims;        /* 0 = off (see the rotary fields above) */
+  float rope_base;
+  const int64_t *rope_pos0; /* [B] position of token 0 of each row, or NULL */
 } hm_linattn_fwd_args;
 
 hm_status hm_linattn_fwd_workspace_size(const hm_linattn_fwd_args *args, size_t *bytes);
@@ -206,6 +235,9 @@ typedef struct {
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
   void *workspace;
   size_t workspace_bytes;
+  int32_t rope_dims;        /* the forward's rotary fields */
+  float rope_base;
+  const int64_t *rope_pos0;
 } hm_linattn_bwd_args;
 
 hm_status hm_linattn_bwd_workspace_size(const hm_linattn_bwd_args *args, size_t *bytes);
@@ -244,6 +276,9 @@ typedef struct {
   const float *conv_wq, *conv_wk, *conv_bq, *conv_bk;
   void *conv_sq, *conv_sk;
   int64_t scw_h, scb_h;
+  int32_t rope_dims;        /* 0 = off (see the rotary fields above) */
+  float rope_base;
+  const int64_t *rope_pos;  /* [B] position of each row's token (required when on) */
 } hm_linattn_step_args;
 
 hm_status hm_linattn_step(const hm_linattn_step_args *args, void *stream);

@@ -4,6 +4,7 @@
 
 #include <utility>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -37,13 +38,16 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
 
 struct Tables {
-  hm::Table parts[5];
+  hm::Table parts[8];
   Tables() {
     parts[0] = hm::table_fwd_bf16();
     parts[1] = hm::table_fwd_bf16_decay();
     parts[2] = hm::table_fwd_f32();
     parts[3] = hm::table_step_feat();
     parts[4] = hm::table_train();
+    parts[5] = hm::table_fwd_rope_bf16();
+    parts[6] = hm::table_fwd_rope_bf16_decay();
+    parts[7] = hm::table_fwd_rope_f32();
   }
 };
 const Tables &tables() {
@@ -74,6 +78,21 @@ const hm::FeatEntry *find_feat(int dt, int pdt, int64_t dk, int64_t fh) {
       if (e.dtype == dt && e.phi_dtype == pdt && e.dk == dk && e.fh == fh) return &e;
     }
   return nullptr;
+}
+
+// MODE_ROPE when the rotary encoding is on
+template <typename A> int rmode(const A *a) { return a->rope_dims ? hm::MODE_ROPE : 0; }
+
+// The rotary fields shared by the entry points (see hm.h).
+hm_status validate_rope(int32_t dims, float base, const int64_t *pos, int64_t f, bool pos_required) {
+  if (dims == 0) return ok();
+  if (dims < 0 || dims > 2 * f || dims % 2)
+    return fail(HM_ERR_SHAPE, "rope_dims %d: 0 or an even number of at most 2f = %lld", dims, (long long)(2 * f));
+  if (dims % 32) return fail(HM_ERR_UNSUPPORTED, "rope_dims %d: multiples of 32 are built", dims);
+  if (!(base > 0.f) || !std::isfinite(base)) return fail(HM_ERR_SHAPE, "rope_base must be positive and finite");
+  if (pos_required && !pos) return fail(HM_ERR_NULL, "rope_pos is required when rope_dims > 0");
+  if ((uintptr_t)pos % 8) return fail(HM_ERR_ALIGN, "rope positions must be 8-byte aligned");
+  return ok();
 }
 
 hm_status check_launch(const char *what) {
@@ -123,21 +142,25 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
   if (a->chunk != 0 && a->chunk != hm::CHUNK) return fail(HM_ERR_UNSUPPORTED, "chunk %d: only 0 (auto) or 64 are built", a->chunk);
+  {
+    const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
+    if (rs != HM_OK) return rs;
+  }
   if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0");
   if (a->dsplit < 0 || a->dsplit > 2) return fail(HM_ERR_UNSUPPORTED, "dsplit must be 0, 1 or 2");
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   // the full-pass kernel for dsplit 1 must exist for the size to count as supported
-  if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) &&
-      !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL))
+  if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)) &&
+      !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a)))
     return fail(HM_ERR_UNSUPPORTED, "no kernel built for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
                 (long long)a->f, (long long)a->dv);
-  if (a->dsplit == 2 && (a->dv % 2 || !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL)))
+  if (a->dsplit == 2 && (a->dv % 2 || !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a))))
     return fail(HM_ERR_UNSUPPORTED, "dsplit=2 is not built for dv=%lld", (long long)a->dv);
-  if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL))
+  if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)))
     return fail(HM_ERR_UNSUPPORTED, "dsplit=1 is not built for dv=%lld", (long long)a->dv);
   if (a->save) {
     if (a->dsplit > 1) return fail(HM_ERR_UNSUPPORTED, "saving for the backward pass runs with dsplit 1");
-    if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_TRAIN))
+    if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_TRAIN | rmode(a)))
       return fail(HM_ERR_UNSUPPORTED, "no training kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
                   (long long)a->d, (long long)a->f, (long long)a->dv);
     if (!aligned16(a->save)) return fail(HM_ERR_ALIGN, "save must be 16-byte aligned");
@@ -178,7 +201,7 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
   } else if (a->dsplit) {
     p.dsplit = a->dsplit;
   } else {
-    const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL) != nullptr;
+    const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)) != nullptr;
     p.dsplit = can1 ? 1 : 2;
   }
   const int64_t nchunks = (a->n + C - 1) / C;
@@ -250,8 +273,8 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   if (a->n == 0 && !a->s_final) return ok();
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int64_t dw = a->dv / pl.dsplit;
-  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, a->save ? hm::MODE_TRAIN : hm::MODE_FULL);
-  const hm::FwdEntry *local = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_LOCAL);
+  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, (a->save ? hm::MODE_TRAIN : hm::MODE_FULL) | rmode(a));
+  const hm::FwdEntry *local = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_LOCAL | rmode(a));
   if (!full || !local) return fail(HM_ERR_UNSUPPORTED, "no kernel for dv/dsplit=%lld", (long long)dw);
   hipStream_t s = (hipStream_t)stream;
 
@@ -276,6 +299,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
   p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
   p.gate = a->gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h; p.sg_t = a->sg_t;
+  p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
   p.seg_len = pl.seg_len;
   p.nseg = pl.segments;
   p.dsplit = pl.dsplit;
@@ -298,7 +322,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
     const hm::FwdEntry *loc = local;
     int lds = pl.dsplit;
     for (int cand = 4; cand > pl.dsplit; cand /= 2) {
-      const hm::FwdEntry *e = a->dv % cand ? nullptr : find_fwd(a->dtype, a->d, a->f, a->dv / cand, decay, hm::MODE_LOCAL);
+      const hm::FwdEntry *e = a->dv % cand ? nullptr : find_fwd(a->dtype, a->d, a->f, a->dv / cand, decay, hm::MODE_LOCAL | rmode(a));
       if (e && BH * (pl.segments - 1) * cand <= 256) {
         loc = e;
         lds = cand;
@@ -371,10 +395,11 @@ BwdLayout bwd_layout(const hm_linattn_bwd_args *a) {
   l.bytes = o;
   return l;
 }
-const hm::BwdEntry *find_bwd(int dt, int64_t dk, int64_t fh, int64_t dv) {
+const hm::BwdEntry *find_bwd(int dt, int64_t dk, int64_t fh, int64_t dv, int rope) {
   const hm::BwdTable t = hm::table_bwd();
   for (int i = 0; i < t.nbwd; ++i)
-    if (t.bwd[i].dtype == dt && t.bwd[i].dk == dk && t.bwd[i].fh == fh && t.bwd[i].dv == dv) return &t.bwd[i];
+    if (t.bwd[i].dtype == dt && t.bwd[i].dk == dk && t.bwd[i].fh == fh && t.bwd[i].dv == dv && t.bwd[i].rope == rope)
+      return &t.bwd[i];
   return nullptr;
 }
 hm_status validate_bwd(const hm_linattn_bwd_args *a) {
@@ -409,7 +434,11 @@ hm_status validate_bwd(const hm_linattn_bwd_args *a) {
     if (!aligned16(p)) return fail(HM_ERR_ALIGN, "tensors, save and workspace must be 16-byte aligned");
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
-  if (!find_bwd(a->dtype, a->d, a->f, a->dv))
+  {
+    const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
+    if (rs != HM_OK) return rs;
+  }
+  if (!find_bwd(a->dtype, a->d, a->f, a->dv, a->rope_dims != 0))
     return fail(HM_ERR_UNSUPPORTED, "no backward kernels for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
                 (long long)a->d, (long long)a->f, (long long)a->dv);
   return ok();
@@ -455,7 +484,8 @@ hm_status hm_linattn_bwd(const hm_linattn_bwd_args *a, void *stream) {
   p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t; p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
   p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
   p.ngrp = wl.ngrp;
-  find_bwd(a->dtype, a->d, a->f, a->dv)->launch(p, (hipStream_t)stream);
+  p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
+  find_bwd(a->dtype, a->d, a->f, a->dv, a->rope_dims != 0)->launch(p, (hipStream_t)stream);
   return check_launch("backward");
 }
 
@@ -494,6 +524,10 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
         ((uintptr_t)a->conv_sq | (uintptr_t)a->conv_sk) & ea)
       return fail(HM_ERR_ALIGN, "conv taps, bias and states must be aligned to their element size");
   }
+  {
+    const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos, a->f, a->B * a->H > 0);
+    if (rs != HM_OK) return rs;
+  }
   const int decay = a->dt != nullptr;
   const hm::StepEntry *e = find_step(a->dtype, a->d, a->f, a->dv, decay);
   if (!e)
@@ -512,6 +546,7 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   p.cwidth = a->conv_width;
   p.cwq = a->conv_wq; p.cwk = a->conv_wk; p.cbq = a->conv_bq; p.cbk = a->conv_bk;
   p.csq = a->conv_sq; p.csk = a->conv_sk; p.scw_h = a->scw_h; p.scb_h = a->scb_h;
+  p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos = a->rope_pos;
   e->launch(p, (unsigned)BH, (hipStream_t)stream);
   return check_launch("decode step");
 }
@@ -597,6 +632,10 @@ hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
       !stride_ok(a->sw_h, a->dtype) || !stride_ok(a->sp_b, a->phi_dtype) || !stride_ok(a->sp_h, a->phi_dtype) ||
       !stride_ok(a->sp_t, a->phi_dtype))
     return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  {
+    const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
+    if (rs != HM_OK) return rs;
+  }
   const hm::FeatEntry *e = find_feat(a->dtype, a->phi_dtype, a->d, a->f);
   if (!e)
     return fail(HM_ERR_UNSUPPORTED, "no featurize kernel for dtype=%d phi_dtype=%d d=%lld f=%lld", a->dtype,
@@ -608,6 +647,7 @@ hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
   p.B = a->B; p.H = a->H; p.n = a->n;
   p.sx_b = a->sx_b; p.sx_h = a->sx_h; p.sx_t = a->sx_t; p.sw_h = a->sw_h;
   p.sp_b = a->sp_b; p.sp_h = a->sp_h; p.sp_t = a->sp_t;
+  p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
   e->launch(p, dim3((unsigned)((a->n + 63) / 64), (unsigned)BH), (hipStream_t)stream);
   return check_launch("featurize");
 }

@@ -27,6 +27,10 @@
 //   through the maps: du'_q = phiq * dphiq (the max shift is a scale);
 //     du'_k = phik * (dphik - phik . dphik) (softmax); du = du'[:f] - du'[f:];
 //     dx = du W^T, dW = sum_t x_t^T du_t.
+//   With the rotary encoding every product above runs on the turned features
+//   (bwd_prep stores them turned); only the maps' backward needs the unturned
+//   phi and dphi, which are the transposed rotation applied to both (the dot
+//   product phik . dphik is the same in either frame).
 // Kernels, launched in this order on one stream:
 //   bwd_prep   (per chunk)  features, dnum, dden, L
 //   bwd_gstate (per (b,h), chunks last to first)  G, g at every chunk end; dS_init
@@ -175,6 +179,55 @@ __device__ __forceinline__ void load_w(T *dst, int ld, const T *w, bool transpos
   }
 }
 
+// du'[f] = phi_u[f] * (dphi_u[f] - dot) in place of dph, for the rows t = 4g + r
+// of a 16-row band whose features sit as dph[ft][r] (column 16 ft + lane % 16):
+// phi is read from the LDS rows ph + (4g + r) * ld in the turned frame, and phi_u,
+// dphi_u are phi and dph turned back (RT = dims / 32 feature tiles pair with the
+// tiles RT later; RT = 0 means no rotation).  pos is the position of row 4g.
+template <int NFT, int RT, typename T>
+__device__ __forceinline__ void phi_dphi_rt(f32x4 *dph, const T *ph, int ld, const double *rev, double pos,
+                                            const float *dot) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ft = 0; ft < NFT; ++ft) {
+    if (ft < RT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const T *row = ph + (4 * g + r) * ld;
+        float c, s, p1 = (float)row[16 * ft + i], p2 = (float)row[16 * (ft + RT) + i];
+        float d1 = dph[ft][r], d2 = dph[ft + RT][r];
+        rope_cs(rev[16 * ft + i], pos + r, c, s);
+        rope_turn<true>(p1, p2, c, s);
+        rope_turn<true>(d1, d2, c, s);
+        dph[ft][r] = p1 * (d1 - dot[r]);
+        dph[ft + RT][r] = p2 * (d2 - dot[r]);
+      }
+    } else if (ft >= 2 * RT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dph[ft][r] = (float)ph[(4 * g + r) * ld + 16 * ft + i] * (dph[ft][r] - dot[r]);
+    }
+  }
+}
+template <int NFT, typename T>
+__device__ __forceinline__ void phi_dphi(f32x4 *dph, const T *ph, int ld, const double *rev, double pos,
+                                         const float *dot, int dims) {
+  switch (dims >> 5) {
+    case 0: phi_dphi_rt<NFT, 0>(dph, ph, ld, rev, pos, dot); break;
+    case 1: phi_dphi_rt<NFT, 1>(dph, ph, ld, rev, pos, dot); break;
+    case 2: if constexpr (NFT >= 4) phi_dphi_rt<NFT, 2>(dph, ph, ld, rev, pos, dot); break;
+    case 3: if constexpr (NFT >= 6) phi_dphi_rt<NFT, 3>(dph, ph, ld, rev, pos, dot); break;
+    case 4: if constexpr (NFT >= 8) phi_dphi_rt<NFT, 4>(dph, ph, ld, rev, pos, dot); break;
+    default: break;
+  }
+}
+// Each thread's share of the rotation rates rope_rev(i) for i < dims/2, into LDS.
+__device__ __forceinline__ void fill_rev(double *rev, const BwdParams &p) {
+  if ((int)threadIdx.x < p.rope_dims / 2) rev[threadIdx.x] = rope_rev(threadIdx.x, p.rope_dims, p.rope_base);
+}
+__device__ __forceinline__ double pos_of(const BwdParams &p, int64_t b) {
+  return p.rope_pos0 ? (double)p.rope_pos0[b] : 0.0;
+}
+
 __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 1);
   v += __shfl_xor(v, 2);
@@ -195,13 +248,14 @@ __device__ __forceinline__ void chunk_range(const BwdParams &p, int grp, int64_t
 // ---------------------------------------------------------------- bwd_prep
 // One workgroup per (b, h, chunk): phiq (unnormalized, as the forward computed
 // it), phik (softmax), dnum, dden and L for the chunk's tokens.
-template <typename T, int DK, int FH, int DV>
+template <typename T, int DK, int FH, int DV, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDW = DK + PAD, E = ep<T>();
   constexpr float L2E = 1.4426950408889634f;
   __shared__ __align__(16) T sW[2][FH * LDW];
   __shared__ __align__(16) T sX[C * LDW];
+  __shared__ double sRev[ROPE ? FH : 1];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // one chunk per workgroup: many small workgroups hide the latency best here
@@ -209,6 +263,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   const int64_t c0 = blockIdx.x % p.nch, c1 = c0 + 1;
   load_w<T, DK, FH>(sW[0], LDW, (const T *)p.wq + h * p.sw_h, true);
   load_w<T, DK, FH>(sW[1], LDW, (const T *)p.wk + h * p.sw_h, true);
+  if constexpr (ROPE) fill_rev(sRev, p);
   for (int64_t c = c0; c < c1; ++c) {
   const int64_t t0 = c * C;
   const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
@@ -239,13 +294,18 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
       }
     const float inv = proj == 1 ? __builtin_amdgcn_rcpf(group_sum(sum)) : 1.f;
     const int t = 16 * w + i;
+    // the feature row of token t: tile rt < FH/16 from +u, the rest from -u
+    f32x4 ph4[F / 16];
+#pragma unroll
+    for (int rt = 0; rt < FH / 16; ++rt) {
+      ph4[rt] = ep_[rt] * inv;
+      ph4[FH / 16 + rt] = em_[rt] * inv;
+    }
+    if constexpr (ROPE) rope_apply<F / 16>(ph4, sRev, g, pos_of(p, b) + (double)(t0 + t), p.rope_dims);
     if (t < nv) {
       T *ph = (T *)(proj == 0 ? p.phq : p.phk) + (bh * p.n + t0 + t) * F;
 #pragma unroll
-      for (int rt = 0; rt < FH / 16; ++rt) {
-        store4(ph + 16 * rt + 4 * g, ep_[rt] * inv);       // four consecutive features per lane
-        store4(ph + FH + 16 * rt + 4 * g, em_[rt] * inv);
-      }
+      for (int ft = 0; ft < F / 16; ++ft) store4(ph + 16 * ft + 4 * g, ph4[ft]);  // four consecutive features per lane
     }
     __syncthreads();
   }
@@ -395,7 +455,7 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_dq
 // dphiq -> du_q -> dq = du_q W_q^T, and this workgroup's share of dW_q.
-template <typename T, int DK, int FH, int DV>
+template <typename T, int DK, int FH, int DV, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
@@ -404,6 +464,7 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
                 OS = OKT + F * LC, ODU = OS + F * LS, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
   __shared__ __align__(16) T sm[TOT];
   __shared__ float sL[C], sdd[C], sz[F];
+  __shared__ double sRev[ROPE ? FH : 1];
   T *sW = sm + OW, *sDN = sm + ON, *sVQ = sm + OVQ, *sA = sm + OA, *sKT = sm + OKT, *sS = sm + OS, *sDu = sm + ODU,
     *sDuT = sm + ODUT, *sXT = sm + OXT;
   constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
@@ -414,6 +475,8 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   int64_t c0, c1;
   chunk_range(p, grp, c0, c1);
   load_w<T, DK, FH>(sW, LW, (const T *)p.wq + h * p.sw_h, false);
+  if constexpr (ROPE) fill_rev(sRev, p);
+  const double pos_b = ROPE ? pos_of(p, b) : 0.0;
   f32x4 dW[NTW];
 #pragma unroll
   for (int m = 0; m < NTW; ++m) dW[m] = zero4();
@@ -470,14 +533,19 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
         if (i == 0 && t < nv) p.eQ[bh * p.n + t0 + t] = q4;
       }
     }
-    // du_q = phiq * dphiq over [u, -u]: du[f] = du'[f] - du'[f + FH]
+    // du_q = phiq * dphiq over [u, -u] (unturned frame): du[f] = du'[f] - du'[f + FH]
+    if constexpr (ROPE) {
+      const float zero[4] = {0.f, 0.f, 0.f, 0.f};
+      phi_dphi<F / 16>(dph, sVQ + 16 * w * LVQ, LVQ, sRev, pos_b + (double)(t0 + 16 * w + 4 * g), zero, p.rope_dims);
+    }
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       f32x4 du;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * w + 4 * g + r, f = 16 * ft + i;
-        du[r] = (float)sVQ[t * LVQ + f] * dph[ft][r] - (float)sVQ[t * LVQ + FH + f] * dph[ft + FT][r];
+        du[r] = ROPE ? dph[ft][r] - dph[ft + FT][r]
+                     : (float)sVQ[t * LVQ + f] * dph[ft][r] - (float)sVQ[t * LVQ + FH + f] * dph[ft + FT][r];
       }
       put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
       put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
@@ -515,7 +583,7 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_dk
 // dphik -> dL_t and du_k (softmax) -> dk = du_k W_k^T, and the share of dW_k.
-template <typename T, int DK, int FH, int DV>
+template <typename T, int DK, int FH, int DV, bool ROPE>
 __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
@@ -524,6 +592,7 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
                 OG = OQT + F * LC, ODU = OG + F * LG, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
   __shared__ __align__(16) T sm[TOT];
   __shared__ float sL[C], sdd[C], sg[F];
+  __shared__ double sRev[ROPE ? FH : 1];
   T *sW = sm + OW, *sV = sm + OV, *sNK = sm + ONK, *sAT = sm + OA, *sQT = sm + OQT, *sG = sm + OG, *sDu = sm + ODU,
     *sDuT = sm + ODUT, *sXT = sm + OXT;
   constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
@@ -534,6 +603,8 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   int64_t c0, c1;
   chunk_range(p, grp, c0, c1);
   load_w<T, DK, FH>(sW, LW, (const T *)p.wk + h * p.sw_h, false);
+  if constexpr (ROPE) fill_rev(sRev, p);
+  const double pos_b = ROPE ? pos_of(p, b) : 0.0;
   f32x4 dW[NTW];
 #pragma unroll
   for (int m = 0; m < NTW; ++m) dW[m] = zero4();
@@ -595,13 +666,18 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
       const float k4 = sum16(ks[r]);
       if (p.a_log && i == 0 && j < nv) p.eK[bh * p.n + t0 + j] = k4;
     }
+    // du_k = phik * (dphik - phik . dphik) over [u, -u] (unturned frame)
+    if constexpr (ROPE)
+      phi_dphi<F / 16>(dph, sNK + 16 * w * LNK, LNK, sRev, pos_b + (double)(t0 + 16 * w + 4 * g), dot, p.rope_dims);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       f32x4 du;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * w + 4 * g + r, f = 16 * ft + i;
-        du[r] = (float)sNK[j * LNK + f] * (dph[ft][r] - dot[r]) - (float)sNK[j * LNK + FH + f] * (dph[ft + FT][r] - dot[r]);
+        du[r] = ROPE ? dph[ft][r] - dph[ft + FT][r]
+                     : (float)sNK[j * LNK + f] * (dph[ft][r] - dot[r]) -
+                           (float)sNK[j * LNK + FH + f] * (dph[ft + FT][r] - dot[r]);
       }
       put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
       put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);

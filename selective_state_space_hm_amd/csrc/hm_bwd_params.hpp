@@ -30,6 +30,9 @@ struct BwdParams {
   int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
   int ngrp;                  // chunk ranges per (b, h) in bwd_dq / bwd_dk / bwd_dv
+  int rope_dims;             // the forward's rotary encoding (0 = off)
+  float rope_base;
+  const int64_t *rope_pos0;  // position of token 0 per batch row (NULL = 0)
 };
 
 }  // namespace hm

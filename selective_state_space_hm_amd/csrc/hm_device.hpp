@@ -151,6 +151,65 @@ __device__ __forceinline__ float silu_f32(float x) {
 
 template <typename T> __device__ __forceinline__ T to_elem(float x) { return (T)x; }
 
+// Rotary position encoding of the features (HedgeMamba explainer §5.2 step 3, in
+// the GPT-NeoX rotate-half form): feature i < dims/2 pairs with i + dims/2 and the
+// pair turns by pos * base^(-2i/dims).  rope_rev is that rate in revolutions per
+// position, in float64; rope_cs reduces pos * rate to [-1/2, 1/2] revolutions in
+// float64, so the hardware sine and cosine (which take revolutions; about 1.2e-7
+// absolute error on that range, measured) see an argument exact to float32
+// rounding at any position.
+__device__ inline double rope_rev(int i, int dims, float base) {
+  return exp2(-2.0 * (double)i / (double)dims * log2((double)base)) * 0.15915494309189535;  // / (2 pi)
+}
+__device__ __forceinline__ void rope_cs(double rev, double pos, float &c, float &s) {
+  double r = pos * rev;
+  r -= __builtin_rint(r);
+  const float x = (float)r;
+  c = __builtin_amdgcn_cosf(x);
+  s = __builtin_amdgcn_sinf(x);
+}
+// (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) forward (INV = false), the transpose
+// (x1 c + x2 s, x2 c - x1 s) for INV = true.
+template <bool INV>
+__device__ __forceinline__ void rope_turn(float &x1, float &x2, float c, float s) {
+  const float a = x1, b = x2;
+  if constexpr (INV) {
+    x1 = __builtin_fmaf(a, c, b * s);
+    x2 = __builtin_fmaf(b, c, -(a * s));
+  } else {
+    x1 = __builtin_fmaf(a, c, -(b * s));
+    x2 = __builtin_fmaf(b, c, a * s);
+  }
+}
+// Features held as 16-feature tiles of one token per lane (tile t, slot r is feature
+// 16t + 4g + r): the pair partner of tile t is tile t + RT, RT = dims/32, in the
+// same lane and slot.  rev[i] is rope_rev(i, ...) for i < dims/2.
+template <int RT, bool INV>
+__device__ __forceinline__ void rope_tiles(f32x4 *ph, const double *rev, int g, double pos) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float c, s, x1 = ph[t][r], x2 = ph[t + RT][r];
+      rope_cs(rev[16 * t + 4 * g + r], pos, c, s);
+      rope_turn<INV>(x1, x2, c, s);
+      ph[t][r] = x1;
+      ph[t + RT][r] = x2;
+    }
+}
+// dims (a multiple of 32, at most 16*NFT) picks the tile pairing at run time; the
+// switch is uniform, each arm fully unrolled.
+template <int NFT, bool INV = false>
+__device__ __forceinline__ void rope_apply(f32x4 *ph, const double *rev, int g, double pos, int dims) {
+  switch (dims >> 5) {
+    case 1: rope_tiles<1, INV>(ph, rev, g, pos); break;
+    case 2: if constexpr (NFT >= 4) rope_tiles<2, INV>(ph, rev, g, pos); break;
+    case 3: if constexpr (NFT >= 6) rope_tiles<3, INV>(ph, rev, g, pos); break;
+    case 4: if constexpr (NFT >= 8) rope_tiles<4, INV>(ph, rev, g, pos); break;
+    default: break;
+  }
+}
+
 // Four consecutive elements as one vector store / load.
 __device__ __forceinline__ void store4(bf16 *p, f32x4 v) {
   *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};

@@ -42,7 +42,7 @@ struct ConvTable {
 
 struct BwdParams;
 struct BwdEntry {
-  int dtype, dk, fh, dv;
+  int dtype, dk, fh, dv, rope;
   void (*launch)(const BwdParams &, hipStream_t);
 };
 struct BwdTable {
@@ -57,6 +57,9 @@ Table table_train();
 Table table_fwd_bf16();
 Table table_fwd_bf16_decay();
 Table table_fwd_f32();
+Table table_fwd_rope_bf16();
+Table table_fwd_rope_bf16_decay();
+Table table_fwd_rope_f32();
 Table table_step_feat();
 
 template <typename T, int DK, int FH, int DW, bool DECAY, int MODE>
@@ -87,3 +90,6 @@ void launch_feat(const FeatParams &p, dim3 grid, hipStream_t s) {
 // both modes of one configuration
 #define HM_FWD_PAIR(T, TC, DK, FH, DW, DEC) \
   HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 0), HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 1)
+// both modes with the rotary encoding (MODE_ROPE = 4)
+#define HM_ROPE_PAIR(T, TC, DK, FH, DW, DEC) \
+  HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 4), HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 5)

@@ -40,8 +40,10 @@
 namespace hm {
 
 constexpr int CHUNK = 64;
-// MODE_TRAIN is the full pass that also saves what the backward pass reads.
-enum { MODE_FULL = 0, MODE_LOCAL = 1, MODE_TRAIN = 2 };
+// MODE_TRAIN is the full pass that also saves what the backward pass reads;
+// MODE_ROPE, or'ed into any of them, turns phi(q) and phi(k) by their positions
+// (rotary encoding, HedgeMamba explainer §5.2 step 3) before they are used.
+enum { MODE_FULL = 0, MODE_LOCAL = 1, MODE_TRAIN = 2, MODE_ROPE = 4 };
 
 struct FwdParams {
   const void *q, *k, *v, *wq, *wk;
@@ -67,6 +69,9 @@ struct FwdParams {
   int nseg;               // segments of the whole sequence
   int nseg_run;           // segments covered by this launch (nseg, or nseg-1 for MODE_LOCAL)
   int dsplit;             // workgroups per item, each owning dv/dsplit columns
+  int rope_dims;          // MODE_ROPE: rotated features (multiple of 32, <= F)
+  float rope_base;
+  const int64_t *rope_pos0;  // MODE_ROPE: position of token 0 per batch row (NULL = 0)
 };
 
 template <typename F> __device__ __forceinline__ F zfrag() { return F{}; }
@@ -118,8 +123,9 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   constexpr int EPL = M::EPL;              // operand elements per lane
   constexpr int PAD = M::PAD;
   constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD, LDO = DW + 32 / (int)sizeof(T);
-  constexpr bool FULL = MODE != MODE_LOCAL;
-  constexpr bool SAVE = MODE == MODE_TRAIN;
+  constexpr bool FULL = (MODE & 3) != MODE_LOCAL;
+  constexpr bool SAVE = (MODE & 3) == MODE_TRAIN;
+  constexpr bool ROPE = (MODE & MODE_ROPE) != 0;
   constexpr int TPF_ = FULL ? 2 : 1;       // featurize tasks per feature wave
   constexpr int KVL = EPL == 8 ? 1 : 4;    // K-steps of the v re-layout per tile
   constexpr float L2E = 1.4426950408889634f;
@@ -142,6 +148,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   __shared__ __align__(16) float sDenPart[NCT][C];
   __shared__ __align__(16) float sDenInter[2][C];
   __shared__ __align__(16) float sZ[2][F];                  // z after each chunk (by chunk parity)
+  __shared__ __align__(16) double sRev[ROPE ? F / 2 : 1];   // rotation rate of each feature pair
 
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: lets the compiler keep it scalar
@@ -172,6 +179,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   T *O = (T *)p.o + b * p.so_b + h * p.so_h;
   const float *DT = DECAY ? p.dt + b * p.sdt_b + h * p.sdt_h : nullptr;
   const float expA = DECAY ? expf(p.a_log[h]) : 1.f;
+  double pos_b = 0.0;  // position of token 0 of this sequence
+  if constexpr (ROPE) {
+    if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
+    pos_b = p.rope_pos0 ? (double)p.rope_pos0[b] : 0.0;
+  }
 
   // W^T into LDS: sW[f][d] = W[d][f].  W is read as 16-byte vectors, all of them
   // issued before the first LDS write.
@@ -428,6 +440,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           // phi(q) unnormalized: a positive per-query factor cancels in o's ratio.
           // den_inter = e^{L_c} phiQ_c . z, with z at the end of the previous chunk.
           features(uq, ph);
+          if constexpr (ROPE) rope_apply<NFT>(ph, sRev, g, pos_b + (double)(tf + cr), p.rope_dims);
 #pragma unroll
           for (int s = 0; s < KF; ++s) qf[s] = M::from_acc(ph, s);
           store_frags(&sQ[bf][cr * LDQ], qf, ph);
@@ -449,6 +462,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           }
 #pragma unroll
           for (int t = 0; t < NFT; ++t) ph[t] *= inv;
+          if constexpr (ROPE) rope_apply<NFT>(ph, sRev, g, pos_b + (double)(tf + cr), p.rope_dims);
 #pragma unroll
           for (int s = 0; s < KF; ++s) kf[s] = M::from_acc(ph, s);
           if constexpr (FULL) {

@@ -28,6 +28,10 @@ struct StepParams {
   void *csq, *csk;
   int cwidth;
   int64_t scw_h, scb_h;
+  // optional rotary encoding of phi(q) and phi(k) (dims 0 = off) at rope_pos[b]
+  int rope_dims;
+  float rope_base;
+  const int64_t *rope_pos;
 };
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
@@ -133,6 +137,20 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
     }
   }
   __syncthreads();
+  if (p.rope_dims > 0) {
+    // rotary encoding (HedgeMamba explainer §5.2 step 3): thread (row w, pair i)
+    // turns features i and i + dims/2 of phi(q) (w = 0) or phi(k) (w = 1)
+    const int hr = p.rope_dims / 2;
+    if (tid < 2 * hr) {
+      const int w = tid / hr, i = tid % hr;
+      float c, s, x1 = sphi[w][i], x2 = sphi[w][i + hr];
+      rope_cs(rope_rev(i, p.rope_dims, p.rope_base), (double)p.rope_pos[b], c, s);
+      rope_turn<false>(x1, x2, c, s);
+      sphi[w][i] = x1;
+      sphi[w][i + hr] = x2;
+    }
+    __syncthreads();
+  }
 
   // 3. update, read out, store.  Thread tid owns column group c4 = tid % RV and
   //    rows f = tid / RV + GROUPS * m.
@@ -178,6 +196,9 @@ struct FeatParams {
   void *phi;
   int64_t B, H, n;
   int64_t sx_b, sx_h, sx_t, sw_h, sp_b, sp_h, sp_t;
+  int rope_dims;              // rotary encoding of phi (0 = off)
+  float rope_base;
+  const int64_t *rope_pos0;   // position of token 0 per batch row (NULL = 0)
 };
 
 // Standalone Hedgehog featurizer (gsyq.cn HedgeMamba explainer §2.1, §5.3):
@@ -190,10 +211,12 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   using frag = typename M::frag;
   constexpr int NFH = FH / 16, NFT = 2 * NFH, KD = DK / M::KS, LDW = DK + M::PAD;
   __shared__ __align__(16) T sW[FH * LDW];
+  __shared__ double sRev[FH];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
   const T *W = (const T *)p.w + h * p.sw_h;
   for (int i = tid; i < DK * FH; i += 256) sW[(i % FH) * LDW + i / FH] = W[i];
+  if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
   const int64_t c = (int64_t)blockIdx.x * 64 + 16 * wv + col;
   const T *X = (const T *)p.x + b * p.sx_b + h * p.sx_h + c * p.sx_t;
   frag xf[KD];
@@ -226,6 +249,10 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
     }
   sum = group_sum(sum);
   const float inv = 1.f / sum;
+  if (p.rope_dims > 0) {
+    const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + c);
+    rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);
+  }
   if (c < p.n) {
     TO *P = (TO *)p.phi + b * p.sp_b + h * p.sp_h + c * p.sp_t;
 #pragma unroll

@@ -1,17 +1,18 @@
-// Training-mode prefill and backward-pass instantiations: bf16 (d, f, dv) =
-// (64, 32, 64) and (128, 64, 128); float32 (16, 16, 16) and (32, 16, 32).
+// Training-mode prefill (with and without the rotary encoding) and backward-pass
+// instantiations: bf16 (d, f, dv) = (64, 32, 64) and (128, 64, 128); float32
+// (16, 16, 16) and (32, 16, 32).
 #include "hm_bwd.hpp"
 #include "hm_kernels.hpp"
 
 namespace hm {
 
-template <typename T, int DK, int FH, int DV>
+template <typename T, int DK, int FH, int DV, bool ROPE>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
   const unsigned BH = (unsigned)(p.B * p.H);
-  if (p.nch > 0) hipLaunchKernelGGL((bwd_prep<T, DK, FH, DV>), dim3(BH * (unsigned)p.nch), dim3(256), 0, s, p);
+  if (p.nch > 0) hipLaunchKernelGGL((bwd_prep<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.nch), dim3(256), 0, s, p);
   hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV>), dim3(BH), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((bwd_dq<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
   if (p.nch > 0) hipLaunchKernelGGL((bwd_dv<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
   if (p.a_log) hipLaunchKernelGGL(bwd_decay, dim3(BH), dim3(256), 0, s, p);  // dt may be NULL only when n = 0
   const int per_head = p.sw_h != 0;
@@ -19,12 +20,15 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
   hipLaunchKernelGGL((bwd_reduce<DK, FH>), dim3((unsigned)((nw + 63) / 64)), dim3(256), 0, s, p, per_head);
 }
 
-#define HM_TRAIN(T, TC, DK, FH, DV) HM_FWD_ENTRY(T, TC, DK, FH, DV, 0, 2), HM_FWD_ENTRY(T, TC, DK, FH, DV, 1, 2)
+#define HM_TRAIN(T, TC, DK, FH, DV)                                                   \
+  HM_FWD_ENTRY(T, TC, DK, FH, DV, 0, 2), HM_FWD_ENTRY(T, TC, DK, FH, DV, 1, 2),      \
+      HM_FWD_ENTRY(T, TC, DK, FH, DV, 0, 6), HM_FWD_ENTRY(T, TC, DK, FH, DV, 1, 6)
 static const FwdEntry kTrain[] = {
     HM_TRAIN(bf16, HM_DT_BF16, 64, 32, 64), HM_TRAIN(bf16, HM_DT_BF16, 128, 64, 128),
     HM_TRAIN(float, HM_DT_F32, 16, 16, 16), HM_TRAIN(float, HM_DT_F32, 32, 16, 32),
 };
-#define HM_BWD(T, TC, DK, FH, DV) {TC, DK, FH, DV, &launch_bwd<T, DK, FH, DV>}
+#define HM_BWD(T, TC, DK, FH, DV) \
+  {TC, DK, FH, DV, 0, &launch_bwd<T, DK, FH, DV, false>}, {TC, DK, FH, DV, 1, &launch_bwd<T, DK, FH, DV, true>}
 static const BwdEntry kBwd[] = {
     HM_BWD(bf16, HM_DT_BF16, 64, 32, 64), HM_BWD(bf16, HM_DT_BF16, 128, 64, 128),
     HM_BWD(float, HM_DT_F32, 16, 16, 16), HM_BWD(float, HM_DT_F32, 32, 16, 32),

@@ -30,7 +30,8 @@ class FeaturizeArgs(C.Structure):
     _fields_ = [("x", p_void), ("w", p_void), ("phi", p_void), ("dtype", i32), ("phi_dtype", i32),
                 ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64),
                 ("sx_b", i64), ("sx_h", i64), ("sx_t", i64), ("sw_h", i64),
-                ("sp_b", i64), ("sp_h", i64), ("sp_t", i64)]
+                ("sp_b", i64), ("sp_h", i64), ("sp_t", i64),
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void)]
 
 
 class FwdArgs(C.Structure):
@@ -43,7 +44,8 @@ class FwdArgs(C.Structure):
                 ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
                 ("workspace", p_void), ("workspace_bytes", C.c_size_t),
                 ("gate", p_void), ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
-                ("save", p_void), ("save_bytes", C.c_size_t)]
+                ("save", p_void), ("save_bytes", C.c_size_t),
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void)]
 
 
 class StepArgs(C.Structure):
@@ -55,7 +57,8 @@ class StepArgs(C.Structure):
                 ("so_b", i64), ("so_h", i64), ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64),
                 ("gate", p_void), ("sg_b", i64), ("sg_h", i64),
                 ("conv_wq", p_void), ("conv_wk", p_void), ("conv_bq", p_void), ("conv_bk", p_void),
-                ("conv_sq", p_void), ("conv_sk", p_void), ("scw_h", i64), ("scb_h", i64)]
+                ("conv_sq", p_void), ("conv_sk", p_void), ("scw_h", i64), ("scb_h", i64),
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos", p_void)]
 
 
 class ConvArgs(C.Structure):
@@ -78,7 +81,8 @@ class BwdArgs(C.Structure):
                 ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
                 ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
                 ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64),
-                ("workspace", p_void), ("workspace_bytes", C.c_size_t)]
+                ("workspace", p_void), ("workspace_bytes", C.c_size_t),
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void)]
 
 
 class HMError(RuntimeError):
@@ -206,14 +210,29 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _rope(a, B, rope_dims, rope_base, pos, field="rope_pos0"):
+    """Fill the rotary fields of an argument struct; pos is a device int64 [B] tensor or None."""
+    if not rope_dims:
+        return
+    if pos is not None:
+        _dev(pos)
+        if pos.dtype != torch.int64 or tuple(pos.shape) != (B,) or not pos.is_contiguous():
+            raise ValueError("rotary positions are a contiguous int64 tensor [B]")
+    a.rope_dims = rope_dims
+    a.rope_base = rope_base
+    setattr(a, field, _ptr(pos))
+
+
 def _w_strides(w):
     if w.dim() == 2:
         return 0
     return w.stride(0)
 
 
-def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Tensor | None = None):
-    """phi = softmax([x W, -x W]) for x [B, H, n, d], W [d, f] or [H, d, f]."""
+def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Tensor | None = None,
+                 rope_dims=0, rope_base=10000.0, rope_pos0=None):
+    """phi = softmax([x W, -x W]) for x [B, H, n, d], W [d, f] or [H, d, f]; with
+    rope_dims > 0 turned by the rotary encoding at positions rope_pos0[b] + t."""
     _dev(x, w)
     B, H, n, d = x.shape
     f = w.shape[-1]
@@ -224,6 +243,7 @@ def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Te
                       sw_h=_w_strides(w), sp_b=phi.stride(0), sp_h=phi.stride(1), sp_t=phi.stride(2))
     if x.stride(3) != 1 or phi.stride(3) != 1 or w.stride(-1) != 1:
         raise ValueError("inner dimensions must be contiguous")
+    _rope(a, B, rope_dims, rope_base, rope_pos0)
     _check(call_featurize(a, _stream()))
     return phi
 
@@ -250,9 +270,11 @@ def fwd_args(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, 
                    sg_t=gate.stride(2) if gate is not None else 0)
 
 
-def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segments=0, dsplit=0, o=None):
+def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segments=0, dsplit=0, o=None,
+                        rope_dims=0, rope_base=10000.0, rope_pos0=None):
     o = o if o is not None else v
     a = fwd_args(q, k, v, w_q, w_k, dt, a_log, o=o, chunk=chunk, segments=segments, dsplit=dsplit)
+    _rope(a, q.shape[0], rope_dims, rope_base, rope_pos0)
     st, plan = call_plan(a)
     _check(st)
     return plan
@@ -264,10 +286,13 @@ def _gate_shape(gate, v):
 
 
 def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
-                   chunk=0, segments=0, dsplit=0, workspace=None, gate=None, save=None):
+                   chunk=0, segments=0, dsplit=0, workspace=None, gate=None, save=None,
+                   rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """Causal prefill.  Returns o [B, H, n, dv] (v's dtype), times SiLU(gate) when a
     gate [B, H, n, dv] is given.  s_final (if given) receives the float32 state
-    [B, H, F*dv + F] after the last token."""
+    [B, H, F*dv + F] after the last token.  rope_dims > 0 turns phi(q) and phi(k)
+    by the rotary encoding at positions rope_pos0[b] + t (rope_pos0 int64 [B] on the
+    GPU, or None for 0)."""
     _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
     _gate_shape(gate, v)
     if dt is not None and dt.dtype != torch.float32 or a_log is not None and a_log.dtype != torch.float32:
@@ -275,6 +300,7 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit, gate)
+    _rope(a, q.shape[0], rope_dims, rope_base, rope_pos0)
     if save is not None:
         if save.numel() * save.element_size() < save_size(q, v, w_q):
             raise ValueError("save buffer too small (see save_size)")
@@ -291,12 +317,15 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     return o
 
 
-def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=None, conv=None):
+def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=None, conv=None,
+                    rope_dims=0, rope_base=10000.0, rope_pos=None):
     """One decode token per (b, h): q, k [B, H, d], v [B, H, dv]; state [B, H, F*dv+F]
     float32 is updated in place.  Returns o [B, H, dv], times SiLU(gate) when a gate
     [B, H, dv] is given.  conv = (w_q, w_k, b_q, b_k, state_q, state_k) runs q and k
     through the short causal conv first (taps float32 [d, K] or [H, d, K], bias
-    float32 [d] / [H, d] or None, states [B, H, K-1, d] updated in place)."""
+    float32 [d] / [H, d] or None, states [B, H, K-1, d] updated in place).  rope_dims > 0
+    turns phi(q) and phi(k) by the rotary encoding at position rope_pos[b] (int64 [B]
+    on the GPU, required)."""
     _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
     _gate_shape(gate, v)
     B, H, d = q.shape
@@ -335,6 +364,7 @@ def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=
         if (cwk.dim() == 3) != (cwq.dim() == 3) or (cbq is None) != (cbk is None) or \
                 (cbk is not None and cbk.dim() != cbq.dim()):
             raise ValueError("conv taps and biases of q and k must have the same layout")
+    _rope(a, B, rope_dims, rope_base, rope_pos, "rope_pos")
     _check(call_step(a, _stream()))
     return o
 
@@ -379,11 +409,11 @@ def save_size(q, v, w_q) -> int:
 
 
 def hm_linattn_bwd(q, k, v, w_q, w_k, d_o, save, dt=None, a_log=None, gate=None, d_s_final=None,
-                   want_d_s_init=False, workspace=None):
+                   want_d_s_init=False, workspace=None, rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """Gradients of the prefill from d_o = dloss/do (save: what the training forward
     saved; gate: the forward's gate; d_s_final: dloss/ds_final).  Returns a dict: q,
     k, v (dtype of q), w_q, w_k (float32, [d, f] or [H, d, f]), and gate, dt, a_log,
-    s_init when applicable."""
+    s_init when applicable.  The rotary fields are the forward's."""
     _dev(q, k, v, w_q, w_k, d_o, save, dt, a_log, gate, d_s_final)
     B, H, n, d = q.shape
     dv = v.shape[-1]
@@ -416,6 +446,7 @@ def hm_linattn_bwd(q, k, v, w_q, w_k, d_o, save, dt=None, a_log=None, gate=None,
                 sg_t=gate.stride(2) if gate is not None else 0, sw_h=_w_strides(w_q),
                 sdt_b=dt.stride(0) if dt is not None else 0, sdt_h=dt.stride(1) if dt is not None else 0,
                 sdt_t=dt.stride(2) if dt is not None else 0)
+    _rope(a, B, rope_dims, rope_base, rope_pos0)
     st, nbytes = call_bwd_workspace_size(a)
     _check(st)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:

@@ -42,7 +42,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 4
+    assert hm.lib().hm_abi_version() == 5
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -302,3 +302,32 @@ def test_backward_validation_and_sizes():
     assert "save" in hm.last_error()
     expect(hm.call_fwd(fwd(save=A + 0xc000000, save_bytes=sb, dsplit=2)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(save=A + 0xc000004, save_bytes=sb)), hm.HM_ERR_ALIGN)
+
+
+def test_rotary_field_validation():
+    P = A + 0xd000000  # fake int64 position array
+    for mk, call in ((fwd, hm.call_fwd), (feat, hm.call_featurize)):
+        expect(call(mk(rope_dims=-32, rope_base=1e4)), hm.HM_ERR_SHAPE)
+        expect(call(mk(rope_dims=33, rope_base=1e4)), hm.HM_ERR_SHAPE)        # odd
+        expect(call(mk(rope_dims=160, rope_base=1e4)), hm.HM_ERR_SHAPE)       # above 2f = 128
+        expect(call(mk(rope_dims=48, rope_base=1e4)), hm.HM_ERR_UNSUPPORTED)  # even, not a multiple of 32
+        expect(call(mk(rope_dims=64, rope_base=0.0)), hm.HM_ERR_SHAPE)
+        expect(call(mk(rope_dims=64, rope_base=-2.0)), hm.HM_ERR_SHAPE)
+        expect(call(mk(rope_dims=64, rope_base=float("inf"))), hm.HM_ERR_SHAPE)
+        expect(call(mk(rope_dims=64, rope_base=float("nan"))), hm.HM_ERR_SHAPE)
+        expect(call(mk(rope_dims=64, rope_base=1e4, rope_pos0=P + 4)), hm.HM_ERR_ALIGN)
+        expect(call(mk(rope_dims=64, rope_base=1e4, B=0)), hm.HM_OK)           # nothing to compute
+    # with the rotation, prefill kernels exist for (128, 64) and (64, 32) only
+    expect(hm.call_fwd(fwd(f=32, rope_dims=32, rope_base=1e4)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(d=64, f=32, rope_dims=64, rope_base=1e4, B=0)), hm.HM_OK)
+    # the training forward too (the size check runs first; B = 0 launches nothing)
+    expect(hm.call_fwd(fwd(B=0, rope_dims=128, rope_base=1e4, save=A + 0xc000000, save_bytes=1 << 30)), hm.HM_OK)
+    # decode: the positions are required when the rotation is on
+    expect(hm.call_step(step(rope_dims=64, rope_base=1e4)), hm.HM_ERR_NULL)
+    expect(hm.call_step(step(rope_dims=64, rope_base=1e4, rope_pos=P + 8 + 4)), hm.HM_ERR_ALIGN)
+    expect(hm.call_step(step(rope_dims=48, rope_base=1e4, rope_pos=P)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(rope_dims=64, rope_base=1e4, B=0)), hm.HM_OK)
+    # backward
+    expect(hm.call_bwd(bwd(rope_dims=96, rope_base=0.5, rope_pos0=P + 2)), hm.HM_ERR_ALIGN)
+    expect(hm.call_bwd(bwd(rope_dims=200, rope_base=1e4)), hm.HM_ERR_SHAPE)
+    expect(hm.call_bwd(bwd(rope_dims=128, rope_base=1e4)), hm.HM_ERR_WORKSPACE)  # valid; no workspace given
