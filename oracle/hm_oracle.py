@@ -25,6 +25,9 @@ What is computed, per (batch b, head h), for tokens t = 0..n-1:
   optionally phi(q_t), phi(k_t) turned by rotary position encoding before
   both sums, so numerator and denominator see the rotated features
                                                                  [HM §5.2 step 3]
+as a variant, a decay per value channel and state (pc_scan): the A / dt / V
+copies of the pages' Mamba-1 wiring, a numerator and a denominator channel per
+value channel with Delta-scaled input                            [HM §2.3, §5.2]
 and, as a separate step ahead of the featurizer, Mamba's short causal conv
 (depthwise over time, K taps per channel, identity at the stage-1 init)
 [HM §2.2, §2.3 item 4, §3.1].
@@ -40,9 +43,10 @@ uses, which [HM §5.2] names): feature i of the leading `dims` pairs with featur
 i + dims/2 and turns by pos * base^(-2i/dims); features past `dims` pass
 through; positions count from a start offset per sequence.
 
-Every function here is pinned by tests/test_oracle.py (and the rotary
-encoding by tests/test_oracle_rope.py) against closed forms, library routines,
-brute force and invariants; there is no parity-unpinned function in this module.
+Every function here is pinned by tests/test_oracle.py (the rotary encoding by
+tests/test_oracle_rope.py, the per-channel scan by tests/test_oracle_pc.py)
+against closed forms, library routines, brute force and invariants; there is no
+parity-unpinned function in this module.
 """
 from __future__ import annotations
 
@@ -325,6 +329,79 @@ def step(S, z, q, k, v, w_q, w_k, dt=None, a_log=None, gate=None, rope_dims=0, r
     o, S2, z2 = forward(q, k, v, w_q, w_k, dt3, a_log, S, z, rope_dims=rope_dims, rope_base=rope_base,
                         rope_pos0=rope_pos)
     return apply_gate(o[:, :, 0, :], gate), S2, z2
+
+
+# --------------------------------------------------------------------------
+# Per-channel decay: the scan the way the pages wire it through Mamba-1's
+# selective scan  [HM §2.3 item 3 and §5.2 step 4: A, dt and V are copied and
+# concatenated, the V copy replaced by ones, so every value channel has a
+# numerator and a denominator channel with the same A row and step size;
+# Mamba's discretization (HM §2.2, SSM §3.2): a = exp(Delta A) with
+# Delta = softplus(dt), input scaled by Delta]
+# --------------------------------------------------------------------------
+def pc_scan(phiq, phik, v, delta, A, sn0=None, sd0=None):
+    """Per (b, h), value channel c and state n (n runs over the F features):
+        a_t[c, n] = exp(delta_t[c] * A[c, n])
+        Sn_t[c, n] = a_t[c, n] Sn_{t-1}[c, n] + delta_t[c] phik_t[n] v_t[c]
+        Sd_t[c, n] = a_t[c, n] Sd_{t-1}[c, n] + delta_t[c] phik_t[n]
+        o_t[c] = sum_n phiq_t[n] Sn_t[c, n] / sum_n phiq_t[n] Sd_t[c, n]
+    phiq, phik [B,H,n,F]; v, delta [B,H,n,dv]; A [H,dv,F] (or [dv,F] shared);
+    sn0, sd0 [B,H,F,dv] initial states (None = zeros).  Token by token,
+    vectorized over (b, h, c, n).  Returns (o [B,H,n,dv], Sn, Sd) with the
+    states laid out [B,H,F,dv]."""
+    phiq = np.asarray(phiq, dtype=np.float64)
+    phik = np.asarray(phik, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    delta = np.asarray(delta, dtype=np.float64)
+    B, H, n, F = phiq.shape
+    dv = v.shape[-1]
+    A = np.asarray(A, dtype=np.float64)
+    At = np.broadcast_to(A if A.ndim == 3 else A[None], (H, dv, F)).transpose(0, 2, 1)   # [H, F, dv]
+    Sn = np.zeros((B, H, F, dv)) if sn0 is None else np.array(sn0, dtype=np.float64)
+    Sd = np.zeros((B, H, F, dv)) if sd0 is None else np.array(sd0, dtype=np.float64)
+    o = np.empty((B, H, n, dv))
+    for t in range(n):
+        dl = delta[:, :, t, None, :]                       # [B,H,1,dv]
+        a = np.exp(dl * At[None])                          # [B,H,F,dv]
+        kk = phik[:, :, t, :, None] * dl                   # [B,H,F,dv]
+        Sn = a * Sn + kk * v[:, :, t, None, :]
+        Sd = a * Sd + kk
+        num = np.einsum("bhf,bhfd->bhd", phiq[:, :, t], Sn)
+        den = np.einsum("bhf,bhfd->bhd", phiq[:, :, t], Sd)
+        o[:, :, t] = num / den
+    return o, Sn, Sd
+
+
+def forward_pc(q, k, v, w_q, w_k, dt, a_log, sn0=None, sd0=None, gate=None):
+    """Featurize q and k, then the per-channel scan with Delta = softplus(dt)
+    (dt [B,H,n,dv]) and A = -exp(A_log) (A_log [H,dv,F] or [dv,F]); the gate as in
+    forward.  Returns (o, Sn_final, Sd_final)."""
+    phiq = hedgehog_features(q, w_q)
+    phik = hedgehog_features(k, w_k)
+    delta = softplus(dt)
+    A = -np.exp(np.asarray(a_log, dtype=np.float64))
+    o, Sn, Sd = pc_scan(phiq, phik, v, delta, A, sn0, sd0)
+    return apply_gate(o, gate), Sn, Sd
+
+
+def step_pc(Sn, Sd, q, k, v, w_q, w_k, dt, a_log, gate=None):
+    """One decode step of the per-channel scan: q, k [B,H,d], v, dt [B,H,dv]."""
+    o, Sn2, Sd2 = forward_pc(np.asarray(q, dtype=np.float64)[:, :, None], np.asarray(k, dtype=np.float64)[:, :, None],
+                             np.asarray(v, dtype=np.float64)[:, :, None], w_q, w_k,
+                             np.asarray(dt, dtype=np.float64)[:, :, None], a_log, Sn, Sd)
+    return apply_gate(o[:, :, 0], gate), Sn2, Sd2
+
+
+def pack_state_pc(Sn, Sd):
+    """Boundary layout of the per-channel state: per (b, h) Sn [F][dv] then Sd [F][dv]."""
+    B, H, F, dv = Sn.shape
+    return np.concatenate([Sn.reshape(B, H, F * dv), Sd.reshape(B, H, F * dv)], axis=-1)
+
+
+def unpack_state_pc(flat, F, dv):
+    flat = np.asarray(flat, dtype=np.float64)
+    B, H, _ = flat.shape
+    return flat[:, :, : F * dv].reshape(B, H, F, dv), flat[:, :, F * dv:].reshape(B, H, F, dv)
 
 
 # --------------------------------------------------------------------------
