@@ -393,15 +393,18 @@ def step_pc(Sn, Sd, q, k, v, w_q, w_k, dt, a_log, gate=None):
 
 
 def pack_state_pc(Sn, Sd):
-    """Boundary layout of the per-channel state: per (b, h) Sn [F][dv] then Sd [F][dv]."""
+    """Boundary layout of the per-channel state, channel-major like A_log: per (b, h)
+    Sn [dv][F] then Sd [dv][F] (the oracle's arrays are [B,H,F,dv])."""
     B, H, F, dv = Sn.shape
-    return np.concatenate([Sn.reshape(B, H, F * dv), Sd.reshape(B, H, F * dv)], axis=-1)
+    return np.concatenate([Sn.transpose(0, 1, 3, 2).reshape(B, H, F * dv),
+                           Sd.transpose(0, 1, 3, 2).reshape(B, H, F * dv)], axis=-1)
 
 
 def unpack_state_pc(flat, F, dv):
     flat = np.asarray(flat, dtype=np.float64)
     B, H, _ = flat.shape
-    return flat[:, :, : F * dv].reshape(B, H, F, dv), flat[:, :, F * dv:].reshape(B, H, F, dv)
+    return (flat[:, :, : F * dv].reshape(B, H, dv, F).transpose(0, 1, 3, 2),
+            flat[:, :, F * dv:].reshape(B, H, dv, F).transpose(0, 1, 3, 2))
 
 
 # --------------------------------------------------------------------------

@@ -124,6 +124,8 @@ def test_split_and_handoff_and_decode_step():
                                c["dt"][:, :, m], c["a_log"])
     np.testing.assert_allclose(o1, o[:, :, m], rtol=1e-12, atol=1e-13)
     flat = orc.pack_state_pc(Sn, Sd)
+    F, dv = Sn.shape[2], Sn.shape[3]
+    assert flat[1, 0, 3 * F + 2] == Sn[1, 0, 2, 3] and flat[0, 1, F * dv + 4 * F + 1] == Sd[0, 1, 1, 4]  # [dv][F]
     Sn2, Sd2 = orc.unpack_state_pc(flat, Sn.shape[2], Sn.shape[3])
     np.testing.assert_array_equal(Sn2, Sn)
     np.testing.assert_array_equal(Sd2, Sd)
