@@ -13,7 +13,8 @@ Prints ONE JSON line.  Beside the headline prefill number it reports:
     4096-token prefix, 512 steps) against HBM bandwidth;
   * prefill_extra: the gated layer, the rotary encoding of 32 and of all 128
     features, the short conv and the stage-2 chain, a training step (forward
-    that saves + backward), the Mamba-decay workloads (n=8192 and n=131072);
+    that saves + backward), the Mamba-decay workloads (n=8192 and n=131072), the
+    per-channel-decay scan on the same layer (ALU-bound) and its decode step;
   * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extra]
@@ -341,13 +342,70 @@ def main():
                           "hbm_frac": bx / (msx * 1e-3) / 1e9 / HBM_PEAK_GBS,
                           "plan": {"chunk": pl[0], "segments": pl[1], "dsplit": pl[2]}})
             del gg, oo
+        extra.append(bench_pc_prefill(torch, hm, inputs, dev))
         result["prefill_extra"] = extra
         result["decode"] = bench_decode(torch, hm, inputs, dev, ws)
+        result["decode"]["per_channel_step"] = bench_pc_decode(torch, hm, inputs, dev)
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(result), flush=True)
+
+
+# VALU issue per (token, channel, state) of the per-channel scan: one quarter-rate
+# exp2 (4 lane-slots of 16) and seven full-rate FMA/MUL ops; a SIMD issues 16
+# lane-ops per clock, 1024 SIMDs at 2.4 GHz.
+PC_SIMD_CYCLES_PER_ELEM = 7 / 16 + 1 / 4
+SIMD_CLOCKS_PER_S = 1024 * 2.4e9
+
+
+def bench_pc_prefill(torch, hm, inputs, dev):
+    """Per-channel-decay prefill on the Pythia-1B-shaped layer (bf16, dt [B,H,n,dv])."""
+    c = inputs.make_pc("pc-pythia1b", 8, 16, 2048, 128, 64, 128, torch.bfloat16)
+    log(f"[bench] per-channel decay prefill B={c.B} H={c.H} n={c.n}")
+    g = {k: getattr(c, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k", "dt", "a_log")}
+    o = torch.empty_like(g["v"])
+
+    def step():
+        hm.hm_linattn_pc_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], o=o)
+
+    ms, _ = time_launches(step, 10, 20, torch)
+    elems = c.B * c.H * c.n * c.dv * 2 * c.f
+    alu_s = elems * PC_SIMD_CYCLES_PER_ELEM / SIMD_CLOCKS_PER_S
+    return {"workload": f"per-channel decay (A_log [H,dv,2f], dt [B,H,n,dv]) B={c.B} H={c.H} n={c.n}, element-wise scan",
+            "ms": ms, "tokens_per_s": c.B * c.n / (ms * 1e-3),
+            "roofline": {"bound": "alu", "achieved_elems_per_s": elems / (ms * 1e-3),
+                         "alu_time_ms": alu_s * 1e3, "frac": alu_s / (ms * 1e-3),
+                         "model": "1 exp2 (quarter rate) + 7 full-rate VALU ops per (token, channel, state)"},
+            "kernel": "hm::pc_fwd_kernel<bf16,128,64,128,64,8>"}
+
+
+def bench_pc_decode(torch, hm, inputs, dev):
+    """Per-channel-decay decode step, B=256 H=16 (state 2 x [128 x 128] fp32 per head)."""
+    B, H, d, f, dv, steps = 256, 16, 128, 64, 128, 256
+    c = inputs.make_pc("pc-decode", B, H, 1, d, f, dv, torch.bfloat16)
+    log(f"[bench] per-channel decode B={B} H={H}: {steps} steps")
+    g = {k: getattr(c, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k", "dt", "a_log")}
+    q1, k1, v1, dt1 = (g["q"][:, :, 0].contiguous(), g["k"][:, :, 0].contiguous(), g["v"][:, :, 0].contiguous(),
+                       g["dt"][:, :, 0].contiguous())
+    state = torch.zeros((B, H, hm.state_numel_pc(f, dv)), dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+
+    def run_all():
+        for _ in range(steps):
+            hm.hm_linattn_pc_step(q1, k1, v1, g["w_q"], g["w_k"], state, dt1, g["a_log"], o=o)
+
+    run_all()
+    torch.cuda.synchronize()
+    ms = time_launches(run_all, 1, 0, torch)[0] / steps
+    nbytes = B * H * (2 * 2 * dv * 2 * f * 4 + 2 * (2 * d + 2 * dv) + 4 * dv) + H * dv * 2 * f * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"per-channel decode B={B} H={H} d={d} f={f} dv={dv}, state 2 x [{dv}x{2 * f}] fp32",
+            "ms_per_step": ms, "tokens_per_s": B / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes},
+            "kernel": "hm::pc_step_kernel<bf16,128,64,128>"}
 
 
 def bench_decode(torch, hm, inputs, dev, ws):

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 5
+#define HM_ABI_VERSION 6
 
 typedef enum {
   HM_OK = 0,
@@ -322,11 +322,84 @@ typedef struct {
 
 hm_status hm_causal_conv(const hm_causal_conv_args *args, void *stream);
 
+/*
+ * hm_linattn_pc_fwd — prefill with a decay per value channel and state: the
+ * scan as the pages wire the mixer through Mamba-1's selective scan ([HM] §2.3
+ * item 3 and §5.2 step 4: A, dt and V are copied and concatenated, the V copy
+ * set to ones, so each value channel c has a numerator and a denominator channel
+ * sharing its A row and step size; Mamba's discretization, [SSM] §3.2).  Per
+ * (b, h), channel c < dv and state n < F = 2f (the feature index):
+ *   Delta_t[c] = softplus(dt[b,h,t,c]),   a_t[c,n] = exp(-Delta_t[c] exp(A_log[h,c,n]))
+ *   Sn[c,n] <- a_t[c,n] Sn[c,n] + Delta_t[c] phi(k_t)[n] v_t[c]
+ *   Sd[c,n] <- a_t[c,n] Sd[c,n] + Delta_t[c] phi(k_t)[n]
+ *   o_t[c]  = sum_n phi(q_t)[n] Sn[c,n] / sum_n phi(q_t)[n] Sd[c,n]
+ * then the optional gate (o *= SiLU(gate)) and, when rope_dims > 0, phi(q) and
+ * phi(k) turned first exactly as in hm_linattn_fwd.
+ *   q, k: [B, H, n, d]; v, o (and gate): [B, H, n, dv] in `dtype` (strides s*_*).
+ *   w_q, w_k: [d, f] (head stride sw_h).
+ *   dt: float32 [B, H, n, dv] (strides sdt_b, sdt_h, sdt_t; channels contiguous).
+ *   a_log: float32 [dv][F] per head, head stride sa_h (0 = shared, dv*F = per head).
+ *   s_init, s_final: optional float32 state, per (b, h) one block of 2*dv*F values:
+ *   Sn [dv][F] then Sd [dv][F]; they may be the same buffer.
+ * The scan is element-wise (a decay per (c, n) does not factor into the chunked
+ * matrix products of hm_linattn_fwd): one exponential per token, channel and state,
+ * float32 throughout, phi kept in float32.  q, k, v, w_q, w_k, o, dt and a_log
+ * are required whenever B*H*n > 0 (with n = 0 only the state is copied or zeroed).
+ * Built: bf16 (d, f, dv) = (128, 64, 128), (64, 32, 64); f32 (16, 16, 16), (32, 16, 32).
+ */
+typedef struct {
+  const void *q, *k, *v, *w_q, *w_k;
+  const float *dt, *a_log;
+  const float *s_init;
+  float *s_final;
+  void *o;
+  const void *gate;
+  int32_t dtype;
+  int32_t rope_dims;        /* 0 = off (see the rotary fields above) */
+  float rope_base;
+  int32_t reserved;
+  const int64_t *rope_pos0; /* [B] position of token 0 of each row, or NULL */
+  int64_t B, H, n, d, f, dv;
+  int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t, sg_b, sg_h, sg_t;
+  int64_t sw_h, sdt_b, sdt_h, sdt_t, sa_h;
+} hm_linattn_pc_args;
+
+hm_status hm_linattn_pc_fwd(const hm_linattn_pc_args *args, void *stream);
+
+/*
+ * hm_linattn_pc_step — one decode token per (b, h) of the per-channel scan above
+ * (the state of hm_linattn_pc_fwd, updated in place): q, k [B, H, d], v, o, gate
+ * [B, H, dv] in `dtype`, dt float32 [B, H, dv] (strides sdt_b, sdt_h), a_log as
+ * above, state float32 [B*H] blocks of 2*dv*F.  The short conv and the rotary
+ * fields work as in hm_linattn_step.  Same sizes as hm_linattn_pc_fwd.
+ */
+typedef struct {
+  const void *q, *k, *v, *w_q, *w_k;
+  const float *dt, *a_log;
+  float *state;
+  void *o;
+  const void *gate;
+  int32_t dtype;
+  int32_t conv_width;
+  int64_t B, H, d, f, dv;
+  int64_t sq_b, sq_h, sk_b, sk_h, sv_b, sv_h, so_b, so_h, sg_b, sg_h;
+  int64_t sw_h, sdt_b, sdt_h, sa_h;
+  const float *conv_wq, *conv_wk, *conv_bq, *conv_bk;
+  void *conv_sq, *conv_sk;
+  int64_t scw_h, scb_h;
+  int32_t rope_dims;
+  float rope_base;
+  const int64_t *rope_pos;
+} hm_linattn_pc_step_args;
+
+hm_status hm_linattn_pc_step(const hm_linattn_pc_step_args *args, void *stream);
+
 const char *hm_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none). */
 const char *hm_last_error_message(void);
 int hm_abi_version(void);
-/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step, 3: causal conv, 4: bwd), for bindings. */
+/* sizeof of the argument structs (0: featurize, 1: fwd, 2: step, 3: causal conv, 4: bwd, 5: pc fwd,
+ * 6: pc step), for bindings. */
 size_t hm_args_size(int which);
 
 #ifdef __cplusplus

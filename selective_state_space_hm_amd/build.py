@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhm.so")
 SOURCES = ["hm_abi.hip", "k_fwd_bf16.hip", "k_fwd_bf16_decay.hip", "k_fwd_f32.hip", "k_step_feat.hip",
-           "k_conv.hip", "k_bwd.hip", "k_fwd_rope_bf16.hip", "k_fwd_rope_bf16_decay.hip", "k_fwd_rope_f32.hip"]
+           "k_conv.hip", "k_bwd.hip", "k_fwd_rope_bf16.hip", "k_fwd_rope_bf16_decay.hip", "k_fwd_rope_f32.hip",
+           "k_pc.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

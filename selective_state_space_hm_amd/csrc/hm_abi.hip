@@ -13,6 +13,7 @@
 #include "hm.h"
 #include "hm_bwd_params.hpp"
 #include "hm_kernels.hpp"
+#include "hm_pc.hpp"
 
 namespace {
 
@@ -490,7 +491,11 @@ hm_status hm_linattn_bwd(const hm_linattn_bwd_args *a, void *stream) {
 }
 
 // ------------------------------------------------------------------ decode
-hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
+}  // extern "C"
+
+namespace {
+// Checks shared by the decode steps (hm_linattn_step, hm_linattn_pc_step).
+hm_status validate_step(const hm_linattn_step_args *a) {
   if (!a) return fail(HM_ERR_NULL, "args is NULL");
   if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
   if (a->B < 0 || a->H < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
@@ -528,13 +533,10 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
     const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos, a->f, a->B * a->H > 0);
     if (rs != HM_OK) return rs;
   }
-  const int decay = a->dt != nullptr;
-  const hm::StepEntry *e = find_step(a->dtype, a->d, a->f, a->dv, decay);
-  if (!e)
-    return fail(HM_ERR_UNSUPPORTED, "no decode kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
-                (long long)a->f, (long long)a->dv);
-  const int64_t BH = a->B * a->H;
-  if (BH == 0) return ok();
+  return ok();
+}
+
+hm::StepParams step_params(const hm_linattn_step_args *a) {
   hm::StepParams p{};
   p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
   p.dt = a->dt; p.a_log = a->a_log; p.state = a->state; p.o = a->o;
@@ -547,8 +549,132 @@ hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
   p.cwq = a->conv_wq; p.cwk = a->conv_wk; p.cbq = a->conv_bq; p.cbk = a->conv_bk;
   p.csq = a->conv_sq; p.csk = a->conv_sk; p.scw_h = a->scw_h; p.scb_h = a->scb_h;
   p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos = a->rope_pos;
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+hm_status hm_linattn_step(const hm_linattn_step_args *a, void *stream) {
+  hm_status st = validate_step(a);
+  if (st != HM_OK) return st;
+  const int decay = a->dt != nullptr;
+  const hm::StepEntry *e = find_step(a->dtype, a->d, a->f, a->dv, decay);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no decode kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
+                (long long)a->f, (long long)a->dv);
+  const int64_t BH = a->B * a->H;
+  if (BH == 0) return ok();
+  const hm::StepParams p = step_params(a);
   e->launch(p, (unsigned)BH, (hipStream_t)stream);
   return check_launch("decode step");
+}
+
+// ------------------------------------------------------------------ per-channel decay
+}  // extern "C"
+
+namespace {
+const hm::PcEntry *find_pc(int dt, int64_t dk, int64_t fh, int64_t dv) {
+  const hm::PcTable t = hm::table_pc();
+  for (int i = 0; i < t.npc; ++i)
+    if (t.pc[i].dtype == dt && t.pc[i].dk == dk && t.pc[i].fh == fh && t.pc[i].dv == dv) return &t.pc[i];
+  return nullptr;
+}
+// A_log: [dv][F] rows per head, shared (sa_h = 0) or one block per head.
+hm_status validate_a_log_pc(const float *a_log, int64_t sa_h, int64_t dv, int64_t F) {
+  if (sa_h != 0 && sa_h != dv * F) return fail(HM_ERR_SHAPE, "sa_h must be 0 (shared A_log) or dv*2f (one per head)");
+  if (!aligned16(a_log)) return fail(HM_ERR_ALIGN, "a_log must be 16-byte aligned");
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+hm_status hm_linattn_pc_fwd(const hm_linattn_pc_args *a, void *stream) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f, dv >= 1");
+  const int64_t BH = a->B * a->H, F = 2 * a->f;
+  if (BH * a->n > 0 && (!a->q || !a->k || !a->v || !a->w_q || !a->w_k || !a->o || !a->dt || !a->a_log))
+    return fail(HM_ERR_NULL, "q, k, v, w_q, w_k, o, dt and a_log must be non-NULL");
+  const int64_t strides[] = {a->sq_b, a->sq_h, a->sq_t, a->sk_b, a->sk_h, a->sk_t, a->sv_b,
+                             a->sv_h, a->sv_t, a->so_b, a->so_h, a->so_t, a->sw_h};
+  for (int64_t s : strides)
+    if (s < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->sdt_b < 0 || a->sdt_h < 0 || a->sdt_t < 0 || a->sg_b < 0 || a->sg_h < 0 || a->sg_t < 0 || a->sa_h < 0)
+    return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if (a->n > 1 && (a->so_t < a->dv || a->sq_t < a->d || a->sk_t < a->d || a->sv_t < a->dv || a->sdt_t < a->dv ||
+                   (a->gate && a->sg_t < a->dv)))
+    return fail(HM_ERR_SHAPE, "token stride smaller than the row length (rows overlap)");
+  const void *ptrs[] = {a->q, a->k, a->v, a->w_q, a->w_k, a->o, a->gate, a->s_init, a->s_final};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return fail(HM_ERR_ALIGN, "q, k, v, w_q, w_k, o, gate and the states must be 16-byte aligned");
+  if ((uintptr_t)a->dt & 3) return fail(HM_ERR_ALIGN, "dt must be 4-byte aligned");
+  for (int64_t s : strides)
+    if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  if (a->gate && (!stride_ok(a->sg_b, a->dtype) || !stride_ok(a->sg_h, a->dtype) || !stride_ok(a->sg_t, a->dtype)))
+    return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
+  hm_status st = validate_a_log_pc(a->a_log, a->sa_h, a->dv, F);
+  if (st != HM_OK) return st;
+  if ((st = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false)) != HM_OK) return st;
+  if (a->s_init && a->s_final && a->s_init != a->s_final) {
+    // each thread reads its own state elements first and writes the same ones last, so
+    // the same buffer is safe; a partial overlap would let workgroups race
+    const char *i0 = (const char *)a->s_init, *f0 = (const char *)a->s_final;
+    const size_t len = (size_t)BH * 2 * a->dv * F * 4;
+    if (i0 < f0 + len && f0 < i0 + len) return fail(HM_ERR_SHAPE, "s_init and s_final overlap without being the same buffer");
+  }
+  const hm::PcEntry *e = find_pc(a->dtype, a->d, a->f, a->dv);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no per-channel kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv);
+  if (BH == 0 || (a->n == 0 && !a->s_final)) return ok();
+  hm::PcParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
+  p.dt = a->dt; p.a_log = a->a_log; p.s_init = a->s_init; p.s_final = a->s_final; p.o = a->o; p.gate = a->gate;
+  p.B = a->B; p.H = a->H; p.n = a->n;
+  p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sq_t = a->sq_t; p.sk_b = a->sk_b; p.sk_h = a->sk_h; p.sk_t = a->sk_t;
+  p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t; p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
+  p.sg_b = a->sg_b; p.sg_h = a->sg_h; p.sg_t = a->sg_t;
+  p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t; p.sa_h = a->sa_h;
+  p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
+  e->fwd(p, (hipStream_t)stream);
+  return check_launch("per-channel prefill");
+}
+
+hm_status hm_linattn_pc_step(const hm_linattn_pc_step_args *a, void *stream) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  // the fields shared with hm_linattn_step pass through its checks
+  hm_linattn_step_args sa{};
+  sa.q = a->q; sa.k = a->k; sa.v = a->v; sa.w_q = a->w_q; sa.w_k = a->w_k;
+  sa.dt = a->dt; sa.a_log = a->a_log; sa.state = a->state; sa.o = a->o;
+  sa.dtype = a->dtype; sa.conv_width = a->conv_width;
+  sa.B = a->B; sa.H = a->H; sa.d = a->d; sa.f = a->f; sa.dv = a->dv;
+  sa.sq_b = a->sq_b; sa.sq_h = a->sq_h; sa.sk_b = a->sk_b; sa.sk_h = a->sk_h; sa.sv_b = a->sv_b; sa.sv_h = a->sv_h;
+  sa.so_b = a->so_b; sa.so_h = a->so_h; sa.sw_h = a->sw_h; sa.sdt_b = a->sdt_b; sa.sdt_h = a->sdt_h;
+  sa.gate = a->gate; sa.sg_b = a->sg_b; sa.sg_h = a->sg_h;
+  sa.conv_wq = a->conv_wq; sa.conv_wk = a->conv_wk; sa.conv_bq = a->conv_bq; sa.conv_bk = a->conv_bk;
+  sa.conv_sq = a->conv_sq; sa.conv_sk = a->conv_sk; sa.scw_h = a->scw_h; sa.scb_h = a->scb_h;
+  sa.rope_dims = a->rope_dims; sa.rope_base = a->rope_base; sa.rope_pos = a->rope_pos;
+  hm_status st = validate_step(&sa);
+  if (st != HM_OK) return st;
+  const int64_t BH = a->B * a->H;
+  if (BH > 0 && (!a->dt || !a->a_log)) return fail(HM_ERR_NULL, "dt and a_log are required");
+  if (a->sa_h < 0) return fail(HM_ERR_SHAPE, "strides must be non-negative");
+  if ((uintptr_t)a->dt & 3) return fail(HM_ERR_ALIGN, "dt must be 4-byte aligned");
+  if ((st = validate_a_log_pc(a->a_log, a->sa_h, a->dv, 2 * a->f)) != HM_OK) return st;
+  const hm::PcEntry *e = find_pc(a->dtype, a->d, a->f, a->dv);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no per-channel kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv);
+  if (BH == 0) return ok();
+  hm::PcStepParams p{};
+  p.s = step_params(&sa);
+  p.dt = a->dt; p.a_log = a->a_log; p.state = a->state;
+  p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sa_h = a->sa_h;
+  e->step(p, (hipStream_t)stream);
+  return check_launch("per-channel decode step");
 }
 
 // ------------------------------------------------------------------ short conv
@@ -677,6 +803,8 @@ size_t hm_args_size(int which) {
     case 2: return sizeof(hm_linattn_step_args);
     case 3: return sizeof(hm_causal_conv_args);
     case 4: return sizeof(hm_linattn_bwd_args);
+    case 5: return sizeof(hm_linattn_pc_args);
+    case 6: return sizeof(hm_linattn_pc_step_args);
     default: return 0;
   }
 }

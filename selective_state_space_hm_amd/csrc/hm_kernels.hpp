@@ -50,7 +50,20 @@ struct BwdTable {
   int nbwd;
 };
 
+struct PcParams;
+struct PcStepParams;
+struct PcEntry {
+  int dtype, dk, fh, dv;
+  void (*fwd)(const PcParams &, hipStream_t);
+  void (*step)(const PcStepParams &, hipStream_t);
+};
+struct PcTable {
+  const PcEntry *pc;
+  int npc;
+};
+
 // one per kernel translation unit
+PcTable table_pc();
 ConvTable table_conv();
 BwdTable table_bwd();
 Table table_train();

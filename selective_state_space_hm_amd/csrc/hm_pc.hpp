@@ -1,0 +1,277 @@
+// Per-channel decay: the scan the way the HedgeMamba explainer (gsyq.cn, §2.3
+// item 3 and §5.2 step 4) wires the mixer through Mamba-1's selective scan.
+// A, dt and V are copied and the V copy is set to ones, so every value channel c
+// of a head has a numerator and a denominator channel that share one decay per
+// state n (n runs over the F Hedgehog features):
+//   Delta_t[c] = softplus(dt_t[c]),  a_t[c, n] = exp(Delta_t[c] A[c, n]),  A = -exp(A_log)
+//   Sn[c, n] <- a Sn[c, n] + Delta_t[c] phik_t[n] v_t[c]
+//   Sd[c, n] <- a Sd[c, n] + Delta_t[c] phik_t[n]
+//   o_t[c] = sum_n phiq_t[n] Sn[c, n] / sum_n phiq_t[n] Sd[c, n]
+// (Mamba's discretization, quant67 SSM lecture §3.2: the input is scaled by Delta.)
+// With a decay per (c, n) the chunked matrix form of the scalar-decay kernels does
+// not apply (the in-chunk weights no longer factor into phiq . phik times one
+// decay), so this is an element-wise scan: one exponential per (token, channel,
+// state), shared by the two copies, and the kernels are bound by that VALU and
+// transcendental issue, not by HBM.
+//
+// State per (b, h): Sn [dv][F] then Sd [dv][F], float32, channel-major like A_log.
+#pragma once
+
+#include "hm_step.hpp"
+
+namespace hm {
+
+struct PcParams {
+  const void *q, *k, *v, *wq, *wk;
+  const float *dt;       // [B, H, n, dv] (strides sdt_*; channels contiguous)
+  const float *a_log;    // [H][dv][F] (head stride sa_h; 0 = shared)
+  const float *s_init;   // [B*H][2][dv][F] or NULL
+  float *s_final;        // same layout, or NULL
+  void *o;
+  const void *gate;      // o's shape or NULL
+  int64_t B, H, n;
+  int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t, sg_b, sg_h, sg_t;
+  int64_t sw_h, sdt_b, sdt_h, sdt_t, sa_h;
+  int rope_dims;             // rotary encoding of the features (0 = off)
+  float rope_base;
+  const int64_t *rope_pos0;  // position of token 0 per batch row (NULL = 0)
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+// Sum over aligned groups of L consecutive lanes (L = 2, 4, 8 or 16), every lane
+// of a group ending with the group's sum: quad permutations, then the half-row
+// and row mirrors (lane i with 7 - i, then with 15 - i).
+template <int L>
+__device__ __forceinline__ float group_lanes_sum(float v) {
+  if constexpr (L >= 2) v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (L >= 4) v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dpp_f32<0x141>(v);  // row_half_mirror
+  if constexpr (L >= 16) v += dpp_f32<0x140>(v); // row_mirror
+  return v;
+}
+
+// ---------------------------------------------------------------- prefill
+// One workgroup per (b, h, group of CPW channels), CPW x LPC threads: thread
+// (channel cl, lane nb of LPC) holds the NPL = F/LPC states n0 .. n0+NPL-1 of its
+// channel for both copies, in registers, for the whole sequence.  Per chunk of 64
+// tokens the waves featurize q and k on the MFMA into LDS (float32 rows, each
+// thread's NPL features padded by 4 so that the LPC distinct 16-byte reads of a
+// wave fall in distinct banks), stage Delta and v, then scan the chunk token by
+// token: NPL exponentials and FMAs per thread, the readout summed over the LPC
+// lanes of a channel with DPP.
+template <typename T, int DK, int FH, int DV, int CPW, int LPC>
+__global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int NT = CPW * LPC, NW = NT / 64, F = 2 * FH, NPL = F / LPC, BLK = NPL + 4, ROW = LPC * BLK;
+  constexpr int C = 64, NFH = FH / 16, NFT = 2 * NFH, KD = DK / M::KS, LDW = DK + M::PAD;
+  constexpr float L2E = 1.4426950408889634f;
+  static_assert(NT % 64 == 0 && NPL >= 4 && NPL % 4 == 0 && LPC <= 16 && DV % CPW == 0, "pc mapping");
+  __shared__ __align__(16) T sW[2][FH * LDW];   // W_q^T, W_k^T
+  __shared__ __align__(16) float sPh[2][C * ROW];  // phi(q) (unnormalized), phi(k) of the chunk
+  __shared__ float sD[C * CPW];                 // Delta of the chunk
+  __shared__ float sVO[C * CPW];                // v of the chunk, then o
+  __shared__ double sRev[FH];                   // rotary rate of each feature pair
+
+  const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int NG = DV / CPW;
+  const int64_t bh = blockIdx.x / NG, b = bh / p.H, h = bh % p.H;
+  const int grp = (int)(blockIdx.x % NG);
+  const int cl = tid / LPC, nb = tid % LPC, c = grp * CPW + cl, n0 = nb * NPL;
+
+  // the thread's A row (times log2 e) and states; with no token W and A are not read
+  float A2[NPL], hn[NPL], hd[NPL];
+  if (p.n > 0) {
+    const T *wq = (const T *)p.wq + h * p.sw_h, *wk = (const T *)p.wk + h * p.sw_h;
+    for (int i = tid; i < DK * FH; i += NT) {
+      sW[0][(i % FH) * LDW + i / FH] = wq[i];
+      sW[1][(i % FH) * LDW + i / FH] = wk[i];
+    }
+    if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
+    const float *al = p.a_log + h * p.sa_h + (int64_t)c * F + n0;
+#pragma unroll
+    for (int k = 0; k < NPL; k += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(al + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) A2[k + e] = -expf(a4[e]) * L2E;
+    }
+  }
+  {
+    const float *si = p.s_init ? p.s_init + bh * (2 * (int64_t)DV * F) + (int64_t)c * F + n0 : nullptr;
+#pragma unroll
+    for (int k = 0; k < NPL; k += 4) {
+      const f32x4 sn = si ? *reinterpret_cast<const f32x4 *>(si + k) : zero4();
+      const f32x4 sd = si ? *reinterpret_cast<const f32x4 *>(si + DV * F + k) : zero4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hn[k + e] = sn[e];
+        hd[k + e] = sd[e];
+      }
+    }
+  }
+  const T *Q = (const T *)p.q + b * p.sq_b + h * p.sq_h;
+  const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
+  const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h + grp * CPW;
+  const float *DT = p.dt + b * p.sdt_b + h * p.sdt_h + grp * CPW;
+  T *O = (T *)p.o + b * p.so_b + h * p.so_h + grp * CPW;
+  const T *G = p.gate ? (const T *)p.gate + b * p.sg_b + h * p.sg_h + grp * CPW : nullptr;
+
+  for (int64_t t0 = 0; t0 < p.n; t0 += C) {
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    __syncthreads();  // W staged; the previous chunk's o rows are stored
+    // featurize: eight 16-token tasks (q tiles 0-3, k tiles 0-3) over the waves
+    for (int task = wv; task < 8; task += NW) {
+      const int proj = task >> 2, tok = 16 * (task & 3) + col;
+      const T *X = (proj == 0 ? Q + (t0 + tok) * p.sq_t : K + (t0 + tok) * p.sk_t);
+      frag xf[KD];
+#pragma unroll
+      for (int s = 0; s < KD; ++s) xf[s] = tok < nv ? M::ld_contig(X + s * M::KS, g) : frag{};
+      f32x4 ph[NFT];
+      const float sum = feature_tiles<T, DK, FH>(xf, sW[proj], ph);
+      const float inv = proj == 1 ? __builtin_amdgcn_rcpf(sum) : 1.f;  // phi(q)'s scale cancels in o
+      if (p.rope_dims > 0) {
+        const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + t0 + tok);
+        rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);
+      }
+      float *row = sPh[proj] + tok * ROW;
+#pragma unroll
+      for (int t = 0; t < NFT; ++t) {
+        const int f = 16 * t + 4 * g;
+        *reinterpret_cast<f32x4 *>(row + (f / NPL) * BLK + f % NPL) = ph[t] * inv;
+      }
+    }
+    for (int i = tid; i < C * CPW; i += NT) {
+      const int tt = i / CPW, cc = i % CPW;
+      const bool ok = tt < nv;
+      sD[i] = ok ? softplus_f32(DT[(t0 + tt) * p.sdt_t + cc]) : 0.f;
+      sVO[i] = ok ? (float)V[(t0 + tt) * p.sv_t + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int t = 0; t < nv; ++t) {
+      const float dl = sD[t * CPW + cl], dlv = dl * sVO[t * CPW + cl];
+      const float *pk = sPh[1] + t * ROW + nb * BLK, *pq = sPh[0] + t * ROW + nb * BLK;
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int k = 0; k < NPL; k += 4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4 *>(pk + k);
+        const f32x4 q4 = *reinterpret_cast<const f32x4 *>(pq + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = __builtin_amdgcn_exp2f(dl * A2[k + e]);
+          hn[k + e] = __builtin_fmaf(a, hn[k + e], k4[e] * dlv);
+          hd[k + e] = __builtin_fmaf(a, hd[k + e], k4[e] * dl);
+          num = __builtin_fmaf(q4[e], hn[k + e], num);
+          den = __builtin_fmaf(q4[e], hd[k + e], den);
+        }
+      }
+      num = group_lanes_sum<LPC>(num);
+      den = group_lanes_sum<LPC>(den);
+      if (nb == 0) sVO[t * CPW + cl] = num / den;  // v[t][cl] was read by every lane of the channel above
+    }
+    __syncthreads();
+    for (int i = tid; i < nv * CPW; i += NT) {
+      const int tt = i / CPW, cc = i % CPW;
+      float o = sVO[i];
+      if (G) o = (float)to_elem<T>(o) * silu_f32((float)G[(t0 + tt) * p.sg_t + cc]);
+      O[(t0 + tt) * p.so_t + cc] = to_elem<T>(o);
+    }
+  }
+  if (p.s_final) {
+    float *sf = p.s_final + bh * (2 * (int64_t)DV * F) + (int64_t)c * F + n0;
+#pragma unroll
+    for (int k = 0; k < NPL; k += 4) {
+      *reinterpret_cast<f32x4 *>(sf + k) = f32x4{hn[k], hn[k + 1], hn[k + 2], hn[k + 3]};
+      *reinterpret_cast<f32x4 *>(sf + DV * F + k) = f32x4{hd[k], hd[k + 1], hd[k + 2], hd[k + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------- decode step
+struct PcStepParams {
+  StepParams s;          // q, k, v, w, o, gate, conv, rotary fields and strides (s.dt, s.a_log unused)
+  const float *dt;       // [B, H, dv] (strides sdt_b, sdt_h)
+  const float *a_log;    // [H][dv][F] (head stride sa_h)
+  float *state;          // [B*H][2][dv][F], in place
+  int64_t sdt_b, sdt_h, sa_h;
+};
+
+// One workgroup of 256 threads per (b, h, group of CPS channels): every thread
+// issues the loads of its PER (channel, 4 states) items of both copies and of A
+// first, featurizes while they are in flight (each group recomputes phi(q), phi(k)
+// of its (b, h): a few thousand FMAs against 2 x 2 x CPS x F x 4 bytes of state),
+// then updates, reads out (sum over the QPC lanes of a channel) and stores in place.
+// Small workgroups let several groups share a CU, so one group's featurization
+// overlaps another's state traffic.  Bound by the state's HBM traffic.
+template <typename T, int DK, int FH, int DV, int CPS>
+__global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
+  constexpr int NT = 256, F = 2 * FH, QPC = F / 4;  // float4 per channel row
+  constexpr int ITEMS = CPS * QPC, PER = (ITEMS + NT - 1) / NT, NG = DV / CPS;
+  constexpr float L2E = 1.4426950408889634f;
+  static_assert(QPC == 32 || QPC == 16 || QPC == 8, "lanes per channel");
+  static_assert(DV % CPS == 0 && 64 % QPC == 0, "channel groups");
+  const StepParams &p = pp.s;
+  __shared__ float sx[2][DK];
+  __shared__ float su[256 / (2 * FH)][2 * FH];
+  __shared__ __align__(16) float sphi[2][F];
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x / NG, b = bh / p.H, h = bh % p.H;
+  const int c0 = (int)(blockIdx.x % NG) * CPS;
+  float *Sn = pp.state + bh * (2 * (int64_t)DV * F) + (int64_t)c0 * F;
+  float *Sd = Sn + DV * F;
+  const float *AL = pp.a_log + h * pp.sa_h + (int64_t)c0 * F;
+  f32x4 vn[PER], vd[PER], va[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + NT * m;
+    if (idx < ITEMS) {
+      vn[m] = reinterpret_cast<const f32x4 *>(Sn)[idx];
+      vd[m] = reinterpret_cast<const f32x4 *>(Sd)[idx];
+      va[m] = reinterpret_cast<const f32x4 *>(AL)[idx];
+    }
+  }
+  step_features<T, DK, FH>(p, b, h, sx, su, sphi);
+  const T *vp = (const T *)p.v + b * p.sv_b + h * p.sv_h + c0;
+  const float *dtp = pp.dt + b * pp.sdt_b + h * pp.sdt_h + c0;
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + NT * m;
+    const int c = idx / QPC, n = 4 * (idx % QPC);
+    float num = 0.f, den = 0.f;
+    if (idx < ITEMS) {
+      const float dl = softplus_f32(dtp[c]), dlv = dl * (float)vp[c];
+      const f32x4 k4 = *reinterpret_cast<const f32x4 *>(&sphi[1][n]);
+      const f32x4 q4 = *reinterpret_cast<const f32x4 *>(&sphi[0][n]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = __builtin_amdgcn_exp2f(-dl * __builtin_amdgcn_exp2f(va[m][e] * L2E) * L2E);
+        vn[m][e] = __builtin_fmaf(a, vn[m][e], k4[e] * dlv);
+        vd[m][e] = __builtin_fmaf(a, vd[m][e], k4[e] * dl);
+        num = __builtin_fmaf(q4[e], vn[m][e], num);
+        den = __builtin_fmaf(q4[e], vd[m][e], den);
+      }
+      reinterpret_cast<f32x4 *>(Sn)[idx] = vn[m];
+      reinterpret_cast<f32x4 *>(Sd)[idx] = vd[m];
+    }
+    // the QPC lanes of channel c are consecutive and aligned
+    if constexpr (QPC == 32) {
+      num = xor16_pair(group_lanes_sum<16>(num), false);
+      den = xor16_pair(group_lanes_sum<16>(den), false);
+    } else {
+      num = group_lanes_sum<QPC>(num);
+      den = group_lanes_sum<QPC>(den);
+    }
+    if (idx < ITEMS && idx % QPC == 0) {
+      float o = num / den;
+      const int64_t cg = c0 + c;
+      T *op = (T *)p.o + b * p.so_b + h * p.so_h;
+      if (p.gate) o = (float)to_elem<T>(o) * silu_f32((float)((const T *)p.gate)[b * p.sg_b + h * p.sg_h + cg]);
+      op[cg] = to_elem<T>(o);
+    }
+  }
+}
+
+}  // namespace hm

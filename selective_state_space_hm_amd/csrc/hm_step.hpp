@@ -36,42 +36,22 @@ struct StepParams {
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
 
-template <typename T, int DK, int FH, int DV, bool DECAY>
-__global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
+// phi(q_t) and phi(k_t) of one (b, h) into sphi[0], sphi[1], worked by the first
+// 256 threads of the workgroup: the token rows are staged as floats (through the
+// short causal conv when one is given), projected by W split over PARTS threads
+// per output, and turned into softmax rows by waves 0 (q) and 1 (k); with
+// rope_dims > 0 both rows are then turned by the rotary encoding.  Every thread
+// of the workgroup must call it (it holds barriers); it ends with a barrier,
+// after which sphi is complete.
+template <typename T, int DK, int FH>
+__device__ __forceinline__ void step_features(const StepParams &p, int64_t b, int64_t h, float (*sx)[DK],
+                                              float (*su)[2 * FH], float (*sphi)[2 * FH]) {
   constexpr int NT = 256;
-  constexpr int F = 2 * FH;
-  constexpr int RV = DV / 4;                 // float4 per state row
-  constexpr int NS4 = F * RV;                // float4 in S
-  constexpr int PER = (NS4 + NT - 1) / NT;   // float4 per thread
-  constexpr int GROUPS = NT / RV;            // threads sharing one column group
   constexpr int PARTS = NT / (2 * FH);       // threads per projection output
   constexpr int DPART = DK / PARTS;
-  static_assert(NT % RV == 0 && NT % (2 * FH) == 0 && DK % PARTS == 0, "step mapping");
-
-  __shared__ float sx[2][DK];
-  __shared__ float su[PARTS][2 * FH];
-  __shared__ __align__(16) float sphi[2][F];  // [0] = phi(q), [1] = phi(k)
-  __shared__ __align__(16) float sred[GROUPS][DV];
-  __shared__ float sden[F / 4 > 0 ? F / 4 : 1];
-  __shared__ float sa;
-
+  static_assert(NT % (2 * FH) == 0 && DK % PARTS == 0, "step mapping");
   const int tid = threadIdx.x;
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / p.H, h = bh % p.H;
-  constexpr int64_t BLK = (int64_t)F * DV + F;
-  float *st = p.state + bh * BLK;
-
-  // 1. issue the state loads
-  f32x4 sv[PER];
-#pragma unroll
-  for (int m = 0; m < PER; ++m) {
-    const int idx = tid + NT * m;
-    if (idx < NS4) sv[m] = reinterpret_cast<const f32x4 *>(st)[idx];
-  }
-  f32x4 zv = zero4();
-  if (tid < F / 4) zv = reinterpret_cast<const f32x4 *>(st + F * DV)[tid];
-
-  // 2. featurize q and k: u[j] = sum_i x[i] W[i][j], split over PARTS threads
+  const int64_t bh = b * p.H + h;
   const T *xq = (const T *)p.q + b * p.sq_b + h * p.sq_h;
   const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
   for (int i = tid; i < 2 * DK; i += NT) {
@@ -97,13 +77,8 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
     }
     sx[proj][c] = xv;
   }
-  if (tid == 0) {
-    float a = 1.f;
-    if constexpr (DECAY) a = __expf(-softplus_f32(p.dt[b * p.sdt_b + h * p.sdt_h]) * expf(p.a_log[h]));
-    sa = a;
-  }
   __syncthreads();
-  {
+  if (tid < NT) {
     const int o = tid % (2 * FH), part = tid / (2 * FH);
     const int proj = o / FH, j = o % FH;
     const T *W = (const T *)(proj == 0 ? p.wq : p.wk) + h * p.sw_h;
@@ -151,7 +126,49 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
     }
     __syncthreads();
   }
+}
 
+template <typename T, int DK, int FH, int DV, bool DECAY>
+__global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
+  constexpr int NT = 256;
+  constexpr int F = 2 * FH;
+  constexpr int RV = DV / 4;                 // float4 per state row
+  constexpr int NS4 = F * RV;                // float4 in S
+  constexpr int PER = (NS4 + NT - 1) / NT;   // float4 per thread
+  constexpr int GROUPS = NT / RV;            // threads sharing one column group
+  constexpr int PARTS = NT / (2 * FH);
+  static_assert(NT % RV == 0, "step mapping");
+
+  __shared__ float sx[2][DK];
+  __shared__ float su[PARTS][2 * FH];
+  __shared__ __align__(16) float sphi[2][F];  // [0] = phi(q), [1] = phi(k)
+  __shared__ __align__(16) float sred[GROUPS][DV];
+  __shared__ float sden[F / 4 > 0 ? F / 4 : 1];
+  __shared__ float sa;
+
+  const int tid = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / p.H, h = bh % p.H;
+  constexpr int64_t BLK = (int64_t)F * DV + F;
+  float *st = p.state + bh * BLK;
+
+  // 1. issue the state loads
+  f32x4 sv[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int idx = tid + NT * m;
+    if (idx < NS4) sv[m] = reinterpret_cast<const f32x4 *>(st)[idx];
+  }
+  f32x4 zv = zero4();
+  if (tid < F / 4) zv = reinterpret_cast<const f32x4 *>(st + F * DV)[tid];
+
+  // 2. the decay, and phi(q), phi(k) while the loads are in flight
+  if (tid == 0) {
+    float a = 1.f;
+    if constexpr (DECAY) a = __expf(-softplus_f32(p.dt[b * p.sdt_b + h * p.sdt_h]) * expf(p.a_log[h]));
+    sa = a;
+  }
+  step_features<T, DK, FH>(p, b, h, sx, su, sphi);
   // 3. update, read out, store.  Thread tid owns column group c4 = tid % RV and
   //    rows f = tid / RV + GROUPS * m.
   const float a = sa;
@@ -201,10 +218,46 @@ struct FeatParams {
   const int64_t *rope_pos0;   // position of token 0 per batch row (NULL = 0)
 };
 
-// Standalone Hedgehog featurizer (gsyq.cn HedgeMamba explainer §2.1, §5.3):
-// phi = softmax([x W, -x W]).  One workgroup = 64 tokens of one (b, h); wave w
-// computes U^T = W^T X^T for token tile w on the MFMA, then the row softmax with
-// cross-lane reductions, and stores phi rows with 8/16-byte vector stores.
+// Hedgehog features of 16 tokens per wave (gsyq.cn HedgeMamba explainer §2.1,
+// §5.3): U^T = W^T X^T on the MFMA from the token rows' operand fragments xf
+// (lane (g, col) holds row col's K-slices) and W^T in LDS (rows f, stride LDW),
+// then exp([u, -u] - max|u|) per token.  On return lane (g, col) holds feature
+// 16t + 4g + r of token col in ph[t][r] (the +u half in tiles t < FH/16), not
+// yet divided by the row sum, which is returned.
+template <typename T, int DK, int FH>
+__device__ __forceinline__ float feature_tiles(const typename Mma<T>::frag *xf, const T *sW, f32x4 *ph) {
+  using M = Mma<T>;
+  constexpr int NFH = FH / 16, KD = DK / M::KS, LDW = DK + M::PAD;
+  const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
+  f32x4 u[NFH];
+#pragma unroll
+  for (int t = 0; t < NFH; ++t) {
+    u[t] = zero4();
+#pragma unroll
+    for (int s = 0; s < KD; ++s) u[t] = M::mma(M::ld_contig(sW + (16 * t + col) * LDW + s * M::KS, g), xf[s], u[t]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int t = 0; t < NFH; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[t][r]));
+  m = group_max(m);
+  float sum = 0.f;
+#pragma unroll
+  for (int t = 0; t < NFH; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ep = __expf(u[t][r] - m), em = __expf(-u[t][r] - m);
+      ph[t][r] = ep;
+      ph[NFH + t][r] = em;
+      sum += ep + em;
+    }
+  return group_sum(sum);
+}
+
+// Standalone Hedgehog featurizer: phi = softmax([x W, -x W]).  One workgroup =
+// 64 tokens of one (b, h); wave w featurizes token tile w (feature_tiles) and
+// stores phi rows with 8/16-byte vector stores.
 template <typename T, typename TO, int DK, int FH>
 __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   using M = Mma<T>;
@@ -223,32 +276,8 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
 #pragma unroll
   for (int s = 0; s < KD; ++s) xf[s] = c < p.n ? M::ld_contig(X + s * M::KS, g) : frag{};
   __syncthreads();
-  f32x4 u[NFH];
-#pragma unroll
-  for (int t = 0; t < NFH; ++t) {
-    u[t] = zero4();
-#pragma unroll
-    for (int s = 0; s < KD; ++s) u[t] = M::mma(M::ld_contig(sW + (16 * t + col) * LDW + s * M::KS, g), xf[s], u[t]);
-  }
-  float m = 0.f;
-#pragma unroll
-  for (int t = 0; t < NFH; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(u[t][r]));
-  m = group_max(m);
   f32x4 ph[NFT];
-  float sum = 0.f;
-#pragma unroll
-  for (int t = 0; t < NFH; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float ep = __expf(u[t][r] - m), em = __expf(-u[t][r] - m);
-      ph[t][r] = ep;
-      ph[NFH + t][r] = em;
-      sum += ep + em;
-    }
-  sum = group_sum(sum);
-  const float inv = 1.f / sum;
+  const float inv = 1.f / feature_tiles<T, DK, FH>(xf, sW, ph);
   if (p.rope_dims > 0) {
     const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + c);
     rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);

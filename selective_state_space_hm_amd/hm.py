@@ -85,6 +85,31 @@ class BwdArgs(C.Structure):
                 ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void)]
 
 
+class PcArgs(C.Structure):
+    _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
+                ("dt", p_void), ("a_log", p_void), ("s_init", p_void), ("s_final", p_void), ("o", p_void),
+                ("gate", p_void), ("dtype", i32), ("rope_dims", i32), ("rope_base", C.c_float), ("reserved", i32),
+                ("rope_pos0", p_void),
+                ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64), ("dv", i64),
+                ("sq_b", i64), ("sq_h", i64), ("sq_t", i64), ("sk_b", i64), ("sk_h", i64), ("sk_t", i64),
+                ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
+                ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
+                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64), ("sa_h", i64)]
+
+
+class PcStepArgs(C.Structure):
+    _fields_ = [("q", p_void), ("k", p_void), ("v", p_void), ("w_q", p_void), ("w_k", p_void),
+                ("dt", p_void), ("a_log", p_void), ("state", p_void), ("o", p_void), ("gate", p_void),
+                ("dtype", i32), ("conv_width", i32),
+                ("B", i64), ("H", i64), ("d", i64), ("f", i64), ("dv", i64),
+                ("sq_b", i64), ("sq_h", i64), ("sk_b", i64), ("sk_h", i64), ("sv_b", i64), ("sv_h", i64),
+                ("so_b", i64), ("so_h", i64), ("sg_b", i64), ("sg_h", i64),
+                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sa_h", i64),
+                ("conv_wq", p_void), ("conv_wk", p_void), ("conv_bq", p_void), ("conv_bk", p_void),
+                ("conv_sq", p_void), ("conv_sk", p_void), ("scw_h", i64), ("scb_h", i64),
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos", p_void)]
+
+
 class HMError(RuntimeError):
     def __init__(self, status, message):
         super().__init__(f"{status_string(status)}: {message}")
@@ -94,7 +119,8 @@ class HMError(RuntimeError):
 _lib = None
 EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
            "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
-           "hm_linattn_bwd", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
+           "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step", "hm_status_string",
+           "hm_last_error_message", "hm_abi_version", "hm_args_size"]
 
 
 def lib():
@@ -113,9 +139,11 @@ def lib():
         L.hm_linattn_save_size.argtypes = [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]
         L.hm_linattn_bwd_workspace_size.argtypes = [C.POINTER(BwdArgs), C.POINTER(C.c_size_t)]
         L.hm_linattn_bwd.argtypes = [C.POINTER(BwdArgs), p_void]
+        L.hm_linattn_pc_fwd.argtypes = [C.POINTER(PcArgs), p_void]
+        L.hm_linattn_pc_step.argtypes = [C.POINTER(PcStepArgs), p_void]
         for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
                    "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
-                   "hm_linattn_bwd"):
+                   "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step"):
             getattr(L, fn).restype = C.c_int
         L.hm_status_string.argtypes = [C.c_int]
         L.hm_status_string.restype = C.c_char_p
@@ -180,6 +208,14 @@ def call_bwd_workspace_size(args: BwdArgs):
     n = C.c_size_t(0)
     st = lib().hm_linattn_bwd_workspace_size(C.byref(args), C.byref(n))
     return st, n.value
+
+
+def call_pc_fwd(args: PcArgs, stream=None) -> int:
+    return lib().hm_linattn_pc_fwd(C.byref(args), stream)
+
+
+def call_pc_step(args: PcStepArgs, stream=None) -> int:
+    return lib().hm_linattn_pc_step(C.byref(args), stream)
 
 
 def call_bwd(args: BwdArgs, stream=None) -> int:
@@ -462,6 +498,83 @@ def hm_linattn_bwd(q, k, v, w_q, w_k, d_o, save, dt=None, a_log=None, gate=None,
     if dsi is not None:
         out["s_init"] = dsi
     return out
+
+
+def _a_log_stride(a_log, dv, F):
+    if a_log.dtype != torch.float32 or tuple(a_log.shape[-2:]) != (dv, F) or not a_log.is_contiguous():
+        raise ValueError("a_log is contiguous float32 [dv, 2f] (shared) or [H, dv, 2f]")
+    return a_log.stride(0) if a_log.dim() == 3 else 0
+
+
+def hm_linattn_pc_fwd(q, k, v, w_q, w_k, dt, a_log, s_init=None, s_final=None, o=None, gate=None,
+                      rope_dims=0, rope_base=10000.0, rope_pos0=None):
+    """Prefill with a decay per value channel and state (the pages' Mamba-1 wiring):
+    dt float32 [B, H, n, dv] (the step size before softplus), a_log float32 [dv, 2f] or
+    [H, dv, 2f].  Returns o [B, H, n, dv]; s_final (if given) receives the float32
+    state [B, H, 2*dv*2f] (Sn [dv][2f] then Sd [dv][2f])."""
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
+    _gate_shape(gate, v)
+    B, H, n, d = q.shape
+    dv = v.shape[-1]
+    f = w_q.shape[-1]
+    if dt.dtype != torch.float32 or tuple(dt.shape) != (B, H, n, dv) or dt.stride(3) != 1:
+        raise ValueError("dt is float32 [B, H, n, dv] with contiguous channels")
+    for t in (q, k, v, o, gate):
+        if t is not None and t.stride(3) != 1:
+            raise ValueError("inner dimensions must be contiguous")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    a = PcArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
+               s_init=_ptr(s_init), s_final=_ptr(s_final), o=_ptr(o), gate=_ptr(gate), dtype=_code(q),
+               B=B, H=H, n=n, d=d, f=f, dv=dv,
+               sq_b=q.stride(0), sq_h=q.stride(1), sq_t=q.stride(2), sk_b=k.stride(0), sk_h=k.stride(1),
+               sk_t=k.stride(2), sv_b=v.stride(0), sv_h=v.stride(1), sv_t=v.stride(2),
+               so_b=o.stride(0), so_h=o.stride(1), so_t=o.stride(2),
+               sg_b=gate.stride(0) if gate is not None else 0, sg_h=gate.stride(1) if gate is not None else 0,
+               sg_t=gate.stride(2) if gate is not None else 0, sw_h=_w_strides(w_q),
+               sdt_b=dt.stride(0), sdt_h=dt.stride(1), sdt_t=dt.stride(2), sa_h=_a_log_stride(a_log, dv, 2 * f))
+    _rope(a, B, rope_dims, rope_base, rope_pos0)
+    _check(call_pc_fwd(a, _stream()))
+    return o
+
+
+def hm_linattn_pc_step(q, k, v, w_q, w_k, state, dt, a_log, o=None, gate=None, conv=None,
+                       rope_dims=0, rope_base=10000.0, rope_pos=None):
+    """One decode token per (b, h) of the per-channel scan: q, k [B, H, d], v [B, H, dv],
+    dt float32 [B, H, dv]; state float32 [B, H, 2*dv*2f] updated in place.  conv and
+    the rotary fields as in hm_linattn_step."""
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
+    _gate_shape(gate, v)
+    B, H, d = q.shape
+    dv = v.shape[-1]
+    f = w_q.shape[-1]
+    if state.dtype != torch.float32:
+        raise TypeError("state is float32")
+    if dt.dtype != torch.float32 or tuple(dt.shape) != (B, H, dv) or dt.stride(2) != 1:
+        raise ValueError("dt is float32 [B, H, dv] with contiguous channels")
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
+    a = PcStepArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
+                   state=_ptr(state), o=_ptr(o), gate=_ptr(gate), dtype=_code(q), B=B, H=H, d=d, f=f, dv=dv,
+                   sq_b=q.stride(0), sq_h=q.stride(1), sk_b=k.stride(0), sk_h=k.stride(1),
+                   sv_b=v.stride(0), sv_h=v.stride(1), so_b=o.stride(0), so_h=o.stride(1),
+                   sg_b=gate.stride(0) if gate is not None else 0, sg_h=gate.stride(1) if gate is not None else 0,
+                   sw_h=_w_strides(w_q), sdt_b=dt.stride(0), sdt_h=dt.stride(1), sa_h=_a_log_stride(a_log, dv, 2 * f))
+    if conv is not None:
+        cwq, cwk, cbq, cbk, csq, csk = conv
+        a.conv_width = cwq.shape[-1]
+        a.conv_wq, a.conv_wk, a.conv_bq, a.conv_bk = _ptr(cwq), _ptr(cwk), _ptr(cbq), _ptr(cbk)
+        a.conv_sq, a.conv_sk = _ptr(csq), _ptr(csk)
+        a.scw_h = cwq.stride(0) if cwq.dim() == 3 else 0
+        a.scb_h = cbq.stride(0) if cbq is not None and cbq.dim() == 2 else 0
+    _rope(a, B, rope_dims, rope_base, rope_pos, "rope_pos")
+    _check(call_pc_step(a, _stream()))
+    return o
+
+
+def state_numel_pc(f: int, dv: int) -> int:
+    """float32 elements of one (b, h) per-channel state block: Sn and Sd, [dv][2f] each."""
+    return 2 * dv * 2 * f
 
 
 def state_numel(f: int, dv: int) -> int:

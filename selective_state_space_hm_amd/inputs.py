@@ -15,6 +15,8 @@ Recipe (every case):
   * dt ~ N(0, 1) float32 [B, H, n];
   * A_log float32 [H], uniform on [lo, hi]: [0, ln 16] for the Mamba-style
     decay, [ln 2^-9, ln 2^-3] for the mild decay that keeps a_t near 0.99;
+  * per-channel-decay cases (make_pc): after W_k, dt float32 [B, H, n, dv] ~ N(0, 1)
+    and A_log float32 [H, dv, 2f] ~ U(ln 2^-4, ln 16);
   * the gate branch's pre-activation (when a case has one) comes from its own
     generator, seeded with 7919 * (seed + 1), ~ N(0, 2^2) in o's shape, so that
     both signs and the saturated ends of SiLU are exercised.
@@ -120,6 +122,27 @@ def mild_decay(seed=0, n=8192, B=2):
 def small(n=37, decay="mamba", dtype=torch.float32, d=16, f=16, dv=16, B=1, H=2, seed=0):
     """Small ragged case for brute-force checks (n not a multiple of any chunk)."""
     return make_prefill(f"small-n{n}", B, H, n, d, f, dv, dtype, None, decay, seed)
+
+
+def make_pc(name, B, H, n, d, f, dv, dtype=torch.bfloat16, seed=0, shared_a=False) -> Case:
+    """Per-channel-decay case: q, k, v, W_q, W_k as in make_prefill (same draw order
+    and distributions, W ~ N(0, 1/d)), then dt float32 [B, H, n, dv] ~ N(0, 1) and
+    A_log float32 [H, dv, 2f] (or [dv, 2f] when shared_a) ~ U(ln 2^-4, ln 16), so that
+    exp(A_log), the per-state decay rate, spans slow and fast states (Mamba-1's own
+    initialisation, A_log[c, n] = ln(n + 1), lies in the same range)."""
+    g = torch.Generator().manual_seed(seed)
+    w_std = 1.0 / math.sqrt(d)
+    q = _normal(g, (B, H, n, d)).to(dtype)
+    k = _normal(g, (B, H, n, d)).to(dtype)
+    v = _normal(g, (B, H, n, dv)).to(dtype)
+    w_q = _normal(g, (d, f), w_std).to(dtype)
+    w_k = _normal(g, (d, f), w_std).to(dtype)
+    dt = _normal(g, (B, H, n, dv))
+    shape = (dv, 2 * f) if shared_a else (H, dv, 2 * f)
+    lo, hi = -4.0 * math.log(2.0), LN16
+    a_log = (lo + (hi - lo) * torch.rand(shape, generator=g, dtype=torch.float64)).to(torch.float32)
+    return Case(name, B, H, n, d, f, dv, dtype, q, k, v, w_q, w_k, dt, a_log,
+                {"seed": seed, "decay": "per-channel", "w_std": w_std})
 
 
 @dataclass

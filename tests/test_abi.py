@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     L = hm.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -38,11 +38,13 @@ def test_struct_layouts_match_binding():
     assert L.hm_args_size(2) == C.sizeof(hm.StepArgs)
     assert L.hm_args_size(3) == C.sizeof(hm.ConvArgs)
     assert L.hm_args_size(4) == C.sizeof(hm.BwdArgs)
-    assert L.hm_args_size(5) == 0
+    assert L.hm_args_size(5) == C.sizeof(hm.PcArgs)
+    assert L.hm_args_size(6) == C.sizeof(hm.PcStepArgs)
+    assert L.hm_args_size(7) == 0
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 5
+    assert hm.lib().hm_abi_version() == 6
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -331,3 +333,55 @@ def test_rotary_field_validation():
     expect(hm.call_bwd(bwd(rope_dims=96, rope_base=0.5, rope_pos0=P + 2)), hm.HM_ERR_ALIGN)
     expect(hm.call_bwd(bwd(rope_dims=200, rope_base=1e4)), hm.HM_ERR_SHAPE)
     expect(hm.call_bwd(bwd(rope_dims=128, rope_base=1e4)), hm.HM_ERR_WORKSPACE)  # valid; no workspace given
+
+
+def pc(B=2, H=16, n=2048, d=128, f=64, dv=128, dtype=hm.HM_BF16, **kw):
+    a = hm.PcArgs(q=A, k=A + 0x1000000, v=A + 0x2000000, w_q=A + 0x3000000, w_k=A + 0x3100000,
+                  dt=A + 0x5000000, a_log=A + 0x6000000, o=A + 0x4000000, dtype=dtype, B=B, H=H, n=n, d=d, f=f,
+                  dv=dv, sq_b=H * n * d, sq_h=n * d, sq_t=d, sk_b=H * n * d, sk_h=n * d, sk_t=d,
+                  sv_b=H * n * dv, sv_h=n * dv, sv_t=dv, so_b=H * n * dv, so_h=n * dv, so_t=dv,
+                  sdt_b=H * n * dv, sdt_h=n * dv, sdt_t=dv, sa_h=dv * 2 * f)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def pc_step(B=256, H=16, d=128, f=64, dv=128, dtype=hm.HM_BF16, **kw):
+    a = hm.PcStepArgs(q=A, k=A + 0x100000, v=A + 0x200000, w_q=A + 0x300000, w_k=A + 0x310000,
+                      dt=A + 0x320000, a_log=A + 0x340000, state=A + 0x400000, o=A + 0x9000000, dtype=dtype,
+                      B=B, H=H, d=d, f=f, dv=dv, sq_b=H * d, sq_h=d, sk_b=H * d, sk_h=d, sv_b=H * dv, sv_h=dv,
+                      so_b=H * dv, so_h=dv, sdt_b=H * dv, sdt_h=dv, sa_h=0)
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def test_per_channel_validation():
+    L = hm.lib()
+    expect(L.hm_linattn_pc_fwd(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_pc_fwd(pc(dt=None)), hm.HM_ERR_NULL)
+    expect(hm.call_pc_fwd(pc(a_log=None)), hm.HM_ERR_NULL)
+    expect(hm.call_pc_fwd(pc(q=None)), hm.HM_ERR_NULL)
+    expect(hm.call_pc_fwd(pc(n=0, q=None, k=None, v=None, o=None, w_q=None, w_k=None)), hm.HM_OK)  # no token, no s_final
+    expect(hm.call_pc_fwd(pc(dtype=4)), hm.HM_ERR_DTYPE)
+    expect(hm.call_pc_fwd(pc(dv=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_pc_fwd(pc(sa_h=7)), hm.HM_ERR_SHAPE)                 # A_log shared or one block per head
+    expect(hm.call_pc_fwd(pc(sdt_t=64)), hm.HM_ERR_SHAPE)               # dt rows overlap
+    expect(hm.call_pc_fwd(pc(a_log=A + 0x6000004)), hm.HM_ERR_ALIGN)
+    expect(hm.call_pc_fwd(pc(dt=A + 0x5000002)), hm.HM_ERR_ALIGN)
+    expect(hm.call_pc_fwd(pc(s_final=A + 0x7000008)), hm.HM_ERR_ALIGN)
+    expect(hm.call_pc_fwd(pc(d=96)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_pc_fwd(pc(f=32)), hm.HM_ERR_UNSUPPORTED)             # (128, 32, 128) is not built
+    expect(hm.call_pc_fwd(pc(rope_dims=48, rope_base=1e4)), hm.HM_ERR_UNSUPPORTED)
+    blk = 2 * 128 * 128 * 4
+    expect(hm.call_pc_fwd(pc(s_init=A + 0x8000000, s_final=A + 0x8000000 + blk)), hm.HM_ERR_SHAPE)  # partial overlap
+    expect(hm.call_pc_fwd(pc(B=0, s_init=A + 0x8000000, s_final=A + 0x8000000)), hm.HM_OK)
+    expect(L.hm_linattn_pc_step(None, None), hm.HM_ERR_NULL)
+    expect(hm.call_pc_step(pc_step(dt=None, a_log=None)), hm.HM_ERR_NULL)
+    expect(hm.call_pc_step(pc_step(state=None)), hm.HM_ERR_NULL)
+    expect(hm.call_pc_step(pc_step(sa_h=5)), hm.HM_ERR_SHAPE)
+    expect(hm.call_pc_step(pc_step(a_log=A + 0x340008)), hm.HM_ERR_ALIGN)
+    expect(hm.call_pc_step(pc_step(d=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_pc_step(pc_step(rope_dims=64, rope_base=1e4)), hm.HM_ERR_NULL)      # positions required
+    expect(hm.call_pc_step(pc_step(conv_width=5)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_pc_step(pc_step(B=0)), hm.HM_OK)
