@@ -103,6 +103,29 @@ __device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, 
     if (idx < N) *reinterpret_cast<V *>(dst + r * ld + pc * E) = x[m];
   }
 }
+// stage() in two halves, for operands whose LDS buffer frees up later: the loads
+// go out with an earlier phase's (one memory round trip less per chunk) and the
+// LDS writes happen once the buffer is free.
+template <typename T, int ROWS, int COLS> struct Staged {
+  static constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + 255) / 256;
+  typename Vec<T>::type x[PER];
+  __device__ __forceinline__ void load(const T *src, int64_t gs, int valid) {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+      x[m] = (idx < N && r < valid) ? *reinterpret_cast<const typename Vec<T>::type *>(src + r * gs + pc * E)
+                                    : typename Vec<T>::type{};
+    }
+  }
+  __device__ __forceinline__ void store(T *dst, int ld) const {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+      if (idx < N) *reinterpret_cast<typename Vec<T>::type *>(dst + r * ld + pc * E) = x[m];
+    }
+  }
+};
+
 // the same rows written transposed: dst[c * ld + r] = scale_r * src[r][c].
 // Consecutive lanes take consecutive source rows (two rows per lane for bf16,
 // packed into one 4-byte write), so the LDS writes of a wave are contiguous.
@@ -483,6 +506,8 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    Staged<T, C, F> phq_next;  // phi(q) rows, written over v once A is formed
+    phq_next.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
     stage<T, C, DV>(sDN, LN, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     stage<T, C, DV>(sVQ, LVQ, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     stage_t<T, C, DK>(sXT, LC, (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
@@ -507,7 +532,7 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
       put<T>(sA + 16 * w * LC + 16 * jt, LC, a);
     }
     __syncthreads();
-    stage<T, C, F>(sVQ, LVQ, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    phq_next.store(sVQ, LVQ);
     __syncthreads();
     // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F]
     f32x4 dph[F / 16];
@@ -611,6 +636,8 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    Staged<T, C, F> phk_next;  // phi(k) rows, written over dnum once A^T is formed
+    phk_next.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
     stage<T, C, DV>(sNK, LNK, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     stage_t<T, C, DK>(sXT, LC, (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
@@ -635,7 +662,7 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
       put<T>(sAT + 16 * w * LC + 16 * tt, LC, a);
     }
     __syncthreads();
-    stage<T, C, F>(sNK, LNK, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    phk_next.store(sNK, LNK);
     __syncthreads();
     // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F]
     const float Lam = sL[nv - 1];
