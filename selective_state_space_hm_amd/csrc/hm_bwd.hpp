@@ -126,6 +126,55 @@ template <typename T, int ROWS, int COLS> struct Staged {
   }
 };
 
+// stage_t() in two halves (no row scale).
+template <typename T, int ROWS, int COLS> struct StagedT {
+  static constexpr int E = ep<T>(), PPR = COLS / E;
+  static constexpr int NP = sizeof(T) == 2 ? ROWS / 2 : ROWS, N = NP * PPR, PER = (N + 255) / 256;
+  typename Vec<T>::type x0[PER], x1[sizeof(T) == 2 ? PER : 1];
+  __device__ __forceinline__ void load(const T *src, int64_t gs, int valid) {
+    typedef typename Vec<T>::type V;
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m;
+      if constexpr (sizeof(T) == 2) {
+        const int r = 2 * (idx % NP), pc = idx / NP;
+        x0[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+        x1[m] = (idx < N && r + 1 < valid) ? *reinterpret_cast<const V *>(src + (r + 1) * gs + pc * E) : V{};
+      } else {
+        const int r = idx % ROWS, pc = idx / ROWS;
+        x0[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
+      }
+    }
+  }
+  // rscale (optional): row r is multiplied by rscale[r] and rounded to T once more
+  __device__ __forceinline__ void store(T *dst, int ld, const float *rscale = nullptr) const {
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int idx = threadIdx.x + 256 * m;
+      if (idx >= N) continue;
+      if constexpr (sizeof(T) == 2) {
+        const int r = 2 * (idx % NP), pc = idx / NP;
+        const float s0 = rscale ? rscale[r] : 1.f, s1 = rscale ? rscale[r + 1] : 1.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          // through named T values: the bit cast of a vector-element expression
+          // itself gave wrong bits here
+          const T lo = rscale ? (T)((float)x0[m][e] * s0) : x0[m][e];
+          const T hi = rscale ? (T)((float)x1[m][e] * s1) : x1[m][e];
+          const uint32_t packed =
+              (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          *reinterpret_cast<uint32_t *>(dst + (pc * E + e) * ld + r) = packed;
+        }
+      } else {
+        const int r = idx % ROWS, pc = idx / ROWS;
+        const float s0 = rscale ? rscale[r] : 1.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dst[(pc * E + e) * ld + r] = rscale ? (T)((float)x0[m][e] * s0) : x0[m][e];
+      }
+    }
+  }
+};
+
 // the same rows written transposed: dst[c * ld + r] = scale_r * src[r][c].
 // Consecutive lanes take consecutive source rows (two rows per lane for bf16,
 // packed into one 4-byte write), so the LDS writes of a wave are contiguous.
@@ -421,6 +470,17 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     }
   }
   if (tid < F && p.ds_final) gz = p.ds_final[bh * BLK + (int64_t)F * DV + tid];
+  // the (earlier) chunk's phi(q) and dnum are fetched while the current chunk's
+  // products run: the chunks are visited one after the other, so each chunk's load
+  // latency would otherwise stand alone
+  StagedT<T, C, F> pf_q;
+  StagedT<T, C, DV> pf_n;
+  if (p.nch > 0) {
+    const int64_t t0 = (p.nch - 1) * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    pf_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    pf_n.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+  }
   for (int64_t c = p.nch - 1; c >= 0; --c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
@@ -442,8 +502,13 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
       sdd[tid] = valid ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
     __syncthreads();
-    stage_t<T, C, F, true>(sA, LDC_, (const T *)p.phq + (bh * p.n + t0) * F, F, nv, seL);
-    stage_t<T, C, DV>(sB, LDC_, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    pf_q.store(sA, LDC_, seL);
+    pf_n.store(sB, LDC_);
+    if (c > 0) {
+      const int64_t tp = t0 - C;  // the previous chunk is always full
+      pf_q.load((const T *)p.phq + (bh * p.n + tp) * F, F, C);
+      pf_n.load((const T *)p.dnum + (bh * p.n + tp) * DV, DV, C);
+    }
     const float eLam = p.dt ? __expf(p.Lc[bh * p.n + t0 + nv - 1]) : 1.f;
     __syncthreads();
 #pragma unroll
@@ -506,13 +571,24 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    // every operand load of the chunk goes out before the first LDS write: one memory
+    // round trip per chunk instead of one per operand
     Staged<T, C, F> phq_next;  // phi(q) rows, written over v once A is formed
+    Staged<T, C, DV> st_dn, st_v;
+    StagedT<T, C, DK> st_x;
+    StagedT<T, C, F> st_k;
+    Staged<T, F, DV> st_s;
+    st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+    st_x.load((const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
+    st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    st_s.load((const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phq_next.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-    stage<T, C, DV>(sDN, LN, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
-    stage<T, C, DV>(sVQ, LVQ, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
-    stage_t<T, C, DK>(sXT, LC, (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
-    stage_t<T, C, F>(sKT, LC, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-    stage<T, F, DV>(sS, LS, (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+    st_dn.store(sDN, LN);
+    st_v.store(sVQ, LVQ);
+    st_x.store(sXT, LC);
+    st_k.store(sKT, LC);
+    st_s.store(sS, LS);
     if (tid < C) {
       sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
@@ -636,13 +712,23 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    // every operand load of the chunk goes out before the first LDS write
     Staged<T, C, F> phk_next;  // phi(k) rows, written over dnum once A^T is formed
+    Staged<T, C, DV> st_dn, st_v;
+    StagedT<T, C, DK> st_x;
+    StagedT<T, C, F> st_q;
+    Staged<T, F, DV> st_g;
+    st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+    st_x.load((const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
+    st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    st_g.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phk_next.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-    stage<T, C, DV>(sNK, LNK, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
-    stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
-    stage_t<T, C, DK>(sXT, LC, (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
-    stage_t<T, C, F>(sQT, LC, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-    stage<T, F, DV>(sG, LG, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+    st_dn.store(sNK, LNK);
+    st_v.store(sV, LV);
+    st_x.store(sXT, LC);
+    st_q.store(sQT, LC);
+    st_g.store(sG, LG);
     if (tid < C) {
       sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
@@ -760,10 +846,20 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    stage<T, C, F>(sK, LF, (const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-    stage<T, C, F>(sQ, LF, (const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-    stage_t<T, C, DV>(sNT, LC, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
-    stage_t<T, F, DV>(sGT, LF, (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+    {
+      // every operand load of the chunk goes out before the first LDS write
+      Staged<T, C, F> st_k, st_q;
+      StagedT<T, C, DV> st_nt;
+      StagedT<T, F, DV> st_gt;
+      st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+      st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+      st_nt.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+      st_gt.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+      st_k.store(sK, LF);
+      st_q.store(sQ, LF);
+      st_nt.store(sNT, LC);
+      st_gt.store(sGT, LF);
+    }
     if (p.a_log) {
       stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
       stage<T, C, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
