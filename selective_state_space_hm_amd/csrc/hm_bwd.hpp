@@ -82,6 +82,33 @@ __device__ __forceinline__ f32x4 mm(const T *A, int la, const T *B, int lb, f32x
   return acc;
 }
 
+// The A-operand fragments of one 16-row band (row lane % 16 at A + row * la, K
+// contiguous), loaded once and reused by every product of a phase that shares them.
+template <typename T, int K> struct Frags {
+  typename Mma<T>::frag f[K / Mma<T>::KS];
+  __device__ __forceinline__ void load(const T *A, int la) {
+    const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < K / Mma<T>::KS; ++s) f[s] = Mma<T>::ld_contig(A + i * la + s * Mma<T>::KS, g);
+  }
+};
+// acc += A * B^T as mm(), with A's fragments preloaded (kept live to the end of the
+// chain like mm's own)
+template <typename T, int K>
+__device__ __forceinline__ f32x4 mm(const Frags<T, K> &a, const T *B, int lb, f32x4 acc) {
+  using M = Mma<T>;
+  constexpr int NK = K / M::KS;
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  typename M::frag b[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) b[s] = M::ld_contig(B + i * lb + s * M::KS, g);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) acc = M::mma(a.f[s], b[s], acc);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a.f[s]), "v"(b[s]), "v"(acc));
+  return acc;
+}
+
 template <typename T> struct Vec { typedef T type __attribute__((ext_vector_type(16 / sizeof(T)))); };
 
 // ROWS x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
@@ -596,9 +623,11 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     if (tid < F) sz[tid] = p.sz[(bh * p.nch + c) * F + tid];
     __syncthreads();
     // A[t][j] = [j <= t] e^{L_t - L_j} (dnum_t . v_j + dden_t); rows t of this wave
+    Frags<T, DV> fdn;  // this wave's dnum rows, shared by the four tiles
+    fdn.load(sDN + 16 * w * LN, LN);
 #pragma unroll
     for (int jt = 0; jt < C / 16; ++jt) {
-      const f32x4 d1 = mm<T, DV>(sDN + 16 * w * LN, LN, sVQ + 16 * jt * LVQ, LVQ, zero4());
+      const f32x4 d1 = mm(fdn, sVQ + 16 * jt * LVQ, LVQ, zero4());
       f32x4 a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -613,10 +642,14 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F]
     f32x4 dph[F / 16];
     float qs[4] = {0.f, 0.f, 0.f, 0.f};  // Q_t partial: phiq_t . (inter part of dphiq_t)
+    Frags<T, C> fa;  // this wave's rows of A and of dnum, shared by the feature tiles
+    Frags<T, DV> fdn2;
+    fa.load(sA + 16 * w * LC, LC);
+    fdn2.load(sDN + 16 * w * LN, LN);
 #pragma unroll
     for (int ft = 0; ft < F / 16; ++ft) {
-      const f32x4 a1 = mm<T, C>(sA + 16 * w * LC, LC, sKT + 16 * ft * LC, LC, zero4());
-      const f32x4 a2 = mm<T, DV>(sDN + 16 * w * LN, LN, sS + 16 * ft * LS, LS, zero4());
+      const f32x4 a1 = mm(fa, sKT + 16 * ft * LC, LC, zero4());
+      const f32x4 a2 = mm(fdn2, sS + 16 * ft * LS, LS, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * w + 4 * g + r;
@@ -654,9 +687,11 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     __syncthreads();
     // dq = du_q W_q^T
     T *DQ = (T *)p.dq + b * p.sq_b + h * p.sq_h + t0 * p.sq_t;
+    Frags<T, FH> fdu;  // this wave's du rows, shared by the d tiles
+    fdu.load(sDu + 16 * w * LW, LW);
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
-      const f32x4 a = mm<T, FH>(sDu + 16 * w * LW, LW, sW + 16 * it * LW, LW, zero4());
+      const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * w + 4 * g + r;
@@ -736,9 +771,11 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     if (tid < F) sg[tid] = p.gz[(bh * p.nch + c) * F + tid];
     __syncthreads();
     // A^T[j][t] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t); rows j of this wave
+    Frags<T, DV> fv;  // this wave's v rows, shared by the four tiles
+    fv.load(sV + 16 * w * LV, LV);
 #pragma unroll
     for (int tt = 0; tt < C / 16; ++tt) {
-      const f32x4 d1 = mm<T, DV>(sV + 16 * w * LV, LV, sNK + 16 * tt * LNK, LNK, zero4());
+      const f32x4 d1 = mm(fv, sNK + 16 * tt * LNK, LNK, zero4());
       f32x4 a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -754,10 +791,14 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     const float Lam = sL[nv - 1];
     f32x4 dph[F / 16];
     float ks[4] = {0.f, 0.f, 0.f, 0.f};  // K_j partial: phik_j . (inter part of dphik_j)
+    Frags<T, C> fat;  // this wave's rows of A^T and of v, shared by the feature tiles
+    Frags<T, DV> fv2;
+    fat.load(sAT + 16 * w * LC, LC);
+    fv2.load(sV + 16 * w * LV, LV);
 #pragma unroll
     for (int ft = 0; ft < F / 16; ++ft) {
-      const f32x4 a1 = mm<T, C>(sAT + 16 * w * LC, LC, sQT + 16 * ft * LC, LC, zero4());
-      const f32x4 a2 = mm<T, DV>(sV + 16 * w * LV, LV, sG + 16 * ft * LG, LG, zero4());
+      const f32x4 a1 = mm(fat, sQT + 16 * ft * LC, LC, zero4());
+      const f32x4 a2 = mm(fv2, sG + 16 * ft * LG, LG, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * w + 4 * g + r;
@@ -797,9 +838,11 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     }
     __syncthreads();
     T *DK_ = (T *)p.dk + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
+    Frags<T, FH> fdu;  // this wave's du rows, shared by the d tiles
+    fdu.load(sDu + 16 * w * LW, LW);
 #pragma unroll
     for (int it = 0; it < DK / 16; ++it) {
-      const f32x4 a = mm<T, FH>(sDu + 16 * w * LW, LW, sW + 16 * it * LW, LW, zero4());
+      const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * w + 4 * g + r;
