@@ -268,13 +268,29 @@ __device__ __forceinline__ void put_t(T *dst, int ld, f32x4 a) {
   for (int r = 0; r < 4; ++r) dst[i * ld + 4 * g + r] = (T)a[r];
 }
 
-// W [d][f] (head h) into LDS, as stored (ld = f + pad) or transposed (ld = d + pad)
+// W [d][f] (head h) into LDS, as stored (ld = f + pad) or transposed (ld = d + pad):
+// 16-byte loads, all issued before the first LDS write (256 threads)
 template <typename T, int DK, int FH>
 __device__ __forceinline__ void load_w(T *dst, int ld, const T *w, bool transposed) {
-  for (int idx = threadIdx.x; idx < DK * FH; idx += blockDim.x) {
-    const int i = idx / FH, f = idx % FH;
-    if (transposed) dst[f * ld + i] = w[idx];
-    else dst[i * ld + f] = w[idx];
+  constexpr int E = ep<T>(), NV = DK * FH / E, PER = (NV + 255) / 256;
+  typedef typename Vec<T>::type V;
+  V x[PER];
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int v = threadIdx.x + 256 * m;
+    x[m] = v < NV ? *reinterpret_cast<const V *>(w + v * E) : V{};
+  }
+#pragma unroll
+  for (int m = 0; m < PER; ++m) {
+    const int v = threadIdx.x + 256 * m;
+    if (v >= NV) continue;
+    const int i = v * E / FH, f0 = v * E % FH;
+    if (transposed) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[(f0 + e) * ld + i] = x[m][e];
+    } else {
+      *reinterpret_cast<V *>(dst + i * ld + f0) = x[m];
+    }
   }
 }
 
@@ -366,10 +382,13 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   for (int64_t c = c0; c < c1; ++c) {
   const int64_t t0 = c * C;
   const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+  // q and k rows go out together; k is written to LDS once q's projection is done
+  Staged<T, C, DK> xq, xk;
+  xq.load((const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
+  xk.load((const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
   for (int proj = 0; proj < 2; ++proj) {
-    const T *X = proj == 0 ? (const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t
-                           : (const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
-    stage<T, C, DK>(sX, LDW, X, proj == 0 ? p.sq_t : p.sk_t, nv);
+    if (proj == 0) xq.store(sX, LDW);
+    else xk.store(sX, LDW);
     __syncthreads();
     // u^T tiles: rows f, columns the wave's 16 tokens
     f32x4 u[FH / 16];
@@ -423,21 +442,42 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   typedef typename Vec<T>::type V;
   const T *DO = (const T *)p.d_o + b * p.so_b + h * p.so_h + t0 * p.so_t;
   const float *O = p.so32 + (bh * p.n + t0) * DV;
-  for (int r0 = 0; r0 < C; r0 += RPP) {
+  constexpr int NIT = C / RPP;
+  // every load of the pass goes out before the first store (the compiler cannot
+  // move loads above stores to other buffers by itself)
+  V xdo[NIT], xg[NIT];
+  f32x4 xo[NIT][E / 4 > 0 ? E / 4 : 1];
+  float xden[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = it * RPP + tid / PPR, pc = tid % PPR;
+    const bool valid = r < nv;
+    xdo[it] = valid ? *reinterpret_cast<const V *>(DO + r * p.so_t + pc * E) : V{};
+#pragma unroll
+    for (int q4 = 0; q4 < E / 4; ++q4)
+      xo[it][q4] = valid ? *reinterpret_cast<const f32x4 *>(O + r * DV + pc * E + 4 * q4) : zero4();
+    xg[it] = (valid && p.gate)
+                 ? *reinterpret_cast<const V *>((const T *)p.gate + b * p.sg_b + h * p.sg_h + (t0 + r) * p.sg_t + pc * E)
+                 : V{};
+    xden[it] = valid ? p.sden[bh * p.n + t0 + r] : 1.f;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r0 = it * RPP;
     const int r = r0 + tid / PPR, pc = tid % PPR;
     const bool valid = r < nv;
     float dv_[E], ov[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) dv_[e] = ov[e] = 0.f;
     if (valid) {
-      const V x = *reinterpret_cast<const V *>(DO + r * p.so_t + pc * E);
+      const V x = xdo[it];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         dv_[e] = (float)x[e];
-        ov[e] = O[r * DV + pc * E + e];
+        ov[e] = xo[it][e / 4][e % 4];
       }
       if (p.gate) {
-        const V gv = *reinterpret_cast<const V *>((const T *)p.gate + b * p.sg_b + h * p.sg_h + (t0 + r) * p.sg_t + pc * E);
+        const V gv = xg[it];
         V dg;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -451,7 +491,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
     // dden from the same rounded dnum the products use: with a fast decay
     // dnum_t . v_t + dden_t = dnum_t . (v_t - o_t) nearly cancels, and the two
     // terms must carry the same rounding of dnum for the difference to survive
-    const float rden = valid ? 1.f / p.sden[bh * p.n + t0 + r] : 0.f;
+    const float rden = valid ? 1.f / xden[it] : 0.f;
     V nv_;
     float part = 0.f;
 #pragma unroll
