@@ -956,9 +956,11 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
     // pair weights W^T[j][t] = [j < t] Pt[j][t] (v_j . dnum_t + dden_t): their sums
     // along t (pairs with key j) and along j (pairs with query t)
     float rowsum[4] = {0.f, 0.f, 0.f, 0.f};
+    Frags<T, F> fk;  // this wave's phi(k) rows, shared by every tile below
+    fk.load(sK + 16 * w * LF, LF);
 #pragma unroll
     for (int tt = 0; tt < C / 16; ++tt) {
-      const f32x4 s = mm<T, F>(sK + 16 * w * LF, LF, sQ + 16 * tt * LF, LF, zero4());
+      const f32x4 s = mm(fk, sQ + 16 * tt * LF, LF, zero4());
       f32x4 a, d1 = zero4();
       if (p.a_log) d1 = mm<T, DV>(sV + 16 * w * LV, LV, sN + 16 * tt * LV, LV, zero4());
       float colsum = 0.f;
@@ -981,8 +983,23 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       // X_c = e^{Lam} (<G_end, S_c> + <g_end, z_c>): pairs spanning the whole chunk
       const T *Sc = (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV);
       const T *Gc = (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
+      typedef typename Vec<T>::type V;
+      constexpr int EV = ep<T>(), NV = F * DV / EV, PV = (NV + 255) / 256;
+      V sv[PV], gv[PV];
+#pragma unroll
+      for (int m = 0; m < PV; ++m) {
+        const bool ok = tid + 256 * m < NV;
+        sv[m] = ok ? reinterpret_cast<const V *>(Sc)[tid + 256 * m] : V{};
+        gv[m] = ok ? reinterpret_cast<const V *>(Gc)[tid + 256 * m] : V{};
+      }
       double x = 0.0;
-      for (int e2 = tid; e2 < F * DV; e2 += 256) x += (double)((float)Sc[e2] * (float)Gc[e2]);
+#pragma unroll
+      for (int m = 0; m < PV; ++m) {
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) part += (float)sv[m][e] * (float)gv[m][e];
+        x += (double)part;
+      }
       if (tid < F) x += (double)p.sz[(bh * p.nch + c) * F + tid] * p.gz[(bh * p.nch + c) * F + tid];
       for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
       if (lane == 0) sX[w] = x;
@@ -1004,10 +1021,12 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
     }
     const float Lam = sL[nv - 1];
     T *DV_ = (T *)p.dv + b * p.sv_b + h * p.sv_h + t0 * p.sv_t;
+    Frags<T, C> fp;  // this wave's rows of the masked scores
+    fp.load(sP + 16 * w * LC, LC);
 #pragma unroll
     for (int ct = 0; ct < DV / 16; ++ct) {
-      const f32x4 a1 = mm<T, C>(sP + 16 * w * LC, LC, sNT + 16 * ct * LC, LC, zero4());
-      const f32x4 a2 = mm<T, F>(sK + 16 * w * LF, LF, sGT + 16 * ct * LF, LF, zero4());
+      const f32x4 a1 = mm(fp, sNT + 16 * ct * LC, LC, zero4());
+      const f32x4 a2 = mm(fk, sGT + 16 * ct * LF, LF, zero4());
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * w + 4 * g + r;
