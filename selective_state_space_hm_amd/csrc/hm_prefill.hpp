@@ -628,13 +628,18 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         if constexpr (SAVE) {
           {
             // the state at the start of chunk j-1 (this iteration's read-out state)
-            T *sv = (T *)p.save_S + (bh * p.nchunks + ts / C) * ((int64_t)F * p.dv) + ncol + col;
+            // the training pass runs with one workgroup per (b, h), so the row stride
+            // is the compile-time DW: one base address per feature tile, the rest
+            // instruction offsets (a run-time stride kept 64 addresses live and spilled)
+            T *sv = (T *)p.save_S + (bh * p.nchunks + ts / C) * ((int64_t)F * DW) + ncol + col;
 #pragma unroll
-            for (int jj = 0; jj < NTW; ++jj)
+            for (int t = 0; t < NFT; ++t) {
+              T *rowp = sv + (16 * t + 4 * g) * DW;
 #pragma unroll
-              for (int t = 0; t < NFT; ++t)
+              for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sv[(int64_t)(16 * t + 4 * g + r) * p.dv + 16 * jj] = (T)S[jj][t][r];
+                for (int jj = 0; jj < NTW; ++jj) rowp[r * DW + 16 * jj] = (T)S[jj][t][r];
+            }
           }
         }
         // v of chunk ts -> accumulator layout: lane (g, col n) holds v[16bt + 4g + r][n]
@@ -701,12 +706,13 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           if constexpr (SAVE) {
             // float32 output rows for the backward pass: lane (g, col) holds token
             // 16bt + col, columns 16 NTW sw + 16 jj + 4g .. +3
+            // (row stride DW: the training pass has one workgroup per (b, h))
+            float *os0 = p.save_o + (bh * p.n + ts + col) * DW + 16 * NTW * sw + 4 * g;
 #pragma unroll
             for (int bt = 0; bt < NCT; ++bt)
               if (ts + 16 * bt + col < t1) {
-                float *os = p.save_o + (bh * p.n + ts + 16 * bt + col) * p.dv + 16 * NTW * sw + 4 * g;
 #pragma unroll
-                for (int jj = 0; jj < NTW; ++jj) *reinterpret_cast<f32x4 *>(os + 16 * jj) = oacc[jj][bt];
+                for (int jj = 0; jj < NTW; ++jj) *reinterpret_cast<f32x4 *>(os0 + 16 * bt * DW + 16 * jj) = oacc[jj][bt];
               }
           }
           // output rows to LDS; they leave for HBM as whole rows in half B
