@@ -105,6 +105,7 @@ hm_status check_launch(const char *what) {
 // ------------------------------------------------------------------ prefill
 struct Plan {
   int chunk, segments, dsplit;
+  int lsub;             // segment-pass slots per segment (pieces of seg_len / lsub tokens)
   int64_t seg_len;
   bool alias;           // s_init and s_final overlap
   bool init_copy;       // s_init is copied into the workspace first
@@ -229,9 +230,24 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
     const size_t len = (size_t)BH * BLK * 4;
     p.alias = i0 < f0 + len && f0 < i0 + len;
   }
+  // The segment pass runs one workgroup per slot.  When its (b, h, segment) items
+  // fill less than half the chip, it cuts every segment into lsub equal pieces
+  // (no work is duplicated; the full pass composes the pieces' maps), as long as
+  // that stays within one workgroup per compute unit.
+  p.lsub = 1;
+  if (p.segments > 1) {
+    const int64_t items = BH * (p.segments - 1) * p.dsplit;
+    for (int cand = 4; cand > 1; cand /= 2) {
+      if (per % cand == 0 && items * cand <= 256) {
+        p.lsub = cand;
+        break;
+      }
+    }
+  }
   p.init_copy = p.alias && (p.segments > 1 || p.dsplit > 1);
-  p.ws_state_floats = p.segments > 1 ? (size_t)(p.segments - 1) * BH * BLK : 0;
-  p.ws_lam_floats = p.segments > 1 ? (size_t)(p.segments - 1) * BH : 0;
+  const int64_t slots = p.segments > 1 ? (int64_t)(p.segments - 1) * p.lsub : 0;
+  p.ws_state_floats = (size_t)slots * BH * BLK;
+  p.ws_lam_floats = (size_t)slots * BH;
   p.ws_lam_floats = (p.ws_lam_floats + 3) / 4 * 4;
   p.ws_init_floats = p.init_copy ? (size_t)BH * BLK : 0;
   return p;
@@ -316,13 +332,15 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   }
 
   auto grid_for = [&](int64_t items, int ds) { return (unsigned)(((items + 7) / 8) * 8 * ds); };
+  const int nslot = pl.segments > 1 ? (pl.segments - 1) * pl.lsub : 0;
   if (pl.segments > 1) {
-    // Segment pass: end state of every segment but the last, segment 0 starting
-    // from s_init (read before anything writes s_final) and the others from zero.
-    // It owns fewer value columns per workgroup when that fills more of the chip.
+    // Segment pass: end state of every slot (piece of a segment) before the last
+    // segment, slot 0 starting from s_init (read before anything writes s_final)
+    // and the others from zero.  With whole segments as slots it owns fewer value
+    // columns per workgroup when that fills more of the chip.
     const hm::FwdEntry *loc = local;
     int lds = pl.dsplit;
-    for (int cand = 4; cand > pl.dsplit; cand /= 2) {
+    for (int cand = 4; pl.lsub == 1 && cand > pl.dsplit; cand /= 2) {
       const hm::FwdEntry *e = a->dv % cand ? nullptr : find_fwd(a->dtype, a->d, a->f, a->dv / cand, decay, hm::MODE_LOCAL | rmode(a));
       if (e && BH * (pl.segments - 1) * cand <= 256) {
         loc = e;
@@ -333,17 +351,24 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
     hm::FwdParams pp = p;
     pp.s_start0 = a->s_init;
     pp.dsplit = lds;
-    pp.nseg_run = pl.segments - 1;
-    pp.nitems = BH * pp.nseg_run;
+    pp.seg_len = pl.seg_len / pl.lsub;
+    pp.nseg_run = nslot;
+    pp.nitems = BH * nslot;
     loc->launch(pp, grid_for(pp.nitems, lds), s);
     if ((st = check_launch("segment pass")) != HM_OK) return st;
   }
-  // Start states of segments 2.. (segment 1 starts from the segment pass's
-  // state directly); the copy of s_init when it aliases s_final.
-  if (pl.segments > 2 || pl.init_copy) {
+  // With two segments the full pass composes the slots of segment 0 as it loads
+  // its start state (the training pass excepted); otherwise the running start
+  // states are composed here in place.  Also the copy of s_init when it aliases
+  // s_final.
+  const bool fuse = pl.segments == 2 && !a->save;
+  const bool compose = nslot > 1 && !fuse;
+  p.lsub = pl.lsub;
+  p.nfuse = fuse ? pl.lsub : 1;
+  if (compose || pl.init_copy) {
     dim3 grid((unsigned)((BLK + 255) / 256), (unsigned)BH);
     hipLaunchKernelGGL(hm::combine_kernel, grid, dim3(256), 0, s, ws_state, ws_lam, a->s_init,
-                       pl.init_copy ? ws_init : nullptr, BH, BLK, pl.segments);
+                       pl.init_copy ? ws_init : nullptr, BH, BLK, compose ? nslot : 0);
     if ((st = check_launch("segment combine")) != HM_OK) return st;
   }
   p.nseg_run = pl.segments;

@@ -45,14 +45,16 @@ constexpr int CHUNK = 64;
 // (rotary encoding, HedgeMamba explainer §5.2 step 3) before they are used.
 enum { MODE_FULL = 0, MODE_LOCAL = 1, MODE_TRAIN = 2, MODE_ROPE = 4 };
 
+constexpr int MAX_FUSE = 4;  // most slots the full pass composes into one start state
+
 struct FwdParams {
   const void *q, *k, *v, *wq, *wk;
   const float *dt, *a_log;
   const float *s_start0;  // start state of segment 0 (NULL = zeros)
   float *s_final;         // written by the last segment (NULL = not written)
   void *o;
-  float *ws_state;        // [nseg-1][B*H][F*dv+F]: local end states, then start states
-  float *ws_lam;          // [nseg-1][B*H]: summed log-decay of each segment
+  float *ws_state;        // [(nseg-1)*lsub][B*H][F*dv+F]: local end states, then start states
+  float *ws_lam;          // [(nseg-1)*lsub][B*H]: summed log-decay of each slot's tokens
   int64_t B, H, n, dv;
   int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t;
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
@@ -67,7 +69,12 @@ struct FwdParams {
   int64_t seg_len;        // tokens per segment, a multiple of CHUNK
   int64_t nitems;         // (b,h,segment) items in this launch
   int nseg;               // segments of the whole sequence
-  int nseg_run;           // segments covered by this launch (nseg, or nseg-1 for MODE_LOCAL)
+  int nseg_run;           // segments covered by this launch (nseg, or the slots for MODE_LOCAL)
+  // The segment pass may cut every segment into lsub pieces (slots of seg_len/lsub
+  // tokens, one workgroup each).  The full pass takes the start state of segment
+  // s >= 1 from slot s*lsub-1, composing on load the nfuse slots that end there.
+  int lsub;
+  int nfuse;              // 1 .. MAX_FUSE; 1 for MODE_TRAIN
   int dsplit;             // workgroups per item, each owning dv/dsplit columns
   int rope_dims;          // MODE_ROPE: rotated features (multiple of 32, <= F)
   float rope_base;
@@ -217,11 +224,20 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     }
   }
 
-  // start state: s_start0 for segment 0 (both passes); the full pass takes the
-  // start states of later segments from the workspace, the segment pass zeros
+  // start state: s_start0 for segment (or slot) 0 in both passes; the segment pass
+  // starts later slots from zero.  The full pass reads the start state of a later
+  // segment from the workspace: slot seg*lsub-1, or the composition of the nfuse
+  // slots ending there, start = e^{lam(u)} start + local(u) ([SSM] §4.2).
   const float *st = nullptr;
+  int nst = 1;  // slots composed into the start state
   if (seg == 0) st = p.s_start0 ? p.s_start0 + bh * BLK : nullptr;
-  else if constexpr (FULL) st = p.ws_state + ((int64_t)(seg - 1) * BH + bh) * BLK;
+  else if constexpr (FULL) {
+    nst = p.nfuse;
+    st = p.ws_state + ((int64_t)(seg * p.lsub - nst) * BH + bh) * BLK;
+  }
+  // slot u of the composition: its state and e^{lam(u)} (u = 1 .. nst-1)
+  auto slot_state = [&](int u) { return st + (int64_t)u * BH * BLK; };
+  auto slot_decay = [&](int u) { return expf(p.ws_lam[(int64_t)(seg * p.lsub - nst + u) * BH + bh]); };
   const int64_t nch = t1 > t0 ? (t1 - t0 + C - 1) / C : 0;
   float *dst = nullptr;  // end state destination
   if constexpr (FULL) {
@@ -251,16 +267,6 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     // end value goes to sZ for the inter-chunk denominators.
     constexpr int ZT = (NFT + 3) / 4;
     f32x4 Z[ZT];
-#pragma unroll
-    for (int i = 0; i < ZT; ++i) {
-      Z[i] = zero4();
-      const int t = ZT * wv + i;
-      if (t < NFT && st && col == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Z[i][r] = st[(int64_t)F * p.dv + 16 * t + 4 * g + r];
-      }
-    }
-    for (int i = tid; i < F; i += 4 * 64) sZ[1][i] = st ? st[(int64_t)F * p.dv + i] : 0.f;
     if constexpr (FULL && EPL == 8) {
       // The intra read-out of token tile b (b even) takes K-steps over tiles b and
       // b+1; score tile (b+1, b) lies above the diagonal and stays zero.
@@ -319,7 +325,24 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         if (nch > 1) load_dt(t0 + C);
       }
     }
+    // z of the start state into sZ[1], every slot's value requested before any is
+    // combined (the feature waves set the pace of the whole workgroup)
+    for (int i = tid; i < F; i += 4 * 64) {
+      float zs[MAX_FUSE];
+#pragma unroll
+      for (int u = 0; u < MAX_FUSE; ++u) zs[u] = st && u < nst ? slot_state(u)[(int64_t)F * p.dv + i] : 0.f;
+      float x = zs[0];
+#pragma unroll
+      for (int u = 1; u < MAX_FUSE; ++u)
+        if (u < nst) x = slot_decay(u) * x + zs[u];
+      sZ[1][i] = x;
+    }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ZT; ++i) {
+      const int t = ZT * wv + i;
+      Z[i] = t < NFT && col == 0 ? *reinterpret_cast<const f32x4 *>(&sZ[1][16 * t + 4 * g]) : zero4();
+    }
 
     // W_k^T fragments stay in registers for the whole segment (A operands); W_q^T
     // is read from LDS per chunk.
@@ -601,6 +624,21 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 
     if (nch > 0) load_v(t0);
     __syncthreads();
+    // The other slots of a composed start state.  This waits for the loads, so it
+    // comes after the barrier: the feature waves featurize the first chunk meanwhile
+    // and S is first read in the next iteration.  (The training pass gets whole start
+    // states: its state waves have no registers to spare.)
+    for (int u = 1; !SAVE && u < nst; ++u) {
+      const float e = slot_decay(u);
+      const float *su = slot_state(u);
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+        for (int t = 0; t < NFT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[jj][t][r] = e * S[jj][t][r] + su[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + 16 * jj + col];
+    }
 
     frag vfr[NTW][KC];  // v of the chunk being read out, tile order
     for (int64_t j = 0; j <= nch; ++j) {
@@ -797,21 +835,22 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   }
 }
 
-// Start states of segments 2..nseg-1 from the segment pass's end states (in
-// place): start(1) = end(0), which already began from s_init, and
-//   start(s) = e^{lam(s-1)} start(s-1) + local(s-1),
-// the composition of affine maps of [SSM] §4.2 with a scalar decay.  Optionally
-// copies s_init to `init_copy` first (used when s_init aliases s_final).
+// Running start states from the segment pass's slots (in place): slot 0 already
+// began from s_init and holds the state after it, and for u = 1 .. nslot-1
+//   state(u) = e^{lam(u)} state(u-1) + local(u),
+// the composition of affine maps of [SSM] §4.2 with a scalar decay; the start
+// state of segment s is then slot s*lsub-1.  Optionally copies s_init to
+// `init_copy` first (used when s_init aliases s_final).
 static __global__ __launch_bounds__(256) void combine_kernel(float *ws_state, const float *ws_lam, const float *s_init,
-                                                      float *init_copy, int64_t BH, int64_t BLK, int nseg) {
+                                                      float *init_copy, int64_t BH, int64_t BLK, int nslot) {
   const int64_t bh = blockIdx.y;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= BLK) return;
   if (init_copy) init_copy[bh * BLK + e] = s_init ? s_init[bh * BLK + e] : 0.f;
-  if (nseg < 3) return;
+  if (nslot < 2) return;
   float cur = ws_state[bh * BLK + e];
-  for (int s = 2; s < nseg; ++s) {
-    const int64_t slot = (int64_t)(s - 1) * BH + bh;
+  for (int u = 1; u < nslot; ++u) {
+    const int64_t slot = (int64_t)u * BH + bh;
     cur = expf(ws_lam[slot]) * cur + ws_state[slot * BLK + e];
     ws_state[slot * BLK + e] = cur;
   }

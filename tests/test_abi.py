@@ -122,8 +122,9 @@ def test_workspace_is_linear_not_quadratic():
     # explicit segment count: the workspace does not depend on n at all
     sizes = [hm.call_workspace_size(fwd(B=1, H=16, n=n, segments=8))[1] for n in (4096, 65536, 1 << 20)]
     assert sizes[0] == sizes[1] == sizes[2]
-    F, dv, BH = 128, 128, 16
-    assert sizes[0] == 7 * BH * (F * dv + F) * 4 + 4 * ((7 * BH + 3) // 4 * 4)
+    # 7 segments before the last; 112 segment-pass items, so each is cut into 2 slots
+    F, dv, BH, slots = 128, 128, 16, 14
+    assert sizes[0] == slots * BH * (F * dv + F) * 4 + 4 * ((slots * BH + 3) // 4 * 4)
     # automatic plans stay bounded by the segment cap as n grows
     auto = [hm.call_workspace_size(fwd(B=1, H=16, n=n, decay=True))[1] for n in (8192, 131072, 1 << 21)]
     assert max(auto) <= 512 * (F * dv + F) * 4 * 2

@@ -103,6 +103,30 @@ def test_fp32_plans_with_initial_state(dv, segments, dsplit):
     assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
 
 
+@pytest.mark.parametrize("decay", ["mild", "mamba"])
+@pytest.mark.parametrize("segments,dsplit", [(2, 1), (2, 2), (4, 1), (3, 1)])
+def test_fp32_segment_pass_slots(decay, segments, dsplit):
+    """n = 500 (8 chunks, ragged tail), B*H = 4: with 2 segments of 4 chunks the
+    segment pass cuts segment 0 into 4 one-chunk slots and the full pass composes
+    them while loading its start state; with 4 segments of 2 chunks it cuts each
+    into 2 slots and the combine pass composes all 6; 3 segments of 3 chunks stay
+    whole.  Against the oracle, from a non-zero initial state."""
+    c = inputs.small(n=500, decay=decay, dtype=torch.float32, d=32, f=16, dv=32, B=2, H=2, seed=21)
+    r = np.random.default_rng(6)
+    kk = r.random((2, 2, 9, 32))
+    kk /= kk.sum(-1, keepdims=True)
+    S0 = np.einsum("bhjf,bhjd->bhfd", kk, r.normal(size=(2, 2, 9, 32)))
+    z0 = kk.sum(2)
+    s_init = torch.tensor(orc.pack_state(S0, z0), dtype=torch.float32, device="cuda")
+    s_final = torch.empty_like(s_init)
+    o = run_fwd(c, s_init=s_init, s_final=s_final, segments=segments, dsplit=dsplit)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c, S0, z0)
+    assert report(f"fp32 slots decay={decay} segs={segments} dsplit={dsplit}", f64(o), ref) <= FP32_TOL
+    Sg, zg = orc.unpack_state(f64(s_final), 32, 32)
+    assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
+
+
 @pytest.mark.parametrize("shape", [(64, 32, 64), (128, 64, 128), (128, 32, 64), (64, 64, 128)])
 @pytest.mark.parametrize("decay", [None, "mild", "mamba"])
 def test_bf16_shapes_ragged(shape, decay):
