@@ -509,20 +509,39 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
 }
 
 // ---------------------------------------------------------------- bwd_gstate
-// One workgroup per (b, h), chunks from last to first: G and g at every chunk's
-// end go to the workspace; after chunk 0 they are the gradient of the initial
-// state.  G [F][DV] lives in accumulators, tile tt = wave + 4m.
-template <typename T, int DK, int FH, int DV>
+// One workgroup per (b, h) and share of the value columns (DS shares of DV/DS;
+// the columns of G are independent), chunks from last to first: G and g at every
+// chunk's end go to the workspace; after chunk 0 they are the gradient of the
+// initial state.  G [F][DV/DS] lives in accumulators, tile tt = wave + 4m; the
+// first share also carries g.  With DS > 1, consecutive workgroups go to
+// different XCDs and the shares of one (b, h) share an XCD (and its copy of phi(q)
+// in L2).
+template <typename T, int DK, int FH, int DV, int DS>
 __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   using namespace bw;
-  constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD;
-  constexpr int CT = DV / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
-  __shared__ __align__(16) T sA[F * LDC_];   // (e^{L_t} phiq_t)^T: [f][t]
-  __shared__ __align__(16) T sB[DV * LDC_];  // dnum^T: [c][t]
-  __shared__ float sdd[C], seL[C];
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD, DVW = DV / DS;
+  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
+  static_assert(DVW % 16 == 0, "whole column tiles per share");
+  __shared__ __align__(16) T sA[F * LDC_];    // (e^{L_t} phiq_t)^T: [f][t]
+  __shared__ __align__(16) T sB[DVW * LDC_];  // dnum^T of the share's columns: [c][t]
+  __shared__ __align__(16) float sdd[C], seL[C];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x;
+  int64_t bh = blockIdx.x;
+  int share = 0;
+  if constexpr (DS > 1) {
+    const int64_t rnd = blockIdx.x >> 3;
+    share = (int)(rnd % DS);
+    bh = (rnd / DS) * 8 + (blockIdx.x & 7);
+    if (bh >= p.B * p.H) return;
+  }
+  const int col0 = share * DVW;
+  const bool zshare = share == 0;  // the share that carries g
+  // g[f] = sum_t (e^{L_t} phiq_t)[f] dden_t: threads 2f and 2f+1 each sum half of
+  // the chunk's tokens; thread 2f owns g[f]
+  const int gf = tid >> 1, gh = tid & 1;
+  const bool gown = zshare && gh == 0 && gf < F;
+  static_assert(2 * F <= 256 && C == 64, "two threads per feature, 32 tokens each");
   const int64_t BLK = (int64_t)F * DV + F;
   f32x4 G[NTT];
   float gz = 0.f;
@@ -533,20 +552,31 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     if (tt < TILES && p.ds_final) {
       const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) G[m][r] = p.ds_final[bh * BLK + (16 * rt + 4 * g + r) * DV + 16 * ct + i];
+      for (int r = 0; r < 4; ++r) G[m][r] = p.ds_final[bh * BLK + (16 * rt + 4 * g + r) * DV + col0 + 16 * ct + i];
     }
   }
-  if (tid < F && p.ds_final) gz = p.ds_final[bh * BLK + (int64_t)F * DV + tid];
+  if (gown && p.ds_final) gz = p.ds_final[bh * BLK + (int64_t)F * DV + gf];
   // the (earlier) chunk's phi(q) and dnum are fetched while the current chunk's
   // products run: the chunks are visited one after the other, so each chunk's load
   // latency would otherwise stand alone
   StagedT<T, C, F> pf_q;
-  StagedT<T, C, DV> pf_n;
+  StagedT<T, C, DVW> pf_n;
+  // and its per-token log-decay and dden (thread t < C holds token t)
+  float pf_L = 0.f, pf_dd = 0.f;
+  bool pf_ok = false;
+  auto load_tok = [&](int64_t t0, int nv) {
+    if (tid < C) {
+      pf_ok = tid < nv;
+      pf_L = pf_ok && p.dt ? p.Lc[bh * p.n + t0 + tid] : 0.f;
+      pf_dd = pf_ok ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+  };
   if (p.nch > 0) {
     const int64_t t0 = (p.nch - 1) * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     pf_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-    pf_n.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    pf_n.load((const T *)p.dnum + (bh * p.n + t0) * DV + col0, DV, nv);
+    load_tok(t0, nv);
   }
   for (int64_t c = p.nch - 1; c >= 0; --c) {
     const int64_t t0 = c * C;
@@ -559,14 +589,13 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
       if (tt < TILES) {
         const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) gs[(16 * rt + 4 * g + r) * DV + 16 * ct + i] = (T)G[m][r];
+        for (int r = 0; r < 4; ++r) gs[(16 * rt + 4 * g + r) * DV + col0 + 16 * ct + i] = (T)G[m][r];
       }
     }
-    if (tid < F) p.gz[(bh * p.nch + c) * F + tid] = gz;
+    if (gown) p.gz[(bh * p.nch + c) * F + gf] = gz;
     if (tid < C) {
-      const bool valid = tid < nv;
-      seL[tid] = valid ? (p.dt ? __expf(p.Lc[bh * p.n + t0 + tid]) : 1.f) : 0.f;
-      sdd[tid] = valid ? p.dden[bh * p.n + t0 + tid] : 0.f;
+      seL[tid] = pf_ok ? (p.dt ? __expf(pf_L) : 1.f) : 0.f;
+      sdd[tid] = pf_dd;
     }
     __syncthreads();
     pf_q.store(sA, LDC_, seL);
@@ -574,9 +603,10 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     if (c > 0) {
       const int64_t tp = t0 - C;  // the previous chunk is always full
       pf_q.load((const T *)p.phq + (bh * p.n + tp) * F, F, C);
-      pf_n.load((const T *)p.dnum + (bh * p.n + tp) * DV, DV, C);
+      pf_n.load((const T *)p.dnum + (bh * p.n + tp) * DV + col0, DV, C);
+      load_tok(tp, C);
     }
-    const float eLam = p.dt ? __expf(p.Lc[bh * p.n + t0 + nv - 1]) : 1.f;
+    const float eLam = seL[nv - 1];  // e^{Lambda} of the chunk (1 without decay)
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
@@ -586,9 +616,22 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
         G[m] = mm<T, C>(sA + 16 * rt * LDC_, LDC_, sB + 16 * ct * LDC_, LDC_, G[m] * eLam);
       }
     }
-    if (tid < F) {
+    if (zshare && gf < F) {
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      const T *row = sA + gf * LDC_ + 32 * gh;
+      const float *dd = sdd + 32 * gh;
       float acc = 0.f;
-      for (int t = 0; t < C; ++t) acc += (float)sA[tid * LDC_ + t] * sdd[t];
+#pragma unroll
+      for (int t = 0; t < 32; t += 4) {
+        const t4 a4 = *reinterpret_cast<const t4 *>(row + t);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dd + t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const T x = a4[e];
+          acc = __builtin_fmaf((float)x, d4[e], acc);
+        }
+      }
+      acc += __shfl_xor(acc, 1);
       gz = eLam * gz + acc;
     }
     __syncthreads();
@@ -600,10 +643,10 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
       if (tt < TILES) {
         const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p.ds_init[bh * BLK + (16 * rt + 4 * g + r) * DV + 16 * ct + i] = G[m][r];
+        for (int r = 0; r < 4; ++r) p.ds_init[bh * BLK + (16 * rt + 4 * g + r) * DV + col0 + 16 * ct + i] = G[m][r];
       }
     }
-    if (tid < F) p.ds_init[bh * BLK + (int64_t)F * DV + tid] = gz;
+    if (gown) p.ds_init[bh * BLK + (int64_t)F * DV + gf] = gz;
   }
 }
 
@@ -651,16 +694,22 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
     st_s.load((const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phq_next.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    float tl = 0.f, tdd = 0.f, tz = 0.f;  // per-token log-decay and dden, z at the chunk start
+    if (tid < C) {
+      tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    if (tid < F) tz = p.sz[(bh * p.nch + c) * F + tid];
     st_dn.store(sDN, LN);
     st_v.store(sVQ, LVQ);
     st_x.store(sXT, LC);
     st_k.store(sKT, LC);
     st_s.store(sS, LS);
     if (tid < C) {
-      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
-      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+      sL[tid] = tl;
+      sdd[tid] = tdd;
     }
-    if (tid < F) sz[tid] = p.sz[(bh * p.nch + c) * F + tid];
+    if (tid < F) sz[tid] = tz;
     __syncthreads();
     // A[t][j] = [j <= t] e^{L_t - L_j} (dnum_t . v_j + dden_t); rows t of this wave
     Frags<T, DV> fdn;  // this wave's dnum rows, shared by the four tiles
@@ -799,16 +848,22 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
     st_g.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phk_next.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    float tl = 0.f, tdd = 0.f, tg = 0.f;  // per-token log-decay and dden, g at the chunk end
+    if (tid < C) {
+      tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+    if (tid < F) tg = p.gz[(bh * p.nch + c) * F + tid];
     st_dn.store(sNK, LNK);
     st_v.store(sV, LV);
     st_x.store(sXT, LC);
     st_q.store(sQT, LC);
     st_g.store(sG, LG);
     if (tid < C) {
-      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
-      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+      sL[tid] = tl;
+      sdd[tid] = tdd;
     }
-    if (tid < F) sg[tid] = p.gz[(bh * p.nch + c) * F + tid];
+    if (tid < F) sg[tid] = tg;
     __syncthreads();
     // A^T[j][t] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t); rows j of this wave
     Frags<T, DV> fv;  // this wave's v rows, shared by the four tiles
@@ -938,18 +993,23 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
       st_nt.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
       st_gt.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+      float tl = 0.f, tdd = 0.f;  // per-token log-decay and dden
+      if (tid < C) {
+        tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+        tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+      }
       st_k.store(sK, LF);
       st_q.store(sQ, LF);
       st_nt.store(sNT, LC);
       st_gt.store(sGT, LF);
+      if (tid < C) {
+        sL[tid] = tl;
+        sdd[tid] = tdd;
+      }
     }
     if (p.a_log) {
       stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
       stage<T, C, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
-    }
-    if (tid < C) {
-      sL[tid] = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
-      sdd[tid] = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
     __syncthreads();
     // Pt[j][t] = [j <= t] e^{L_t - L_j} phik_j . phiq_t, and for the decay gradient the

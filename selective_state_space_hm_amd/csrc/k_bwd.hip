@@ -10,7 +10,18 @@ template <typename T, int DK, int FH, int DV, bool ROPE>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
   const unsigned BH = (unsigned)(p.B * p.H);
   if (p.nch > 0) hipLaunchKernelGGL((bwd_prep<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.nch), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV>), dim3(BH), dim3(256), 0, s, p);
+  // the gradient-state pass visits the chunks one after another, so with fewer
+  // (b, h) than compute units it splits the value columns in two
+  // (a four-way split measured slower on the Pythia layer: 105 vs 91 us)
+  if constexpr (DV % 32 == 0) {
+    if (BH < 256) {
+      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 2>), dim3((BH + 7) / 8 * 16), dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(256), 0, s, p);
+    }
+  } else {
+    hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(256), 0, s, p);
+  }
   hipLaunchKernelGGL((bwd_dq<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
   hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
   if (p.nch > 0) hipLaunchKernelGGL((bwd_dv<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
