@@ -65,9 +65,16 @@ def prefill_flops_algorithmic(B, H, n, d, f, dv):
     return B * H * n * (4 * d * f + 4 * F * (dv + 1))
 
 
-def segment_pass_split(B, H, nseg, dv, dsplit):
-    """Column split of the segment pass, as the library chooses it: the widest of 4
-    or 2 (32 columns at least) that keeps the pass within 256 workgroups."""
+def segment_pass_split(B, H, nseg, per, dv, dsplit):
+    """Column split of the segment pass, as the library chooses it.  When its items
+    fill at most half the chip it cuts each segment into 4 or 2 slots (a divisor
+    of the segment's chunks) and keeps the full pass's columns; otherwise it takes
+    the widest column split of 4 or 2 (32 columns at least) that keeps the pass
+    within 256 workgroups."""
+    items = B * H * (nseg - 1) * dsplit
+    for cand in (4, 2):
+        if per % cand == 0 and items * cand <= 256:
+            return dsplit
     for cand in (4, 2):
         if cand > dsplit and dv % cand == 0 and dv // cand >= 32 and B * H * (nseg - 1) * cand <= 256:
             return cand
@@ -92,7 +99,7 @@ def prefill_mfma_count(plan, B, H, n, d, f, dv):
     chunks = (n + C - 1) // C
     per = -(-chunks // segments)
     nseg = -(-chunks // per)
-    ls = segment_pass_split(B, H, nseg, dv, dsplit)
+    ls = segment_pass_split(B, H, nseg, per, dv, dsplit)
     vtl = dv // ls // 16
     local = NCT * NFH * KD + NCT * NFT + NFT * KC + vtl * NCT + vtl * NFT * KC
     local_chunks = per * (nseg - 1)
