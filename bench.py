@@ -15,6 +15,8 @@ Prints ONE JSON line.  Beside the headline prefill number it reports:
     features, the short conv and the stage-2 chain, a training step (forward
     that saves + backward), the Mamba-decay workloads (n=8192 and n=131072), the
     per-channel-decay scan on the same layer (ALU-bound) and its decode step;
+  * distribution: median / p10 / p90 of single calls, warm and with the caches
+    overwritten before each call (cold);
   * cpu_baseline: the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extra]
@@ -124,6 +126,26 @@ def time_launches(fn, steps, warmup, torch):
     return s.elapsed_time(e) / steps, wall
 
 
+def step_distribution(fn, reps, torch, flush=None):
+    """Per-call GPU times (ms) of fn(), each call bracketed by its own HIP events:
+    median, p10 and p90.  With `flush`, it runs before every call and overwrites
+    L2 and the 256 MB MALL (a cold start for the call's inputs)."""
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        e.synchronize()
+        times.append(s.elapsed_time(e))
+    times.sort()
+    pick = lambda q: times[min(len(times) - 1, int(q * (len(times) - 1) + 0.5))]
+    return {"median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9), "reps": reps}
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The float64 oracle's recurrent form on the same inputs, all (b, h) at once,
     token slices continued through the carried state until the time budget is used."""
@@ -215,6 +237,15 @@ def main():
 
     log(f"[bench] prefill plan (chunk, segments, dsplit) = {plan}; timing {args.steps} steps")
     ms, wall = time_launches(step, args.steps, args.warmup, torch)
+    # per-call spread, warm (back to back) and cold (caches overwritten before each call)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    dist = {"warm": step_distribution(step, 50, torch),
+            "cold": step_distribution(step, 50, torch, flush=lambda: scratch.fill_(1)),
+            "note": "single calls, each between its own event pair with the host waiting in between (so "
+                    "each includes the gap between its two launches and the GPU idles between calls); cold: a "
+                    "512 MiB fill before each call evicts L2 and the MALL, whose dirty lines are written back "
+                    "while the call runs. The headline value times back-to-back calls on the same inputs"}
+    del scratch
     B, H, n, d, f, dv = case.B, case.H, case.n, case.d, case.f, case.dv
     tokens = B * n
     nbytes = prefill_bytes(B, H, n, d, f, dv, False)
@@ -250,6 +281,7 @@ def main():
                  "algorithmic_frac": algo / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                  "peak_tflops": BF16_PEAK_TFLOPS},
         "wall_s_timed": wall,
+        "distribution": dist,
     }
     if not args.no_extra:
         extra = []
