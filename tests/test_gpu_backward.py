@@ -128,6 +128,27 @@ def test_backward_state_gradients_fp32(segments):
     check_a_log(f"bwd segs={segments} da_log", gr["a_log"], ref, c, FP32_TOL)
 
 
+def test_backward_many_heads_whole_gradient_state():
+    """B*H = 256: the gradient-state pass runs one workgroup per (b, h) over all
+    value columns (below 256 it splits them in two); with dS_final in and
+    dS_init out, so the z-gradient path is checked too."""
+    c = inputs.make_prefill("bw256", 16, 16, 70, 32, 16, 32, torch.float32, None, "mild", seed=31)
+    gen = torch.Generator().manual_seed(31)
+    d_o = torch.randn((16, 16, 70, 32), generator=gen)
+    d_sf = torch.randn((16, 16, hm.state_numel(16, 32)), generator=gen)
+    s_init = torch.zeros((16, 16, hm.state_numel(16, 32)), device="cuda")  # its gradient does not depend on it
+    g, wq, wk, o, save, _ = run_train(c, s_init=s_init)
+    gr = hm.hm_linattn_bwd(g["q"], g["k"], g["v"], wq, wk, d_o.cuda(), save, g["dt"], g["a_log"],
+                           d_s_final=d_sf.cuda(), want_d_s_init=True)
+    torch.cuda.synchronize()
+    ref = oracle_grads(c, d_o, s_init=s_init.cpu(), d_s_final=d_sf)
+    for name in ("q", "k", "v", "w_q", "w_k", "dt"):
+        check(f"bwd B*H=256 d{name}", gr[name], ref[name], FP32_TOL)
+    got_S, got_z = orc.unpack_state(f64(gr["s_init"]), 32, 32)
+    check("bwd B*H=256 d s_init (S)", got_S, ref["s_init"], FP32_TOL)
+    check("bwd B*H=256 d s_init (z)", got_z, ref["z_init"], FP32_TOL)
+
+
 def test_backward_per_head_weights_bf16():
     c = inputs.make_prefill("bwh", 2, 3, 150, 64, 32, 64, torch.bfloat16, None, "mild", seed=12)
     gen = torch.Generator().manual_seed(2)
