@@ -139,8 +139,9 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   [SSM] §4.2).  dsplit: 0 = automatic, 1 or 2 = number of workgroups that
  *   share one (b, h), each owning dv/dsplit value columns.
  *   workspace: device scratch of at least hm_linattn_fwd_workspace_size() bytes
- *   (it may be NULL when that size is 0).  Its size grows with B*H*segments,
- *   never with n^2.
+ *   (it may be NULL when that size is 0).  Its size grows with B*H*segments (up
+ *   to 4 state blocks per segment: the segment pass may cut a segment into
+ *   equal pieces when that fills more of the GPU), never with n^2.
  *   save: optional (NULL = inference), hm_linattn_save_size() bytes: the forward
  *   also keeps what hm_linattn_bwd reads (chunk-start states, denominators); it
  *   then runs with dsplit 1.  Built for the sizes hm_linattn_bwd lists.
