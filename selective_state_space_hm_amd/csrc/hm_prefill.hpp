@@ -631,6 +631,26 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         else vsel[jj][s] = M::select([&](int) { return 4 * s + g == col; });
       }
 
+    // the gate rows of the chunk at ts into sG, one 16-byte piece per lane and pass
+    // (no registers held while the read-out runs); in half B each lane reads back
+    // the pieces it brought in
+    auto issue_gate_rows = [&](int64_t ts) {
+      if constexpr (FULL) {
+        if (p.gate) {
+          constexpr int EP = 16 / (int)sizeof(T), PPR = DW / EP, NIT = C * PPR / (NS * 64);
+          const T *gb = (const T *)p.gate + b * p.sg_b + h * p.sg_h + ts * p.sg_t + half * DW;
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
+            if (ts + row < t1)
+              __builtin_amdgcn_global_load_lds(
+                  (const __attribute__((address_space(1))) void *)(gb + (int64_t)row * p.sg_t + pc * EP),
+                  (__attribute__((address_space(3))) void *)&sG[(it * NS + sw) * 64 * EP], 16, 0, 0);
+          }
+        }
+      }
+    };
+
     if (nch > 0) load_v(t0);
     __syncthreads();
     // The other slots of a composed start state.  This waits for the loads, so it
@@ -656,6 +676,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       const int ds = (int)((j + 2) % 3);
       // ---- half A: read-out of chunk j-1
       if (j >= 1) {
+        if constexpr (SAVE) issue_gate_rows(ts);
         if constexpr (SAVE) {
           {
             // the state at the start of chunk j-1 (this iteration's read-out state)
@@ -686,25 +707,13 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
           for (int s = 0; s < KC; ++s) vfr[jj][s] = M::from_acc(vacc, s);
         }
-        if constexpr (FULL) {
-          if (p.gate) {
-            // gate rows of chunk j-1 go straight to LDS (no registers held while the
-            // read-out runs); each lane later reads back the 16 bytes it brought in.
-            // Issued once the re-layout above has consumed this chunk's v rows: the
-            // wait for those is then not a wait for the gate rows as well
-            // (measured 2-6 % faster on the gated layer)
-            constexpr int EP = 16 / (int)sizeof(T), PPR = DW / EP, NIT = C * PPR / (NS * 64);
-            const T *gb = (const T *)p.gate + b * p.sg_b + h * p.sg_h + ts * p.sg_t + half * DW;
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-              const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
-              if (ts + row < t1)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(gb + (int64_t)row * p.sg_t + pc * EP),
-                    (__attribute__((address_space(3))) void *)&sG[(it * NS + sw) * 64 * EP], 16, 0, 0);
-            }
-          }
-        }
+        // gate rows of chunk j-1 straight to LDS (see issue_gate_rows); without the
+        // training saves they go out once the re-layout has consumed this chunk's v
+        // rows, so that the wait for those is not also a wait for the gate rows
+        // (measured 2-6 % faster on the gated layer).  With the saves they go out
+        // first: a pending LDS load makes the barrier ending this half wait for every
+        // outstanding global access, which there includes the saved state's stores.
+        if constexpr (!SAVE) issue_gate_rows(ts);
         if (j < nch) load_v(ts + C);
         if constexpr (FULL) {
           frag sfr[NTW][KF];
