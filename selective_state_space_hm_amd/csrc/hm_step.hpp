@@ -4,9 +4,12 @@
 // per-step cost is the fixed-size state, quant67 SSM lecture §5.1): one
 // workgroup per (b, h).  The kernel is bound by HBM traffic on the state
 // (F*dv + F floats read and written once), so it is organised around that:
-// every thread issues all of its 16-byte state loads first, computes the two
-// Hedgehog features and the decay while they are in flight, then updates,
-// reads out and stores its slice with 16-byte accesses.
+// W and the token's q, k values are fetched first (W straight into LDS), then
+// every thread issues all of its 16-byte state loads, computes the two Hedgehog
+// features and the decay from LDS and registers while they are in flight, then
+// updates, reads out and stores its slice with 16-byte accesses.  (Loads retire
+// in order, so a global load issued after the state loads and waited for during
+// the featurization would wait for the whole state.)
 #pragma once
 
 #include "hm_device.hpp"
@@ -42,10 +45,13 @@ template <typename T> __device__ __forceinline__ float ldf(const T *p) { return 
 // per output, and turned into softmax rows by waves 0 (q) and 1 (k); with
 // rope_dims > 0 both rows are then turned by the rotary encoding.  Every thread
 // of the workgroup must call it (it holds barriers); it ends with a barrier,
-// after which sphi is complete.
+// after which sphi is complete.  Given sW (an LDS copy of W_q then W_k, complete
+// for every thread) and xpre (this thread's token value), it reads no global
+// memory unless the short conv or the rotary encoding is on.
 template <typename T, int DK, int FH>
 __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, int64_t h, float (*sx)[DK],
-                                              float (*su)[2 * FH], float (*sphi)[2 * FH]) {
+                                              float (*su)[2 * FH], float (*sphi)[2 * FH], const T *sW = nullptr,
+                                              const T *xpre = nullptr) {
   constexpr int NT = 256;
   constexpr int PARTS = NT / (2 * FH);       // threads per projection output
   constexpr int DPART = DK / PARTS;
@@ -56,7 +62,7 @@ __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, in
   const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
   for (int i = tid; i < 2 * DK; i += NT) {
     const int proj = i / DK, c = i % DK;
-    const T xt = (proj == 0 ? xq : xk)[c];
+    const T xt = xpre ? *xpre : (proj == 0 ? xq : xk)[c];
     float xv = (float)xt;
     if (p.cwidth > 0) {
       // the mixer's short causal conv on this channel, in the order of the
@@ -81,7 +87,7 @@ __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, in
   if (tid < NT) {
     const int o = tid % (2 * FH), part = tid / (2 * FH);
     const int proj = o / FH, j = o % FH;
-    const T *W = (const T *)(proj == 0 ? p.wq : p.wk) + h * p.sw_h;
+    const T *W = sW ? sW + proj * (DK * FH) : (const T *)(proj == 0 ? p.wq : p.wk) + h * p.sw_h;
     float acc = 0.f;
 #pragma unroll 8
     for (int i = part * DPART; i < (part + 1) * DPART; ++i) acc += sx[proj][i] * ldf(W + i * FH + j);
@@ -128,6 +134,28 @@ __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, in
   }
 }
 
+// W_q then W_k of head h into LDS (sW: [2][DK*FH]) with asynchronous 16-byte
+// global-to-LDS loads by the first 256 threads; piece i lands at sW + i*EP
+// elements.  Complete for every thread after the next barrier.
+template <typename T, int DK, int FH>
+__device__ __forceinline__ void stage_w_lds(const StepParams &p, int64_t h, T *sW) {
+  constexpr int EP = 16 / (int)sizeof(T), PER_MAT = DK * FH / EP, NP = 2 * PER_MAT, NIT = (NP + 255) / 256;
+  static_assert(PER_MAT % 64 == 0, "whole waves of pieces");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid >= 256) return;
+#pragma unroll
+  for (int m = 0; m < NIT; ++m) {
+    const int wbase = m * 256 + w * 64;  // first piece of this wave's load
+    if (wbase < NP) {
+      const int piece = wbase + lane;
+      const T *src = (const T *)(piece < PER_MAT ? p.wq : p.wk) + h * p.sw_h + (piece % PER_MAT) * EP;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                       (__attribute__((address_space(3))) void *)(sW + wbase * EP), 16, 0, 0);
+    }
+  }
+}
+
 template <typename T, int DK, int FH, int DV, bool DECAY>
 __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
   constexpr int NT = 256;
@@ -145,12 +173,31 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
   __shared__ __align__(16) float sred[GROUPS][DV];
   __shared__ float sden[F / 4 > 0 ? F / 4 : 1];
   __shared__ float sa;
+  __shared__ __align__(16) T sW[2 * DK * FH];  // W_q, W_k of the head
 
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / p.H, h = bh % p.H;
   constexpr int64_t BLK = (int64_t)F * DV + F;
   float *st = p.state + bh * BLK;
+
+  // 0. W into LDS and this thread's token value (q or k channel), and the decay's
+  //    inputs, before anything else: with them in hand the featurization below
+  //    needs no global memory (without the short conv or the rotary encoding) and
+  //    runs while the state loads are in flight
+  static_assert(2 * DK <= NT, "one token value per thread");
+  stage_w_lds<T, DK, FH>(p, h, sW);
+  T xpre{};
+  if (tid < 2 * DK) xpre = ((const T *)(tid < DK ? p.q : p.k) + b * (tid < DK ? p.sq_b : p.sk_b) +
+                            h * (tid < DK ? p.sq_h : p.sk_h))[tid % DK];
+  float dtv = 0.f, alog = 0.f;
+  if constexpr (DECAY) {
+    if (tid == 0) {
+      dtv = p.dt[b * p.sdt_b + h * p.sdt_h];
+      alog = p.a_log[h];
+    }
+  }
+  __syncthreads();
 
   // 1. issue the state loads
   f32x4 sv[PER];
@@ -165,10 +212,10 @@ __global__ __launch_bounds__(256) void step_kernel(const StepParams p) {
   // 2. the decay, and phi(q), phi(k) while the loads are in flight
   if (tid == 0) {
     float a = 1.f;
-    if constexpr (DECAY) a = __expf(-softplus_f32(p.dt[b * p.sdt_b + h * p.sdt_h]) * expf(p.a_log[h]));
+    if constexpr (DECAY) a = __expf(-softplus_f32(dtv) * expf(alog));
     sa = a;
   }
-  step_features<T, DK, FH>(p, b, h, sx, su, sphi);
+  step_features<T, DK, FH>(p, b, h, sx, su, sphi, sW, &xpre);
   // 3. update, read out, store.  Thread tid owns column group c4 = tid % RV and
   //    rows f = tid / RV + GROUPS * m.
   const float a = sa;
