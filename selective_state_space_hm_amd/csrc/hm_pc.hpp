@@ -120,16 +120,43 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
   T *O = (T *)p.o + b * p.so_b + h * p.so_h + grp * CPW;
   const T *G = p.gate ? (const T *)p.gate + b * p.sg_b + h * p.sg_h + grp * CPW : nullptr;
 
+  // A chunk's q, k rows, dt and v are loaded into registers one chunk ahead, during
+  // the previous chunk's scan: with one workgroup per compute unit nothing else
+  // would cover their latency.
+  constexpr int TPW = (8 + NW - 1) / NW;  // featurize tasks per wave
+  constexpr int IT = (C * CPW + NT - 1) / NT;  // staged (token, channel) items per thread
+  frag xn[TPW][KD];
+  float dtn[IT], vnx[IT];
+  auto prefetch = [&](int64_t tc) {
+    const int nvc = (int)(p.n - tc < C ? p.n - tc : C);
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int task = wv + u * NW;
+      const int proj = task >> 2, tok = 16 * (task & 3) + col;
+      const T *X = (proj == 0 ? Q + (tc + tok) * p.sq_t : K + (tc + tok) * p.sk_t);
+#pragma unroll
+      for (int s = 0; s < KD; ++s) xn[u][s] = task < 8 && tok < nvc ? M::ld_contig(X + s * M::KS, g) : frag{};
+    }
+#pragma unroll
+    for (int m = 0; m < IT; ++m) {
+      const int i = tid + m * NT, tt = i / CPW, cc = i % CPW;
+      const bool ok = i < C * CPW && tt < nvc;
+      dtn[m] = ok ? DT[(tc + tt) * p.sdt_t + cc] : 0.f;
+      vnx[m] = ok ? (float)V[(tc + tt) * p.sv_t + cc] : 0.f;
+    }
+  };
+  if (p.n > 0) prefetch(0);
+
   for (int64_t t0 = 0; t0 < p.n; t0 += C) {
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     __syncthreads();  // W staged; the previous chunk's o rows are stored
     // featurize: eight 16-token tasks (q tiles 0-3, k tiles 0-3) over the waves
-    for (int task = wv; task < 8; task += NW) {
-      const int proj = task >> 2, tok = 16 * (task & 3) + col;
-      const T *X = (proj == 0 ? Q + (t0 + tok) * p.sq_t : K + (t0 + tok) * p.sk_t);
-      frag xf[KD];
 #pragma unroll
-      for (int s = 0; s < KD; ++s) xf[s] = tok < nv ? M::ld_contig(X + s * M::KS, g) : frag{};
+    for (int u = 0; u < TPW; ++u) {
+      const int task = wv + u * NW;
+      if (task >= 8) continue;
+      const int proj = task >> 2, tok = 16 * (task & 3) + col;
+      const frag *xf = xn[u];
       f32x4 ph[NFT];
       const float sum = feature_tiles<T, DK, FH>(xf, sW[proj], ph);
       const float inv = proj == 1 ? __builtin_amdgcn_rcpf(sum) : 1.f;  // phi(q)'s scale cancels in o
@@ -144,13 +171,16 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
         *reinterpret_cast<f32x4 *>(row + (f / NPL) * BLK + f % NPL) = ph[t] * inv;
       }
     }
-    for (int i = tid; i < C * CPW; i += NT) {
-      const int tt = i / CPW, cc = i % CPW;
-      const bool ok = tt < nv;
-      sD[i] = ok ? softplus_f32(DT[(t0 + tt) * p.sdt_t + cc]) : 0.f;
-      sVO[i] = ok ? (float)V[(t0 + tt) * p.sv_t + cc] : 0.f;
+#pragma unroll
+    for (int m = 0; m < IT; ++m) {
+      const int i = tid + m * NT, tt = i / CPW;
+      if (i < C * CPW) {
+        sD[i] = tt < nv ? softplus_f32(dtn[m]) : 0.f;
+        sVO[i] = vnx[m];
+      }
     }
     __syncthreads();
+    if (t0 + C < p.n) prefetch(t0 + C);
     for (int t = 0; t < nv; ++t) {
       const float dl = sD[t * CPW + cl], dlv = dl * sVO[t * CPW + cl];
       const float *pk = sPh[1] + t * ROW + nb * BLK, *pq = sPh[0] + t * ROW + nb * BLK;
