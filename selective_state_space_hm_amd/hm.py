@@ -265,13 +265,85 @@ def _w_strides(w):
     return w.stride(0)
 
 
+# ------------------------------------------------------------ argument checks
+# The C ABI sees raw pointers only, so a tensor of the wrong size, dtype or
+# layout would be read or written out of bounds on the GPU.  These checks run
+# before anything is marshalled.
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_shape(t, shape, name):
+    _need(t is not None and tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, "
+          f"got {None if t is None else tuple(t.shape)}")
+
+
+def _check_same_dtype(ref, *named):
+    for name, t in named:
+        if t is not None and t.dtype != ref.dtype:
+            raise ValueError(f"{name} must have q's dtype {ref.dtype}, got {t.dtype}")
+
+
+def _check_w(w, d, f, H, name):
+    """W is [d, f] (shared) or [H, d, f] (per head), rows contiguous: a transposed
+    view (stride (1, d)) would be read as row-major and give wrong results."""
+    _need(w.dim() in (2, 3), f"{name} must be [d, f] or [H, d, f], got {tuple(w.shape)}")
+    _need(tuple(w.shape[-2:]) == (d, f), f"{name} must be [{d}, {f}] per head, got {tuple(w.shape)}")
+    _need(w.dim() == 2 or w.shape[0] == H, f"per-head {name} must have {H} heads, got {w.shape[0]}")
+    _need(w.stride(-1) == 1 and (d == 1 or w.stride(-2) == f),
+          f"{name} must be row-major with contiguous rows (strides (f, 1)), got strides {tuple(w.stride())}")
+
+
+def _check_f32(t, shape, name, contiguous=True):
+    if t is None:
+        return
+    _need(t.dtype == torch.float32, f"{name} must be float32, got {t.dtype}")
+    _check_shape(t, shape, name)
+    _need(not contiguous or t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _check_decay(dt, a_log, dt_shape, H):
+    _need((dt is None) == (a_log is None), "dt and a_log must be given together")
+    if dt is None:
+        return
+    _need(dt.dtype == torch.float32 and a_log.dtype == torch.float32, "dt and a_log are float32")
+    _check_shape(dt, dt_shape, "dt")
+    _need(dt.stride(-1) == 1 or dt.shape[-1] == 1, "dt must be contiguous along its last axis")
+    _check_f32(a_log, (H,), "a_log")
+
+
+def _check_attn(q, k, v, w_q, w_k, o=None, gate=None, token_axis=True):
+    """q, k [B, H, (n,) d]; v, o, gate [B, H, (n,) dv]; one dtype; W [d, f] or [H, d, f]."""
+    nd = 4 if token_axis else 3
+    _need(q.dim() == nd, f"q must have {nd} dimensions, got {tuple(q.shape)}")
+    _check_shape(k, q.shape, "k")
+    _need(v.dim() == nd and tuple(v.shape[:-1]) == tuple(q.shape[:-1]),
+          f"v must be {tuple(q.shape[:-1]) + ('dv',)}, got {tuple(v.shape)}")
+    if o is not None:
+        _check_shape(o, v.shape, "o")
+    if gate is not None:
+        _check_shape(gate, v.shape, "gate")
+    _check_same_dtype(q, ("k", k), ("v", v), ("w_q", w_q), ("w_k", w_k), ("o", o), ("gate", gate))
+    d, f = q.shape[-1], w_q.shape[-1]
+    _check_w(w_q, d, f, q.shape[1], "w_q")
+    _check_w(w_k, d, f, q.shape[1], "w_k")
+    _need(w_q.dim() == w_k.dim() and (w_q.dim() == 2 or w_q.stride(0) == w_k.stride(0)),
+          "w_q and w_k must have the same layout (both shared or both per head, same head stride)")
+
+
 def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Tensor | None = None,
                  rope_dims=0, rope_base=10000.0, rope_pos0=None):
     """phi = softmax([x W, -x W]) for x [B, H, n, d], W [d, f] or [H, d, f]; with
     rope_dims > 0 turned by the rotary encoding at positions rope_pos0[b] + t."""
-    _dev(x, w)
+    _need(x.dim() == 4, f"x must be [B, H, n, d], got {tuple(x.shape)}")
     B, H, n, d = x.shape
     f = w.shape[-1]
+    _check_same_dtype(x, ("w", w))
+    _check_w(w, d, f, H, "w")
+    if phi is not None:
+        _check_shape(phi, (B, H, n, 2 * f), "phi")
+    _dev(x, w, phi)
     if phi is None:
         phi = torch.empty((B, H, n, 2 * f), dtype=phi_dtype or x.dtype, device=x.device)
     a = FeaturizeArgs(x=_ptr(x), w=_ptr(w), phi=_ptr(phi), dtype=_code(x), phi_dtype=_code(phi),
@@ -308,17 +380,14 @@ def fwd_args(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, 
 
 def hm_linattn_fwd_plan(q, k, v, w_q, w_k, dt=None, a_log=None, chunk=0, segments=0, dsplit=0, o=None,
                         rope_dims=0, rope_base=10000.0, rope_pos0=None):
+    _check_attn(q, k, v, w_q, w_k, o)
+    _check_decay(dt, a_log, tuple(q.shape[:3]), q.shape[1])
     o = o if o is not None else v
     a = fwd_args(q, k, v, w_q, w_k, dt, a_log, o=o, chunk=chunk, segments=segments, dsplit=dsplit)
     _rope(a, q.shape[0], rope_dims, rope_base, rope_pos0)
     st, plan = call_plan(a)
     _check(st)
     return plan
-
-
-def _gate_shape(gate, v):
-    if gate is not None and (gate.shape != v.shape or gate.dtype != v.dtype):
-        raise ValueError("gate must have v's shape and dtype")
 
 
 def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
@@ -329,10 +398,13 @@ def hm_linattn_fwd(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=
     [B, H, F*dv + F] after the last token.  rope_dims > 0 turns phi(q) and phi(k)
     by the rotary encoding at positions rope_pos0[b] + t (rope_pos0 int64 [B] on the
     GPU, or None for 0)."""
-    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
-    _gate_shape(gate, v)
-    if dt is not None and dt.dtype != torch.float32 or a_log is not None and a_log.dtype != torch.float32:
-        raise TypeError("dt and A_log are float32")
+    _check_attn(q, k, v, w_q, w_k, o, gate)
+    B, H, n, _ = q.shape
+    _check_decay(dt, a_log, (B, H, n), H)
+    blk = state_numel(w_q.shape[-1], v.shape[-1])
+    _check_f32(s_init, (B, H, blk), "s_init")
+    _check_f32(s_final, (B, H, blk), "s_final")
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate, save, workspace)
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
     a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit, gate)
@@ -362,15 +434,15 @@ def hm_linattn_step(q, k, v, w_q, w_k, state, dt=None, a_log=None, o=None, gate=
     float32 [d] / [H, d] or None, states [B, H, K-1, d] updated in place).  rope_dims > 0
     turns phi(q) and phi(k) by the rotary encoding at position rope_pos[b] (int64 [B]
     on the GPU, required)."""
-    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
-    _gate_shape(gate, v)
+    _check_attn(q, k, v, w_q, w_k, o, gate, token_axis=False)
     B, H, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
+    _check_decay(dt, a_log, (B, H), H)
+    _check_f32(state, (B, H, state_numel(f, dv)), "state")
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
     if o is None:
         o = torch.empty((B, H, dv), dtype=v.dtype, device=v.device)
-    if state.dtype != torch.float32:
-        raise TypeError("state is float32")
     a = StepArgs(q=_ptr(q), k=_ptr(k), v=_ptr(v), w_q=_ptr(w_q), w_k=_ptr(w_k), dt=_ptr(dt), a_log=_ptr(a_log),
                  state=_ptr(state), o=_ptr(o), dtype=_code(q), B=B, H=H, d=d, f=f, dv=dv,
                  sq_b=q.stride(0), sq_h=q.stride(1), sk_b=k.stride(0), sk_h=k.stride(1),
@@ -450,15 +522,18 @@ def hm_linattn_bwd(q, k, v, w_q, w_k, d_o, save, dt=None, a_log=None, gate=None,
     saved; gate: the forward's gate; d_s_final: dloss/ds_final).  Returns a dict: q,
     k, v (dtype of q), w_q, w_k (float32, [d, f] or [H, d, f]), and gate, dt, a_log,
     s_init when applicable.  The rotary fields are the forward's."""
-    _dev(q, k, v, w_q, w_k, d_o, save, dt, a_log, gate, d_s_final)
+    _check_attn(q, k, v, w_q, w_k, d_o, gate)
     B, H, n, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
+    _check_decay(dt, a_log, (B, H, n), H)
+    _check_f32(d_s_final, (B, H, state_numel(f, dv)), "d_s_final")
+    _need(save.numel() * save.element_size() >= save_size(q, v, w_q), "save buffer too small (see save_size)")
+    _dev(q, k, v, w_q, w_k, d_o, save, dt, a_log, gate, d_s_final, workspace)
     for t in (q, k, v, d_o, gate):
         if t is not None and t.stride(3) != 1:
             raise ValueError("inner dimensions must be contiguous")
-    _gate_shape(gate, v)
-    if w_q.dim() == 3 and not w_q.is_contiguous():
+    if w_q.dim() == 3 and not (w_q.is_contiguous() and w_k.is_contiguous()):
         raise ValueError("per-head W must be contiguous [H, d, f]")
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
@@ -512,11 +587,13 @@ def hm_linattn_pc_fwd(q, k, v, w_q, w_k, dt, a_log, s_init=None, s_final=None, o
     dt float32 [B, H, n, dv] (the step size before softplus), a_log float32 [dv, 2f] or
     [H, dv, 2f].  Returns o [B, H, n, dv]; s_final (if given) receives the float32
     state [B, H, 2*dv*2f] (Sn [dv][2f] then Sd [dv][2f])."""
-    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
-    _gate_shape(gate, v)
+    _check_attn(q, k, v, w_q, w_k, o, gate)
     B, H, n, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
+    _check_f32(s_init, (B, H, state_numel_pc(f, dv)), "s_init")
+    _check_f32(s_final, (B, H, state_numel_pc(f, dv)), "s_final")
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate)
     if dt.dtype != torch.float32 or tuple(dt.shape) != (B, H, n, dv) or dt.stride(3) != 1:
         raise ValueError("dt is float32 [B, H, n, dv] with contiguous channels")
     for t in (q, k, v, o, gate):
@@ -543,13 +620,12 @@ def hm_linattn_pc_step(q, k, v, w_q, w_k, state, dt, a_log, o=None, gate=None, c
     """One decode token per (b, h) of the per-channel scan: q, k [B, H, d], v [B, H, dv],
     dt float32 [B, H, dv]; state float32 [B, H, 2*dv*2f] updated in place.  conv and
     the rotary fields as in hm_linattn_step."""
-    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
-    _gate_shape(gate, v)
+    _check_attn(q, k, v, w_q, w_k, o, gate, token_axis=False)
     B, H, d = q.shape
     dv = v.shape[-1]
     f = w_q.shape[-1]
-    if state.dtype != torch.float32:
-        raise TypeError("state is float32")
+    _check_f32(state, (B, H, state_numel_pc(f, dv)), "state")
+    _dev(q, k, v, w_q, w_k, state, dt, a_log, o, gate, *(conv or ()))
     if dt.dtype != torch.float32 or tuple(dt.shape) != (B, H, dv) or dt.stride(2) != 1:
         raise ValueError("dt is float32 [B, H, dv] with contiguous channels")
     if o is None:

@@ -66,3 +66,29 @@ def oracle_heads(case, heads, s_init=None, z_init=None):
 def run_fwd(case, dev="cuda", **kw):
     g = to_dev(case, dev)
     return hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], **kw)
+
+
+def with_abs(v):
+    """v with |v| appended along the value axis: one oracle pass then yields the
+    output over v and the output over |v| (the first-order rounding bound below)."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.concatenate([v, np.abs(v)], axis=-1)
+
+
+def check_bound(name, got, ref, ref_abs, tol):
+    """Element-wise check of outputs that are convex combinations of the v_j (positive
+    features): o_t = sum_j w_tj v_j / sum_j w_tj with every weight carried to a small
+    relative error gives |d o_t| <= eps (sum_j w_tj |v_j| / sum_j w_tj + |o_t|), i.e.
+    eps times (the output over |v|) + |o_t|.  Asserts every element's error within tol
+    times that bound, so a single wrong row or column fails even where it barely moves
+    the rel-L2; prints the rel-L2, max-abs and the worst bound ratio."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = np.asarray(ref_abs, dtype=np.float64) + np.abs(ref)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    ratio = np.abs(got - ref) / np.maximum(bound, 1e-300)
+    r = report(name, got, ref)
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    print(f"[parity] {name}: max |err| / bound {ratio.max():.3e} at {tuple(int(i) for i in worst)}", flush=True)
+    assert ratio.max() <= tol, f"{name}: element {worst} error {ratio.max():.3e} x its bound"
+    return r

@@ -386,3 +386,101 @@ def test_per_channel_validation():
     expect(hm.call_pc_step(pc_step(rope_dims=64, rope_base=1e4)), hm.HM_ERR_NULL)      # positions required
     expect(hm.call_pc_step(pc_step(conv_width=5)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_pc_step(pc_step(B=0)), hm.HM_OK)
+
+
+# ------------------------------------------------------------ binding checks
+# The torch binding validates sizes, dtypes and layouts before it marshals a
+# pointer: the C ABI only sees raw addresses, so an undersized state or a
+# transposed W would otherwise be read or written wrongly on the GPU.  The checks
+# run before the device check, so CPU tensors exercise them here; a well-formed
+# CPU call stops at "must be on the GPU".
+def _cpu_layer(B=2, H=3, n=5, d=32, f=16, dv=32, dtype=None):
+    import torch
+    dtype = dtype or torch.bfloat16
+    g = torch.Generator().manual_seed(0)
+    mk = lambda *s: torch.randn(s, generator=g).to(dtype)
+    return mk(B, H, n, d), mk(B, H, n, d), mk(B, H, n, dv), mk(d, f), mk(d, f)
+
+
+def _bad(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_rejects_bad_prefill_tensors():
+    import torch
+    q, k, v, wq, wk = _cpu_layer()
+    B, H, n, d = q.shape
+    f, dv = wq.shape[1], v.shape[-1]
+    blk = hm.state_numel(f, dv)
+    fwd = hm.hm_linattn_fwd
+    _bad(lambda: fwd(q, k, v, wq, wk), "on the GPU")                               # well formed
+    _bad(lambda: fwd(q, k[:, :, :4], v, wq, wk), "k must have shape")
+    _bad(lambda: fwd(q, k, v[:, :, :4], wq, wk), "v must be")
+    _bad(lambda: fwd(q, k.float(), v, wq, wk), "k must have q's dtype")
+    _bad(lambda: fwd(q, k, v.float(), wq, wk), "v must have q's dtype")
+    _bad(lambda: fwd(q, k, v, wq.float(), wk), "w_q must have q's dtype")
+    _bad(lambda: fwd(q, k, v, wq, wk, o=torch.empty(B, H, n, dv)), "o must have q's dtype")
+    _bad(lambda: fwd(q, k, v, wq, wk, o=torch.empty(B, H, n, dv - 8, dtype=q.dtype)), "o must have shape")
+    # a transposed view of a [f, d] weight has the right shape but strides (1, d)
+    _bad(lambda: fwd(q, k, v, wq.t().contiguous().t(), wk), "row-major")
+    _bad(lambda: fwd(q, k, v, wq[:16], wk), r"w_q must be \[32, 16\]")
+    _bad(lambda: fwd(q, k, v, wq.expand(H + 1, d, f), wk.expand(H + 1, d, f)), "3 heads")
+    _bad(lambda: fwd(q, k, v, wq.expand(H, d, f).contiguous(), wk), "same layout")
+    _bad(lambda: fwd(q, k, v, wq, wk, s_init=torch.zeros(B, H, blk - 1)), "s_init must have shape")
+    _bad(lambda: fwd(q, k, v, wq, wk, s_final=torch.zeros(B, H, blk, dtype=torch.bfloat16)), "s_final must be float32")
+    _bad(lambda: fwd(q, k, v, wq, wk, s_final=torch.zeros(B, blk, H).transpose(1, 2)), "contiguous")
+    _bad(lambda: fwd(q, k, v, wq, wk, gate=torch.zeros(B, H, n, dv + 8, dtype=q.dtype)), "gate must have shape")
+    _bad(lambda: fwd(q, k, v, wq, wk, dt=torch.zeros(B, H, n)), "given together")
+    _bad(lambda: fwd(q, k, v, wq, wk, dt=torch.zeros(B, H, n + 1), a_log=torch.zeros(H)), "dt must have shape")
+    _bad(lambda: fwd(q, k, v, wq, wk, dt=torch.zeros(B, H, n), a_log=torch.zeros(H + 1)), "a_log must have shape")
+    _bad(lambda: fwd(q, k, v, wq, wk, dt=torch.zeros(B, H, n, dtype=torch.float64), a_log=torch.zeros(H)), "float32")
+    _bad(lambda: hm.hm_linattn_fwd_plan(q, k, v, wq.t().contiguous().t(), wk), "row-major")
+
+
+def test_binding_rejects_bad_step_and_featurize_tensors():
+    import torch
+    q, k, v, wq, wk = _cpu_layer()
+    B, H, d = q.shape[0], q.shape[1], q.shape[-1]
+    f, dv = wq.shape[1], v.shape[-1]
+    q1, k1, v1 = q[:, :, 0], k[:, :, 0], v[:, :, 0]
+    st = torch.zeros(B, H, hm.state_numel(f, dv))
+    step = hm.hm_linattn_step
+    _bad(lambda: step(q1, k1, v1, wq, wk, st), "on the GPU")                       # well formed
+    _bad(lambda: step(q1, k1, v1, wq, wk, st[:, :, :-4]), "state must have shape")
+    _bad(lambda: step(q1, k1, v1, wq, wk, st.to(torch.bfloat16)), "state must be float32")
+    _bad(lambda: step(q1, k1, v1, wq, wk, st, dt=torch.zeros(B, H + 1), a_log=torch.zeros(H)), "dt must have shape")
+    _bad(lambda: step(q1, k1.float(), v1, wq, wk, st), "k must have q's dtype")
+    _bad(lambda: step(q1, k1, v1, wq.t().contiguous().t(), wk, st), "row-major")
+    _bad(lambda: step(q1, k1, v1, wq, wk, st, o=torch.empty(B, H, dv + 8, dtype=q.dtype)), "o must have shape")
+    _bad(lambda: step(q, k, v, wq, wk, st), "3 dimensions")
+    _bad(lambda: hm.hm_featurize(q, wq.t().contiguous().t()), "row-major")
+    _bad(lambda: hm.hm_featurize(q, wq.float()), "dtype")
+    _bad(lambda: hm.hm_featurize(q, wq, phi=torch.empty(B, H, q.shape[2], f, dtype=q.dtype)), "phi must have shape")
+    _bad(lambda: hm.hm_featurize(q, wq), "on the GPU")
+
+
+def test_binding_rejects_bad_backward_and_per_channel_tensors():
+    import torch
+    q, k, v, wq, wk = _cpu_layer()
+    B, H, n, d = q.shape
+    f, dv = wq.shape[1], v.shape[-1]
+    save = torch.empty(hm.save_size(q, v, wq), dtype=torch.uint8)
+    d_o = torch.randn(B, H, n, dv).to(q.dtype)
+    bwd = hm.hm_linattn_bwd
+    _bad(lambda: bwd(q, k, v, wq, wk, d_o, save), "on the GPU")                    # well formed
+    _bad(lambda: bwd(q, k, v, wq, wk, d_o[:, :, :3], save), "o must have shape")
+    _bad(lambda: bwd(q, k, v, wq, wk, d_o, save[:-16]), "save buffer too small")
+    _bad(lambda: bwd(q, k, v, wq, wk, d_o, save, d_s_final=torch.zeros(B, H, 7)), "d_s_final must have shape")
+    _bad(lambda: bwd(q, k, v, wq.t().contiguous().t(), wk, d_o, save), "row-major")
+    F = 2 * f
+    dt = torch.zeros(B, H, n, dv)
+    al = torch.zeros(H, dv, F)
+    pc = hm.hm_linattn_pc_fwd
+    _bad(lambda: pc(q, k, v, wq, wk, dt, al), "on the GPU")                        # well formed
+    _bad(lambda: pc(q, k, v, wq, wk, dt, al, s_final=torch.zeros(B, H, hm.state_numel(f, dv))), "s_final must have shape")
+    _bad(lambda: pc(q, k.float(), v, wq, wk, dt, al), "k must have q's dtype")
+    st = torch.zeros(B, H, hm.state_numel_pc(f, dv))
+    _bad(lambda: hm.hm_linattn_pc_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], wq, wk, st[..., :-1], dt[:, :, 0], al),
+         "state must have shape")
+

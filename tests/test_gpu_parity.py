@@ -227,10 +227,16 @@ def test_split_handoff_with_aliased_state(segments, dsplit):
 @pytest.mark.parametrize("dtype,shape", [(torch.float32, (16, 16, 16)), (torch.float32, (32, 16, 32)),
                                          (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64))])
 @pytest.mark.parametrize("decay", [True, False])
-def test_decode_steps(dtype, shape, decay):
+@pytest.mark.parametrize("per_head", [False, True])
+def test_decode_steps(dtype, shape, decay, per_head):
     d, f, dv = shape
     B, H, steps = 3, 2, 40
     dc = inputs.decode_setup(B, H, d, f, dv, prefix=50, steps=steps, decay=decay, dtype=dtype, seed=d)
+    if per_head:
+        # one W per head ([H, d, f]): the decode step stages each head's own W
+        gw = torch.Generator().manual_seed(77)
+        dc.w_q = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
+        dc.w_k = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
     pk = orc.hedgehog_features(f64(dc.prefix_k), f64(dc.w_k))
     la = orc.log_decay(f64(dc.prefix_dt), f64(dc.a_log)) if decay else None
     S, z = orc.prefix_state(pk, f64(dc.prefix_v), la)
@@ -246,7 +252,7 @@ def test_decode_steps(dtype, shape, decay):
                             f64(dt) if decay else None, f64(dc.a_log) if decay else None)
         worst = max(worst, rel_l2(f64(o), ot))
     Sg, zg = orc.unpack_state(f64(state), 2 * f, dv)
-    print(f"[parity] decode {dtype} {shape} decay={decay}: worst step rel-L2 {worst:.3e}, "
+    print(f"[parity] decode {dtype} {shape} decay={decay} per_head={per_head}: worst step rel-L2 {worst:.3e}, "
           f"state rel-L2 {rel_l2(Sg, S):.3e}", flush=True)
     assert worst <= tol_for(dtype)
     assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)

@@ -165,12 +165,17 @@ def test_full_size_sampled_heads():
 @pytest.mark.parametrize("dtype,shape", [(torch.float32, (16, 16, 16)), (torch.float32, (32, 16, 32)),
                                          (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64))])
 @pytest.mark.parametrize("rope", [False, True])
-def test_decode_chain(dtype, shape, rope):
+@pytest.mark.parametrize("per_head", [False, True])
+def test_decode_chain(dtype, shape, rope, per_head):
     """Prefill a prefix, then decode step by step, gated; every step against the
-    oracle (output and state)."""
+    oracle (output and state).  per_head: one W per head ([H, d, f])."""
     d, f, dv = shape
     B, H, pre, steps = 3, 2, 40, 5
     c = inputs.make_pc("pc", B, H, pre + steps, d, f, dv, dtype, seed=d + 1)
+    if per_head:
+        gw = torch.Generator().manual_seed(78)
+        c.w_q = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
+        c.w_k = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
     gate = inputs.gate(c.v.shape, dtype, seed=6)
     g = dev(c)
     gg = gate.cuda()
