@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 6
+#define HM_ABI_VERSION 7
 
 typedef enum {
   HM_OK = 0,
@@ -188,6 +188,29 @@ hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *args, int32_t *chunk,
                               int32_t *segments, int32_t *dsplit);
 
 hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
+
+/*
+ * hm_linattn_fwd_noalloc — hm_linattn_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same prefill, kernels and plan, with the workspace taken from a
+ * scratch array the library holds on each GPU instead of from the caller.
+ * `workspace` and `workspace_bytes` are ignored; every other field is as for
+ * hm_linattn_fwd (the caller still passes all inputs and outputs, `save` included).
+ *   - The scratch is HM_NOALLOC_SCRATCH_BYTES (40 MiB) per GPU, a static device
+ *     array that each GPU the library runs on holds until the process ends.  Every
+ *     automatic plan fits (its segment states stay within 256 state blocks plus a
+ *     copy of s_init); a plan that needs more (many explicit `segments` with many
+ *     heads) returns HM_ERR_WORKSPACE and launches nothing.
+ *   - The first call with a device current looks up that device's scratch address
+ *     (hipGetSymbolAddress); a failure there returns HM_ERR_HIP.  No call allocates
+ *     or frees memory.
+ *   - Every call on one GPU shares that GPU's scratch: calls that may overlap on one
+ *     GPU (other streams, other threads) race and must be ordered by the caller.
+ *     Nothing in the scratch needs to start at zero: each call writes every value
+ *     it later reads.
+ */
+#define HM_NOALLOC_SCRATCH_BYTES (40 << 20)
+hm_status hm_linattn_fwd_noalloc(const hm_linattn_fwd_args *args, void *stream);
 
 /* Bytes of the `save` buffer a training forward needs (only B, H, n, f, dv and
  * dtype of args are read). */

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "hm.h"
@@ -275,16 +276,13 @@ hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *a, int32_t *chunk, int3
   return ok();
 }
 
-hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
-  hm_status st = validate_fwd(a);
-  if (st != HM_OK) return st;
-  const Plan pl = make_plan(a);
-  if (pl.bytes() > 0) {
-    if (!a->workspace) return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.bytes());
-    if (a->workspace_bytes < pl.bytes())
-      return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.bytes(), a->workspace_bytes);
-    if (!aligned16(a->workspace)) return fail(HM_ERR_ALIGN, "workspace must be 16-byte aligned");
-  }
+}  // extern "C"
+
+namespace {
+// The prefill after validation and planning, with the workspace `wsp` (at least
+// pl.bytes() bytes, 16-byte aligned; NULL when that is 0).
+hm_status run_fwd(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, void *stream) {
+  hm_status st = HM_OK;
   const int64_t BH = a->B * a->H;
   if (BH == 0) return ok();
   if (a->n == 0 && !a->s_final) return ok();
@@ -295,7 +293,7 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   if (!full || !local) return fail(HM_ERR_UNSUPPORTED, "no kernel for dv/dsplit=%lld", (long long)dw);
   hipStream_t s = (hipStream_t)stream;
 
-  float *ws = (float *)a->workspace;
+  float *ws = (float *)wsp;
   float *ws_state = ws;
   float *ws_lam = ws ? ws + pl.ws_state_floats : nullptr;
   float *ws_init = ws ? ws + pl.ws_state_floats + pl.ws_lam_floats : nullptr;
@@ -375,6 +373,65 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
   p.nitems = BH * pl.segments;
   full->launch(p, grid_for(p.nitems, pl.dsplit), s);
   return check_launch("prefill");
+}
+
+// Scratch of hm_linattn_fwd_noalloc: one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory: its
+// device address comes from hipGetSymbolAddress, once per device, and only that
+// address is passed on.
+static __device__ __align__(256) unsigned char scratch[HM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call made with
+// that device current.
+hm_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(HM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(HM_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(HM_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+extern "C" {
+
+hm_status hm_linattn_fwd(const hm_linattn_fwd_args *a, void *stream) {
+  hm_status st = validate_fwd(a);
+  if (st != HM_OK) return st;
+  const Plan pl = make_plan(a);
+  if (pl.bytes() > 0) {
+    if (!a->workspace) return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", pl.bytes());
+    if (a->workspace_bytes < pl.bytes())
+      return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", pl.bytes(), a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(HM_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return run_fwd(a, pl, a->workspace, stream);
+}
+
+hm_status hm_linattn_fwd_noalloc(const hm_linattn_fwd_args *a, void *stream) {
+  hm_status st = validate_fwd(a);
+  if (st != HM_OK) return st;
+  const Plan pl = make_plan(a);
+  if (pl.bytes() > (size_t)HM_NOALLOC_SCRATCH_BYTES)
+    return fail(HM_ERR_WORKSPACE,
+                "this plan needs %zu bytes of scratch, above the %d bytes hm_linattn_fwd_noalloc holds per device "
+                "(fewer segments, or hm_linattn_fwd with a workspace)",
+                pl.bytes(), HM_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (pl.bytes() > 0 && (st = scratch_for_current_device(&ws)) != HM_OK) return st;
+  return run_fwd(a, pl, ws, stream);
 }
 
 hm_status hm_linattn_save_size(const hm_linattn_fwd_args *a, size_t *bytes) {

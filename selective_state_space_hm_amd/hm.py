@@ -118,6 +118,7 @@ class HMError(RuntimeError):
 
 _lib = None
 EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
+           "hm_linattn_fwd_noalloc",
            "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
            "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step", "hm_status_string",
            "hm_last_error_message", "hm_abi_version", "hm_args_size"]
@@ -134,6 +135,7 @@ def lib():
         L.hm_linattn_fwd_workspace_size.argtypes = [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]
         L.hm_linattn_fwd_plan.argtypes = [C.POINTER(FwdArgs), C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)]
         L.hm_linattn_fwd.argtypes = [C.POINTER(FwdArgs), p_void]
+        L.hm_linattn_fwd_noalloc.argtypes = [C.POINTER(FwdArgs), p_void]
         L.hm_linattn_step.argtypes = [C.POINTER(StepArgs), p_void]
         L.hm_causal_conv.argtypes = [C.POINTER(ConvArgs), p_void]
         L.hm_linattn_save_size.argtypes = [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]
@@ -142,6 +144,7 @@ def lib():
         L.hm_linattn_pc_fwd.argtypes = [C.POINTER(PcArgs), p_void]
         L.hm_linattn_pc_step.argtypes = [C.POINTER(PcStepArgs), p_void]
         for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
+                   "hm_linattn_fwd_noalloc",
                    "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
                    "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step"):
             getattr(L, fn).restype = C.c_int
@@ -176,6 +179,10 @@ def call_featurize(args: FeaturizeArgs, stream=None) -> int:
 
 def call_fwd(args: FwdArgs, stream=None) -> int:
     return lib().hm_linattn_fwd(C.byref(args), stream)
+
+
+def call_fwd_noalloc(args: FwdArgs, stream=None) -> int:
+    return lib().hm_linattn_fwd_noalloc(C.byref(args), stream)
 
 
 def call_workspace_size(args: FwdArgs):
@@ -505,6 +512,32 @@ def hm_causal_conv(x, w, bias=None, prev=None, final_rows=None, y=None):
                  sb_h=bias.stride(0) if bias is not None and bias.dim() == 2 else 0)
     _check(call_conv(a, _stream()))
     return y
+
+
+def hm_linattn_fwd_noalloc(q, k, v, w_q, w_k, dt=None, a_log=None, s_init=None, s_final=None, o=None,
+                           chunk=0, segments=0, dsplit=0, gate=None, save=None, rope_dims=0, rope_base=10000.0,
+                           rope_pos0=None):
+    """hm_linattn_fwd without a workspace: the library's per-GPU scratch stands in
+    for it (see include/hm.h).  Calls that overlap on one GPU race.  o is allocated
+    here only when not given."""
+    _check_attn(q, k, v, w_q, w_k, o, gate)
+    B, H, n, _ = q.shape
+    _check_decay(dt, a_log, (B, H, n), H)
+    blk = state_numel(w_q.shape[-1], v.shape[-1])
+    _check_f32(s_init, (B, H, blk), "s_init")
+    _check_f32(s_final, (B, H, blk), "s_final")
+    _dev(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, gate, save)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    a = fwd_args(q, k, v, w_q, w_k, dt, a_log, s_init, s_final, o, chunk, segments, dsplit, gate)
+    _rope(a, B, rope_dims, rope_base, rope_pos0)
+    if save is not None:
+        if save.numel() * save.element_size() < save_size(q, v, w_q):
+            raise ValueError("save buffer too small (see save_size)")
+        a.save = save.data_ptr()
+        a.save_bytes = save.numel() * save.element_size()
+    _check(call_fwd_noalloc(a, _stream()))
+    return o
 
 
 def save_size(q, v, w_q) -> int:

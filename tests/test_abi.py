@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     L = hm.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -44,7 +44,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 6
+    assert hm.lib().hm_abi_version() == 7
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -484,3 +484,20 @@ def test_binding_rejects_bad_backward_and_per_channel_tensors():
     _bad(lambda: hm.hm_linattn_pc_step(q[:, :, 0], k[:, :, 0], v[:, :, 0], wq, wk, st[..., :-1], dt[:, :, 0], al),
          "state must have shape")
 
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """hm_linattn_fwd_noalloc checks the plan's scratch need against its fixed per-GPU
+    array before any HIP call: 7 segment states of 128 heads (59 MB) exceed 40 MiB."""
+    a = hm.FwdArgs(q=A, k=A, v=A, w_q=A, w_k=A, o=A, dtype=hm.HM_BF16, B=8, H=16, n=2048, d=128, f=64, dv=128,
+                   sq_t=128, sk_t=128, sv_t=128, so_t=128, segments=8)
+    st, need = hm.call_workspace_size(a)
+    assert st == hm.HM_OK and need > (40 << 20)
+    assert hm.call_fwd_noalloc(a) == hm.HM_ERR_WORKSPACE
+    assert "40" in hm.last_error() or str(40 << 20) in hm.last_error()
+    # invalid arguments are rejected exactly as hm_linattn_fwd rejects them
+    a.segments = 0
+    a.chunk = 96
+    assert hm.call_fwd_noalloc(a) == hm.HM_ERR_UNSUPPORTED
+    a.chunk = 0
+    a.q = A + 8
+    assert hm.call_fwd_noalloc(a) == hm.HM_ERR_ALIGN
