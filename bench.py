@@ -102,27 +102,39 @@ def segment_pass_split(B, H, nseg, per, dv, dsplit):
 
 def prefill_mfma_count(plan, B, H, n, d, f, dv):
     """MFMA instructions (16x16x32 bf16) the prefill kernels issue, from the loop
-    structure of the chunk kernel, per 64-token chunk and workgroup:
+    structure of the chunk kernel, per 64-token block and workgroup:
       feature waves: featurize q and k, phi(k)^T re-layout, the ten causal score
       tiles, the z update (ones-column products);
-      state waves: v re-layout, inter read-out, intra read-out, state update.
-    The segment pass featurizes k only and updates the state only."""
+      state waves: v re-layout, inter read-out, intra read-out, state update;
+    with 128-token chunks the second block of each chunk adds the 16 off-diagonal
+    score tiles and their share of the intra read-out.  The segment pass (64-token
+    blocks at any chunk length) featurizes k only and updates the state only."""
     chunk, segments, dsplit = plan
-    C = chunk
+    C = 64
     NCT, NFH, NFT = C // 16, f // 16, 2 * f // 16
     KD, KF, KC = d // 32, NFT // 2, NCT // 2
     vt = dv // dsplit // 16                        # value tiles per workgroup
     intra_steps = sum(bt // 2 + 1 for bt in range(NCT))
     full = (2 * NCT * NFH * KD + NCT * NFT + sum(NCT - a for a in range(NCT)) * KF + NFT * KC
             + vt * NCT + vt * NCT * KF + vt * NFT * KC + vt * intra_steps)
-    chunks = (n + C - 1) // C
+    offdiag = NCT * NCT * KF + vt * NCT * KC
+    chunks = (n + chunk - 1) // chunk
     per = -(-chunks // segments)
     nseg = -(-chunks // per)
+    seg_len = per * chunk
+    full_total = 0
+    for sgi in range(nseg):
+        blocks = -(-min(seg_len, n - sgi * seg_len) // C)
+        full_total += blocks * full + (blocks // 2 if chunk == 128 else 0) * offdiag
     ls = segment_pass_split(B, H, nseg, per, dv, dsplit)
     vtl = dv // ls // 16
     local = NCT * NFH * KD + NCT * NFT + NFT * KC + vtl * NCT + vtl * NFT * KC
-    local_chunks = per * (nseg - 1)
-    return B * H * (dsplit * full * chunks + ls * local * local_chunks)
+    local_blocks = (seg_len // C) * (nseg - 1)
+    return B * H * (dsplit * full_total + ls * local * local_blocks)
+
+
+CHUNK_256_REASON = ("not built: a 256-token chunk's phi(q), phi(k) and v alone take 192 KB of LDS in bf16 at "
+                    "2f = dv = 128, above the 160 KB of a compute unit")
 
 
 # ---------------------------------------------------------------- timing
@@ -433,7 +445,8 @@ def main():
 
     log("[bench] generating the long-context workload B=1 H=16 n=131072")
     case = inputs.long_context()
-    head = prefill_block(torch, hm, case, dev, ws, args.steps, args.warmup, args.warmup_ms, "headline", args.chunk,
+    head = prefill_block(torch, hm, case, dev, ws, args.steps, args.warmup, args.warmup_ms,
+                         "headline" if args.chunk in (0, 64) else f"headline_c{args.chunk}", args.chunk,
                          distribution=args.part == "all")
     result = {
         "metric": METRIC,
@@ -457,6 +470,19 @@ def main():
     }
     if "distribution" in head:
         result["distribution"] = head["distribution"]
+    if args.part == "all" and args.chunk == 0:
+        # chunk-length sweep of the headline workload: time, HBM fraction and both MFMA fractions
+        sweep = []
+        for ch in (64, 128):
+            r = prefill_block(torch, hm, case, dev, ws, args.steps, args.warmup, args.warmup_ms,
+                              "headline" if ch == 64 else f"headline_c{ch}", ch, distribution=False)
+            sweep.append({"chunk": ch, "ms": r["ms"], "tokens_per_s": r["tokens_per_s"], "plan": r["plan"],
+                          "hbm_frac": r["roofline"]["frac"], "traffic": r["roofline"]["traffic"],
+                          "mfma_executed_frac": r["mfma"]["executed_frac"],
+                          "mfma_algorithmic_frac": r["mfma"]["algorithmic_frac"],
+                          "executed_mfma_per_call": r["mfma"]["executed_mfma_per_call"]})
+        sweep.append({"chunk": 256, "status": CHUNK_256_REASON})
+        result["chunk_sweep"] = sweep
     if args.part == "headline":
         print(json.dumps(result), flush=True)
         return

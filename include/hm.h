@@ -66,6 +66,15 @@
  *       hm_linattn_fwd, hm_linattn_step:
  *         bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}
  *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}
+ *       Not built, and why:
+ *         f32 at d = 128, f = 64: the full pass keeps W_q^T, W_k^T, two blocks of
+ *           phi(q) rows and of phi(k)^T, the score tile and the output rows in LDS:
+ *           157 KB in bf16, twice that in f32 (the bf16 path is the one measured);
+ *         bf16 at d = 16: the bf16 MFMA (16x16x32) takes K in steps of 32, so d
+ *           must be a multiple of 32 (d = 32 is built by hm_featurize only: the
+ *           prefill instantiates the measured widths and the two f32 test widths);
+ *         f = 16 in bf16: phi has 32 features, one 32-wide MFMA step; not
+ *           instantiated (f32 covers the small widths).
  *       hm_featurize:
  *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
  *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}
@@ -133,7 +142,13 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   w_q, w_k: [d, f] each (head stride sw_h).
  *   s_init: optional initial state (NULL = zeros); s_final: optional, receives the
  *   state after token n-1.  They may point to the same buffer.
- *   chunk: 0 = automatic, else 64 (the only chunk length built).
+ *   chunk: the chunk length of the chunk-wise form, 0 = automatic (64), 64 or
+ *   128.  A 128-token chunk reads its outputs against the state at the chunk's
+ *   start plus the masked, decayed scores of all its earlier tokens, and passes the
+ *   state once per chunk; it is built for the plain prefill (no `save`, gate or
+ *   rotary encoding: HM_ERR_UNSUPPORTED) at every size below.  256 is
+ *   HM_ERR_UNSUPPORTED: a 256-token chunk's phi(q), phi(k) and v alone take 192 KB of
+ *   LDS in bf16 at 2f = dv = 128, above the 160 KB of a compute unit.
  *   segments: 0 = automatic, else the number of sequence segments scanned in
  *   parallel (their start states are joined by the affine composition of
  *   [SSM] §4.2).  dsplit: 0 = automatic, 1 or 2 = number of workgroups that

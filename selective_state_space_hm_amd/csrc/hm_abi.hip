@@ -40,7 +40,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
 
 struct Tables {
-  hm::Table parts[8];
+  hm::Table parts[9];
   Tables() {
     parts[0] = hm::table_fwd_bf16();
     parts[1] = hm::table_fwd_bf16_decay();
@@ -50,6 +50,7 @@ struct Tables {
     parts[5] = hm::table_fwd_rope_bf16();
     parts[6] = hm::table_fwd_rope_bf16_decay();
     parts[7] = hm::table_fwd_rope_f32();
+    parts[8] = hm::table_fwd_c128();
   }
 };
 const Tables &tables() {
@@ -57,11 +58,13 @@ const Tables &tables() {
   return t;
 }
 
-const hm::FwdEntry *find_fwd(int dt, int64_t dk, int64_t fh, int64_t dw, int decay, int mode) {
+const hm::FwdEntry *find_fwd(int dt, int64_t dk, int64_t fh, int64_t dw, int decay, int mode, int chunk = hm::CHUNK) {
   for (const auto &part : tables().parts)
     for (int i = 0; i < part.nfwd; ++i) {
       const auto &e = part.fwd[i];
-      if (e.dtype == dt && e.dk == dk && e.fh == fh && e.dw == dw && e.decay == decay && e.mode == mode) return &e;
+      if (e.dtype == dt && e.dk == dk && e.fh == fh && e.dw == dw && e.decay == decay && e.mode == mode &&
+          e.chunk == chunk)
+        return &e;
     }
   return nullptr;
 }
@@ -144,7 +147,15 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
     return fail(HM_ERR_ALIGN, "state buffers must be 16-byte aligned");
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
-  if (a->chunk != 0 && a->chunk != hm::CHUNK) return fail(HM_ERR_UNSUPPORTED, "chunk %d: only 0 (auto) or 64 are built", a->chunk);
+  if (a->chunk == 256)
+    return fail(HM_ERR_UNSUPPORTED,
+                "chunk 256 is not built: a 256-token chunk's phi(q), phi(k) and v alone take 192 KB of LDS "
+                "in bf16 at 2f = dv = 128, above the 160 KB of a compute unit (built: 0 = auto, 64, 128)");
+  if (a->chunk != 0 && a->chunk != 64 && a->chunk != 128)
+    return fail(HM_ERR_UNSUPPORTED, "chunk %d: built are 0 (auto), 64 and 128", a->chunk);
+  if (a->chunk == 128 && (a->save || a->gate || a->rope_dims))
+    return fail(HM_ERR_UNSUPPORTED, "chunk 128 is built for the plain prefill: no training saves, gate or rotary "
+                                    "encoding (use chunk 64 for those)");
   {
     const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
     if (rs != HM_OK) return rs;
@@ -152,14 +163,15 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
   if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0");
   if (a->dsplit < 0 || a->dsplit > 2) return fail(HM_ERR_UNSUPPORTED, "dsplit must be 0, 1 or 2");
   const int decay = a->dt != nullptr && a->a_log != nullptr;
+  const int ch = a->chunk ? a->chunk : hm::CHUNK;
   // the full-pass kernel for dsplit 1 must exist for the size to count as supported
-  if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)) &&
-      !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a)))
-    return fail(HM_ERR_UNSUPPORTED, "no kernel built for dtype=%d d=%lld f=%lld dv=%lld", a->dtype, (long long)a->d,
-                (long long)a->f, (long long)a->dv);
-  if (a->dsplit == 2 && (a->dv % 2 || !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a))))
+  if (!find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a), ch) &&
+      !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a), ch))
+    return fail(HM_ERR_UNSUPPORTED, "no kernel built for dtype=%d d=%lld f=%lld dv=%lld chunk=%d", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv, ch);
+  if (a->dsplit == 2 && (a->dv % 2 || !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a), ch)))
     return fail(HM_ERR_UNSUPPORTED, "dsplit=2 is not built for dv=%lld", (long long)a->dv);
-  if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)))
+  if (a->dsplit == 1 && !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a), ch))
     return fail(HM_ERR_UNSUPPORTED, "dsplit=1 is not built for dv=%lld", (long long)a->dv);
   if (a->save) {
     if (a->dsplit > 1) return fail(HM_ERR_UNSUPPORTED, "saving for the backward pass runs with dsplit 1");
@@ -195,7 +207,8 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
   const int64_t BH = a->B * a->H;
   const int64_t F = 2 * a->f;
   const int64_t BLK = F * a->dv + F;
-  const int C = hm::CHUNK;
+  // chunk: 64 unless asked (128-token chunks add intra-chunk work for fewer state passes)
+  const int C = a->chunk ? a->chunk : hm::CHUNK;
   p.chunk = C;
   // dsplit: one workgroup owns all value columns of a (b, h) whenever that
   // kernel is built (splitting duplicates the featurization and measured slower)
@@ -204,7 +217,7 @@ Plan make_plan(const hm_linattn_fwd_args *a) {
   } else if (a->dsplit) {
     p.dsplit = a->dsplit;
   } else {
-    const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a)) != nullptr;
+    const bool can1 = find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a), C) != nullptr;
     p.dsplit = can1 ? 1 : 2;
   }
   const int64_t nchunks = (a->n + C - 1) / C;
@@ -288,7 +301,10 @@ hm_status run_fwd(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, void 
   if (a->n == 0 && !a->s_final) return ok();
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int64_t dw = a->dv / pl.dsplit;
-  const hm::FwdEntry *full = find_fwd(a->dtype, a->d, a->f, dw, decay, (a->save ? hm::MODE_TRAIN : hm::MODE_FULL) | rmode(a));
+  // the full pass at the plan's chunk length; the segment pass works in 64-token
+  // chunks at any chunk length (the end state is the same sum)
+  const hm::FwdEntry *full =
+      find_fwd(a->dtype, a->d, a->f, dw, decay, (a->save ? hm::MODE_TRAIN : hm::MODE_FULL) | rmode(a), pl.chunk);
   const hm::FwdEntry *local = find_fwd(a->dtype, a->d, a->f, dw, decay, hm::MODE_LOCAL | rmode(a));
   if (!full || !local) return fail(HM_ERR_UNSUPPORTED, "no kernel for dv/dsplit=%lld", (long long)dw);
   hipStream_t s = (hipStream_t)stream;
@@ -366,7 +382,7 @@ hm_status run_fwd(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, void 
   if (compose || pl.init_copy) {
     dim3 grid((unsigned)((BLK + 255) / 256), (unsigned)BH);
     hipLaunchKernelGGL(hm::combine_kernel, grid, dim3(256), 0, s, ws_state, ws_lam, a->s_init,
-                       pl.init_copy ? ws_init : nullptr, BH, BLK, compose ? nslot : 0);
+                       pl.init_copy ? ws_init : nullptr, BH, BLK, compose ? nslot : 0, pl.lsub);
     if ((st = check_launch("segment combine")) != HM_OK) return st;
   }
   p.nseg_run = pl.segments;

@@ -11,7 +11,7 @@
 namespace hm {
 
 struct FwdEntry {
-  int dtype, dk, fh, dw, decay, mode;
+  int dtype, dk, fh, dw, decay, mode, chunk;
   void (*launch)(const FwdParams &, unsigned grid, hipStream_t);
 };
 struct StepEntry {
@@ -73,11 +73,12 @@ Table table_fwd_f32();
 Table table_fwd_rope_bf16();
 Table table_fwd_rope_bf16_decay();
 Table table_fwd_rope_f32();
+Table table_fwd_c128();
 Table table_step_feat();
 
-template <typename T, int DK, int FH, int DW, bool DECAY, int MODE>
+template <typename T, int DK, int FH, int DW, bool DECAY, int MODE, int CH>
 void launch_fwd(const FwdParams &p, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_kernel<T, DK, FH, DW, DECAY, MODE>), dim3(grid), dim3(fwd_waves(DW) * 64), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<T, DK, FH, DW, DECAY, MODE, CH>), dim3(grid), dim3(fwd_waves(DW) * 64), 0, s, p);
 }
 template <typename T, int DK, int FH, int DV, bool DECAY>
 void launch_step(const StepParams &p, unsigned grid, hipStream_t s) {
@@ -99,7 +100,10 @@ void launch_feat(const FeatParams &p, dim3 grid, hipStream_t s) {
 #define HM_DT_BF16 1
 
 #define HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, MODE) \
-  {TC, DK, FH, DW, DEC, MODE, &hm::launch_fwd<T, DK, FH, DW, (DEC != 0), MODE>}
+  {TC, DK, FH, DW, DEC, MODE, 64, &hm::launch_fwd<T, DK, FH, DW, (DEC != 0), MODE, 64>}
+// the full pass with 128-token chunks
+#define HM_FWD_C128(T, TC, DK, FH, DW, DEC) \
+  {TC, DK, FH, DW, DEC, 0, 128, &hm::launch_fwd<T, DK, FH, DW, (DEC != 0), 0, 128>}
 // both modes of one configuration
 #define HM_FWD_PAIR(T, TC, DK, FH, DW, DEC) \
   HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 0), HM_FWD_ENTRY(T, TC, DK, FH, DW, DEC, 1)

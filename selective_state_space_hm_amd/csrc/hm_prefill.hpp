@@ -112,11 +112,21 @@ __device__ __forceinline__ const T *at(const T *base, uint32_t byte_off) {
   return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
-template <typename T, int DK, int FH, int DW, bool DECAY, int MODE>
+// CH is the chunk length: 64, or 128 (full pass only).  The waves always work on
+// 64-token blocks.  With 128-token chunks the two blocks of a chunk are read out
+// against the state at the chunk's start, the second block's intra-chunk part
+// also takes its scores against the first block's keys (16 off-diagonal tiles),
+// and the state update of both blocks is applied once the chunk has been read out
+// (in order: S = e^{L_1}(e^{L_0} S + K0~^T V0) + K1~^T V1, the same sums).
+template <typename T, int DK, int FH, int DW, bool DECAY, int MODE, int CH>
 __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int C = CHUNK;
+  constexpr int C = CHUNK;                 // block length
+  constexpr int MB = CH / C;               // blocks per chunk
+  static_assert(MB == 1 || (MB == 2 && (MODE & 3) == MODE_FULL), "128-token chunks: full pass without saves");
+  constexpr int NKT = MB == 1 ? 2 : 3;     // phi(k)^T block buffers (a chunk's two blocks stay until its update)
+  constexpr int NDB = MB == 1 ? 3 : 4;     // decay-factor block buffers
   constexpr int F = 2 * FH;
   constexpr int NS = fwd_state_waves(DW);  // state waves
   constexpr int NTW = DW / (16 * NS);      // value tiles per state wave
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   constexpr int EPL = M::EPL;              // operand elements per lane
   constexpr int PAD = M::PAD;
   constexpr int LDW = DK + PAD, LDQ = F + PAD, LDC = C + PAD, LDO = DW + 32 / (int)sizeof(T);
+  constexpr int LDP = MB * C + PAD;        // score rows: the chunk's keys
   constexpr bool FULL = (MODE & 3) != MODE_LOCAL;
   constexpr bool SAVE = (MODE & 3) == MODE_TRAIN;
   constexpr bool ROPE = (MODE & MODE_ROPE) != 0;
@@ -141,18 +152,22 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
   static_assert(DK % M::KS == 0 && F % M::KS == 0, "K multiples");
 
   __shared__ __align__(16) T sWq[FULL ? FH * LDW : 8];    // W^T: sW[f][d] = W[d][f]
-  __shared__ __align__(16) T sWk[FH * LDW];
-  __shared__ __align__(16) T sKt[2][F * LDC];               // decay-weighted phi(k)^T, tile order
+  __shared__ __align__(16) T sKt[NKT][F * LDC];             // decay-weighted phi(k)^T per block, tile order
+  // W_k^T is read only before the block loop (into registers): with a third phi(k)^T
+  // buffer (first written at block 2) it shares that buffer
+  __shared__ __align__(16) T sWk_own[MB == 1 ? FH * LDW : 8];
+  static_assert(MB == 1 || FH * LDW <= F * LDC, "W_k^T fits the shared buffer");
+  T *const sWk = MB == 1 ? sWk_own : sKt[NKT - 1];
   __shared__ __align__(16) T sQ[FULL ? 2 : 1][FULL ? C * LDQ : 8];  // phi(q) (unnormalized), tile order
   __shared__ __align__(16) T sK0[FULL ? 16 * LDQ : 8];              // phi(k) of token tile 0, tile order
-  __shared__ __align__(16) T sP[FULL ? C * LDC : 8];                 // masked decayed scores
+  __shared__ __align__(16) T sP[FULL ? C * LDP : 8];                 // masked decayed scores, keys of the chunk
   __shared__ __align__(16) T sO[FULL ? C * LDO : 8];                 // normalized output rows
-  __shared__ __align__(16) T sG[FULL ? C * DW : 8];                  // gate rows, in store-piece order
-  __shared__ __align__(16) double sL[3][C];                 // inclusive log-decay prefix, float64
-  __shared__ __align__(16) float seL[3][C];
-  __shared__ __align__(16) float seK[3][C];
-  __shared__ float sLast[3];
-  __shared__ __align__(16) float sDenPart[NCT][C];
+  __shared__ __align__(16) T sG[FULL && MB == 1 ? C * DW : 8];       // gate rows, in store-piece order
+  __shared__ __align__(16) double sL[NDB][C];               // inclusive log-decay prefix per block, float64
+  __shared__ __align__(16) float seL[NDB][C];
+  __shared__ __align__(16) float seK[NDB][C];
+  __shared__ float sLast[NDB];
+  __shared__ __align__(16) float sDenPart[MB * NCT][C];     // score row sums per key tile of the chunk
   __shared__ __align__(16) float sDenInter[2][C];
   __shared__ __align__(16) float sZ[2][F];                  // z after each chunk (by chunk parity)
   __shared__ __align__(16) double sRev[ROPE ? F / 2 : 1];   // rotation rate of each feature pair
@@ -267,14 +282,19 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     // end value goes to sZ for the inter-chunk denominators.
     constexpr int ZT = (NFT + 3) / 4;
     f32x4 Z[ZT];
-    if constexpr (FULL && EPL == 8) {
-      // The intra read-out of token tile b (b even) takes K-steps over tiles b and
-      // b+1; score tile (b+1, b) lies above the diagonal and stays zero.
-      if (wv == 0) {
+    // The intra read-out of token tile b (b even) takes K-steps over tiles b and
+    // b+1; score tile (b+1, b) lies above the diagonal and must read as zero.  It is
+    // zeroed once where the last block of a chunk keeps its diagonal scores, and, with
+    // two blocks per chunk, again at every first block (the second block's
+    // off-diagonal scores overwrite those places).
+    auto zero_above = [&](int kt0) {
+      if constexpr (FULL && EPL == 8) {
 #pragma unroll
-        for (int b2 = 0; b2 < NCT; b2 += 2) store4(&sP[(16 * b2 + col) * LDC + M::tpos(16 * (b2 + 1) + 4 * g)], zero4());
+        for (int b2 = 0; b2 < NCT; b2 += 2)
+          store4(&sP[(16 * b2 + col) * LDP + M::tpos(16 * (kt0 + b2 + 1) + 4 * g)], zero4());
       }
-    }
+    };
+    if (wv == 0) zero_above(NCT * (MB - 1));
 
     frag xf[TPF_][KD];
     auto load_xi = [&](int64_t tc, int i) {
@@ -390,10 +410,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       return group_sum(sum);
     };
 
-    // score tile (a, bt) of the chunk in buffers bf / df: Pt[c'][c] for c' in tile
+    // score tile (a, bt) of the block in buffers bf / df: Pt[c'][c] for c' in tile
     // a (A operand rows), c in tile bt (B operand columns), masked to c' <= c and
-    // decay-weighted, into sP (row c, tile order over c'); row sums into sDenPart.
-    auto score_tile = [&](int a, int bt, const frag *fa, const frag *fb, int df) {
+    // decay-weighted, into sP (row c, tile order over the chunk's keys, the block's
+    // keys from key tile kt0 on); row sums into sDenPart.
+    auto score_tile = [&](int a, int bt, const frag *fa, const frag *fb, int df, int kt0) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < KF; ++s) acc = M::mma(fa[s], fb[s], acc);
@@ -419,20 +440,42 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           w[r] = xv;
         }
       }
-      store4(&sP[cc * LDC + M::tpos(16 * a + 4 * g)], w);
+      store4(&sP[cc * LDP + M::tpos(16 * (kt0 + a) + 4 * g)], w);
       // row sums of the weights as rounded for the product with V, so that each output
       // is an exact convex combination under one set of weights: o_t - v_t then keeps
       // its relative accuracy when a fast decay makes it small (the backward pass
       // differentiates through it)
       const float dsum = group_sum((float)(T)w[0] + (float)(T)w[1] + (float)(T)w[2] + (float)(T)w[3]);
+      if (g == 0) sDenPart[kt0 + a][cc] = dsum;
+    };
+    // Off-diagonal score tile of a two-block chunk: keys c' in tile a of the chunk's
+    // first block (decay buffer dfp), queries c in tile bt of its second block (df),
+    // all c' < c: weight e^{L_c - L_c'} with L counted from the chunk's start, i.e.
+    // e^{Lb1_c + (Lb0_last - Lb0_c')} with the blocks' own inclusive prefixes.
+    auto score_tile_off = [&](int a, int bt, const frag *fa, const frag *fb, int df, int dfp) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int s = 0; s < KF; ++s) acc = M::mma(fa[s], fb[s], acc);
+      const int cc = 16 * bt + col;
+      f32x4 w = acc;
+      if constexpr (DECAY) {
+        const double lc = sL[df][cc] + sL[dfp][C - 1];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w[r] = acc[r] * __expf((float)(lc - sL[dfp][16 * a + 4 * g + r]));
+      }
+      store4(&sP[cc * LDP + M::tpos(16 * a + 4 * g)], w);
+      const float dsum = group_sum((float)(T)w[0] + (float)(T)w[1] + (float)(T)w[2] + (float)(T)w[3]);
       if (g == 0) sDenPart[a][cc] = dsum;
     };
+    frag kf_prev[MB > 1 ? KF : 1];  // phi(k) of this wave's tile of the chunk's first block
 
     for (int64_t j = 0; j <= nch; ++j) {
       const int64_t tf = t0 + j * C;
       const int bf = (int)(j & 1);
-      const int df = (int)(j % 3);
-      const int cr = 16 * wv + col;  // this lane's token row in the chunk
+      const int kb = (int)(j % NKT);
+      const int df = (int)(j % NDB);
+      const int bi = MB == 1 ? 0 : (int)(j % MB);  // block within its chunk (segments start on chunk bounds)
+      const int cr = 16 * wv + col;  // this lane's token row in the block
       frag qf[FULL ? KF : 1], kf[KF];  // phiQ, phiK of token tile wv (tile order)
       // ---- half A: featurize token tile wv of chunk j
       if constexpr (SAVE) {
@@ -475,7 +518,9 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
           for (int s = 0; s < KF; ++s) qf[s] = M::from_acc(ph, s);
           store_frags(&sQ[bf][cr * LDQ], qf, ph);
-          const float *zp = sZ[(j + 1) & 1];
+          // z at the chunk's start: after the previous block, or (second block of a chunk)
+          // after the block before that, whose buffer is rewritten only in this half B
+          const float *zp = sZ[bi == 0 ? (j + 1) & 1 : j & 1];
           float dz = 0.f;
 #pragma unroll
           for (int t = 0; t < NFT; ++t) {
@@ -484,7 +529,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             for (int r = 0; r < 4; ++r) dz = __builtin_fmaf(ph[t][r], z4[r], dz);
           }
           dz = group_sum(dz);
-          if (g == 0) sDenInter[bf][cr] = DECAY ? dz * seL[df][cr] : dz;
+          if (g == 0) {
+            float sc = DECAY ? seL[df][cr] : 1.f;  // e^{L} from the chunk's start
+            if (MB > 1 && DECAY && bi == 1) sc *= sLast[(j - 1) % NDB];
+            sDenInter[bf][cr] = dz * sc;
+          }
           if (j + 1 < nch) load_xi(tf + C, XQ);
         }
         {
@@ -521,7 +570,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
             for (int uo = u0; uo < u0 + 4 && uo < NFT; ++uo) {
               if constexpr (DECAY) tr[uo - u0] *= w4;
-              store4(&sKt[bf][(16 * uo + col) * LDC + M::tpos(16 * wv + 4 * g)], tr[uo - u0]);
+              store4(&sKt[kb][(16 * uo + col) * LDC + M::tpos(16 * wv + 4 * g)], tr[uo - u0]);
             }
           }
         }
@@ -542,16 +591,37 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
                 for (int s = 0; s < KF; ++s) bq[i][s] = M::ld_tile(&sQ[bf][(16 * (wv + 1 + i) + col) * LDQ], s, g);
               }
-            score_tile(wv, wv, kf, qf, df);
+            score_tile(wv, wv, kf, qf, df, NCT * bi);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-              if (i < nb) score_tile(wv, wv + 1 + i, kf, bq[i], df);
+              if (i < nb) score_tile(wv, wv + 1 + i, kf, bq[i], df, NCT * bi);
           } else {
             frag ak[KF];
 #pragma unroll
             for (int s = 0; s < KF; ++s) ak[s] = M::ld_tile(&sK0[col * LDQ], s, g);
-            score_tile(wv, wv, kf, qf, df);
-            score_tile(0, wv, ak, qf, df);
+            score_tile(wv, wv, kf, qf, df, NCT * bi);
+            score_tile(0, wv, ak, qf, df, NCT * bi);
+          }
+          if constexpr (MB > 1) {
+            if (bi == 0) {
+              // first block of a chunk: keep this tile's phi(k) for the second block's
+              // off-diagonal scores, and clear the places those leave above the diagonal
+              if (wv == 0) zero_above(0);
+#pragma unroll
+              for (int s = 0; s < KF; ++s) kf_prev[s] = kf[s];
+            } else {
+              // second block: the 16 tiles against the first block's keys; wave w owns key
+              // tile w and takes each query tile's phi(q), its own from registers
+              const int dfp = (int)((j - 1) % NDB);
+#pragma unroll
+              for (int bt = 0; bt < NCT; ++bt) {
+                frag fq[KF];
+#pragma unroll
+                for (int s = 0; s < KF; ++s)
+                  fq[s] = bt == wv ? qf[s] : M::ld_tile(&sQ[bf][(16 * bt + col) * LDQ], s, g);
+                score_tile_off(wv, bt, kf_prev, fq, df, dfp);
+              }
+            }
           }
         }
         // z <- e^{L_last} z + sum_c' phi~(k_c'): phi~(k)^T times a ones column
@@ -562,7 +632,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           if (t < NFT) {
             frag ak[KC];
 #pragma unroll
-            for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[bf][(16 * t + col) * LDC], s, g);
+            for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[kb][(16 * t + col) * LDC], s, g);
             if constexpr (DECAY) Z[i] *= el;
 #pragma unroll
             for (int s = 0; s < KC; ++s) Z[i] = M::mma(ak[s], ones, Z[i]);
@@ -570,7 +640,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           }
         }
         if (wv == 1 && j + 1 < nch) {
-          decay(tf + C, (int)((j + 1) % 3));
+          decay(tf + C, (int)((j + 1) % NDB));
           if (j + 2 < nch) load_dt(tf + 2 * C);
         }
       }
@@ -635,7 +705,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     // (no registers held while the read-out runs); in half B each lane reads back
     // the pieces it brought in
     auto issue_gate_rows = [&](int64_t ts) {
-      if constexpr (FULL) {
+      if constexpr (FULL && MB == 1) {
         if (p.gate) {
           constexpr int EP = 16 / (int)sizeof(T), PPR = DW / EP, NIT = C * PPR / (NS * 64);
           const T *gb = (const T *)p.gate + b * p.sg_b + h * p.sg_h + ts * p.sg_t + half * DW;
@@ -669,11 +739,35 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             S[jj][t][r] = e * S[jj][t][r] + su[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + 16 * jj + col];
     }
 
-    frag vfr[NTW][KC];  // v of the chunk being read out, tile order
+    frag vfr[NTW][KC];  // v of the block being read out, tile order
+    frag vfr_prev[MB > 1 ? NTW : 1][MB > 1 ? KC : 1];  // v of the chunk's first block (two-block chunks)
+    // S += phi~(K)^T V over one block (its phi(k)^T buffer, its v fragments), after
+    // S *= e^{L_last} of that block
+    auto update_state = [&](const T *kt, const frag (*vb)[KC], int dbuf) {
+      if constexpr (DECAY) {
+        const float el = sLast[dbuf];
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+          for (int t = 0; t < NFT; ++t) S[jj][t] *= el;
+      }
+#pragma unroll
+      for (int t = 0; t < NFT; ++t) {
+        frag ak[KC];
+#pragma unroll
+        for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&kt[(16 * t + col) * LDC], s, g);
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+          for (int s = 0; s < KC; ++s) S[jj][t] = M::mma(ak[s], vb[jj][s], S[jj][t]);
+      }
+    };
     for (int64_t j = 0; j <= nch; ++j) {
-      const int64_t ts = t0 + (j - 1) * C;  // chunk handled in this iteration (j >= 1)
+      const int64_t ts = t0 + (j - 1) * C;  // block handled in this iteration (j >= 1)
       const int bs = (int)((j + 1) & 1);
-      const int ds = (int)((j + 2) % 3);
+      const int ks = (int)((j - 1 + NKT) % NKT);
+      const int ds = (int)((j - 1 + NDB) % NDB);
+      const int bi = MB == 1 ? 0 : (int)((j - 1 + MB) % MB);  // block within its chunk
       // ---- half A: read-out of chunk j-1
       if (j >= 1) {
         if constexpr (SAVE) issue_gate_rows(ts);
@@ -727,8 +821,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             const int cc = 16 * bt + col;
             den[bt] = sDenInter[bs][cc];
 #pragma unroll
-            for (int a = 0; a <= bt; ++a) den[bt] += sDenPart[a][cc];
+            for (int a = 0; a < MB * NCT; ++a)
+              if (a <= NCT * bi + bt) den[bt] += sDenPart[a][cc];
           }
+          // e^{L} from the chunk's start: the second block of a chunk adds its first's total
+          const float cscale = MB > 1 && DECAY && bi == 1 ? sLast[(j - 2 + NDB) % NDB] : 1.f;
           if (SAVE && sw == 0 && g == 0 && half == 0) {
 #pragma unroll
             for (int bt = 0; bt < NCT; ++bt)
@@ -741,18 +838,27 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             frag bq[KF];
 #pragma unroll
             for (int s = 0; s < KF; ++s) bq[s] = M::ld_tile(&sQ[bs][cc * LDQ], s, g);
-            frag bp[M::steps_upto(NCT - 1)];
+            frag bp[M::steps_upto(MB * NCT - 1)];
 #pragma unroll
-            for (int s = 0; s < M::steps_upto(bt); ++s) bp[s] = M::ld_tile(&sP[cc * LDC], s, g);
+            for (int s = 0; s < M::steps_upto(MB * NCT - 1); ++s)
+              if (s < M::steps_upto(NCT * bi + bt)) bp[s] = M::ld_tile(&sP[cc * LDP], s, g);
 #pragma unroll
             for (int jj = 0; jj < NTW; ++jj) {
               // inter: S^T phiQ^T e^{L_c};  intra: V^T Pt
               f32x4 acc = zero4();
 #pragma unroll
               for (int s = 0; s < KF; ++s) acc = M::mma(sfr[jj][s], bq[s], acc);
-              if constexpr (DECAY) acc *= seL[ds][cc];
+              if constexpr (DECAY) acc *= seL[ds][cc] * cscale;
+              if (MB == 1 || bi == 0) {
 #pragma unroll
-              for (int s = 0; s < M::steps_upto(bt); ++s) acc = M::mma(vfr[jj][s], bp[s], acc);
+                for (int s = 0; s < M::steps_upto(bt); ++s) acc = M::mma(vfr[jj][s], bp[s], acc);
+              } else if constexpr (MB > 1) {
+                // keys of the chunk's first block, then of this block
+#pragma unroll
+                for (int s = 0; s < KC; ++s) acc = M::mma(vfr_prev[jj][s], bp[s], acc);
+#pragma unroll
+                for (int s = 0; s < M::steps_upto(bt); ++s) acc = M::mma(vfr[jj][s], bp[KC + s], acc);
+              }
               oacc[jj][bt] = acc;
             }
           }
@@ -791,7 +897,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           constexpr int NIT = C * PPR / (NS * 64);         // pieces per lane
           static_assert(NIT * NS * 64 == C * PPR, "whole rows per pass");
           T *ob = O + ts * p.so_t + half * DW;
-          if (p.gate) {
+          if (MB == 1 && p.gate) {
             // mixer gate: o * SiLU(g) on the rounded output, the gate rows from LDS;
             // two pieces at a time so that the gate adds few live registers
             constexpr int GB = NIT < 2 ? NIT : 2;
@@ -825,22 +931,21 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             }
           }
         }
-        if constexpr (DECAY) {
-          const float el = sLast[ds];
+        if constexpr (MB == 1) {
+          update_state(sKt[ks], vfr, ds);
+        } else {
+          // the chunk's update once both blocks are read out (or at the segment's end)
+          if (bi == MB - 1) {
+            update_state(sKt[(j - 2 + NKT) % NKT], vfr_prev, (int)((j - 2 + NDB) % NDB));
+            update_state(sKt[ks], vfr, ds);
+          } else if (j == nch) {
+            update_state(sKt[ks], vfr, ds);
+          } else {
 #pragma unroll
-          for (int jj = 0; jj < NTW; ++jj)
+            for (int jj = 0; jj < NTW; ++jj)
 #pragma unroll
-            for (int t = 0; t < NFT; ++t) S[jj][t] *= el;
-        }
-#pragma unroll
-        for (int t = 0; t < NFT; ++t) {
-          frag ak[KC];
-#pragma unroll
-          for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[bs][(16 * t + col) * LDC], s, g);
-#pragma unroll
-          for (int jj = 0; jj < NTW; ++jj)
-#pragma unroll
-            for (int s = 0; s < KC; ++s) S[jj][t] = M::mma(ak[s], vfr[jj][s], S[jj][t]);
+              for (int s = 0; s < KC; ++s) vfr_prev[jj][s] = vfr[jj][s];
+          }
         }
       }
       __syncthreads();
@@ -860,10 +965,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 // began from s_init and holds the state after it, and for u = 1 .. nslot-1
 //   state(u) = e^{lam(u)} state(u-1) + local(u),
 // the composition of affine maps of [SSM] §4.2 with a scalar decay; the start
-// state of segment s is then slot s*lsub-1.  Optionally copies s_init to
-// `init_copy` first (used when s_init aliases s_final).
+// state of segment s is then slot s*lsub-1, and only those slots are written back
+// (the running value stays in a register).  Optionally copies s_init to `init_copy`
+// first (used when s_init aliases s_final).
 static __global__ __launch_bounds__(256) void combine_kernel(float *ws_state, const float *ws_lam, const float *s_init,
-                                                      float *init_copy, int64_t BH, int64_t BLK, int nslot) {
+                                                      float *init_copy, int64_t BH, int64_t BLK, int nslot, int lsub) {
   const int64_t bh = blockIdx.y;
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= BLK) return;
@@ -873,7 +979,7 @@ static __global__ __launch_bounds__(256) void combine_kernel(float *ws_state, co
   for (int u = 1; u < nslot; ++u) {
     const int64_t slot = (int64_t)u * BH + bh;
     cur = expf(ws_lam[slot]) * cur + ws_state[slot * BLK + e];
-    ws_state[slot * BLK + e] = cur;
+    if ((u + 1) % lsub == 0) ws_state[slot * BLK + e] = cur;
   }
 }
 
