@@ -158,8 +158,10 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   to 4 state blocks per segment: the segment pass may cut a segment into
  *   equal pieces when that fills more of the GPU), never with n^2.
  *   save: optional (NULL = inference), hm_linattn_save_size() bytes: the forward
- *   also keeps what hm_linattn_bwd reads (chunk-start states, denominators); it
- *   then runs with dsplit 1.  Built for the sizes hm_linattn_bwd lists.
+ *   also keeps what hm_linattn_bwd reads (a float32 state checkpoint at the start
+ *   of each of the backward's chunk ranges, at most 256 / (B*H) of them per
+ *   (b, h), the denominators and the float32 output before the gate); it then
+ *   runs with dsplit 1.  Built for the sizes hm_linattn_bwd lists.
  *   gate: optional [B, H, n, dv] in `dtype` (strides sg_*), the pre-activation of
  *   the mixer's gate branch; when given, o = (normalized output) * SiLU(gate),
  *   rounded once to `dtype` after the normalized output was rounded (NULL = no
@@ -248,8 +250,9 @@ hm_status hm_linattn_save_size(const hm_linattn_fwd_args *args, size_t *bytes);
  * dloss/ds_final (float32, state layout).  Outputs must not overlap inputs.
  * Math: with dnum_t = dO_t / den_t and dden_t = -(dO_t . o_t) / den_t, the gradient
  * of the state at each chunk end, G <- e^{Lam} G + sum_t e^{L_t} phi(q_t) dnum_t^T,
- * runs from the last chunk back (chunk-start states come from `save`, nothing is
- * recomputed sequentially in the forward direction); d log a_t is the sum, over
+ * runs from the last chunk back.  The state at every chunk start is recomputed
+ * from the nearest checkpoint in `save` (the forward's state update, one pass per
+ * chunk range, the ranges in parallel); d log a_t is the sum, over
  * the (query, key) pairs whose decay product contains a_t, of their weight times
  * its loss gradient, taken per chunk without differences of nearly equal terms.
  * Products in the dtype on MFMA with float32 accumulation; the decay gradient's

@@ -183,19 +183,38 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
   return ok();
 }
 
-// What the training forward saves, per (b, h): the state at every chunk start in
-// the dtype [nch][F][dv], z there in float32 [nch][F], and the per-token
-// denominator in float32 [n]; regions 256-byte aligned.
+// The backward's per-chunk kernels split each (b, h) into ngrp ranges of `per`
+// chunks, enough (b, h, range) workgroups to fill the 256 compute units.
+struct BwdGroups {
+  int64_t ngrp, per, nck;  // ranges, chunks per range, ranges that hold chunks
+};
+BwdGroups bwd_groups(int64_t BH, int64_t n) {
+  const int64_t nch = (n + hm::CHUNK - 1) / hm::CHUNK;
+  int64_t ng = BH > 0 ? (256 + BH - 1) / BH : 1;
+  if (ng > nch) ng = nch;
+  if (ng < 1) ng = 1;
+  BwdGroups gr{};
+  gr.ngrp = ng;
+  gr.per = nch > 0 ? (nch + ng - 1) / ng : 1;
+  gr.nck = nch > 0 ? (nch + gr.per - 1) / gr.per : 0;
+  return gr;
+}
+// What the training forward saves, per (b, h): the float32 state at the start of
+// each of the backward's chunk ranges [nck][F*dv + F] (the checkpoints from which
+// the backward recomputes every chunk-start state), the per-token denominator in
+// float32 [n] and the float32 output before the gate [n][dv]; regions 256-byte
+// aligned.
 struct SaveLayout {
-  size_t off_S, off_z, off_den, off_o, bytes;
+  size_t off_ck, off_den, off_o, bytes;
 };
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 SaveLayout save_layout(int dtype, int64_t BH, int64_t n, int64_t f, int64_t dv) {
-  const int64_t nch = (n + hm::CHUNK - 1) / hm::CHUNK, F = 2 * f;
+  (void)dtype;
+  const int64_t F = 2 * f;
+  const BwdGroups gr = bwd_groups(BH, n);
   SaveLayout l{};
-  l.off_S = 0;
-  l.off_z = align256((size_t)(BH * nch * F * dv) * esize(dtype));
-  l.off_den = l.off_z + align256((size_t)(BH * nch * F) * 4);
+  l.off_ck = 0;
+  l.off_den = align256((size_t)(BH * gr.nck * (F * dv + F)) * 4);
   l.off_o = l.off_den + align256((size_t)(BH * n) * 4);
   l.bytes = l.off_o + align256((size_t)(BH * n * dv) * 4);
   return l;
@@ -339,10 +358,12 @@ hm_status run_fwd(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, void 
     const SaveLayout sl = save_layout(a->dtype, BH, a->n, a->f, a->dv);
     if (a->save_bytes < sl.bytes)
       return fail(HM_ERR_WORKSPACE, "save buffer of %zu bytes required, got %zu", sl.bytes, a->save_bytes);
-    p.save_S = (char *)a->save + sl.off_S;
-    p.save_z = (float *)((char *)a->save + sl.off_z);
+    const BwdGroups gr = bwd_groups(BH, a->n);
+    p.save_ck = (float *)((char *)a->save + sl.off_ck);
     p.save_den = (float *)((char *)a->save + sl.off_den);
     p.save_o = (float *)((char *)a->save + sl.off_o);
+    p.ck_every = gr.per;
+    p.nck = gr.nck;
   }
 
   auto grid_for = [&](int64_t items, int ds) { return (unsigned)(((items + 7) / 8) * 8 * ds); };
@@ -463,7 +484,7 @@ hm_status hm_linattn_save_size(const hm_linattn_fwd_args *a, size_t *bytes) {
 // ------------------------------------------------------------------ backward
 namespace {
 struct BwdLayout {
-  size_t phq, phk, dnum, dden, Lc, eQ, eK, eW, Xc, gS, gz, dwq, dwk, da, bytes;
+  size_t phq, phk, dnum, dden, Lc, eQ, eK, eW, Xc, gS, gz, wS, wz, dwq, dwk, da, bytes;
   int ngrp;
 };
 BwdLayout bwd_layout(const hm_linattn_bwd_args *a) {
@@ -471,9 +492,7 @@ BwdLayout bwd_layout(const hm_linattn_bwd_args *a) {
   const int64_t BH = a->B * a->H, n = a->n, F = 2 * a->f, nch = (n + hm::CHUNK - 1) / hm::CHUNK;
   const size_t es = esize(a->dtype);
   // enough (b, h, chunk range) workgroups to fill the 256 compute units
-  int64_t ng = BH > 0 ? (256 + BH - 1) / BH : 1;
-  if (ng > nch) ng = nch;
-  if (ng < 1) ng = 1;
+  const int64_t ng = bwd_groups(BH, n).ngrp;
   l.ngrp = (int)ng;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align256(bytes); return at; };
@@ -488,6 +507,8 @@ BwdLayout bwd_layout(const hm_linattn_bwd_args *a) {
   l.Xc = take((size_t)(BH * nch) * 4);
   l.gS = take((size_t)(BH * nch * F * a->dv) * es);
   l.gz = take((size_t)(BH * nch * F) * 4);
+  l.wS = take((size_t)(BH * nch * F * a->dv) * es);
+  l.wz = take((size_t)(BH * nch * F) * 4);
   l.dwq = take((size_t)(BH * ng * a->d * a->f) * 4);
   l.dwk = take((size_t)(BH * ng * a->d * a->f) * 4);
   l.da = take((size_t)BH * 4);
@@ -568,7 +589,8 @@ hm_status hm_linattn_bwd(const hm_linattn_bwd_args *a, void *stream) {
   p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
   p.dt = a->n > 0 ? a->dt : nullptr; p.a_log = a->a_log; p.d_o = a->d_o; p.ds_final = a->d_s_final;
   p.gate = a->gate; p.d_gate = a->d_gate; p.sg_b = a->sg_b; p.sg_h = a->sg_h; p.sg_t = a->sg_t;
-  p.sS = sv + sl.off_S; p.sz = (const float *)(sv + sl.off_z); p.sden = (const float *)(sv + sl.off_den);
+  p.sck = (const float *)(sv + sl.off_ck); p.sden = (const float *)(sv + sl.off_den);
+  p.wS = ws + wl.wS; p.wz = (float *)(ws + wl.wz);
   p.so32 = (const float *)(sv + sl.off_o);
   p.phq = ws + wl.phq; p.phk = ws + wl.phk; p.dnum = ws + wl.dnum;
   p.dden = (float *)(ws + wl.dden); p.Lc = (float *)(ws + wl.Lc);

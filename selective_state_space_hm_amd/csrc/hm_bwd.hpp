@@ -31,8 +31,13 @@
 //   (bwd_prep stores them turned); only the maps' backward needs the unturned
 //   phi and dphi, which are the transposed rotation applied to both (the dot
 //   product phik . dphik is the same in either frame).
+// The training forward keeps the state only at the start of every chunk range of
+// the per-chunk kernels (a checkpoint per range; the quant67 SSM lecture §4.3:
+// recompute rather than store the intermediate states); bwd_states rebuilds the
+// chunk-start states S_c, z_c from them.
 // Kernels, launched in this order on one stream:
 //   bwd_prep   (per chunk)  features, dnum, dden, L
+//   bwd_states (per (b,h), a range of chunks, first to last)  S_c, z_c from the checkpoint
 //   bwd_gstate (per (b,h), chunks last to first)  G, g at every chunk end; dS_init
 //   bwd_dq     (per (b,h), a range of chunks)  dq, partial dW_q, Q_s
 //   bwd_dk     (same)  dk, partial dW_k, K_j
@@ -109,7 +114,76 @@ __device__ __forceinline__ f32x4 mm(const Frags<T, K> &a, const T *B, int lb, f3
   return acc;
 }
 
+// acc += A * B^T as mm(), with B's fragments preloaded
+template <typename T, int K>
+__device__ __forceinline__ f32x4 mm(const T *A, int la, const Frags<T, K> &b, f32x4 acc) {
+  using M = Mma<T>;
+  constexpr int NK = K / M::KS;
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  typename M::frag a[NK];
+#pragma unroll
+  for (int s = 0; s < NK; ++s) a[s] = M::ld_contig(A + i * la + s * M::KS, g);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) acc = M::mma(a[s], b.f[s], acc);
+#pragma unroll
+  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a[s]), "v"(b.f[s]), "v"(acc));
+  return acc;
+}
+
+// S[m] = e * S[m] + A_rt B_ct^T over tiles tt = wave + 4m (rt = tt / CT, ct = tt % CT)
+// of an [F][CT * 16] accumulator, A and B rows K-contiguous in LDS.  When CT divides
+// 4 every tile of a wave has the same ct, and B's fragments are read once.
+template <typename T, int K, int NTT, int TILES, int CT>
+__device__ __forceinline__ void tiles_mm(f32x4 (&S)[NTT], float e, const T *A, const T *B, int ld) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (4 % CT == 0) {
+    Frags<T, K> fb;
+    fb.load(B + 16 * (w % CT) * ld, ld);
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TILES) S[m] = mm<T, K>(A + 16 * (tt / CT) * ld, ld, fb, S[m] * e);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NTT; ++m) {
+      const int tt = w + 4 * m;
+      if (tt < TILES) S[m] = mm<T, K>(A + 16 * (tt / CT) * ld, ld, B + 16 * (tt % CT) * ld, ld, S[m] * e);
+    }
+  }
+}
+
 template <typename T> struct Vec { typedef T type __attribute__((ext_vector_type(16 / sizeof(T)))); };
+
+// A workgroup's [ROWS][COLS] state tile, rounded to T, from accumulator tiles to
+// global rows (stride gs elements) in two steps: tile_to_lds() writes element
+// (16 rt + 4g + r, 16 ct + i) of tile tt = wave + 4m into LDS rows (stride lo);
+// after a barrier, lds_to_global() sends whole 16-byte pieces.  Four 2-byte stores
+// per tile and lane become one 16-byte store per lane and pass: measured in the
+// chunk-serial kernels, issuing the scattered stores took a quarter of their time.
+template <typename T, int NTT, int TILES, int CT>
+__device__ __forceinline__ void tile_to_lds(T *dst, int lo, const f32x4 (&X)[NTT]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int m = 0; m < NTT; ++m) {
+    const int tt = w + 4 * m;
+    if (tt < TILES) {
+      const int rt = tt / CT, ct = tt % CT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(16 * rt + 4 * g + r) * lo + 16 * ct + i] = (T)X[m][r];
+    }
+  }
+}
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void lds_to_global(T *dst, int64_t gs, const T *src, int lo) {
+  constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR;
+  typedef typename Vec<T>::type V;
+#pragma unroll
+  for (int idx = threadIdx.x; idx < N; idx += 256) {
+    const int r = idx / PPR, pc = idx % PPR;
+    *reinterpret_cast<V *>(dst + r * gs + pc * E) = *reinterpret_cast<const V *>(src + r * lo + pc * E);
+  }
+}
 
 // ROWS x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
 // beyond `valid` zeroed; 16-byte pieces, every load of a thread issued before its
@@ -508,6 +582,114 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------- bwd_states
+// The state at the start of every chunk, from the checkpoint the training forward
+// kept at the start of each chunk range: one workgroup per (b, h), range (the
+// ranges of bwd_dq / bwd_dk / bwd_dv) and share of the value columns (DS shares
+// of DV/DS; the columns of S are independent), chunks first to last,
+//   S <- e^{Lam} S + sum_j e^{Lam - L_j} phik_j v_j^T,   z likewise with v_j = 1,
+// (the forward's state update, on the phik rows bwd_prep wrote), S_c in the dtype
+// and z_c in float32 to the workspace before each chunk's update.  S [F][DV/DS]
+// lives in accumulators, tile tt = wave + 4m, as G in bwd_gstate; in the first
+// share thread 2f owns z[f].  The shares of one (b, h, range) go to one XCD
+// (they read the same phik rows through its L2).  The next chunk's operands are
+// fetched while the current chunk's products run.
+template <typename T, int DK, int FH, int DV, int DS>
+__global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
+  using namespace bw;
+  constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD, DVW = DV / DS;
+  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
+  static_assert(2 * F <= 256 && C == 64, "two threads per feature for z, 32 tokens each");
+  static_assert(DVW % 16 == 0, "whole column tiles per share");
+  __shared__ __align__(16) T sA[F * LDC_];    // (e^{Lam - L_j} phik_j)^T: [f][j]
+  __shared__ __align__(16) T sB[DVW * LDC_];  // v^T of the share's columns: [c][j]
+  constexpr int LO = DVW + PAD;
+  __shared__ __align__(16) T sOut[F * LO];    // S_c of the share's columns, rounded to T
+  __shared__ __align__(16) float sw[C];       // e^{Lam - L_j}, 0 past the sequence's end
+  __shared__ float sLam[1];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t item = blockIdx.x;  // (b, h) * ngrp + range
+  int share = 0;
+  if constexpr (DS > 1) {
+    const int64_t rnd = blockIdx.x >> 3;
+    share = (int)(rnd % DS);
+    item = (rnd / DS) * 8 + (blockIdx.x & 7);
+    if (item >= p.B * p.H * p.ngrp) return;
+  }
+  const int grp = (int)(item % p.ngrp);
+  const int64_t bh = item / p.ngrp, b = bh / p.H, h = bh % p.H;
+  const int col0 = share * DVW;
+  const bool zshare = share == 0;
+  int64_t c0, c1;
+  chunk_range(p, grp, c0, c1);
+  if (c0 >= c1) return;
+  const int64_t BLK = (int64_t)F * DV + F;
+  // checkpoint grp of this (b, h): the ranges that hold chunks, ceil(nch / per) of them
+  const int64_t per = (p.nch + p.ngrp - 1) / p.ngrp, nck = (p.nch + per - 1) / per;
+  const float *ck = p.sck + (bh * nck + grp) * BLK;
+  f32x4 S[NTT];
+#pragma unroll
+  for (int m = 0; m < NTT; ++m) {
+    S[m] = zero4();
+    const int tt = w + 4 * m;
+    if (tt < TILES) {
+      const int rt = tt / CT, ct = tt % CT;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[m][r] = ck[(16 * rt + 4 * g + r) * DV + col0 + 16 * ct + i];
+    }
+  }
+  const int zf_ = tid >> 1, zh = tid & 1;
+  const bool zown = zshare && zh == 0 && zf_ < F;
+  float zf = zown ? ck[(int64_t)F * DV + zf_] : 0.f;
+  StagedT<T, C, F> pf_k;
+  StagedT<T, C, DVW> pf_v;
+  float pf_L = 0.f;  // thread t < C: the chunk-local log-decay prefix of token t
+  auto load_chunk = [&](int64_t t0, int nv) {
+    pf_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    pf_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t + col0, p.sv_t, nv);
+    if (tid < C) pf_L = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;
+  };
+  load_chunk(c0 * C, (int)(p.n - c0 * C < C ? p.n - c0 * C : C));
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    // the state at the start of chunk c
+    tile_to_lds<T, NTT, TILES, CT>(sOut, LO, S);
+    if (zown) p.wz[(bh * p.nch + c) * F + zf_] = zf;
+    if (tid == nv - 1) sLam[0] = pf_L;
+    __syncthreads();
+    lds_to_global<T, F, DVW>((T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
+    if (tid < C) sw[tid] = tid < nv ? (p.dt ? __expf(sLam[0] - pf_L) : 1.f) : 0.f;
+    __syncthreads();
+    pf_k.store(sA, LDC_, sw);
+    pf_v.store(sB, LDC_);
+    const float eLam = p.dt ? __expf(sLam[0]) : 1.f;
+    if (c + 1 < c1) load_chunk(t0 + C, (int)(p.n - t0 - C < C ? p.n - t0 - C : C));
+    __syncthreads();
+    tiles_mm<T, C, NTT, TILES, CT>(S, eLam, sA, sB, LDC_);
+    if (zshare && zf_ < F) {
+      // z[f] += sum_j of the phik row as the products used it (rounded to the dtype):
+      // threads 2f and 2f+1 each sum 32 tokens
+      typedef T t4 __attribute__((ext_vector_type(4)));
+      const T *row = sA + zf_ * LDC_ + 32 * zh;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < 32; t += 4) {
+        const t4 a4 = *reinterpret_cast<const t4 *>(row + t);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const T x = a4[e];
+          acc += (float)x;
+        }
+      }
+      acc += __shfl_xor(acc, 1);
+      zf = eLam * zf + acc;
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- bwd_gstate
 // One workgroup per (b, h) and share of the value columns (DS shares of DV/DS;
 // the columns of G are independent), chunks from last to first: G and g at every
@@ -524,6 +706,8 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   static_assert(DVW % 16 == 0, "whole column tiles per share");
   __shared__ __align__(16) T sA[F * LDC_];    // (e^{L_t} phiq_t)^T: [f][t]
   __shared__ __align__(16) T sB[DVW * LDC_];  // dnum^T of the share's columns: [c][t]
+  constexpr int LO = DVW + PAD;
+  __shared__ __align__(16) T sOut[F * LO];    // G of the share's columns, rounded to T
   __shared__ __align__(16) float sdd[C], seL[C];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -582,22 +766,14 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     // G, g at the end of chunk c
-    T *gs = (T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
-#pragma unroll
-    for (int m = 0; m < NTT; ++m) {
-      const int tt = w + 4 * m;
-      if (tt < TILES) {
-        const int rt = tt / CT, ct = tt % CT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gs[(16 * rt + 4 * g + r) * DV + col0 + 16 * ct + i] = (T)G[m][r];
-      }
-    }
+    tile_to_lds<T, NTT, TILES, CT>(sOut, LO, G);
     if (gown) p.gz[(bh * p.nch + c) * F + gf] = gz;
     if (tid < C) {
       seL[tid] = pf_ok ? (p.dt ? __expf(pf_L) : 1.f) : 0.f;
       sdd[tid] = pf_dd;
     }
     __syncthreads();
+    lds_to_global<T, F, DVW>((T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
     pf_q.store(sA, LDC_, seL);
     pf_n.store(sB, LDC_);
     if (c > 0) {
@@ -608,14 +784,7 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     }
     const float eLam = seL[nv - 1];  // e^{Lambda} of the chunk (1 without decay)
     __syncthreads();
-#pragma unroll
-    for (int m = 0; m < NTT; ++m) {
-      const int tt = w + 4 * m;
-      if (tt < TILES) {
-        const int rt = tt / CT, ct = tt % CT;
-        G[m] = mm<T, C>(sA + 16 * rt * LDC_, LDC_, sB + 16 * ct * LDC_, LDC_, G[m] * eLam);
-      }
-    }
+    tiles_mm<T, C, NTT, TILES, CT>(G, eLam, sA, sB, LDC_);
     if (zshare && gf < F) {
       typedef T t4 __attribute__((ext_vector_type(4)));
       const T *row = sA + gf * LDC_ + 32 * gh;
@@ -692,14 +861,14 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     st_x.load((const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
     st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-    st_s.load((const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+    st_s.load((const T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phq_next.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
     float tl = 0.f, tdd = 0.f, tz = 0.f;  // per-token log-decay and dden, z at the chunk start
     if (tid < C) {
       tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
-    if (tid < F) tz = p.sz[(bh * p.nch + c) * F + tid];
+    if (tid < F) tz = p.wz[(bh * p.nch + c) * F + tid];
     st_dn.store(sDN, LN);
     st_v.store(sVQ, LVQ);
     st_x.store(sXT, LC);
@@ -1041,7 +1210,7 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
     }
     if (p.a_log) {
       // X_c = e^{Lam} (<G_end, S_c> + <g_end, z_c>): pairs spanning the whole chunk
-      const T *Sc = (const T *)p.sS + (bh * p.nch + c) * ((int64_t)F * DV);
+      const T *Sc = (const T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV);
       const T *Gc = (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
       typedef typename Vec<T>::type V;
       constexpr int EV = ep<T>(), NV = F * DV / EV, PV = (NV + 255) / 256;
@@ -1060,7 +1229,7 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
         for (int e = 0; e < EV; ++e) part += (float)sv[m][e] * (float)gv[m][e];
         x += (double)part;
       }
-      if (tid < F) x += (double)p.sz[(bh * p.nch + c) * F + tid] * p.gz[(bh * p.nch + c) * F + tid];
+      if (tid < F) x += (double)p.wz[(bh * p.nch + c) * F + tid] * p.gz[(bh * p.nch + c) * F + tid];
       for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
       if (lane == 0) sX[w] = x;
     }

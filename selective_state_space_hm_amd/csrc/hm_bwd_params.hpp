@@ -14,8 +14,11 @@ struct BwdParams {
   int64_t sg_b, sg_h, sg_t;
   const float *ds_final;     // dloss/ds_final (NULL = 0)
   const float *so32;         // saved float32 output before the gate [BH][n][dv]
-  const void *sS;            // saved chunk-start states [BH][nch][F][dv] (dtype)
-  const float *sz, *sden;    // [BH][nch][F], [BH][n]
+  const float *sck;          // saved checkpoints: the float32 state at the start of every chunk range
+                             // of the per-chunk kernels, [BH][ngrp][F*dv + F] (state layout)
+  const float *sden;         // saved denominators [BH][n]
+  void *wS;                  // workspace [BH][nch][F][dv] (dtype): chunk-start states, recomputed
+  float *wz;                 // workspace [BH][nch][F]: z at every chunk start
   void *phq, *phk, *dnum;    // workspace [BH][n][F], [BH][n][F], [BH][n][dv] (dtype)
   float *dden, *Lc;          // workspace [BH][n]
   float *eQ, *eK, *eW;       // workspace [BH][n]: per-token pieces of d log a (see bwd_decay)

@@ -60,12 +60,14 @@ struct FwdParams {
   int64_t sw_h, sdt_b, sdt_h, sdt_t;
   const void *gate;       // optional gate pre-activation, o's shape (NULL = none)
   int64_t sg_b, sg_h, sg_t;
-  // MODE_TRAIN only: the state at the start of every
-  // chunk [B*H][nchunks][F][dv] in the dtype, z there [B*H][nchunks][F] and the
-  // per-token denominator [B*H][n] (unnormalized phi(q), as used for o)
-  void *save_S;
-  float *save_z, *save_den, *save_o;  // save_o: the output before any gate, [B*H][n][dv]
+  // MODE_TRAIN only: checkpoints, the float32 state (S then z, state layout) at the
+  // start of every ck_every-th chunk [B*H][ceil(nchunks / ck_every)][F*dv + F], the
+  // per-token denominator [B*H][n] (unnormalized phi(q), as used for o) and the
+  // output before any gate [B*H][n][dv] in float32
+  float *save_ck, *save_den, *save_o;
   int64_t nchunks;
+  int64_t ck_every;       // chunks per checkpoint (the backward's chunk ranges)
+  int64_t nck;            // checkpoints per (b, h)
   int64_t seg_len;        // tokens per segment, a multiple of CHUNK
   int64_t nitems;         // (b,h,segment) items in this launch
   int nseg;               // segments of the whole sequence
@@ -479,9 +481,9 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       frag qf[FULL ? KF : 1], kf[KF];  // phiQ, phiK of token tile wv (tile order)
       // ---- half A: featurize token tile wv of chunk j
       if constexpr (SAVE) {
-        if (j < nch && wv == 2 && half == 0) {
-          const float *zp = sZ[(j + 1) & 1];  // z at the start of chunk j
-          float *zs = p.save_z + (bh * p.nchunks + tf / C) * F;
+        if (j < nch && wv == 2 && half == 0 && (tf / C) % p.ck_every == 0) {
+          const float *zp = sZ[(j + 1) & 1];  // z at the start of chunk j, a checkpoint
+          float *zs = p.save_ck + (bh * p.nck + tf / C / p.ck_every) * BLK + (int64_t)F * p.dv;
           for (int i = lane; i < F; i += 64) zs[i] = zp[i];
         }
       }
@@ -772,19 +774,19 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       if (j >= 1) {
         if constexpr (SAVE) issue_gate_rows(ts);
         if constexpr (SAVE) {
-          {
-            // the state at the start of chunk j-1 (this iteration's read-out state)
-            // the training pass runs with one workgroup per (b, h), so the row stride
-            // is the compile-time DW: one base address per feature tile, the rest
-            // instruction offsets (a run-time stride kept 64 addresses live and spilled)
-            T *sv = (T *)p.save_S + (bh * p.nchunks + ts / C) * ((int64_t)F * DW) + ncol + col;
+          if ((ts / C) % p.ck_every == 0) {
+            // a checkpoint: the float32 state at the start of chunk j-1 (this
+            // iteration's read-out state).  The training pass runs with one workgroup
+            // per (b, h), so the row stride is the compile-time DW: one base address per
+            // feature tile, the rest instruction offsets
+            float *sv = p.save_ck + (bh * p.nck + ts / C / p.ck_every) * BLK + ncol + col;
 #pragma unroll
             for (int t = 0; t < NFT; ++t) {
-              T *rowp = sv + (16 * t + 4 * g) * DW;
+              float *rowp = sv + (16 * t + 4 * g) * DW;
 #pragma unroll
               for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int jj = 0; jj < NTW; ++jj) rowp[r * DW + 16 * jj] = (T)S[jj][t][r];
+                for (int jj = 0; jj < NTW; ++jj) rowp[r * DW + 16 * jj] = S[jj][t][r];
             }
           }
         }

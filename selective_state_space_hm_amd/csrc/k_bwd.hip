@@ -10,6 +10,18 @@ template <typename T, int DK, int FH, int DV, bool ROPE>
 void launch_bwd(const BwdParams &p, hipStream_t s) {
   const unsigned BH = (unsigned)(p.B * p.H);
   if (p.nch > 0) hipLaunchKernelGGL((bwd_prep<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.nch), dim3(256), 0, s, p);
+  // the chunk-start states, recomputed from the forward's checkpoints; each range is
+  // a chain of chunks, so the value columns are split in two to put two workgroups
+  // on every compute unit (measured on the Pythia layer: 75 us unsplit, 66 us in
+  // two, 89 us in four, where the redundant phi(k) reads take over)
+  if (p.nch > 0) {
+    const unsigned items = BH * (unsigned)p.ngrp;
+    if constexpr (DV % 32 == 0) {
+      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 2>), dim3((items + 7) / 8 * 16), dim3(256), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 1>), dim3(items), dim3(256), 0, s, p);
+    }
+  }
   // the gradient-state pass visits the chunks one after another, so with fewer
   // (b, h) than compute units it splits the value columns in two
   // (a four-way split measured slower on the Pythia layer: 105 vs 91 us)

@@ -313,7 +313,9 @@ def test_backward_validation_and_sizes():
     a = hm.FwdArgs(dtype=hm.HM_BF16, B=8, H=16, n=2048, d=128, f=64, dv=128)
     st, sb = hm.call_save_size(a)
     expect(st, hm.HM_OK)
-    assert sb == BH * 32 * F * 128 * 2 + BH * 32 * F * 4 + BH * n * 4 + BH * n * 128 * 4
+    # float32 checkpoints at the start of the backward's chunk ranges (256 workgroups over
+    # 128 (b, h): 2 ranges of 16 chunks each), denominators, float32 output before the gate
+    assert sb == BH * 2 * (F * 128 + F) * 4 + BH * n * 4 + BH * n * 128 * 4
     expect(hm.call_fwd(fwd(B=8, segments=1, save=A + 0xc000000, save_bytes=sb - 1)), hm.HM_ERR_WORKSPACE)
     assert "save" in hm.last_error()
     expect(hm.call_fwd(fwd(save=A + 0xc000000, save_bytes=sb, dsplit=2)), hm.HM_ERR_UNSUPPORTED)
