@@ -407,10 +407,10 @@ def main():
                     help="least wall time of back-to-back calls before each timed loop (clock ramp)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline and the other prefill configs only")
-    ap.add_argument("--part", choices=["all", "headline", "pythia", "decay", "decode", "copy"], default="all",
+    ap.add_argument("--part", choices=["all", "headline", "pythia", "decay", "decode", "pc", "copy"], default="all",
                     help="headline/pythia/decay: one prefill config only (for profiling runs); decode: only the "
-                         "decode benchmark; copy: one 256 MiB device copy, the reference run that calibrates "
-                         "rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+                         "decode benchmark; pc: only the per-channel-decay prefill and decode; copy: one 256 MiB "
+                         "device copy, the reference run that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--chunk", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -435,6 +435,10 @@ def main():
     ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
     if args.part == "decode":
         print(json.dumps({"decode": bench_decode(torch, hm, inputs, dev, ws)}), flush=True)
+        return
+    if args.part == "pc":
+        print(json.dumps({"pc_prefill": bench_pc_prefill(torch, hm, inputs, dev, args),
+                          "pc_decode": bench_pc_decode(torch, hm, inputs, dev)}), flush=True)
         return
     if args.part in ("pythia", "decay"):
         c = inputs.pythia1b() if args.part == "pythia" else inputs.mamba_decay()
