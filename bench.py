@@ -438,6 +438,7 @@ def main():
         return
     if args.part == "pc":
         print(json.dumps({"pc_prefill": bench_pc_prefill(torch, hm, inputs, dev, args),
+                          "pc_long": bench_pc_long(torch, hm, inputs, dev, args),
                           "pc_decode": bench_pc_decode(torch, hm, inputs, dev)}), flush=True)
         return
     if args.part in ("pythia", "decay"):
@@ -504,6 +505,7 @@ def main():
         result["featurize"] = bench_featurize(torch, hm, inputs, dev, args)
         result["prefill_extra"] = bench_prefill_extra(torch, hm, inputs, dev, ws, args)
         result["prefill_extra"].append(bench_pc_prefill(torch, hm, inputs, dev, args))
+        result["prefill_extra"].append(bench_pc_long(torch, hm, inputs, dev, args))
         result["decode"] = bench_decode(torch, hm, inputs, dev, ws)
         result["decode"]["per_channel_step"] = bench_pc_decode(torch, hm, inputs, dev)
     if not args.no_cpu_baseline:
@@ -633,6 +635,37 @@ def bench_pc_prefill(torch, hm, inputs, dev, args):
                          "alu_time_ms": alu_s * 1e3, "frac": alu_s / (ms * 1e-3),
                          "model": "1 exp2 (quarter rate) + 7 full-rate VALU ops per (token, channel, state)"},
             "kernel": "hm::pc_fwd_kernel<bf16,128,64,128,64,8>"}
+
+
+def bench_pc_long(torch, hm, inputs, dev, args):
+    """Per-channel-decay prefill on the long-context shape (B=1, H=16, n=131072, bf16):
+    32 workgroups cover the sequence unsplit; the automatic plan scans it in segments
+    (segment pass, element-wise composition, full pass).  Both timed."""
+    c = inputs.make_pc("pc-long", 1, 16, 131072, 128, 64, 128, torch.bfloat16, seed=0)
+    log(f"[bench] per-channel decay prefill B={c.B} H={c.H} n={c.n}: segmented and unsplit")
+    g = {k: getattr(c, k).to(dev) for k in ("q", "k", "v", "w_q", "w_k", "dt", "a_log")}
+    o = torch.empty_like(g["v"])
+    plan = hm.hm_linattn_pc_plan(g["q"], g["v"], g["w_q"])
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+
+    def run(segments):
+        return lambda: hm.hm_linattn_pc_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], o=o,
+                                            segments=segments, workspace=ws)
+
+    ms_seg = time_launches(run(0), 5, 2, torch, args.warmup_ms)[0]
+    ms_one = time_launches(run(1), 2, 1, torch, 0.0)[0]
+    elems = c.B * c.H * c.n * c.dv * 2 * c.f
+    alu_s = elems * PC_SIMD_CYCLES_PER_ELEM / SIMD_CLOCKS_PER_S
+    seg_len = -(-(-(-c.n // 64)) // plan) * 64
+    work = (c.n + (plan - 1) * seg_len) / c.n  # scan work of both passes over the method's
+    return {"workload": f"per-channel decay long context B={c.B} H={c.H} n={c.n} d={c.d} f={c.f} dv={c.dv} bf16",
+            "segments": plan, "ms": ms_seg, "tokens_per_s": c.B * c.n / (ms_seg * 1e-3),
+            "ms_unsplit": ms_one, "speedup_vs_unsplit": ms_one / ms_seg,
+            "roofline": {"bound": "alu", "alu_time_ms": alu_s * 1e3, "frac": alu_s / (ms_seg * 1e-3),
+                         "scan_work_over_method": work,
+                         "model": "1 exp2 (quarter rate) + 7 full-rate VALU ops per (token, channel, state) of "
+                                  "the method; the segment pass repeats the scan of all segments but the last"},
+            "kernels": "hm::pc_fwd_kernel<...,LOCAL> + pc_combine_kernel + hm::pc_fwd_kernel<...>"}
 
 
 def bench_pc_decode(torch, hm, inputs, dev):

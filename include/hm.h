@@ -93,7 +93,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 7
+#define HM_ABI_VERSION 8
 
 typedef enum {
   HM_OK = 0,
@@ -387,6 +387,18 @@ hm_status hm_causal_conv(const hm_causal_conv_args *args, void *stream);
  * matrix products of hm_linattn_fwd): one exponential per token, channel and state,
  * float32 throughout, phi kept in float32.  q, k, v, w_q, w_k, o, dt and a_log
  * are required whenever B*H*n > 0 (with n = 0 only the state is copied or zeroed).
+ * segments: 0 = automatic, else the number of sequence segments scanned in
+ * parallel (at most one per 64-token chunk).  A segment pass scans every segment
+ * but the last from a zero state; the start states then follow by the
+ * element-wise affine composition (a segment's decay product is
+ * exp(-exp(A_log[c,n]) * sum of Delta_t[c] over it), [SSM] §4.2), and the full
+ * pass scans every segment from its start state.  This doubles the scan work of
+ * all segments but the last, so the automatic plan splits only when fewer than 65
+ * workgroups (one per (b, h) and 64 channels) would cover the GPU's 256 compute
+ * units: then into up to 256 / workgroups segments of at least four chunks.
+ * workspace: hm_linattn_pc_fwd_workspace_size() bytes, 16-byte aligned (NULL when
+ * that size is 0): per (b, h) one state block per segment and dv floats per
+ * segment boundary.
  * Built: bf16 (d, f, dv) = (128, 64, 128), (64, 32, 64); f32 (16, 16, 16), (32, 16, 32).
  */
 typedef struct {
@@ -404,9 +416,18 @@ typedef struct {
   int64_t B, H, n, d, f, dv;
   int64_t sq_b, sq_h, sq_t, sk_b, sk_h, sk_t, sv_b, sv_h, sv_t, so_b, so_h, so_t, sg_b, sg_h, sg_t;
   int64_t sw_h, sdt_b, sdt_h, sdt_t, sa_h;
+  int32_t segments;         /* 0 = automatic (see above) */
+  int32_t reserved2;
+  void *workspace;
+  size_t workspace_bytes;
 } hm_linattn_pc_args;
 
 hm_status hm_linattn_pc_fwd(const hm_linattn_pc_args *args, void *stream);
+/* The segment count hm_linattn_pc_fwd will use for these sizes, and the workspace
+ * bytes it needs (0 when it runs as one segment).  Only the sizes, dtype and
+ * segments of args are read. */
+hm_status hm_linattn_pc_fwd_plan(const hm_linattn_pc_args *args, int32_t *segments);
+hm_status hm_linattn_pc_fwd_workspace_size(const hm_linattn_pc_args *args, size_t *bytes);
 
 /*
  * hm_linattn_pc_step — one decode token per (b, h) of the per-channel scan above

@@ -710,8 +710,75 @@ hm_status validate_a_log_pc(const float *a_log, int64_t sa_h, int64_t dv, int64_
 
 extern "C" {
 
+// Segments of the per-channel prefill: automatic when fewer than 65 workgroups
+// (one per (b, h) and cpw channels) would run, up to 256 / workgroups segments of
+// at least four chunks; workspace = one state block per segment and (b, h) plus dv
+// floats per segment boundary.
+struct PcPlan {
+  int nseg;
+  int64_t seg_len;
+  size_t off_dsum, bytes;
+};
+PcPlan pc_plan(const hm_linattn_pc_args *a, int cpw) {
+  const int64_t BH = a->B * a->H, nch = (a->n + hm::CHUNK - 1) / hm::CHUNK, F = 2 * a->f;
+  int64_t ns = a->segments;
+  if (ns <= 0) {
+    const int64_t wgs = BH * (a->dv / cpw);
+    ns = 1;
+    if (wgs > 0 && wgs <= 64) {
+      ns = 256 / wgs;
+      if (ns > nch / 4) ns = nch / 4;
+    }
+  }
+  if (ns > nch) ns = nch;
+  if (ns < 1) ns = 1;
+  PcPlan pl{};
+  pl.seg_len = ((nch + ns - 1) / ns) * hm::CHUNK;
+  pl.nseg = a->n > 0 ? (int)((a->n + pl.seg_len - 1) / pl.seg_len) : 1;
+  if (pl.nseg <= 1) {
+    pl.nseg = 1;
+    pl.seg_len = a->n;
+    return pl;
+  }
+  pl.off_dsum = align256((size_t)(BH * pl.nseg * 2 * a->dv * F) * 4);
+  pl.bytes = pl.off_dsum + (size_t)(BH * (pl.nseg - 1) * a->dv) * 4;
+  return pl;
+}
+hm_status pc_plan_checked(const hm_linattn_pc_args *a, PcPlan *pl) {
+  if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
+  if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
+    return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f, dv >= 1");
+  if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0 (0 = automatic)");
+  const hm::PcEntry *e = find_pc(a->dtype, a->d, a->f, a->dv);
+  if (!e)
+    return fail(HM_ERR_UNSUPPORTED, "no per-channel kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv);
+  *pl = pc_plan(a, e->cpw);
+  return ok();
+}
+
+hm_status hm_linattn_pc_fwd_plan(const hm_linattn_pc_args *a, int32_t *segments) {
+  if (!segments) return fail(HM_ERR_NULL, "segments is NULL");
+  PcPlan pl{};
+  const hm_status st = pc_plan_checked(a, &pl);
+  if (st != HM_OK) return st;
+  *segments = pl.nseg;
+  return ok();
+}
+
+hm_status hm_linattn_pc_fwd_workspace_size(const hm_linattn_pc_args *a, size_t *bytes) {
+  if (!bytes) return fail(HM_ERR_NULL, "bytes is NULL");
+  PcPlan pl{};
+  const hm_status st = pc_plan_checked(a, &pl);
+  if (st != HM_OK) return st;
+  *bytes = pl.bytes;
+  return ok();
+}
+
 hm_status hm_linattn_pc_fwd(const hm_linattn_pc_args *a, void *stream) {
   if (!a) return fail(HM_ERR_NULL, "args is NULL");
+  if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0 (0 = automatic)");
   if (a->dtype != HM_F32 && a->dtype != HM_BF16) return fail(HM_ERR_DTYPE, "dtype %d is not HM_F32 or HM_BF16", a->dtype);
   if (a->B < 0 || a->H < 0 || a->n < 0 || a->d <= 0 || a->f <= 0 || a->dv <= 0)
     return fail(HM_ERR_SHAPE, "sizes must be B, H, n >= 0 and d, f, dv >= 1");
@@ -749,8 +816,21 @@ hm_status hm_linattn_pc_fwd(const hm_linattn_pc_args *a, void *stream) {
   if (!e)
     return fail(HM_ERR_UNSUPPORTED, "no per-channel kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
                 (long long)a->d, (long long)a->f, (long long)a->dv);
+  const PcPlan pl = pc_plan(a, e->cpw);
+  if (pl.bytes > 0) {
+    if (!a->workspace || a->workspace_bytes < pl.bytes)
+      return fail(HM_ERR_WORKSPACE, "workspace of %zu bytes needed for %d segments (got %zu)", pl.bytes, pl.nseg,
+                  a->workspace ? a->workspace_bytes : (size_t)0);
+    if (!aligned16(a->workspace)) return fail(HM_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
   if (BH == 0 || (a->n == 0 && !a->s_final)) return ok();
   hm::PcParams p{};
+  p.nseg = pl.nseg;
+  p.seg_len = pl.seg_len;
+  if (pl.nseg > 1) {
+    p.slots = (float *)a->workspace;
+    p.dsum = (float *)((char *)a->workspace + pl.off_dsum);
+  }
   p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
   p.dt = a->dt; p.a_log = a->a_log; p.s_init = a->s_init; p.s_final = a->s_final; p.o = a->o; p.gate = a->gate;
   p.B = a->B; p.H = a->H; p.n = a->n;

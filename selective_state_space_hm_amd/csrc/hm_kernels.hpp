@@ -54,6 +54,7 @@ struct PcParams;
 struct PcStepParams;
 struct PcEntry {
   int dtype, dk, fh, dv;
+  int cpw;  // value channels per prefill workgroup
   void (*fwd)(const PcParams &, hipStream_t);
   void (*step)(const PcStepParams &, hipStream_t);
 };

@@ -35,6 +35,16 @@ struct PcParams {
   int rope_dims;             // rotary encoding of the features (0 = off)
   float rope_base;
   const int64_t *rope_pos0;  // position of token 0 per batch row (NULL = 0)
+  // Segments: the sequence is cut into nseg segments of seg_len tokens (a multiple
+  // of the 64-token chunk; nseg = 1: one segment, seg_len >= n).  With nseg > 1 the
+  // workspace holds, per (b, h), slots [nseg][2][dv][F] (slot s: the start state of
+  // segment s; the segment pass first leaves the end state of segment s - 1, from a
+  // zero start, in slot s) and dsum [nseg - 1][dv] (the sum of Delta_t[c] over
+  // segment s).
+  int64_t seg_len;
+  int nseg;
+  float *slots;
+  float *dsum;
 };
 
 template <int CTRL>
@@ -54,15 +64,17 @@ __device__ __forceinline__ float group_lanes_sum(float v) {
 }
 
 // ---------------------------------------------------------------- prefill
-// One workgroup per (b, h, group of CPW channels), CPW x LPC threads: thread
+// One workgroup per (b, h, segment, group of CPW channels), CPW x LPC threads: thread
 // (channel cl, lane nb of LPC) holds the NPL = F/LPC states n0 .. n0+NPL-1 of its
 // channel for both copies, in registers, for the whole sequence.  Per chunk of 64
 // tokens the waves featurize q and k on the MFMA into LDS (float32 rows, each
 // thread's NPL features padded by 4 so that the LPC distinct 16-byte reads of a
 // wave fall in distinct banks), stage Delta and v, then scan the chunk token by
 // token: NPL exponentials and FMAs per thread, the readout summed over the LPC
-// lanes of a channel with DPP.
-template <typename T, int DK, int FH, int DV, int CPW, int LPC>
+// lanes of a channel with DPP.  LOCAL: the segment pass (segments 0 .. nseg-2 from
+// a zero state; end state and the segment's Delta sums to the workspace, no
+// read-out).  Otherwise every segment from its start state (s_init or its slot).
+template <typename T, int DK, int FH, int DV, int CPW, int LPC, bool LOCAL>
 __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -79,13 +91,30 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
   const int tid = threadIdx.x, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int NG = DV / CPW;
-  const int64_t bh = blockIdx.x / NG, b = bh / p.H, h = bh % p.H;
+  const int nrun = LOCAL ? p.nseg - 1 : p.nseg;  // segments of this launch
+  const int64_t item = blockIdx.x / NG, bh = item / nrun, b = bh / p.H, h = bh % p.H;
+  const int seg = (int)(item % nrun);
   const int grp = (int)(blockIdx.x % NG);
   const int cl = tid / LPC, nb = tid % LPC, c = grp * CPW + cl, n0 = nb * NPL;
+  const int64_t ts = seg * p.seg_len;                                   // first token of the segment
+  const int64_t nloc = p.n - ts < p.seg_len ? p.n - ts : p.seg_len;     // its tokens
+  constexpr int64_t SB = 2 * (int64_t)DV * F;                           // state block
+  // where the segment starts from and where its end state goes
+  const float *sbase = nullptr;
+  float *fbase = nullptr;
+  if (LOCAL) {
+    fbase = p.slots + (bh * p.nseg + seg + 1) * SB;
+  } else if (p.nseg > 1) {
+    sbase = p.slots + (bh * p.nseg + seg) * SB;
+    fbase = seg == p.nseg - 1 && p.s_final ? p.s_final + bh * SB : nullptr;
+  } else {
+    sbase = p.s_init ? p.s_init + bh * SB : nullptr;
+    fbase = p.s_final ? p.s_final + bh * SB : nullptr;
+  }
 
   // the thread's A row (times log2 e) and states; with no token W and A are not read
   float A2[NPL], hn[NPL], hd[NPL];
-  if (p.n > 0) {
+  if (nloc > 0) {
     const T *wq = (const T *)p.wq + h * p.sw_h, *wk = (const T *)p.wk + h * p.sw_h;
     for (int i = tid; i < DK * FH; i += NT) {
       sW[0][(i % FH) * LDW + i / FH] = wq[i];
@@ -101,7 +130,7 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
     }
   }
   {
-    const float *si = p.s_init ? p.s_init + bh * (2 * (int64_t)DV * F) + (int64_t)c * F + n0 : nullptr;
+    const float *si = sbase ? sbase + (int64_t)c * F + n0 : nullptr;
 #pragma unroll
     for (int k = 0; k < NPL; k += 4) {
       const f32x4 sn = si ? *reinterpret_cast<const f32x4 *>(si + k) : zero4();
@@ -113,12 +142,12 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
       }
     }
   }
-  const T *Q = (const T *)p.q + b * p.sq_b + h * p.sq_h;
-  const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
-  const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h + grp * CPW;
-  const float *DT = p.dt + b * p.sdt_b + h * p.sdt_h + grp * CPW;
-  T *O = (T *)p.o + b * p.so_b + h * p.so_h + grp * CPW;
-  const T *G = p.gate ? (const T *)p.gate + b * p.sg_b + h * p.sg_h + grp * CPW : nullptr;
+  const T *Q = (const T *)p.q + b * p.sq_b + h * p.sq_h + ts * p.sq_t;
+  const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h + ts * p.sk_t;
+  const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h + ts * p.sv_t + grp * CPW;
+  const float *DT = p.dt + b * p.sdt_b + h * p.sdt_h + ts * p.sdt_t + grp * CPW;
+  T *O = (T *)p.o + b * p.so_b + h * p.so_h + ts * p.so_t + grp * CPW;
+  const T *G = p.gate ? (const T *)p.gate + b * p.sg_b + h * p.sg_h + ts * p.sg_t + grp * CPW : nullptr;
 
   // A chunk's q, k rows, dt and v are loaded into registers one chunk ahead, during
   // the previous chunk's scan: with one workgroup per compute unit nothing else
@@ -128,11 +157,12 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
   frag xn[TPW][KD];
   float dtn[IT], vnx[IT];
   auto prefetch = [&](int64_t tc) {
-    const int nvc = (int)(p.n - tc < C ? p.n - tc : C);
+    const int nvc = (int)(nloc - tc < C ? nloc - tc : C);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int task = wv + u * NW;
       const int proj = task >> 2, tok = 16 * (task & 3) + col;
+      if (LOCAL && proj == 0) continue;  // the segment pass needs no phi(q)
       const T *X = (proj == 0 ? Q + (tc + tok) * p.sq_t : K + (tc + tok) * p.sk_t);
 #pragma unroll
       for (int s = 0; s < KD; ++s) xn[u][s] = task < 8 && tok < nvc ? M::ld_contig(X + s * M::KS, g) : frag{};
@@ -145,10 +175,11 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
       vnx[m] = ok ? (float)V[(tc + tt) * p.sv_t + cc] : 0.f;
     }
   };
-  if (p.n > 0) prefetch(0);
+  if (nloc > 0) prefetch(0);
+  double dsum = 0.0;  // LOCAL: the segment's sum of Delta_t[c]
 
-  for (int64_t t0 = 0; t0 < p.n; t0 += C) {
-    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+  for (int64_t t0 = 0; t0 < nloc; t0 += C) {
+    const int nv = (int)(nloc - t0 < C ? nloc - t0 : C);
     __syncthreads();  // W staged; the previous chunk's o rows are stored
     // featurize: eight 16-token tasks (q tiles 0-3, k tiles 0-3) over the waves
 #pragma unroll
@@ -156,12 +187,13 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
       const int task = wv + u * NW;
       if (task >= 8) continue;
       const int proj = task >> 2, tok = 16 * (task & 3) + col;
+      if (LOCAL && proj == 0) continue;
       const frag *xf = xn[u];
       f32x4 ph[NFT];
       const float sum = feature_tiles<T, DK, FH>(xf, sW[proj], ph);
       const float inv = proj == 1 ? __builtin_amdgcn_rcpf(sum) : 1.f;  // phi(q)'s scale cancels in o
       if (p.rope_dims > 0) {
-        const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + t0 + tok);
+        const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + ts + t0 + tok);
         rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);
       }
       float *row = sPh[proj] + tok * ROW;
@@ -180,9 +212,10 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
       }
     }
     __syncthreads();
-    if (t0 + C < p.n) prefetch(t0 + C);
+    if (t0 + C < nloc) prefetch(t0 + C);
     for (int t = 0; t < nv; ++t) {
       const float dl = sD[t * CPW + cl], dlv = dl * sVO[t * CPW + cl];
+      if constexpr (LOCAL) dsum += (double)dl;
       const float *pk = sPh[1] + t * ROW + nb * BLK, *pq = sPh[0] + t * ROW + nb * BLK;
       float num = 0.f, den = 0.f;
 #pragma unroll
@@ -199,29 +232,61 @@ __global__ __launch_bounds__(CPW * LPC) void pc_fwd_kernel(const PcParams p) {
           // 12.9 VALU instructions per (token, channel, state), 8 of arithmetic)
           hn[k + e] = __builtin_fmaf(k4[e], dlv, a * hn[k + e]);
           hd[k + e] = __builtin_fmaf(k4[e], dl, a * hd[k + e]);
-          num = __builtin_fmaf(q4[e], hn[k + e], num);
-          den = __builtin_fmaf(q4[e], hd[k + e], den);
+          if constexpr (!LOCAL) {
+            num = __builtin_fmaf(q4[e], hn[k + e], num);
+            den = __builtin_fmaf(q4[e], hd[k + e], den);
+          }
         }
       }
-      num = group_lanes_sum<LPC>(num);
-      den = group_lanes_sum<LPC>(den);
-      if (nb == 0) sVO[t * CPW + cl] = num / den;  // v[t][cl] was read by every lane of the channel above
+      if constexpr (!LOCAL) {
+        num = group_lanes_sum<LPC>(num);
+        den = group_lanes_sum<LPC>(den);
+        if (nb == 0) sVO[t * CPW + cl] = num / den;  // v[t][cl] was read by every lane of the channel above
+      }
     }
     __syncthreads();
-    for (int i = tid; i < nv * CPW; i += NT) {
+    for (int i = tid; !LOCAL && i < nv * CPW; i += NT) {
       const int tt = i / CPW, cc = i % CPW;
       float o = sVO[i];
       if (G) o = (float)to_elem<T>(o) * silu_f32((float)G[(t0 + tt) * p.sg_t + cc]);
       O[(t0 + tt) * p.so_t + cc] = to_elem<T>(o);
     }
   }
-  if (p.s_final) {
-    float *sf = p.s_final + bh * (2 * (int64_t)DV * F) + (int64_t)c * F + n0;
+  if constexpr (LOCAL) {
+    if (nb == 0) p.dsum[(bh * (p.nseg - 1) + seg) * DV + c] = (float)dsum;
+  }
+  if (fbase) {
+    float *sf = fbase + (int64_t)c * F + n0;
 #pragma unroll
     for (int k = 0; k < NPL; k += 4) {
       *reinterpret_cast<f32x4 *>(sf + k) = f32x4{hn[k], hn[k + 1], hn[k + 2], hn[k + 3]};
       *reinterpret_cast<f32x4 *>(sf + DV * F + k) = f32x4{hd[k], hd[k + 1], hd[k + 2], hd[k + 3]};
     }
+  }
+}
+
+// Start states of the segments from the segment pass: slot 0 gets s_init (or zero),
+// then for s = 0 .. nseg-2
+//   slot[s+1] <- D_s * slot[s] + slot[s+1],   D_s[c][n] = 2^(A2[c][n] dsum_s[c]),
+// with A2 = -exp(A_log) log2(e) as in the scan: the product of the segment's per-token
+// decays a_t[c][n] = 2^(A2[c][n] Delta_t[c]) (the affine composition of the
+// associative scan, quant67 SSM lecture §4.2, element by element).  One thread per
+// (b, h, state element); the chain over the segments is short.
+template <int DV, int F>
+__global__ __launch_bounds__(256) void pc_combine_kernel(const PcParams p) {
+  constexpr int64_t SB = 2 * (int64_t)DV * F;
+  constexpr float L2E = 1.4426950408889634f;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x, bh = idx / SB, e = idx % SB;
+  if (bh >= p.B * p.H) return;
+  const int64_t h = bh % p.H, cn = e % (DV * F), c = cn / F;
+  const float A2 = -expf(p.a_log[h * p.sa_h + cn]) * L2E;
+  float *slot = p.slots + bh * p.nseg * SB + e;
+  float s = p.s_init ? p.s_init[bh * SB + e] : 0.f;
+  slot[0] = s;
+  for (int sg = 0; sg + 1 < p.nseg; ++sg) {
+    const float d = __builtin_amdgcn_exp2f(A2 * p.dsum[(bh * (p.nseg - 1) + sg) * DV + c]);
+    s = __builtin_fmaf(d, s, slot[(sg + 1) * SB]);
+    slot[(sg + 1) * SB] = s;
   }
 }
 

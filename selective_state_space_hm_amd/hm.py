@@ -94,7 +94,8 @@ class PcArgs(C.Structure):
                 ("sq_b", i64), ("sq_h", i64), ("sq_t", i64), ("sk_b", i64), ("sk_h", i64), ("sk_t", i64),
                 ("sv_b", i64), ("sv_h", i64), ("sv_t", i64), ("so_b", i64), ("so_h", i64), ("so_t", i64),
                 ("sg_b", i64), ("sg_h", i64), ("sg_t", i64),
-                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64), ("sa_h", i64)]
+                ("sw_h", i64), ("sdt_b", i64), ("sdt_h", i64), ("sdt_t", i64), ("sa_h", i64),
+                ("segments", i32), ("reserved2", i32), ("workspace", p_void), ("workspace_bytes", C.c_size_t)]
 
 
 class PcStepArgs(C.Structure):
@@ -120,8 +121,8 @@ _lib = None
 EXPORTS = ["hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
            "hm_linattn_fwd_noalloc",
            "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
-           "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step", "hm_status_string",
-           "hm_last_error_message", "hm_abi_version", "hm_args_size"]
+           "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_fwd_plan", "hm_linattn_pc_fwd_workspace_size",
+           "hm_linattn_pc_step", "hm_status_string", "hm_last_error_message", "hm_abi_version", "hm_args_size"]
 
 
 def lib():
@@ -142,11 +143,14 @@ def lib():
         L.hm_linattn_bwd_workspace_size.argtypes = [C.POINTER(BwdArgs), C.POINTER(C.c_size_t)]
         L.hm_linattn_bwd.argtypes = [C.POINTER(BwdArgs), p_void]
         L.hm_linattn_pc_fwd.argtypes = [C.POINTER(PcArgs), p_void]
+        L.hm_linattn_pc_fwd_plan.argtypes = [C.POINTER(PcArgs), C.POINTER(i32)]
+        L.hm_linattn_pc_fwd_workspace_size.argtypes = [C.POINTER(PcArgs), C.POINTER(C.c_size_t)]
         L.hm_linattn_pc_step.argtypes = [C.POINTER(PcStepArgs), p_void]
         for fn in ("hm_featurize", "hm_linattn_fwd_workspace_size", "hm_linattn_fwd_plan", "hm_linattn_fwd",
                    "hm_linattn_fwd_noalloc",
                    "hm_linattn_step", "hm_causal_conv", "hm_linattn_save_size", "hm_linattn_bwd_workspace_size",
-                   "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_step"):
+                   "hm_linattn_bwd", "hm_linattn_pc_fwd", "hm_linattn_pc_fwd_plan",
+                   "hm_linattn_pc_fwd_workspace_size", "hm_linattn_pc_step"):
             getattr(L, fn).restype = C.c_int
         L.hm_status_string.argtypes = [C.c_int]
         L.hm_status_string.restype = C.c_char_p
@@ -219,6 +223,18 @@ def call_bwd_workspace_size(args: BwdArgs):
 
 def call_pc_fwd(args: PcArgs, stream=None) -> int:
     return lib().hm_linattn_pc_fwd(C.byref(args), stream)
+
+
+def call_pc_plan(args: PcArgs):
+    n = i32(0)
+    st = lib().hm_linattn_pc_fwd_plan(C.byref(args), C.byref(n))
+    return st, n.value
+
+
+def call_pc_workspace_size(args: PcArgs):
+    n = C.c_size_t(0)
+    st = lib().hm_linattn_pc_fwd_workspace_size(C.byref(args), C.byref(n))
+    return st, n.value
 
 
 def call_pc_step(args: PcStepArgs, stream=None) -> int:
@@ -614,12 +630,23 @@ def _a_log_stride(a_log, dv, F):
     return a_log.stride(0) if a_log.dim() == 3 else 0
 
 
+def hm_linattn_pc_plan(q, v, w_q, segments=0) -> int:
+    """The number of sequence segments hm_linattn_pc_fwd runs for these sizes."""
+    B, H, n, d = q.shape
+    a = PcArgs(dtype=_code(q), B=B, H=H, n=n, d=d, f=w_q.shape[-1], dv=v.shape[-1], segments=segments)
+    st, ns = call_pc_plan(a)
+    _check(st)
+    return ns
+
+
 def hm_linattn_pc_fwd(q, k, v, w_q, w_k, dt, a_log, s_init=None, s_final=None, o=None, gate=None,
-                      rope_dims=0, rope_base=10000.0, rope_pos0=None):
+                      rope_dims=0, rope_base=10000.0, rope_pos0=None, segments=0, workspace=None):
     """Prefill with a decay per value channel and state (the pages' Mamba-1 wiring):
     dt float32 [B, H, n, dv] (the step size before softplus), a_log float32 [dv, 2f] or
     [H, dv, 2f].  Returns o [B, H, n, dv]; s_final (if given) receives the float32
-    state [B, H, 2*dv*2f] (Sn [dv][2f] then Sd [dv][2f])."""
+    state [B, H, 2*dv*2f] (Sn [dv][2f] then Sd [dv][2f]).  segments: 0 = automatic,
+    else the number of sequence segments scanned in parallel; workspace: a uint8
+    device buffer (allocated here when None or too small)."""
     _check_attn(q, k, v, w_q, w_k, o, gate)
     B, H, n, d = q.shape
     dv = v.shape[-1]
@@ -642,8 +669,16 @@ def hm_linattn_pc_fwd(q, k, v, w_q, w_k, dt, a_log, s_init=None, s_final=None, o
                so_b=o.stride(0), so_h=o.stride(1), so_t=o.stride(2),
                sg_b=gate.stride(0) if gate is not None else 0, sg_h=gate.stride(1) if gate is not None else 0,
                sg_t=gate.stride(2) if gate is not None else 0, sw_h=_w_strides(w_q),
-               sdt_b=dt.stride(0), sdt_h=dt.stride(1), sdt_t=dt.stride(2), sa_h=_a_log_stride(a_log, dv, 2 * f))
+               sdt_b=dt.stride(0), sdt_h=dt.stride(1), sdt_t=dt.stride(2), sa_h=_a_log_stride(a_log, dv, 2 * f),
+               segments=segments)
     _rope(a, B, rope_dims, rope_base, rope_pos0)
+    st, nbytes = call_pc_workspace_size(a)
+    _check(st)
+    if nbytes > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check(call_pc_fwd(a, _stream()))
     return o
 

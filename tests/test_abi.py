@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     L = hm.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -44,7 +44,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 7
+    assert hm.lib().hm_abi_version() == 8
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
@@ -370,6 +370,36 @@ def pc_step(B=256, H=16, d=128, f=64, dv=128, dtype=hm.HM_BF16, **kw):
     for k_, v_ in kw.items():
         setattr(a, k_, v_)
     return a
+
+
+def test_per_channel_segment_plan():
+    """Automatic segments only when fewer than 65 workgroups (one per (b, h) and 64
+    channels) would run: up to 256 / workgroups segments of at least four chunks."""
+    def plan(**kw):
+        st, ns = hm.call_pc_plan(pc(**kw))
+        expect(st, hm.HM_OK)
+        st, nb = hm.call_pc_workspace_size(pc(**kw))
+        expect(st, hm.HM_OK)
+        return ns, nb
+    blk = 2 * 128 * 128 * 4
+    ns, nb = plan()                                   # B*H = 32, 2 channel groups: 64 workgroups
+    assert ns == 4 and nb == (32 * 4 * blk + 255) // 256 * 256 + 32 * 3 * 128 * 4
+    assert plan(B=1, n=131072)[0] == 8                # 32 workgroups: 8 segments of 256 chunks
+    assert plan(B=8) == (1, 0)                        # 256 workgroups: one segment, no workspace
+    assert plan(B=1, n=256)[0] == 1                   # four chunks: too short to split
+    assert plan(segments=3)[0] == 3                   # 11 + 11 + 10 chunks
+    assert plan(segments=100)[0] == 32                # at most one segment per chunk
+    assert plan(n=100, segments=5)[0] == 2
+    assert plan(segments=1) == (1, 0)
+    assert plan(n=0) == (1, 0)
+    expect(hm.call_pc_plan(pc(segments=-1))[0], hm.HM_ERR_SHAPE)
+    expect(hm.call_pc_plan(pc(d=96))[0], hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_pc_fwd(pc(segments=-2)), hm.HM_ERR_SHAPE)
+    expect(hm.call_pc_fwd(pc()), hm.HM_ERR_WORKSPACE)                  # 4 segments, no workspace
+    assert "workspace" in hm.last_error()
+    expect(hm.call_pc_fwd(pc(workspace=A + 0xa000000, workspace_bytes=nb - 1)), hm.HM_ERR_WORKSPACE)
+    expect(hm.call_pc_fwd(pc(workspace=A + 0xa000008, workspace_bytes=nb)), hm.HM_ERR_ALIGN)
+    expect(hm.call_pc_fwd(pc(B=0, workspace=None)), hm.HM_OK)         # nothing to run
 
 
 def test_per_channel_validation():

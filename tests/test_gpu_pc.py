@@ -234,3 +234,76 @@ def test_decode_fused_conv_matches_conv_then_step():
     torch.cuda.synchronize()
     assert torch.equal(o_f, o_s)
     assert torch.equal(st, st2)
+
+
+def positive_pc_state(B, H, F, dv, seed):
+    """A start state a prefix of tokens could have left: Sd > 0, Sn = sums of phi v."""
+    r = np.random.default_rng(seed)
+    w = r.random((B, H, 5, F))
+    w /= w.sum(-1, keepdims=True)
+    vv = r.normal(size=(B, H, 5, dv))
+    Sn = np.einsum("bhjf,bhjd->bhfd", w, vv)
+    Sd = np.einsum("bhjf,bhjd->bhfd", w, np.ones_like(vv))
+    return torch.tensor(orc.pack_state_pc(Sn, Sd), dtype=torch.float32, device="cuda"), Sn, Sd
+
+
+@pytest.mark.parametrize("segments", [2, 3, 64, 0])
+@pytest.mark.parametrize("n", [130, 333, 700])
+@pytest.mark.parametrize("shape", [(16, 16, 16), (32, 16, 32)])
+def test_prefill_segments_fp32(segments, n, shape):
+    """The sequence cut into segments scanned in parallel (segment pass, element-wise
+    composition of the start states, full pass) against the oracle, from a start state,
+    with s_final; 64 segments cap at one per chunk, 0 is the automatic plan."""
+    d, f, dv = shape
+    c = inputs.make_pc("pcseg", 2, 3, n, d, f, dv, torch.float32, seed=n + d + segments)
+    g = dev(c)
+    s0, Sn0, Sd0 = positive_pc_state(2, 3, 2 * f, dv, seed=n)
+    sf = torch.full_like(s0, float("nan"))
+    plan = hm.hm_linattn_pc_plan(g["q"], g["v"], g["w_q"], segments=segments)
+    o = hm.hm_linattn_pc_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], s_init=s0,
+                             s_final=sf, segments=segments)
+    torch.cuda.synchronize()
+    assert plan == (min(segments, -(-n // 64)) if segments else plan) and plan >= 1
+    ref, Sn, Sd = oracle(c, Sn0, Sd0)
+    name = f"pc fp32 {shape} n={n} segments={segments} (plan {plan})"
+    assert report(f"{name} o", f64(o), ref) <= FP32_TOL
+    assert report(f"{name} state", f64(sf), orc.pack_state_pc(Sn, Sd)) <= FP32_TOL
+
+
+def test_prefill_segments_in_place_gate_rope():
+    """Segments with s_init and s_final the same buffer (zeros), the gate and the rotary
+    encoding (positions offset by each segment's first token).  The turned features are
+    signed, so each output is held to FP32_TOL times its first-order rounding bound."""
+    B, H, n, d, f, dv = 2, 2, 500, 32, 16, 32
+    c = inputs.make_pc("pcseg", B, H, n, d, f, dv, torch.float32, seed=21)
+    g = dev(c)
+    gate = inputs.gate(c.v.shape, torch.float32, seed=8)
+    pos0 = torch.tensor([7, 300], dtype=torch.int64)
+    st = torch.zeros((B, H, hm.state_numel_pc(f, dv)), device="cuda")
+    o = hm.hm_linattn_pc_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], s_init=st, s_final=st,
+                             gate=gate.cuda(), rope_dims=32, rope_pos0=pos0.cuda(), segments=4)
+    torch.cuda.synchronize()
+    ref, Sn, Sd = oracle(c, gate=f64(gate), rope=(32, pos0.numpy()))
+    ref0, _, _ = oracle(c, rope=(32, pos0.numpy()))
+    bound, margin = pc_bound(c, (32, pos0.numpy()), ref0)
+    print(f"[parity] min den/D {margin:.3f}", flush=True)
+    check_bound("pc fp32 segments in place + gate + rope", f64(o), ref, bound * np.abs(orc.silu(f64(gate))), FP32_TOL)
+    assert report("pc fp32 segments in place state", f64(st), orc.pack_state_pc(Sn, Sd)) <= FP32_TOL
+
+
+@pytest.mark.parametrize("segments", [1, 0, 7])
+def test_prefill_segments_bf16_long(segments):
+    """A long sequence on few heads (B=1, H=2, n=16384, the Pythia-shaped head): the
+    automatic plan cuts it into 64 segments of four chunks; every output against the
+    oracle, and the segmented outputs against the unsegmented ones."""
+    c = inputs.make_pc("pclong", 1, 2, 16384, 128, 64, 128, torch.bfloat16, seed=5)
+    g = dev(c)
+    sf = torch.empty((1, 2, hm.state_numel_pc(64, 128)), device="cuda")
+    plan = hm.hm_linattn_pc_plan(g["q"], g["v"], g["w_q"], segments=segments)
+    assert plan == {1: 1, 0: 64, 7: 7}[segments]
+    o = hm.hm_linattn_pc_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], s_final=sf,
+                             segments=segments)
+    torch.cuda.synchronize()
+    ref, Sn, Sd = oracle(c)
+    assert report(f"pc bf16 long segments={segments} (plan {plan}) o", f64(o), ref) <= BF16_TOL
+    assert report(f"pc bf16 long segments={segments} state", f64(sf), orc.pack_state_pc(Sn, Sd)) <= BF16_TOL
