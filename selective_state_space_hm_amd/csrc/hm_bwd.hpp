@@ -174,6 +174,18 @@ __device__ __forceinline__ void tile_to_lds(T *dst, int lo, const f32x4 (&X)[NTT
     }
   }
 }
+// The first `valid` of ROWS rows [COLS] from LDS (stride lo) to global rows (stride
+// gs elements) as 16-byte pieces.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void rows_to_global(T *dst, int64_t gs, const T *src, int lo, int valid) {
+  constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR;
+  typedef typename Vec<T>::type V;
+#pragma unroll
+  for (int idx = threadIdx.x; idx < N; idx += 256) {
+    const int r = idx / PPR, pc = idx % PPR;
+    if (r < valid) *reinterpret_cast<V *>(dst + r * gs + pc * E) = *reinterpret_cast<const V *>(src + r * lo + pc * E);
+  }
+}
 template <typename T, int ROWS, int COLS>
 __device__ __forceinline__ void lds_to_global(T *dst, int64_t gs, const T *src, int lo) {
   constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR;
@@ -943,7 +955,8 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
       put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
     }
     __syncthreads();
-    // dq = du_q W_q^T
+    // dq = du_q W_q^T (stored straight from the accumulators: staging the rows
+    // through LDS for 16-byte stores measured 6 us slower on the Pythia layer)
     T *DQ = (T *)p.dq + b * p.sq_b + h * p.sq_h + t0 * p.sq_t;
     Frags<T, FH> fdu;  // this wave's du rows, shared by the d tiles
     fdu.load(sDu + 16 * w * LW, LW);
@@ -1150,6 +1163,12 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
   const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
   int64_t c0, c1;
   chunk_range(p, grp, c0, c1);
+  static_assert(LF >= DV + PAD, "dv rows fit the phi(q) buffer");
+  // dv rows of a chunk are formed in sQ (dead by then) and leave as 16-byte row
+  // pieces at the top of the next iteration, while its operand loads are in flight
+  // (155 -> 147 us on the Pythia layer; the same for dq and dk measured slower)
+  T *DV_ = nullptr;
+  int nv_prev = 0;
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
@@ -1166,6 +1185,10 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       if (tid < C) {
         tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
         tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+      }
+      if (c > c0) {
+        rows_to_global<T, C, DV>(DV_, p.sv_t, sQ, LF, nv_prev);
+        __syncthreads();
       }
       st_k.store(sK, LF);
       st_q.store(sQ, LF);
@@ -1249,7 +1272,8 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       }
     }
     const float Lam = sL[nv - 1];
-    T *DV_ = (T *)p.dv + b * p.sv_b + h * p.sv_h + t0 * p.sv_t;
+    DV_ = (T *)p.dv + b * p.sv_b + h * p.sv_h + t0 * p.sv_t;
+    nv_prev = nv;
     Frags<T, C> fp;  // this wave's rows of the masked scores
     fp.load(sP + 16 * w * LC, LC);
 #pragma unroll
@@ -1260,11 +1284,12 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * w + 4 * g + r;
         const float e = p.dt ? __expf(Lam - sL[j]) : 1.f;
-        if (j < nv) DV_[j * p.sv_t + 16 * ct + i] = (T)(a1[r] + e * a2[r]);
+        sQ[j * LF + 16 * ct + i] = (T)(a1[r] + e * a2[r]);  // rows into sQ
       }
     }
     __syncthreads();
   }
+  if (c1 > c0) rows_to_global<T, C, DV>(DV_, p.sv_t, sQ, LF, nv_prev);
 }
 
 // ---------------------------------------------------------------- bwd_decay
@@ -1303,21 +1328,25 @@ __global__ __launch_bounds__(256) void bwd_decay(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_reduce
 // dW = sum of the workgroup shares (over every (b, h) for a shared W, over b for
-// per-head W): 64 consecutive weight elements per workgroup, the shares split over
-// four thread groups; dA_log[h] = sum_b of the (b, h) shares.
+// per-head W): 32 consecutive weight elements per workgroup, the shares split over
+// eight thread groups, each walking its shares eight loads at a time; dA_log[h] =
+// sum_b of the (b, h) shares.  (64 elements over four groups, one load pair at a
+// time: 30 us on the Pythia layer for 17 MB of shares, latency-bound.)
 template <int DK, int FH>
 __global__ __launch_bounds__(256) void bwd_reduce(const BwdParams p, int per_head) {
-  __shared__ float sq[4][64], sk[4][64];
+  constexpr int EW = 32, NG = 256 / EW;
+  __shared__ float sq[NG][EW], sk[NG][EW];
   constexpr int64_t W = (int64_t)DK * FH;
-  const int tid = threadIdx.x, el = tid & 63, pg = tid >> 6;
-  const int64_t e = (int64_t)blockIdx.x * 64 + el;  // over nh * W
+  const int tid = threadIdx.x, el = tid % EW, pg = tid / EW;
+  const int64_t e = (int64_t)blockIdx.x * EW + el;  // over nh * W
   const int64_t nh = per_head ? p.H : 1;
   float aq = 0.f, ak = 0.f;
   if (e < nh * W) {
     const int64_t h = e / W, x = e % W;
     // the shares of head h (per-head W) or of every head, slot = (bh * ngrp + grp)
     const int64_t nslot = per_head ? p.B * p.ngrp : p.B * p.H * p.ngrp;
-    for (int64_t k2 = pg; k2 < nslot; k2 += 4) {
+#pragma unroll 8
+    for (int64_t k2 = pg; k2 < nslot; k2 += NG) {
       int64_t slot;
       if (per_head) {
         const int64_t bb = k2 / p.ngrp, gI = k2 % p.ngrp;
@@ -1333,8 +1362,14 @@ __global__ __launch_bounds__(256) void bwd_reduce(const BwdParams p, int per_hea
   sk[pg][el] = ak;
   __syncthreads();
   if (pg == 0 && e < nh * W) {
-    p.dwq[e] = sq[0][el] + sq[1][el] + sq[2][el] + sq[3][el];
-    p.dwk[e] = sk[0][el] + sk[1][el] + sk[2][el] + sk[3][el];
+    float tq = 0.f, tk = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < NG; ++g2) {
+      tq += sq[g2][el];
+      tk += sk[g2][el];
+    }
+    p.dwq[e] = tq;
+    p.dwk[e] = tk;
   }
   if (p.da_log && blockIdx.x == 0) {
     for (int64_t hh = tid; hh < p.H; hh += 256) {
