@@ -64,17 +64,19 @@
  *     propagate to the outputs.
  *   - Supported sizes (anything else is HM_ERR_UNSUPPORTED):
  *       hm_linattn_fwd, hm_linattn_step:
- *         bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}
+ *         bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}; also
+ *                (d, f, dv) = (32, 16, 32), and dv = 32 at (64, 32) and (128, 64)
+ *                (hm_linattn_fwd: dv = 32 at every (d, f) of the first line, and
+ *                (32, 16, 64) as two 32-column workgroups, dsplit 2)
  *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}
  *       Not built, and why:
  *         f32 at d = 128, f = 64: the full pass keeps W_q^T, W_k^T, two blocks of
  *           phi(q) rows and of phi(k)^T, the score tile and the output rows in LDS:
  *           157 KB in bf16, twice that in f32 (the bf16 path is the one measured);
  *         bf16 at d = 16: the bf16 MFMA (16x16x32) takes K in steps of 32, so d
- *           must be a multiple of 32 (d = 32 is built by hm_featurize only: the
- *           prefill instantiates the measured widths and the two f32 test widths);
- *         f = 16 in bf16: phi has 32 features, one 32-wide MFMA step; not
- *           instantiated (f32 covers the small widths).
+ *           must be a multiple of 32;
+ *         f = 16 in bf16 with d > 32 or dv > 32: not instantiated (the widths
+ *           the pages measure are built, plus the one small bf16 shape).
  *       hm_featurize:
  *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
  *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}

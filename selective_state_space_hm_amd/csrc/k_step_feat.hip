@@ -9,7 +9,8 @@ static const StepEntry kStep[] = {
     HM_STEP(bf16, HM_DT_BF16, 64, 64, 64),   HM_STEP(bf16, HM_DT_BF16, 64, 64, 128),
     HM_STEP(bf16, HM_DT_BF16, 128, 32, 64),  HM_STEP(bf16, HM_DT_BF16, 128, 32, 128),
     HM_STEP(bf16, HM_DT_BF16, 128, 64, 64),  HM_STEP(bf16, HM_DT_BF16, 128, 64, 128),
-    HM_STEP(float, HM_DT_F32, 16, 16, 16),   HM_STEP(float, HM_DT_F32, 16, 16, 32),
+    HM_STEP(bf16, HM_DT_BF16, 32, 16, 32),   HM_STEP(bf16, HM_DT_BF16, 64, 32, 32),
+    HM_STEP(bf16, HM_DT_BF16, 128, 64, 32),  HM_STEP(float, HM_DT_F32, 16, 16, 16),   HM_STEP(float, HM_DT_F32, 16, 16, 32),
     HM_STEP(float, HM_DT_F32, 32, 16, 16),   HM_STEP(float, HM_DT_F32, 32, 16, 32),
 };
 #define HM_FEAT(T, TC, TO, TOC, DK, FH) {TC, TOC, DK, FH, &launch_feat<T, TO, DK, FH>}

@@ -92,6 +92,12 @@ def test_fwd_validation_errors():
     expect(hm.call_fwd(fwd(d=96)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(f=48)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(dtype=hm.HM_F32)), hm.HM_ERR_UNSUPPORTED)  # f32 at d=128 not built
+    # the small bf16 shapes are built (their plans resolve); d = 16 is not
+    expect(hm.call_plan(fwd(d=32, f=16, dv=32))[0], hm.HM_OK)
+    expect(hm.call_plan(fwd(dv=32))[0], hm.HM_OK)
+    expect(hm.call_fwd(fwd(d=16, f=16, dv=32)), hm.HM_ERR_UNSUPPORTED)
+    assert hm.call_plan(fwd(d=32, f=16, dv=64)) == (hm.HM_OK, (64, 4, 2))  # two 32-column workgroups
+    expect(hm.call_fwd(fwd(d=32, f=16, dv=64, dsplit=1)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=96)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=256)), hm.HM_ERR_UNSUPPORTED)
     assert "192 KB" in hm.last_error()                 # the stated reason: LDS per compute unit
@@ -194,6 +200,7 @@ def test_step_validation_errors():
     expect(hm.call_step(step(state=A + 8)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(sq_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(d=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(d=64, f=64, dv=32)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_step(step(gate=A + 0xa000008, sg_b=16 * 128, sg_h=128)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=16 * 128, sg_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=-1, sg_h=128)), hm.HM_ERR_SHAPE)

@@ -127,7 +127,8 @@ def test_fp32_segment_pass_slots(decay, segments, dsplit):
     assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
 
 
-@pytest.mark.parametrize("shape", [(64, 32, 64), (128, 64, 128), (128, 32, 64), (64, 64, 128)])
+@pytest.mark.parametrize("shape", [(64, 32, 64), (128, 64, 128), (128, 32, 64), (64, 64, 128), (32, 16, 32),
+                                   (64, 32, 32), (128, 64, 32), (32, 16, 64)])
 @pytest.mark.parametrize("decay", [None, "mild", "mamba"])
 def test_bf16_shapes_ragged(shape, decay):
     d, f, dv = shape
@@ -225,7 +226,8 @@ def test_split_handoff_with_aliased_state(segments, dsplit):
 
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("dtype,shape", [(torch.float32, (16, 16, 16)), (torch.float32, (32, 16, 32)),
-                                         (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64))])
+                                         (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64)),
+                                         (torch.bfloat16, (32, 16, 32)), (torch.bfloat16, (128, 64, 32))])
 @pytest.mark.parametrize("decay", [True, False])
 @pytest.mark.parametrize("per_head", [False, True])
 def test_decode_steps(dtype, shape, decay, per_head):
