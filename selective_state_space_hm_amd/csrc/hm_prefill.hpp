@@ -120,6 +120,27 @@ __device__ __forceinline__ const T *at(const T *base, uint32_t byte_off) {
 // also takes its scores against the first block's keys (16 off-diagonal tiles),
 // and the state update of both blocks is applied once the chunk has been read out
 // (in order: S = e^{L_1}(e^{L_0} S + K0~^T V0) + K1~^T V1, the same sums).
+// Decay factors of one 64-token block by one wave (lane = token): the inclusive
+// log-decay prefix L, e^{L}, e^{L_last - L} (0 past the sequence's end) and
+// e^{L_last}; lam accumulates L_last.  The prefix sums are carried in float64:
+// differences L_c - L_c' of large prefix sums would lose ~|L| * 2^-24 in float32,
+// and |L| reaches the thousands.
+template <bool DECAY>
+__device__ __forceinline__ void decay_factors(double *sLb, float *seLb, float *seKb, float &sLastb, bool valid,
+                                              float dtn, float expA, double &lam, int lane) {
+  if constexpr (DECAY) {
+    const double L = wave_inclusive_scan(valid ? (double)(-softplus_f32(dtn) * expA) : 0.0);
+    const double Ll = lane63(L);
+    sLb[lane] = L;
+    seLb[lane] = __expf((float)L);
+    seKb[lane] = valid ? __expf((float)(Ll - L)) : 0.f;
+    if (lane == 0) sLastb = __expf((float)Ll);
+    lam += Ll;
+  } else {
+    if (lane == 0) sLastb = 1.f;
+  }
+}
+
 template <typename T, int DK, int FH, int DW, bool DECAY, int MODE, int CH>
 __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams p) {
   using M = Mma<T>;
@@ -313,23 +334,10 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     auto load_dt = [&](int64_t tc) {
       if constexpr (DECAY) dtn = tc + lane < t1 ? DT[(tc + lane) * p.sdt_t] : 0.f;
     };
-    // Wave 1: decay factors of the chunk starting at tc into buffer `bufi`.  The
-    // prefix sums are carried in float64: differences L_c - L_c' of large prefix
-    // sums would lose ~|L| * 2^-24 in float32, and |L| reaches the thousands.
+    // Wave 1: decay factors of the chunk starting at tc into buffer `bufi`
     double lam = 0.0;
     auto decay = [&](int64_t tc, int bufi) {
-      const bool valid = tc + lane < t1;
-      if constexpr (DECAY) {
-        const double L = wave_inclusive_scan(valid ? (double)(-softplus_f32(dtn) * expA) : 0.0);
-        const double Ll = lane63(L);
-        sL[bufi][lane] = L;
-        seL[bufi][lane] = __expf((float)L);
-        seK[bufi][lane] = valid ? __expf((float)(Ll - L)) : 0.f;
-        if (lane == 0) sLast[bufi] = __expf((float)Ll);
-        lam += Ll;
-      } else {
-        if (lane == 0) sLast[bufi] = 1.f;
-      }
+      decay_factors<DECAY>(sL[bufi], seL[bufi], seK[bufi], sLast[bufi], tc + lane < t1, dtn, expA, lam, lane);
     };
     constexpr int NKS = EPL == 8 ? 2 : 4;
     frag ksel[NKS];
@@ -342,7 +350,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 
     if (nch > 0) {
       load_x(t0);
-      if (wv == 1) {
+      if (FULL && wv == 1) {
         load_dt(t0);
         decay(t0, 0);
         if (nch > 1) load_dt(t0 + C);
@@ -577,9 +585,11 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           }
         }
       }
-      __syncthreads();
+      // The segment pass has one barrier per chunk: its state waves carry z and the
+      // decay factors (see there), so the feature waves only featurize.
+      if constexpr (FULL) __syncthreads();
       // ---- half B: score tiles and z over chunk j, decay of chunk j+1 (wave 1)
-      if (j < nch) {
+      if (FULL && j < nch) {
         if constexpr (FULL) {
           // Ten causal tiles (a <= b): wave w forms (w, w) from its own phiK and
           // phiQ, wave w < 3 also (w, b) for b = w+1 .. min(w+2, 3) with phiQ of
@@ -648,8 +658,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       }
       __syncthreads();
     }
-    if (!FULL && half == 0 && wv == 1 && lane == 0) p.ws_lam[(int64_t)seg * BH + bh] = (float)lam;
-    if (dst && col == 0 && half == 0) {
+    if (FULL && dst && col == 0 && half == 0) {
 #pragma unroll
       for (int i = 0; i < ZT; ++i) {
         const int t = ZT * wv + i;
@@ -723,6 +732,35 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       }
     };
 
+    // Segment pass: z of the segment (tiles ZTS*sw ..) lives in the state waves, and
+    // one state wave (the second, when there are several) computes the decay factors,
+    // one chunk ahead of the featurization
+    constexpr int ZTS = (NFT + NS - 1) / NS;
+    const int dwave = NS > 1 ? 1 : 0;
+    f32x4 Zs[FULL ? 1 : ZTS];
+    const frag ones = M::select([&](int) { return col == 0; });
+    float dtn = 0.f;
+    auto load_dt = [&](int64_t tc) {
+      if constexpr (DECAY) dtn = tc + lane < t1 ? DT[(tc + lane) * p.sdt_t] : 0.f;
+    };
+    double lam = 0.0;
+    auto decay = [&](int64_t tc, int bufi) {
+      decay_factors<DECAY>(sL[bufi], seL[bufi], seK[bufi], sLast[bufi], tc + lane < t1, dtn, expA, lam, lane);
+    };
+    if constexpr (!FULL) {
+#pragma unroll
+      for (int i = 0; i < ZTS; ++i) {
+        const int t = ZTS * sw + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          Zs[i][r] = st && t < NFT && col == 0 ? st[(int64_t)F * p.dv + 16 * t + 4 * g + r] : 0.f;
+      }
+      if (nch > 0 && sw == dwave) {
+        load_dt(t0);
+        decay(t0, 0);
+        if (nch > 1) load_dt(t0 + C);
+      }
+    }
     if (nch > 0) load_v(t0);
     __syncthreads();
     // The other slots of a composed start state.  This waits for the loads, so it
@@ -811,6 +849,26 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         // outstanding global access, which there includes the saved state's stores.
         if constexpr (!SAVE) issue_gate_rows(ts);
         if (j < nch) load_v(ts + C);
+        // The segment pass has no read-out: its state waves advance S over chunk j-1
+        // here, beside the featurization of chunk j (its phi(k)^T, decay factors and
+        // v fragments are complete), instead of after it in half B.
+        if constexpr (!FULL) {
+          update_state(sKt[ks], vfr, ds);
+          // z <- e^{L_last} z + sum_c' phi~(k_c'): phi~(k)^T times a ones column
+          const float el = DECAY ? sLast[ds] : 1.f;
+#pragma unroll
+          for (int i = 0; i < ZTS; ++i) {
+            const int t = ZTS * sw + i;
+            if (t < NFT) {
+              frag ak[KC];
+#pragma unroll
+              for (int s = 0; s < KC; ++s) ak[s] = M::ld_tile(&sKt[ks][(16 * t + col) * LDC], s, g);
+              if constexpr (DECAY) Zs[i] *= el;
+#pragma unroll
+              for (int s = 0; s < KC; ++s) Zs[i] = M::mma(ak[s], ones, Zs[i]);
+            }
+          }
+        }
         if constexpr (FULL) {
           frag sfr[NTW][KF];
 #pragma unroll
@@ -890,9 +948,16 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             for (int jj = 0; jj < NTW; ++jj) store4(orow + 16 * bt * LDO + 16 * jj, oacc[jj][bt]);
         }
       }
-      __syncthreads();
+      if constexpr (!FULL) {
+        // decay factors of chunk j+1 (read by the feature waves next iteration)
+        if (sw == dwave && j + 1 < nch) {
+          decay(t0 + (j + 1) * C, (int)((j + 1) % NDB));
+          if (j + 2 < nch) load_dt(t0 + (j + 2) * C);
+        }
+      }
+      if constexpr (FULL) __syncthreads();
       // ---- half B: output rows of chunk j-1 to HBM, state update over chunk j-1
-      if (j >= 1) {
+      if (FULL && j >= 1) {
         if constexpr (FULL) {
           constexpr int EP = 16 / (int)sizeof(T);          // elements per 16-byte piece
           constexpr int PPR = DW / EP;                      // pieces per row
@@ -934,7 +999,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
           }
         }
         if constexpr (MB == 1) {
-          update_state(sKt[ks], vfr, ds);
+          if constexpr (FULL) update_state(sKt[ks], vfr, ds);
         } else {
           // the chunk's update once both blocks are read out (or at the segment's end)
           if (bi == MB - 1) {
@@ -959,6 +1024,21 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         for (int t = 0; t < NFT; ++t)
 #pragma unroll
           for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * t + 4 * g + r) * p.dv + ncol + 16 * jj + col] = S[jj][t][r];
+    }
+    if constexpr (!FULL) {
+      if (half == 0) {
+        if (dst && col == 0) {
+#pragma unroll
+          for (int i = 0; i < ZTS; ++i) {
+            const int t = ZTS * sw + i;
+            if (t < NFT) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) dst[(int64_t)F * p.dv + 16 * t + 4 * g + r] = Zs[i][r];
+            }
+          }
+        }
+        if (sw == dwave && lane == 0) p.ws_lam[(int64_t)seg * BH + bh] = (float)lam;
+      }
     }
   }
 }
