@@ -219,13 +219,13 @@ __device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, 
 // stage() in two halves, for operands whose LDS buffer frees up later: the loads
 // go out with an earlier phase's (one memory round trip less per chunk) and the
 // LDS writes happen once the buffer is free.
-template <typename T, int ROWS, int COLS> struct Staged {
-  static constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + 255) / 256;
+template <typename T, int ROWS, int COLS, int NT = 256> struct Staged {
+  static constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + NT - 1) / NT;
   typename Vec<T>::type x[PER];
   __device__ __forceinline__ void load(const T *src, int64_t gs, int valid) {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+      const int idx = threadIdx.x + NT * m, r = idx / PPR, pc = idx % PPR;
       x[m] = (idx < N && r < valid) ? *reinterpret_cast<const typename Vec<T>::type *>(src + r * gs + pc * E)
                                     : typename Vec<T>::type{};
     }
@@ -233,22 +233,22 @@ template <typename T, int ROWS, int COLS> struct Staged {
   __device__ __forceinline__ void store(T *dst, int ld) const {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+      const int idx = threadIdx.x + NT * m, r = idx / PPR, pc = idx % PPR;
       if (idx < N) *reinterpret_cast<typename Vec<T>::type *>(dst + r * ld + pc * E) = x[m];
     }
   }
 };
 
 // stage_t() in two halves (no row scale).
-template <typename T, int ROWS, int COLS> struct StagedT {
+template <typename T, int ROWS, int COLS, int NT = 256> struct StagedT {
   static constexpr int E = ep<T>(), PPR = COLS / E;
-  static constexpr int NP = sizeof(T) == 2 ? ROWS / 2 : ROWS, N = NP * PPR, PER = (N + 255) / 256;
+  static constexpr int NP = sizeof(T) == 2 ? ROWS / 2 : ROWS, N = NP * PPR, PER = (N + NT - 1) / NT;
   typename Vec<T>::type x0[PER], x1[sizeof(T) == 2 ? PER : 1];
   __device__ __forceinline__ void load(const T *src, int64_t gs, int valid) {
     typedef typename Vec<T>::type V;
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = threadIdx.x + 256 * m;
+      const int idx = threadIdx.x + NT * m;
       if constexpr (sizeof(T) == 2) {
         const int r = 2 * (idx % NP), pc = idx / NP;
         x0[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
@@ -263,7 +263,7 @@ template <typename T, int ROWS, int COLS> struct StagedT {
   __device__ __forceinline__ void store(T *dst, int ld, const float *rscale = nullptr) const {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
-      const int idx = threadIdx.x + 256 * m;
+      const int idx = threadIdx.x + NT * m;
       if (idx >= N) continue;
       if constexpr (sizeof(T) == 2) {
         const int r = 2 * (idx % NP), pc = idx / NP;
@@ -355,20 +355,20 @@ __device__ __forceinline__ void put_t(T *dst, int ld, f32x4 a) {
 }
 
 // W [d][f] (head h) into LDS, as stored (ld = f + pad) or transposed (ld = d + pad):
-// 16-byte loads, all issued before the first LDS write (256 threads)
-template <typename T, int DK, int FH>
+// 16-byte loads, all issued before the first LDS write (NT threads)
+template <typename T, int DK, int FH, int NT = 256>
 __device__ __forceinline__ void load_w(T *dst, int ld, const T *w, bool transposed) {
-  constexpr int E = ep<T>(), NV = DK * FH / E, PER = (NV + 255) / 256;
+  constexpr int E = ep<T>(), NV = DK * FH / E, PER = (NV + NT - 1) / NT;
   typedef typename Vec<T>::type V;
   V x[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
-    const int v = threadIdx.x + 256 * m;
+    const int v = threadIdx.x + NT * m;
     x[m] = v < NV ? *reinterpret_cast<const V *>(w + v * E) : V{};
   }
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
-    const int v = threadIdx.x + 256 * m;
+    const int v = threadIdx.x + NT * m;
     if (v >= NV) continue;
     const int i = v * E / FH, f0 = v * E % FH;
     if (transposed) {
@@ -834,26 +834,36 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_dq
 // dphiq -> du_q -> dq = du_q W_q^T, and this workgroup's share of dW_q.
+// Waves of a bwd_dq workgroup: two per SIMD, each 16-row band of the chunk split
+// between two waves by column tiles, so that one wave's MFMA chains and LDS waits
+// overlap the other's.  The rotary variants keep one wave per band: the rotation pairs
+// feature tiles across that split.
+constexpr int bwd_waves(bool rope) { return rope ? 4 : 8; }
+
 template <typename T, int DK, int FH, int DV, bool ROPE>
-__global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
+__global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dq(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int NW = bwd_waves(ROPE), NT = 64 * NW, NH = NW / 4;  // waves, threads, waves per 16-row band
   constexpr int LW = FH + PAD, LN = DV + PAD, LVQ = (DV > F ? DV : F) + PAD, LC = C + PAD, LS = DV + PAD;
   constexpr int OW = 0, ON = OW + DK * LW, OVQ = ON + C * LN, OA = OVQ + C * LVQ, OKT = OA + C * LC,
                 OS = OKT + F * LC, ODU = OS + F * LS, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
   __shared__ __align__(16) T sm[TOT];
-  __shared__ float sL[C], sdd[C], sz[F];
+  __shared__ float sL[C], sdd[C], sz[F], sQs[NH][C];
   __shared__ double sRev[ROPE ? FH : 1];
   T *sW = sm + OW, *sDN = sm + ON, *sVQ = sm + OVQ, *sA = sm + OA, *sKT = sm + OKT, *sS = sm + OS, *sDu = sm + ODU,
     *sDuT = sm + ODUT, *sXT = sm + OXT;
-  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
+  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + NW - 1) / NW;
+  constexpr int MJ = (C / 16) / NH, MF = (FT + NH - 1) / NH, MD = (DK / 16 + NH - 1) / NH;  // tiles per wave
+  static_assert((C / 16) % NH == 0, "key tiles split evenly");
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3, hw = w >> 2;  // the wave's row band and its share of the band's column tiles
   const int grp = blockIdx.x % p.ngrp;
   const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
   int64_t c0, c1;
   chunk_range(p, grp, c0, c1);
-  load_w<T, DK, FH>(sW, LW, (const T *)p.wq + h * p.sw_h, false);
+  load_w<T, DK, FH, NT>(sW, LW, (const T *)p.wq + h * p.sw_h, false);
   if constexpr (ROPE) fill_rev(sRev, p);
   const double pos_b = ROPE ? pos_of(p, b) : 0.0;
   f32x4 dW[NTW];
@@ -864,11 +874,11 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     // every operand load of the chunk goes out before the first LDS write: one memory
     // round trip per chunk instead of one per operand
-    Staged<T, C, F> phq_next;  // phi(q) rows, written over v once A is formed
-    Staged<T, C, DV> st_dn, st_v;
-    StagedT<T, C, DK> st_x;
-    StagedT<T, C, F> st_k;
-    Staged<T, F, DV> st_s;
+    Staged<T, C, F, NT> phq_next;  // phi(q) rows, written over v once A is formed
+    Staged<T, C, DV, NT> st_dn, st_v;
+    StagedT<T, C, DK, NT> st_x;
+    StagedT<T, C, F, NT> st_k;
+    Staged<T, F, DV, NT> st_s;
     st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     st_x.load((const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
@@ -892,87 +902,127 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
     }
     if (tid < F) sz[tid] = tz;
     __syncthreads();
-    // A[t][j] = [j <= t] e^{L_t - L_j} (dnum_t . v_j + dden_t); rows t of this wave
-    Frags<T, DV> fdn;  // this wave's dnum rows, shared by the four tiles
-    fdn.load(sDN + 16 * w * LN, LN);
+    // A[t][j] = [j <= t] e^{L_t - L_j} (dnum_t . v_j + dden_t); rows t of this wave's
+    // band, key tiles jt = hw + NH m
+    Frags<T, DV> fdn;  // the band's dnum rows, shared by the wave's tiles
+    fdn.load(sDN + 16 * rt * LN, LN);
 #pragma unroll
-    for (int jt = 0; jt < C / 16; ++jt) {
+    for (int m = 0; m < MJ; ++m) {
+      const int jt = hw + NH * m;
       const f32x4 d1 = mm(fdn, sVQ + 16 * jt * LVQ, LVQ, zero4());
       f32x4 a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r, j = 16 * jt + i;
+        const int t = 16 * rt + 4 * g + r, j = 16 * jt + i;
         a[r] = j <= t ? __expf(sL[t] - sL[j]) * (d1[r] + sdd[t]) : 0.f;
       }
-      put<T>(sA + 16 * w * LC + 16 * jt, LC, a);
+      put<T>(sA + 16 * rt * LC + 16 * jt, LC, a);
     }
     __syncthreads();
     phq_next.store(sVQ, LVQ);
     __syncthreads();
-    // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F]
-    f32x4 dph[F / 16];
+    // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F], for
+    // the feature tiles ft = hw + NH m and ft + FT (the pair that du combines)
+    f32x4 dph[MF][2];
     float qs[4] = {0.f, 0.f, 0.f, 0.f};  // Q_t partial: phiq_t . (inter part of dphiq_t)
-    Frags<T, C> fa;  // this wave's rows of A and of dnum, shared by the feature tiles
+    Frags<T, C> fa;  // the band's rows of A and of dnum, shared by the feature tiles
     Frags<T, DV> fdn2;
-    fa.load(sA + 16 * w * LC, LC);
-    fdn2.load(sDN + 16 * w * LN, LN);
+    fa.load(sA + 16 * rt * LC, LC);
+    fdn2.load(sDN + 16 * rt * LN, LN);
 #pragma unroll
-    for (int ft = 0; ft < F / 16; ++ft) {
-      const f32x4 a1 = mm(fa, sKT + 16 * ft * LC, LC, zero4());
-      const f32x4 a2 = mm(fdn2, sS + 16 * ft * LS, LS, zero4());
+    for (int m = 0; m < MF; ++m) {
+      const int fb = hw + NH * m;
+      if (fb < FT) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r;
-        const float eL = t < nv ? (p.dt ? __expf(sL[t]) : 1.f) : 0.f;
-        const float inter = eL * (a2[r] + sdd[t] * sz[16 * ft + i]);
-        dph[ft][r] = a1[r] + inter;
-        qs[r] += (float)sVQ[t * LVQ + 16 * ft + i] * inter;
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ft = fb + hf * FT;
+          const f32x4 a1 = mm(fa, sKT + 16 * ft * LC, LC, zero4());
+          const f32x4 a2 = mm(fdn2, sS + 16 * ft * LS, LS, zero4());
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * rt + 4 * g + r;
+            const float eL = t < nv ? (p.dt ? __expf(sL[t]) : 1.f) : 0.f;
+            const float inter = eL * (a2[r] + sdd[t] * sz[16 * ft + i]);
+            dph[m][hf][r] = a1[r] + inter;
+            qs[r] += (float)sVQ[t * LVQ + 16 * ft + i] * inter;
+          }
+        }
       }
     }
     if (p.a_log) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r;
+        const int t = 16 * rt + 4 * g + r;
         const float q4 = sum16(qs[r]);
-        if (i == 0 && t < nv) p.eQ[bh * p.n + t0 + t] = q4;
+        if constexpr (NH == 1) {
+          if (i == 0 && t < nv) p.eQ[bh * p.n + t0 + t] = q4;
+        } else {
+          if (i == 0) sQs[hw][t] = q4;  // the band's waves' partials are added below
+        }
       }
     }
     // du_q = phiq * dphiq over [u, -u] (unturned frame): du[f] = du'[f] - du'[f + FH]
     if constexpr (ROPE) {
+      static_assert(NH == 1, "the rotation pairs feature tiles across the column split");
+      f32x4 d[F / 16];
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        d[m] = dph[m][0];
+        d[m + FT] = dph[m][1];
+      }
       const float zero[4] = {0.f, 0.f, 0.f, 0.f};
-      phi_dphi<F / 16>(dph, sVQ + 16 * w * LVQ, LVQ, sRev, pos_b + (double)(t0 + 16 * w + 4 * g), zero, p.rope_dims);
+      phi_dphi<F / 16>(d, sVQ + 16 * rt * LVQ, LVQ, sRev, pos_b + (double)(t0 + 16 * rt + 4 * g), zero, p.rope_dims);
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        dph[m][0] = d[m];
+        dph[m][1] = d[m + FT];
+      }
     }
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      f32x4 du;
+    for (int m = 0; m < MF; ++m) {
+      const int ft = hw + NH * m;
+      if (ft < FT) {
+        f32x4 du;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r, f = 16 * ft + i;
-        du[r] = ROPE ? dph[ft][r] - dph[ft + FT][r]
-                     : (float)sVQ[t * LVQ + f] * dph[ft][r] - (float)sVQ[t * LVQ + FH + f] * dph[ft + FT][r];
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * rt + 4 * g + r, f = 16 * ft + i;
+          du[r] = ROPE ? dph[m][0][r] - dph[m][1][r]
+                       : (float)sVQ[t * LVQ + f] * dph[m][0][r] - (float)sVQ[t * LVQ + FH + f] * dph[m][1][r];
+        }
+        put<T>(sDu + 16 * rt * LW + 16 * ft, LW, du);
+        put_t<T>(sDuT + 16 * ft * LC + 16 * rt, LC, du);
       }
-      put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
-      put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
     }
     __syncthreads();
+    if constexpr (NH > 1) {
+      if (p.a_log && tid < nv) {
+        float q = 0.f;
+#pragma unroll
+        for (int u = 0; u < NH; ++u) q += sQs[u][tid];
+        p.eQ[bh * p.n + t0 + tid] = q;
+      }
+    }
     // dq = du_q W_q^T (stored straight from the accumulators: staging the rows
     // through LDS for 16-byte stores measured 6 us slower on the Pythia layer)
     T *DQ = (T *)p.dq + b * p.sq_b + h * p.sq_h + t0 * p.sq_t;
-    Frags<T, FH> fdu;  // this wave's du rows, shared by the d tiles
-    fdu.load(sDu + 16 * w * LW, LW);
+    Frags<T, FH> fdu;  // the band's du rows, shared by the wave's d tiles
+    fdu.load(sDu + 16 * rt * LW, LW);
 #pragma unroll
-    for (int it = 0; it < DK / 16; ++it) {
-      const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
+    for (int m = 0; m < MD; ++m) {
+      const int it = hw + NH * m;
+      if (it < DK / 16) {
+        const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r;
-        if (t < nv) DQ[t * p.sq_t + 16 * it + i] = (T)a[r];
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * rt + 4 * g + r;
+          if (t < nv) DQ[t * p.sq_t + 16 * it + i] = (T)a[r];
+        }
       }
     }
     // dW_q += X_q^T du_q
 #pragma unroll
     for (int m = 0; m < NTW; ++m) {
-      const int tt = w + 4 * m;
+      const int tt = w + NW * m;
       if (tt < TW) dW[m] = mm<T, C>(sXT + 16 * (tt / FT) * LC, LC, sDuT + 16 * (tt % FT) * LC, LC, dW[m]);
     }
     __syncthreads();
@@ -980,7 +1030,7 @@ __global__ __launch_bounds__(256) void bwd_dq(const BwdParams p) {
   float *part = p.dwq_part + (bh * p.ngrp + grp) * (int64_t)(DK * FH);
 #pragma unroll
   for (int m = 0; m < NTW; ++m) {
-    const int tt = w + 4 * m;
+    const int tt = w + NW * m;
     if (tt < TW) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[(16 * (tt / FT) + 4 * g + r) * FH + 16 * (tt % FT) + i] = dW[m][r];
