@@ -176,12 +176,12 @@ __device__ __forceinline__ void tile_to_lds(T *dst, int lo, const f32x4 (&X)[NTT
 }
 // The first `valid` of ROWS rows [COLS] from LDS (stride lo) to global rows (stride
 // gs elements) as 16-byte pieces.
-template <typename T, int ROWS, int COLS>
+template <typename T, int ROWS, int COLS, int NT = 256>
 __device__ __forceinline__ void rows_to_global(T *dst, int64_t gs, const T *src, int lo, int valid) {
   constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR;
   typedef typename Vec<T>::type V;
 #pragma unroll
-  for (int idx = threadIdx.x; idx < N; idx += 256) {
+  for (int idx = threadIdx.x; idx < N; idx += NT) {
     const int r = idx / PPR, pc = idx % PPR;
     if (r < valid) *reinterpret_cast<V *>(dst + r * gs + pc * E) = *reinterpret_cast<const V *>(src + r * lo + pc * E);
   }
@@ -200,19 +200,19 @@ __device__ __forceinline__ void lds_to_global(T *dst, int64_t gs, const T *src, 
 // ROWS x COLS from global rows (stride gs elements) into LDS rows (ld), rows at or
 // beyond `valid` zeroed; 16-byte pieces, every load of a thread issued before its
 // first LDS write (compile-time trip counts, fully unrolled).
-template <typename T, int ROWS, int COLS>
+template <typename T, int ROWS, int COLS, int NT = 256>
 __device__ __forceinline__ void stage(T *dst, int ld, const T *src, int64_t gs, int valid) {
-  constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + 255) / 256;
+  constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR, PER = (N + NT - 1) / NT;
   typedef typename Vec<T>::type V;
   V x[PER];
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
-    const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+    const int idx = threadIdx.x + NT * m, r = idx / PPR, pc = idx % PPR;
     x[m] = (idx < N && r < valid) ? *reinterpret_cast<const V *>(src + r * gs + pc * E) : V{};
   }
 #pragma unroll
   for (int m = 0; m < PER; ++m) {
-    const int idx = threadIdx.x + 256 * m, r = idx / PPR, pc = idx % PPR;
+    const int idx = threadIdx.x + NT * m, r = idx / PPR, pc = idx % PPR;
     if (idx < N) *reinterpret_cast<V *>(dst + r * ld + pc * E) = x[m];
   }
 }
@@ -1041,25 +1041,29 @@ __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dq(const BwdParams p
 // ---------------------------------------------------------------- bwd_dk
 // dphik -> dL_t and du_k (softmax) -> dk = du_k W_k^T, and the share of dW_k.
 template <typename T, int DK, int FH, int DV, bool ROPE>
-__global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
+__global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dk(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int NW = bwd_waves(ROPE), NT = 64 * NW, NH = NW / 4;  // waves, threads, waves per 16-row band
   constexpr int LW = FH + PAD, LV = DV + PAD, LNK = (DV > F ? DV : F) + PAD, LC = C + PAD, LG = DV + PAD;
   constexpr int OW = 0, OV = OW + DK * LW, ONK = OV + C * LV, OA = ONK + C * LNK, OQT = OA + C * LC,
                 OG = OQT + F * LC, ODU = OG + F * LG, ODUT = ODU + C * LW, OXT = ODUT + FH * LC, TOT = OXT + DK * LC;
   __shared__ __align__(16) T sm[TOT];
-  __shared__ float sL[C], sdd[C], sg[F];
+  __shared__ float sL[C], sdd[C], sg[F], sDot[NH][C], sKs[NH][C];
   __shared__ double sRev[ROPE ? FH : 1];
   T *sW = sm + OW, *sV = sm + OV, *sNK = sm + ONK, *sAT = sm + OA, *sQT = sm + OQT, *sG = sm + OG, *sDu = sm + ODU,
     *sDuT = sm + ODUT, *sXT = sm + OXT;
-  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + 3) / 4;
+  constexpr int FT = FH / 16, TW = (DK / 16) * FT, NTW = (TW + NW - 1) / NW;
+  constexpr int MJ = (C / 16) / NH, MF = (FT + NH - 1) / NH, MD = (DK / 16 + NH - 1) / NH;  // tiles per wave
+  static_assert((C / 16) % NH == 0, "query tiles split evenly");
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3, hw = w >> 2;  // the wave's row band and its share of the band's column tiles
   const int grp = blockIdx.x % p.ngrp;
   const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
   int64_t c0, c1;
   chunk_range(p, grp, c0, c1);
-  load_w<T, DK, FH>(sW, LW, (const T *)p.wk + h * p.sw_h, false);
+  load_w<T, DK, FH, NT>(sW, LW, (const T *)p.wk + h * p.sw_h, false);
   if constexpr (ROPE) fill_rev(sRev, p);
   const double pos_b = ROPE ? pos_of(p, b) : 0.0;
   f32x4 dW[NTW];
@@ -1069,11 +1073,11 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     // every operand load of the chunk goes out before the first LDS write
-    Staged<T, C, F> phk_next;  // phi(k) rows, written over dnum once A^T is formed
-    Staged<T, C, DV> st_dn, st_v;
-    StagedT<T, C, DK> st_x;
-    StagedT<T, C, F> st_q;
-    Staged<T, F, DV> st_g;
+    Staged<T, C, F, NT> phk_next;  // phi(k) rows, written over dnum once A^T is formed
+    Staged<T, C, DV, NT> st_dn, st_v;
+    StagedT<T, C, DK, NT> st_x;
+    StagedT<T, C, F, NT> st_q;
+    Staged<T, F, DV, NT> st_g;
     st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     st_x.load((const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
@@ -1097,88 +1101,142 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
     }
     if (tid < F) sg[tid] = tg;
     __syncthreads();
-    // A^T[j][t] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t); rows j of this wave
-    Frags<T, DV> fv;  // this wave's v rows, shared by the four tiles
-    fv.load(sV + 16 * w * LV, LV);
+    // A^T[j][t] = [j <= t] e^{L_t - L_j} (v_j . dnum_t + dden_t); rows j of this wave's
+    // band, query tiles tt = hw + NH m
+    Frags<T, DV> fv;  // the band's v rows, shared by the wave's tiles
+    fv.load(sV + 16 * rt * LV, LV);
 #pragma unroll
-    for (int tt = 0; tt < C / 16; ++tt) {
+    for (int m = 0; m < MJ; ++m) {
+      const int tt = hw + NH * m;
       const f32x4 d1 = mm(fv, sNK + 16 * tt * LNK, LNK, zero4());
       f32x4 a;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r, t = 16 * tt + i;
+        const int j = 16 * rt + 4 * g + r, t = 16 * tt + i;
         a[r] = j <= t ? __expf(sL[t] - sL[j]) * (d1[r] + sdd[t]) : 0.f;
       }
-      put<T>(sAT + 16 * w * LC + 16 * tt, LC, a);
+      put<T>(sAT + 16 * rt * LC + 16 * tt, LC, a);
     }
     __syncthreads();
     phk_next.store(sNK, LNK);
     __syncthreads();
-    // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F]
+    // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F], for the
+    // feature tiles ft = hw + NH m and ft + FT (the pair that du combines)
     const float Lam = sL[nv - 1];
-    f32x4 dph[F / 16];
+    f32x4 dph[MF][2];
     float ks[4] = {0.f, 0.f, 0.f, 0.f};  // K_j partial: phik_j . (inter part of dphik_j)
-    Frags<T, C> fat;  // this wave's rows of A^T and of v, shared by the feature tiles
+    float ds[4] = {0.f, 0.f, 0.f, 0.f};  // phik_j . dphik_j partial
+    Frags<T, C> fat;  // the band's rows of A^T and of v, shared by the feature tiles
     Frags<T, DV> fv2;
-    fat.load(sAT + 16 * w * LC, LC);
-    fv2.load(sV + 16 * w * LV, LV);
+    fat.load(sAT + 16 * rt * LC, LC);
+    fv2.load(sV + 16 * rt * LV, LV);
 #pragma unroll
-    for (int ft = 0; ft < F / 16; ++ft) {
-      const f32x4 a1 = mm(fat, sQT + 16 * ft * LC, LC, zero4());
-      const f32x4 a2 = mm(fv2, sG + 16 * ft * LG, LG, zero4());
+    for (int m = 0; m < MF; ++m) {
+      const int fb = hw + NH * m;
+      if (fb < FT) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r;
-        const float e = j < nv ? (p.dt ? __expf(Lam - sL[j]) : 1.f) : 0.f;
-        const float inter = e * (a2[r] + sg[16 * ft + i]);
-        dph[ft][r] = a1[r] + inter;
-        ks[r] += (float)sNK[j * LNK + 16 * ft + i] * inter;
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ft = fb + hf * FT;
+          const f32x4 a1 = mm(fat, sQT + 16 * ft * LC, LC, zero4());
+          const f32x4 a2 = mm(fv2, sG + 16 * ft * LG, LG, zero4());
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * rt + 4 * g + r;
+            const float e = j < nv ? (p.dt ? __expf(Lam - sL[j]) : 1.f) : 0.f;
+            const float inter = e * (a2[r] + sg[16 * ft + i]);
+            const float phk = (float)sNK[j * LNK + 16 * ft + i];
+            dph[m][hf][r] = a1[r] + inter;
+            ks[r] += phk * inter;
+            ds[r] += phk * dph[m][hf][r];
+          }
+        }
       }
     }
-    // phik . dphik per token for the softmax backward
+    // phik . dphik per token for the softmax backward, and K_j
     float dot[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int j = 16 * w + 4 * g + r;
-      float s = 0.f;
-#pragma unroll
-      for (int ft = 0; ft < F / 16; ++ft) s += (float)sNK[j * LNK + 16 * ft + i] * dph[ft][r];
-      dot[r] = sum16(s);
+      const int j = 16 * rt + 4 * g + r;
+      dot[r] = sum16(ds[r]);
       const float k4 = sum16(ks[r]);
-      if (p.a_log && i == 0 && j < nv) p.eK[bh * p.n + t0 + j] = k4;
+      if constexpr (NH == 1) {
+        if (p.a_log && i == 0 && j < nv) p.eK[bh * p.n + t0 + j] = k4;
+      } else {
+        if (i == 0) {
+          sDot[hw][j] = dot[r];
+          sKs[hw][j] = k4;
+        }
+      }
     }
-    // du_k = phik * (dphik - phik . dphik) over [u, -u] (unturned frame)
-    if constexpr (ROPE)
-      phi_dphi<F / 16>(dph, sNK + 16 * w * LNK, LNK, sRev, pos_b + (double)(t0 + 16 * w + 4 * g), dot, p.rope_dims);
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      f32x4 du;
+    if constexpr (NH > 1) {
+      // the band's waves hold halves of each row: add their partials
+      __syncthreads();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r, f = 16 * ft + i;
-        du[r] = ROPE ? dph[ft][r] - dph[ft + FT][r]
-                     : (float)sNK[j * LNK + f] * (dph[ft][r] - dot[r]) -
-                           (float)sNK[j * LNK + FH + f] * (dph[ft + FT][r] - dot[r]);
+        const int j = 16 * rt + 4 * g + r;
+        float d = 0.f;
+#pragma unroll
+        for (int u = 0; u < NH; ++u) d += sDot[u][j];
+        dot[r] = d;
       }
-      put<T>(sDu + 16 * w * LW + 16 * ft, LW, du);
-      put_t<T>(sDuT + 16 * ft * LC + 16 * w, LC, du);
+      if (p.a_log && tid < nv) {
+        float k = 0.f;
+#pragma unroll
+        for (int u = 0; u < NH; ++u) k += sKs[u][tid];
+        p.eK[bh * p.n + t0 + tid] = k;
+      }
+    }
+    // du_k = phik * (dphik - phik . dphik) over [u, -u] (unturned frame)
+    if constexpr (ROPE) {
+      static_assert(NH == 1, "the rotation pairs feature tiles across the column split");
+      f32x4 d[F / 16];
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        d[m] = dph[m][0];
+        d[m + FT] = dph[m][1];
+      }
+      phi_dphi<F / 16>(d, sNK + 16 * rt * LNK, LNK, sRev, pos_b + (double)(t0 + 16 * rt + 4 * g), dot, p.rope_dims);
+#pragma unroll
+      for (int m = 0; m < MF; ++m) {
+        dph[m][0] = d[m];
+        dph[m][1] = d[m + FT];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MF; ++m) {
+      const int ft = hw + NH * m;
+      if (ft < FT) {
+        f32x4 du;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * rt + 4 * g + r, f = 16 * ft + i;
+          du[r] = ROPE ? dph[m][0][r] - dph[m][1][r]
+                       : (float)sNK[j * LNK + f] * (dph[m][0][r] - dot[r]) -
+                             (float)sNK[j * LNK + FH + f] * (dph[m][1][r] - dot[r]);
+        }
+        put<T>(sDu + 16 * rt * LW + 16 * ft, LW, du);
+        put_t<T>(sDuT + 16 * ft * LC + 16 * rt, LC, du);
+      }
     }
     __syncthreads();
     T *DK_ = (T *)p.dk + b * p.sk_b + h * p.sk_h + t0 * p.sk_t;
-    Frags<T, FH> fdu;  // this wave's du rows, shared by the d tiles
-    fdu.load(sDu + 16 * w * LW, LW);
+    Frags<T, FH> fdu;  // the band's du rows, shared by the wave's d tiles
+    fdu.load(sDu + 16 * rt * LW, LW);
 #pragma unroll
-    for (int it = 0; it < DK / 16; ++it) {
-      const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
+    for (int m = 0; m < MD; ++m) {
+      const int it = hw + NH * m;
+      if (it < DK / 16) {
+        const f32x4 a = mm(fdu, sW + 16 * it * LW, LW, zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r;
-        if (j < nv) DK_[j * p.sk_t + 16 * it + i] = (T)a[r];
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * rt + 4 * g + r;
+          if (j < nv) DK_[j * p.sk_t + 16 * it + i] = (T)a[r];
+        }
       }
     }
 #pragma unroll
     for (int m = 0; m < NTW; ++m) {
-      const int tt = w + 4 * m;
+      const int tt = w + NW * m;
       if (tt < TW) dW[m] = mm<T, C>(sXT + 16 * (tt / FT) * LC, LC, sDuT + 16 * (tt % FT) * LC, LC, dW[m]);
     }
     __syncthreads();
@@ -1186,7 +1244,7 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
   float *part = p.dwk_part + (bh * p.ngrp + grp) * (int64_t)(DK * FH);
 #pragma unroll
   for (int m = 0; m < NTW; ++m) {
-    const int tt = w + 4 * m;
+    const int tt = w + NW * m;
     if (tt < TW) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[(16 * (tt / FT) + 4 * g + r) * FH + 16 * (tt % FT) + i] = dW[m][r];
@@ -1197,18 +1255,22 @@ __global__ __launch_bounds__(256) void bwd_dk(const BwdParams p) {
 // ---------------------------------------------------------------- bwd_dv
 // dv[j] = sum_t [j <= t] e^{L_t - L_j} (phiq_t . phik_j) dnum_t + e^{Lam - L_j} G^T phik_j
 template <typename T, int DK, int FH, int DV>
-__global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
+__global__ __launch_bounds__(bwd_waves(false) * 64) void bwd_dv(const BwdParams p) {
   using namespace bw;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD;
+  constexpr int NW = bwd_waves(false), NT = 64 * NW, NH = NW / 4;  // waves, threads, waves per 16-row band
   constexpr int LF = F + PAD, LC = C + PAD, LV = DV + PAD;
   constexpr int OK_ = 0, OQ = OK_ + C * LF, OP = OQ + C * LF, ONT = OP + C * LC, OGT = ONT + DV * LC,
                 OV = OGT + DV * LF, ON = OV + C * LV, TOT = ON + C * LV;
+  constexpr int MT = (C / 16) / NH, MV = (DV / 16 + NH - 1) / NH;  // tiles per wave
+  static_assert((C / 16) % NH == 0, "query tiles split evenly");
   __shared__ __align__(16) T sm[TOT];
-  __shared__ float sL[C], sdd[C], sCol[4][C];
-  __shared__ double sX[4];
+  __shared__ float sL[C], sdd[C], sCol[4][C], sRow[NH][C];
+  __shared__ double sX[NW];
   T *sK = sm + OK_, *sQ = sm + OQ, *sP = sm + OP, *sNT = sm + ONT, *sGT = sm + OGT, *sV = sm + OV, *sN = sm + ON;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = w & 3, hw = w >> 2;  // the wave's row band and its share of the band's column tiles
   const int grp = blockIdx.x % p.ngrp;
   const int64_t bh = blockIdx.x / p.ngrp, b = bh / p.H, h = bh % p.H;
   int64_t c0, c1;
@@ -1224,9 +1286,9 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     {
       // every operand load of the chunk goes out before the first LDS write
-      Staged<T, C, F> st_k, st_q;
-      StagedT<T, C, DV> st_nt;
-      StagedT<T, F, DV> st_gt;
+      Staged<T, C, F, NT> st_k, st_q;
+      StagedT<T, C, DV, NT> st_nt;
+      StagedT<T, F, DV, NT> st_gt;
       st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
       st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
       st_nt.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
@@ -1237,7 +1299,7 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
         tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
       }
       if (c > c0) {
-        rows_to_global<T, C, DV>(DV_, p.sv_t, sQ, LF, nv_prev);
+        rows_to_global<T, C, DV, NT>(DV_, p.sv_t, sQ, LF, nv_prev);
         __syncthreads();
       }
       st_k.store(sK, LF);
@@ -1250,25 +1312,27 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       }
     }
     if (p.a_log) {
-      stage<T, C, DV>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
-      stage<T, C, DV>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+      stage<T, C, DV, NT>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
+      stage<T, C, DV, NT>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     }
     __syncthreads();
     // Pt[j][t] = [j <= t] e^{L_t - L_j} phik_j . phiq_t, and for the decay gradient the
     // pair weights W^T[j][t] = [j < t] Pt[j][t] (v_j . dnum_t + dden_t): their sums
-    // along t (pairs with key j) and along j (pairs with query t)
+    // along t (pairs with key j) and along j (pairs with query t); rows j of the wave's
+    // band, query tiles tt = hw + NH m
     float rowsum[4] = {0.f, 0.f, 0.f, 0.f};
-    Frags<T, F> fk;  // this wave's phi(k) rows, shared by every tile below
-    fk.load(sK + 16 * w * LF, LF);
+    Frags<T, F> fk;  // the band's phi(k) rows, shared by every tile below
+    fk.load(sK + 16 * rt * LF, LF);
 #pragma unroll
-    for (int tt = 0; tt < C / 16; ++tt) {
+    for (int m = 0; m < MT; ++m) {
+      const int tt = hw + NH * m;
       const f32x4 s = mm(fk, sQ + 16 * tt * LF, LF, zero4());
       f32x4 a, d1 = zero4();
-      if (p.a_log) d1 = mm<T, DV>(sV + 16 * w * LV, LV, sN + 16 * tt * LV, LV, zero4());
+      if (p.a_log) d1 = mm<T, DV>(sV + 16 * rt * LV, LV, sN + 16 * tt * LV, LV, zero4());
       float colsum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r, t = 16 * tt + i;
+        const int j = 16 * rt + 4 * g + r, t = 16 * tt + i;
         a[r] = j <= t ? __expf(sL[t] - sL[j]) * s[r] : 0.f;
         const float wt = j < t ? a[r] * (d1[r] + sdd[t]) : 0.f;
         rowsum[r] += wt;
@@ -1277,22 +1341,27 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
       if (p.a_log) {
         colsum += __shfl_xor(colsum, 16);
         colsum += __shfl_xor(colsum, 32);
-        if (g == 0) sCol[w][16 * tt + i] = colsum;
+        if (g == 0) sCol[rt][16 * tt + i] = colsum;
       }
-      put<T>(sP + 16 * w * LC + 16 * tt, LC, a);
+      put<T>(sP + 16 * rt * LC + 16 * tt, LC, a);
     }
     if (p.a_log) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float rs = sum16(rowsum[r]);
+        if (i == 0) sRow[hw][16 * rt + 4 * g + r] = rs;
+      }
       // X_c = e^{Lam} (<G_end, S_c> + <g_end, z_c>): pairs spanning the whole chunk
       const T *Sc = (const T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV);
       const T *Gc = (const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV);
       typedef typename Vec<T>::type V;
-      constexpr int EV = ep<T>(), NV = F * DV / EV, PV = (NV + 255) / 256;
+      constexpr int EV = ep<T>(), NV = F * DV / EV, PV = (NV + NT - 1) / NT;
       V sv[PV], gv[PV];
 #pragma unroll
       for (int m = 0; m < PV; ++m) {
-        const bool ok = tid + 256 * m < NV;
-        sv[m] = ok ? reinterpret_cast<const V *>(Sc)[tid + 256 * m] : V{};
-        gv[m] = ok ? reinterpret_cast<const V *>(Gc)[tid + 256 * m] : V{};
+        const bool ok = tid + NT * m < NV;
+        sv[m] = ok ? reinterpret_cast<const V *>(Sc)[tid + NT * m] : V{};
+        gv[m] = ok ? reinterpret_cast<const V *>(Gc)[tid + NT * m] : V{};
       }
       double x = 0.0;
 #pragma unroll
@@ -1310,36 +1379,42 @@ __global__ __launch_bounds__(256) void bwd_dv(const BwdParams p) {
     if (p.a_log) {
       // per token: (pairs with key u, query later in the chunk) - (pairs with query u,
       // key earlier in the chunk); the chunk-level constant X_c
+      if (tid < nv) {
+        float rs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r;
-        const float rs = sum16(rowsum[r]);
-        if (i == 0 && j < nv) p.eW[bh * p.n + t0 + j] = rs - (sCol[0][j] + sCol[1][j] + sCol[2][j] + sCol[3][j]);
+        for (int u = 0; u < NH; ++u) rs += sRow[u][tid];
+        p.eW[bh * p.n + t0 + tid] = rs - (sCol[0][tid] + sCol[1][tid] + sCol[2][tid] + sCol[3][tid]);
       }
       if (tid == 0) {
         const float eLam = p.dt ? __expf(sL[nv - 1]) : 1.f;
-        p.Xc[bh * p.nch + c] = (float)((sX[0] + sX[1] + sX[2] + sX[3]) * eLam);
+        double xs = 0.0;
+#pragma unroll
+        for (int u = 0; u < NW; ++u) xs += sX[u];
+        p.Xc[bh * p.nch + c] = (float)(xs * eLam);
       }
     }
     const float Lam = sL[nv - 1];
     DV_ = (T *)p.dv + b * p.sv_b + h * p.sv_h + t0 * p.sv_t;
     nv_prev = nv;
-    Frags<T, C> fp;  // this wave's rows of the masked scores
-    fp.load(sP + 16 * w * LC, LC);
+    Frags<T, C> fp;  // the band's rows of the masked scores
+    fp.load(sP + 16 * rt * LC, LC);
 #pragma unroll
-    for (int ct = 0; ct < DV / 16; ++ct) {
-      const f32x4 a1 = mm(fp, sNT + 16 * ct * LC, LC, zero4());
-      const f32x4 a2 = mm(fk, sGT + 16 * ct * LF, LF, zero4());
+    for (int m = 0; m < MV; ++m) {
+      const int ct = hw + NH * m;
+      if (ct < DV / 16) {
+        const f32x4 a1 = mm(fp, sNT + 16 * ct * LC, LC, zero4());
+        const f32x4 a2 = mm(fk, sGT + 16 * ct * LF, LF, zero4());
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 16 * w + 4 * g + r;
-        const float e = p.dt ? __expf(Lam - sL[j]) : 1.f;
-        sQ[j * LF + 16 * ct + i] = (T)(a1[r] + e * a2[r]);  // rows into sQ
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * rt + 4 * g + r;
+          const float e = p.dt ? __expf(Lam - sL[j]) : 1.f;
+          sQ[j * LF + 16 * ct + i] = (T)(a1[r] + e * a2[r]);  // rows into sQ
+        }
       }
     }
     __syncthreads();
   }
-  if (c1 > c0) rows_to_global<T, C, DV>(DV_, p.sv_t, sQ, LF, nv_prev);
+  if (c1 > c0) rows_to_global<T, C, DV, NT>(DV_, p.sv_t, sQ, LF, nv_prev);
 }
 
 // ---------------------------------------------------------------- bwd_decay

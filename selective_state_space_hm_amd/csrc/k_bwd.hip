@@ -35,8 +35,8 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
     hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(256), 0, s, p);
   }
   hipLaunchKernelGGL((bwd_dq<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(bwd_waves(ROPE) * 64), 0, s, p);
-  hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
-  if (p.nch > 0) hipLaunchKernelGGL((bwd_dv<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(bwd_waves(ROPE) * 64), 0, s, p);
+  if (p.nch > 0) hipLaunchKernelGGL((bwd_dv<T, DK, FH, DV>), dim3(BH * (unsigned)p.ngrp), dim3(bwd_waves(false) * 64), 0, s, p);
   if (p.a_log) hipLaunchKernelGGL(bwd_decay, dim3(BH), dim3(256), 0, s, p);  // dt may be NULL only when n = 0
   const int per_head = p.sw_h != 0;
   const int64_t nw = (per_head ? p.H : 1) * (int64_t)DK * FH;
