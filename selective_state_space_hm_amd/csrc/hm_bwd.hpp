@@ -130,24 +130,24 @@ __device__ __forceinline__ f32x4 mm(const T *A, int la, const Frags<T, K> &b, f3
   return acc;
 }
 
-// S[m] = e * S[m] + A_rt B_ct^T over tiles tt = wave + 4m (rt = tt / CT, ct = tt % CT)
+// S[m] = e * S[m] + A_rt B_ct^T over tiles tt = wave + NW m (rt = tt / CT, ct = tt % CT)
 // of an [F][CT * 16] accumulator, A and B rows K-contiguous in LDS.  When CT divides
-// 4 every tile of a wave has the same ct, and B's fragments are read once.
-template <typename T, int K, int NTT, int TILES, int CT>
+// NW every tile of a wave has the same ct, and B's fragments are read once.
+template <typename T, int K, int NTT, int TILES, int CT, int NW = 4>
 __device__ __forceinline__ void tiles_mm(f32x4 (&S)[NTT], float e, const T *A, const T *B, int ld) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if constexpr (4 % CT == 0) {
+  if constexpr (NW % CT == 0) {
     Frags<T, K> fb;
     fb.load(B + 16 * (w % CT) * ld, ld);
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-      const int tt = w + 4 * m;
+      const int tt = w + NW * m;
       if (tt < TILES) S[m] = mm<T, K>(A + 16 * (tt / CT) * ld, ld, fb, S[m] * e);
     }
   } else {
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-      const int tt = w + 4 * m;
+      const int tt = w + NW * m;
       if (tt < TILES) S[m] = mm<T, K>(A + 16 * (tt / CT) * ld, ld, B + 16 * (tt % CT) * ld, ld, S[m] * e);
     }
   }
@@ -157,16 +157,16 @@ template <typename T> struct Vec { typedef T type __attribute__((ext_vector_type
 
 // A workgroup's [ROWS][COLS] state tile, rounded to T, from accumulator tiles to
 // global rows (stride gs elements) in two steps: tile_to_lds() writes element
-// (16 rt + 4g + r, 16 ct + i) of tile tt = wave + 4m into LDS rows (stride lo);
+// (16 rt + 4g + r, 16 ct + i) of tile tt = wave + NW m into LDS rows (stride lo);
 // after a barrier, lds_to_global() sends whole 16-byte pieces.  Four 2-byte stores
 // per tile and lane become one 16-byte store per lane and pass: measured in the
 // chunk-serial kernels, issuing the scattered stores took a quarter of their time.
-template <typename T, int NTT, int TILES, int CT>
+template <typename T, int NTT, int TILES, int CT, int NW = 4>
 __device__ __forceinline__ void tile_to_lds(T *dst, int lo, const f32x4 (&X)[NTT]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, i = lane & 15, w = threadIdx.x >> 6;
 #pragma unroll
   for (int m = 0; m < NTT; ++m) {
-    const int tt = w + 4 * m;
+    const int tt = w + NW * m;
     if (tt < TILES) {
       const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
@@ -186,12 +186,12 @@ __device__ __forceinline__ void rows_to_global(T *dst, int64_t gs, const T *src,
     if (r < valid) *reinterpret_cast<V *>(dst + r * gs + pc * E) = *reinterpret_cast<const V *>(src + r * lo + pc * E);
   }
 }
-template <typename T, int ROWS, int COLS>
+template <typename T, int ROWS, int COLS, int NT = 256>
 __device__ __forceinline__ void lds_to_global(T *dst, int64_t gs, const T *src, int lo) {
   constexpr int E = ep<T>(), PPR = COLS / E, N = ROWS * PPR;
   typedef typename Vec<T>::type V;
 #pragma unroll
-  for (int idx = threadIdx.x; idx < N; idx += 256) {
+  for (int idx = threadIdx.x; idx < N; idx += NT) {
     const int r = idx / PPR, pc = idx % PPR;
     *reinterpret_cast<V *>(dst + r * gs + pc * E) = *reinterpret_cast<const V *>(src + r * lo + pc * E);
   }
@@ -446,6 +446,16 @@ __device__ __forceinline__ void chunk_range(const BwdParams &p, int grp, int64_t
   c1 = c0 + per < p.nch ? c0 + per : p.nch;
 }
 
+// Waves of a bwd_states / bwd_gstate workgroup: each wave carries TILES / 8 of the
+// share's state tiles through the chunks, two waves per SIMD.
+constexpr int kChainWaves = 8;
+
+// Waves of a bwd_dq workgroup: two per SIMD, each 16-row band of the chunk split
+// between two waves by column tiles, so that one wave's MFMA chains and LDS waits
+// overlap the other's.  The rotary variants keep one wave per band: the rotation pairs
+// feature tiles across that split.
+constexpr int bwd_waves(bool rope) { return rope ? 4 : 8; }
+
 // ---------------------------------------------------------------- bwd_prep
 // One workgroup per (b, h, chunk): phiq (unnormalized, as the forward computed
 // it), phik (softmax), dnum, dden and L for the chunk's tokens.
@@ -607,11 +617,12 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
 // (they read the same phik rows through its L2).  The next chunk's operands are
 // fetched while the current chunk's products run.
 template <typename T, int DK, int FH, int DV, int DS>
-__global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
+__global__ __launch_bounds__(kChainWaves * 64) void bwd_states(const BwdParams p) {
   using namespace bw;
+  constexpr int NW = kChainWaves, NT = 64 * NW;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD, DVW = DV / DS;
-  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
-  static_assert(2 * F <= 256 && C == 64, "two threads per feature for z, 32 tokens each");
+  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + NW - 1) / NW;
+  static_assert(2 * F <= NT && C == 64, "two threads per feature for z, 32 tokens each");
   static_assert(DVW % 16 == 0, "whole column tiles per share");
   __shared__ __align__(16) T sA[F * LDC_];    // (e^{Lam - L_j} phik_j)^T: [f][j]
   __shared__ __align__(16) T sB[DVW * LDC_];  // v^T of the share's columns: [c][j]
@@ -644,7 +655,7 @@ __global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
 #pragma unroll
   for (int m = 0; m < NTT; ++m) {
     S[m] = zero4();
-    const int tt = w + 4 * m;
+    const int tt = w + NW * m;
     if (tt < TILES) {
       const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
@@ -654,8 +665,8 @@ __global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
   const int zf_ = tid >> 1, zh = tid & 1;
   const bool zown = zshare && zh == 0 && zf_ < F;
   float zf = zown ? ck[(int64_t)F * DV + zf_] : 0.f;
-  StagedT<T, C, F> pf_k;
-  StagedT<T, C, DVW> pf_v;
+  StagedT<T, C, F, NT> pf_k;
+  StagedT<T, C, DVW, NT> pf_v;
   float pf_L = 0.f;  // thread t < C: the chunk-local log-decay prefix of token t
   auto load_chunk = [&](int64_t t0, int nv) {
     pf_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
@@ -667,11 +678,11 @@ __global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     // the state at the start of chunk c
-    tile_to_lds<T, NTT, TILES, CT>(sOut, LO, S);
+    tile_to_lds<T, NTT, TILES, CT, NW>(sOut, LO, S);
     if (zown) p.wz[(bh * p.nch + c) * F + zf_] = zf;
     if (tid == nv - 1) sLam[0] = pf_L;
     __syncthreads();
-    lds_to_global<T, F, DVW>((T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
+    lds_to_global<T, F, DVW, NT>((T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
     if (tid < C) sw[tid] = tid < nv ? (p.dt ? __expf(sLam[0] - pf_L) : 1.f) : 0.f;
     __syncthreads();
     pf_k.store(sA, LDC_, sw);
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
     const float eLam = p.dt ? __expf(sLam[0]) : 1.f;
     if (c + 1 < c1) load_chunk(t0 + C, (int)(p.n - t0 - C < C ? p.n - t0 - C : C));
     __syncthreads();
-    tiles_mm<T, C, NTT, TILES, CT>(S, eLam, sA, sB, LDC_);
+    tiles_mm<T, C, NTT, TILES, CT, NW>(S, eLam, sA, sB, LDC_);
     if (zshare && zf_ < F) {
       // z[f] += sum_j of the phik row as the products used it (rounded to the dtype):
       // threads 2f and 2f+1 each sum 32 tokens
@@ -711,10 +722,11 @@ __global__ __launch_bounds__(256) void bwd_states(const BwdParams p) {
 // different XCDs and the shares of one (b, h) share an XCD (and its copy of phi(q)
 // in L2).
 template <typename T, int DK, int FH, int DV, int DS>
-__global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
+__global__ __launch_bounds__(kChainWaves * 64) void bwd_gstate(const BwdParams p) {
   using namespace bw;
+  constexpr int NW = kChainWaves, NT = 64 * NW;
   constexpr int F = 2 * FH, PAD = Mma<T>::PAD, LDC_ = C + PAD, DVW = DV / DS;
-  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + 3) / 4;
+  constexpr int CT = DVW / 16, TILES = (F / 16) * CT, NTT = (TILES + NW - 1) / NW;
   static_assert(DVW % 16 == 0, "whole column tiles per share");
   __shared__ __align__(16) T sA[F * LDC_];    // (e^{L_t} phiq_t)^T: [f][t]
   __shared__ __align__(16) T sB[DVW * LDC_];  // dnum^T of the share's columns: [c][t]
@@ -737,14 +749,14 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   // the chunk's tokens; thread 2f owns g[f]
   const int gf = tid >> 1, gh = tid & 1;
   const bool gown = zshare && gh == 0 && gf < F;
-  static_assert(2 * F <= 256 && C == 64, "two threads per feature, 32 tokens each");
+  static_assert(2 * F <= NT && C == 64, "two threads per feature, 32 tokens each");
   const int64_t BLK = (int64_t)F * DV + F;
   f32x4 G[NTT];
   float gz = 0.f;
 #pragma unroll
   for (int m = 0; m < NTT; ++m) {
     G[m] = zero4();
-    const int tt = w + 4 * m;
+    const int tt = w + NW * m;
     if (tt < TILES && p.ds_final) {
       const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
@@ -755,8 +767,8 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   // the (earlier) chunk's phi(q) and dnum are fetched while the current chunk's
   // products run: the chunks are visited one after the other, so each chunk's load
   // latency would otherwise stand alone
-  StagedT<T, C, F> pf_q;
-  StagedT<T, C, DVW> pf_n;
+  StagedT<T, C, F, NT> pf_q;
+  StagedT<T, C, DVW, NT> pf_n;
   // and its per-token log-decay and dden (thread t < C holds token t)
   float pf_L = 0.f, pf_dd = 0.f;
   bool pf_ok = false;
@@ -778,14 +790,14 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     // G, g at the end of chunk c
-    tile_to_lds<T, NTT, TILES, CT>(sOut, LO, G);
+    tile_to_lds<T, NTT, TILES, CT, NW>(sOut, LO, G);
     if (gown) p.gz[(bh * p.nch + c) * F + gf] = gz;
     if (tid < C) {
       seL[tid] = pf_ok ? (p.dt ? __expf(pf_L) : 1.f) : 0.f;
       sdd[tid] = pf_dd;
     }
     __syncthreads();
-    lds_to_global<T, F, DVW>((T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
+    lds_to_global<T, F, DVW, NT>((T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV) + col0, DV, sOut, LO);
     pf_q.store(sA, LDC_, seL);
     pf_n.store(sB, LDC_);
     if (c > 0) {
@@ -796,7 +808,7 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
     }
     const float eLam = seL[nv - 1];  // e^{Lambda} of the chunk (1 without decay)
     __syncthreads();
-    tiles_mm<T, C, NTT, TILES, CT>(G, eLam, sA, sB, LDC_);
+    tiles_mm<T, C, NTT, TILES, CT, NW>(G, eLam, sA, sB, LDC_);
     if (zshare && gf < F) {
       typedef T t4 __attribute__((ext_vector_type(4)));
       const T *row = sA + gf * LDC_ + 32 * gh;
@@ -820,7 +832,7 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
   if (p.ds_init) {
 #pragma unroll
     for (int m = 0; m < NTT; ++m) {
-      const int tt = w + 4 * m;
+      const int tt = w + NW * m;
       if (tt < TILES) {
         const int rt = tt / CT, ct = tt % CT;
 #pragma unroll
@@ -834,12 +846,6 @@ __global__ __launch_bounds__(256) void bwd_gstate(const BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_dq
 // dphiq -> du_q -> dq = du_q W_q^T, and this workgroup's share of dW_q.
-// Waves of a bwd_dq workgroup: two per SIMD, each 16-row band of the chunk split
-// between two waves by column tiles, so that one wave's MFMA chains and LDS waits
-// overlap the other's.  The rotary variants keep one wave per band: the rotation pairs
-// feature tiles across that split.
-constexpr int bwd_waves(bool rope) { return rope ? 4 : 8; }
-
 template <typename T, int DK, int FH, int DV, bool ROPE>
 __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dq(const BwdParams p) {
   using namespace bw;

@@ -17,9 +17,9 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
   if (p.nch > 0) {
     const unsigned items = BH * (unsigned)p.ngrp;
     if constexpr (DV % 32 == 0) {
-      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 2>), dim3((items + 7) / 8 * 16), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 2>), dim3((items + 7) / 8 * 16), dim3(kChainWaves * 64), 0, s, p);
     } else {
-      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 1>), dim3(items), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_states<T, DK, FH, DV, 1>), dim3(items), dim3(kChainWaves * 64), 0, s, p);
     }
   }
   // the gradient-state pass visits the chunks one after another, so with fewer
@@ -27,12 +27,12 @@ void launch_bwd(const BwdParams &p, hipStream_t s) {
   // (a four-way split measured slower on the Pythia layer: 105 vs 91 us)
   if constexpr (DV % 32 == 0) {
     if (BH < 256) {
-      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 2>), dim3((BH + 7) / 8 * 16), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 2>), dim3((BH + 7) / 8 * 16), dim3(kChainWaves * 64), 0, s, p);
     } else {
-      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(kChainWaves * 64), 0, s, p);
     }
   } else {
-    hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_gstate<T, DK, FH, DV, 1>), dim3(BH), dim3(kChainWaves * 64), 0, s, p);
   }
   hipLaunchKernelGGL((bwd_dq<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(bwd_waves(ROPE) * 64), 0, s, p);
   hipLaunchKernelGGL((bwd_dk<T, DK, FH, DV, ROPE>), dim3(BH * (unsigned)p.ngrp), dim3(bwd_waves(ROPE) * 64), 0, s, p);
