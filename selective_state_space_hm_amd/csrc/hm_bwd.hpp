@@ -875,28 +875,38 @@ __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dq(const BwdParams p
   f32x4 dW[NTW];
 #pragma unroll
   for (int m = 0; m < NTW; ++m) dW[m] = zero4();
-  for (int64_t c = c0; c < c1; ++c) {
+  // A chunk's operands are fetched while the previous chunk's products run (the chunks
+  // of a range are visited one after another, so each load latency would otherwise
+  // stand alone); all of them go out before the first LDS write.  The four-wave
+  // (rotary) variants hold twice the registers per thread for them and fetch at the
+  // chunk's top instead.
+  constexpr bool PREFETCH = NH > 1;
+  Staged<T, C, F, NT> phq_next;  // phi(q) rows, written over v once A is formed
+  Staged<T, C, DV, NT> st_dn, st_v;
+  StagedT<T, C, DK, NT> st_x;
+  StagedT<T, C, F, NT> st_k;
+  Staged<T, F, DV, NT> st_s;
+  float tl = 0.f, tdd = 0.f, tz = 0.f;  // per-token log-decay and dden, z at the chunk start
+  auto fetch = [&](int64_t c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    // every operand load of the chunk goes out before the first LDS write: one memory
-    // round trip per chunk instead of one per operand
-    Staged<T, C, F, NT> phq_next;  // phi(q) rows, written over v once A is formed
-    Staged<T, C, DV, NT> st_dn, st_v;
-    StagedT<T, C, DK, NT> st_x;
-    StagedT<T, C, F, NT> st_k;
-    Staged<T, F, DV, NT> st_s;
     st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     st_x.load((const T *)p.q + b * p.sq_b + h * p.sq_h + t0 * p.sq_t, p.sq_t, nv);
     st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
     st_s.load((const T *)p.wS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phq_next.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-    float tl = 0.f, tdd = 0.f, tz = 0.f;  // per-token log-decay and dden, z at the chunk start
     if (tid < C) {
       tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
     if (tid < F) tz = p.wz[(bh * p.nch + c) * F + tid];
+  };
+  if (PREFETCH && c0 < c1) fetch(c0);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    if constexpr (!PREFETCH) fetch(c);
     st_dn.store(sDN, LN);
     st_v.store(sVQ, LVQ);
     st_x.store(sXT, LC);
@@ -926,6 +936,7 @@ __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dq(const BwdParams p
     }
     __syncthreads();
     phq_next.store(sVQ, LVQ);
+    if (PREFETCH && c + 1 < c1) fetch(c + 1);
     __syncthreads();
     // dphiq[t][F] = sum_j A[t][j] phik[j][F] + e^{L_t} (S_c dnum_t + dden_t z_c)[F], for
     // the feature tiles ft = hw + NH m and ft + FT (the pair that du combines)
@@ -1075,27 +1086,34 @@ __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dk(const BwdParams p
   f32x4 dW[NTW];
 #pragma unroll
   for (int m = 0; m < NTW; ++m) dW[m] = zero4();
-  for (int64_t c = c0; c < c1; ++c) {
+  // the next chunk's operands are fetched during this chunk's products, as in bwd_dq
+  constexpr bool PREFETCH = NH > 1;
+  Staged<T, C, F, NT> phk_next;  // phi(k) rows, written over dnum once A^T is formed
+  Staged<T, C, DV, NT> st_dn, st_v;
+  StagedT<T, C, DK, NT> st_x;
+  StagedT<T, C, F, NT> st_q;
+  Staged<T, F, DV, NT> st_g;
+  float tl = 0.f, tdd = 0.f, tg = 0.f;  // per-token log-decay and dden, g at the chunk end
+  auto fetch = [&](int64_t c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
-    // every operand load of the chunk goes out before the first LDS write
-    Staged<T, C, F, NT> phk_next;  // phi(k) rows, written over dnum once A^T is formed
-    Staged<T, C, DV, NT> st_dn, st_v;
-    StagedT<T, C, DK, NT> st_x;
-    StagedT<T, C, F, NT> st_q;
-    Staged<T, F, DV, NT> st_g;
     st_dn.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     st_v.load((const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
     st_x.load((const T *)p.k + b * p.sk_b + h * p.sk_h + t0 * p.sk_t, p.sk_t, nv);
     st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
     st_g.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
     phk_next.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-    float tl = 0.f, tdd = 0.f, tg = 0.f;  // per-token log-decay and dden, g at the chunk end
     if (tid < C) {
       tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
       tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
     }
     if (tid < F) tg = p.gz[(bh * p.nch + c) * F + tid];
+  };
+  if (PREFETCH && c0 < c1) fetch(c0);
+  for (int64_t c = c0; c < c1; ++c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    if constexpr (!PREFETCH) fetch(c);
     st_dn.store(sNK, LNK);
     st_v.store(sV, LV);
     st_x.store(sXT, LC);
@@ -1125,6 +1143,7 @@ __global__ __launch_bounds__(bwd_waves(ROPE) * 64) void bwd_dk(const BwdParams p
     }
     __syncthreads();
     phk_next.store(sNK, LNK);
+    if (PREFETCH && c + 1 < c1) fetch(c + 1);
     __syncthreads();
     // dphik[j][F] = sum_t A^T[j][t] phiq[t][F] + e^{Lam - L_j} (G v_j + g)[F], for the
     // feature tiles ft = hw + NH m and ft + FT (the pair that du combines)
@@ -1287,23 +1306,28 @@ __global__ __launch_bounds__(bwd_waves(false) * 64) void bwd_dv(const BwdParams 
   // (155 -> 147 us on the Pythia layer; the same for dq and dk measured slower)
   T *DV_ = nullptr;
   int nv_prev = 0;
+  // the next chunk's operands are fetched during this chunk's products, as in bwd_dq
+  Staged<T, C, F, NT> st_k, st_q;
+  StagedT<T, C, DV, NT> st_nt;
+  StagedT<T, F, DV, NT> st_gt;
+  float tl = 0.f, tdd = 0.f;  // per-token log-decay and dden
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * C;
+    const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
+    st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
+    st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
+    st_nt.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
+    st_gt.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
+    if (tid < C) {
+      tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
+      tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
+    }
+  };
+  if (c0 < c1) fetch(c0);
   for (int64_t c = c0; c < c1; ++c) {
     const int64_t t0 = c * C;
     const int nv = (int)(p.n - t0 < C ? p.n - t0 : C);
     {
-      // every operand load of the chunk goes out before the first LDS write
-      Staged<T, C, F, NT> st_k, st_q;
-      StagedT<T, C, DV, NT> st_nt;
-      StagedT<T, F, DV, NT> st_gt;
-      st_k.load((const T *)p.phk + (bh * p.n + t0) * F, F, nv);
-      st_q.load((const T *)p.phq + (bh * p.n + t0) * F, F, nv);
-      st_nt.load((const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
-      st_gt.load((const T *)p.gS + (bh * p.nch + c) * ((int64_t)F * DV), DV, F);
-      float tl = 0.f, tdd = 0.f;  // per-token log-decay and dden
-      if (tid < C) {
-        tl = p.dt ? p.Lc[bh * p.n + t0 + (tid < nv ? tid : nv - 1)] : 0.f;  // padding rows: log a = 0
-        tdd = tid < nv ? p.dden[bh * p.n + t0 + tid] : 0.f;
-      }
       if (c > c0) {
         rows_to_global<T, C, DV, NT>(DV_, p.sv_t, sQ, LF, nv_prev);
         __syncthreads();
@@ -1321,6 +1345,7 @@ __global__ __launch_bounds__(bwd_waves(false) * 64) void bwd_dv(const BwdParams 
       stage<T, C, DV, NT>(sV, LV, (const T *)p.v + b * p.sv_b + h * p.sv_h + t0 * p.sv_t, p.sv_t, nv);
       stage<T, C, DV, NT>(sN, LV, (const T *)p.dnum + (bh * p.n + t0) * DV, DV, nv);
     }
+    if (c + 1 < c1) fetch(c + 1);
     __syncthreads();
     // Pt[j][t] = [j <= t] e^{L_t - L_j} phik_j . phiq_t, and for the decay gradient the
     // pair weights W^T[j][t] = [j < t] Pt[j][t] (v_j . dnum_t + dden_t): their sums
