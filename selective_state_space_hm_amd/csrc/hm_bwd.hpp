@@ -67,8 +67,10 @@ template <typename T> constexpr int ep() { return 16 / (int)sizeof(T); }
 // The operand registers stay allocated until the chain's result has been read:
 // measured on gfx950, a VALU write (here an accumulator read into a VGPR that had
 // just been freed) to a source register of an MFMA still waiting on the previous
-// MFMA of its chain changed that MFMA's operand; the empty asm below keeps every
-// fragment live past the point where the result is available.
+// MFMA of its chain changed that MFMA's operand.  The empty asm below reads every
+// fragment and passes the accumulator through, so the fragments stay live until the
+// result is available and later uses of the result come after it.  It is not
+// volatile: independent work (the next product's LDS reads) may still move above it.
 template <typename T, int K>
 __device__ __forceinline__ f32x4 mm(const T *A, int la, const T *B, int lb, f32x4 acc) {
   using M = Mma<T>;
@@ -83,7 +85,7 @@ __device__ __forceinline__ f32x4 mm(const T *A, int la, const T *B, int lb, f32x
 #pragma unroll
   for (int s = 0; s < NK; ++s) acc = M::mma(a[s], b[s], acc);
 #pragma unroll
-  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a[s]), "v"(b[s]), "v"(acc));
+  for (int s = 0; s < NK; ++s) asm("" : "+v"(acc) : "v"(a[s]), "v"(b[s]));
   return acc;
 }
 
@@ -110,7 +112,7 @@ __device__ __forceinline__ f32x4 mm(const Frags<T, K> &a, const T *B, int lb, f3
 #pragma unroll
   for (int s = 0; s < NK; ++s) acc = M::mma(a.f[s], b[s], acc);
 #pragma unroll
-  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a.f[s]), "v"(b[s]), "v"(acc));
+  for (int s = 0; s < NK; ++s) asm("" : "+v"(acc) : "v"(a.f[s]), "v"(b[s]));
   return acc;
 }
 
@@ -126,7 +128,7 @@ __device__ __forceinline__ f32x4 mm(const T *A, int la, const Frags<T, K> &b, f3
 #pragma unroll
   for (int s = 0; s < NK; ++s) acc = M::mma(a[s], b.f[s], acc);
 #pragma unroll
-  for (int s = 0; s < NK; ++s) asm volatile("" ::"v"(a[s]), "v"(b.f[s]), "v"(acc));
+  for (int s = 0; s < NK; ++s) asm("" : "+v"(acc) : "v"(a[s]), "v"(b.f[s]));
   return acc;
 }
 
