@@ -974,7 +974,8 @@ hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
   p.sx_b = a->sx_b; p.sx_h = a->sx_h; p.sx_t = a->sx_t; p.sw_h = a->sw_h;
   p.sp_b = a->sp_b; p.sp_h = a->sp_h; p.sp_t = a->sp_t;
   p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
-  e->launch(p, dim3((unsigned)((a->n + 63) / 64), (unsigned)BH), (hipStream_t)stream);
+  const int64_t per = 64 * hm::kFeatBlocks;  // tokens per workgroup
+  e->launch(p, dim3((unsigned)((a->n + per - 1) / per), (unsigned)BH), (hipStream_t)stream);
   return check_launch("featurize");
 }
 

@@ -303,8 +303,10 @@ __device__ __forceinline__ float feature_tiles(const typename Mma<T>::frag *xf, 
 }
 
 // Standalone Hedgehog featurizer: phi = softmax([x W, -x W]).  One workgroup =
-// 64 tokens of one (b, h); wave w featurizes token tile w (feature_tiles) and
-// stores phi rows with 8/16-byte vector stores.
+// kFeatBlocks 64-token blocks of one (b, h), so that W^T is staged once per 256
+// tokens; wave w featurizes token tile w of each block, the next block's x rows in
+// flight meanwhile, and stores phi rows with 8/16-byte vector stores.
+constexpr int kFeatBlocks = 4;
 template <typename T, typename TO, int DK, int FH>
 __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   using M = Mma<T>;
@@ -314,25 +316,54 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   __shared__ double sRev[FH];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
-  const T *W = (const T *)p.w + h * p.sw_h;
-  for (int i = tid; i < DK * FH; i += 256) sW[(i % FH) * LDW + i / FH] = W[i];
-  if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
-  const int64_t c = (int64_t)blockIdx.x * 64 + 16 * wv + col;
-  const T *X = (const T *)p.x + b * p.sx_b + h * p.sx_h + c * p.sx_t;
-  frag xf[KD];
+  {
+    // W^T: sW[f][d] = W[d][f], W read as 16-byte vectors, all issued before the first LDS write
+    constexpr int EP = 16 / (int)sizeof(T), NV = DK * FH / EP, VPT = (NV + 255) / 256;
+    typedef T tvec __attribute__((ext_vector_type(EP)));
+    const T *W = (const T *)p.w + h * p.sw_h;
+    tvec wv4[VPT];
 #pragma unroll
-  for (int s = 0; s < KD; ++s) xf[s] = c < p.n ? M::ld_contig(X + s * M::KS, g) : frag{};
-  __syncthreads();
-  f32x4 ph[NFT];
-  const float inv = 1.f / feature_tiles<T, DK, FH>(xf, sW, ph);
-  if (p.rope_dims > 0) {
-    const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + c);
-    rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);
+    for (int i = 0; i < VPT; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NV) wv4[i] = *reinterpret_cast<const tvec *>(W + v * EP);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int v = tid + 256 * i;
+      if (v < NV) {
+        const int d = v * EP / FH, f0 = v * EP % FH;
+#pragma unroll
+        for (int e = 0; e < EP; ++e) sW[(f0 + e) * LDW + d] = wv4[i][e];
+      }
+    }
   }
-  if (c < p.n) {
-    TO *P = (TO *)p.phi + b * p.sp_b + h * p.sp_h + c * p.sp_t;
+  if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
+  const int64_t c0 = (int64_t)blockIdx.x * 64 * kFeatBlocks + 16 * wv + col;  // this lane's token in block 0
+  const T *X0 = (const T *)p.x + b * p.sx_b + h * p.sx_h;
+  frag xf[KD], xn[KD];
+  auto load_x = [&](frag *x, int64_t c) {
 #pragma unroll
-    for (int t = 0; t < NFT; ++t) store4(P + 16 * t + 4 * g, ph[t] * inv);
+    for (int s = 0; s < KD; ++s) x[s] = c < p.n ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g) : frag{};
+  };
+  load_x(xf, c0);
+  __syncthreads();
+  for (int r = 0; r < kFeatBlocks; ++r) {
+    const int64_t c = c0 + 64 * r;
+    if (c - 16 * wv - col >= p.n) break;  // the workgroup's last block (uniform over the workgroup)
+    if (r + 1 < kFeatBlocks) load_x(xn, c + 64);
+    f32x4 ph[NFT];
+    const float inv = 1.f / feature_tiles<T, DK, FH>(xf, sW, ph);
+    if (p.rope_dims > 0) {
+      const double pos = (double)((p.rope_pos0 ? p.rope_pos0[b] : 0) + c);
+      rope_apply<NFT>(ph, sRev, g, pos, p.rope_dims);
+    }
+    if (c < p.n) {
+      TO *P = (TO *)p.phi + b * p.sp_b + h * p.sp_h + c * p.sp_t;
+#pragma unroll
+      for (int t = 0; t < NFT; ++t) store4(P + 16 * t + 4 * g, ph[t] * inv);
+    }
+#pragma unroll
+    for (int s = 0; s < KD; ++s) xf[s] = xn[s];
   }
 }
 

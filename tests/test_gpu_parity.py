@@ -30,17 +30,19 @@ def full_oracle(case, s_init=None, z_init=None, form="recurrent"):
 
 
 # ------------------------------------------------------------------ featurize
-@pytest.mark.parametrize("dtype,phi_dtype,d,f", [
-    (torch.float32, torch.float32, 16, 16), (torch.float32, torch.float32, 128, 64),
-    (torch.float32, torch.float32, 64, 32), (torch.bfloat16, torch.bfloat16, 128, 64),
-    (torch.bfloat16, torch.float32, 128, 64), (torch.bfloat16, torch.float32, 32, 16)])
-def test_featurize(dtype, phi_dtype, d, f):
-    c = inputs.make_prefill("feat", 2, 3, 77, d, f, 16, dtype, None, None, seed=3)
+@pytest.mark.parametrize("dtype,phi_dtype,d,f,n", [
+    (torch.float32, torch.float32, 16, 16, 77), (torch.float32, torch.float32, 128, 64, 77),
+    (torch.float32, torch.float32, 64, 32, 77), (torch.bfloat16, torch.bfloat16, 128, 64, 77),
+    (torch.bfloat16, torch.float32, 128, 64, 77), (torch.bfloat16, torch.float32, 32, 16, 77),
+    # several workgroups of four 64-token blocks, the last one ragged
+    (torch.bfloat16, torch.bfloat16, 128, 64, 600), (torch.float32, torch.float32, 64, 32, 600)])
+def test_featurize(dtype, phi_dtype, d, f, n):
+    c = inputs.make_prefill("feat", 2, 3, n, d, f, 16, dtype, None, None, seed=3)
     phi = hm.hm_featurize(c.q.cuda(), c.w_q.cuda(), phi_dtype=phi_dtype)
     torch.cuda.synchronize()
     ref = orc.hedgehog_features(f64(c.q), f64(c.w_q))
     got = f64(phi)
-    r = report(f"featurize {dtype} -> {phi_dtype} d={d} f={f}", got, ref)
+    r = report(f"featurize {dtype} -> {phi_dtype} d={d} f={f} n={n}", got, ref)
     # float32 output: the float32 softmax itself; bf16 output adds one rounding (2^-9)
     assert r <= (FP32_TOL if phi_dtype == torch.float32 else 4e-3)
     np.testing.assert_allclose(got.sum(-1), 1.0, rtol=0, atol=1e-5 if phi_dtype == torch.float32 else 2e-2)
