@@ -334,7 +334,8 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
     auto load_dt = [&](int64_t tc) {
       if constexpr (DECAY) dtn = tc + lane < t1 ? DT[(tc + lane) * p.sdt_t] : 0.f;
     };
-    // Wave 1: decay factors of the chunk starting at tc into buffer `bufi`
+    // Wave 2 (one of the two with two score tiles): decay factors of the chunk starting
+    // at tc into buffer `bufi`
     double lam = 0.0;
     auto decay = [&](int64_t tc, int bufi) {
       decay_factors<DECAY>(sL[bufi], seL[bufi], seK[bufi], sLast[bufi], tc + lane < t1, dtn, expA, lam, lane);
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 
     if (nch > 0) {
       load_x(t0);
-      if (FULL && wv == 1) {
+      if (FULL && wv == 2) {
         load_dt(t0);
         decay(t0, 0);
         if (nch > 1) load_dt(t0 + C);
@@ -588,7 +589,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
       // The segment pass has one barrier per chunk: its state waves carry z and the
       // decay factors (see there), so the feature waves only featurize.
       if constexpr (FULL) __syncthreads();
-      // ---- half B: score tiles and z over chunk j, decay of chunk j+1 (wave 1)
+      // ---- half B: score tiles and z over chunk j, decay of chunk j+1 (wave 2)
       if (FULL && j < nch) {
         if constexpr (FULL) {
           // Ten causal tiles (a <= b): wave w forms (w, w) from its own phiK and
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
             if (col == 0) *reinterpret_cast<f32x4 *>(&sZ[bf][16 * t + 4 * g]) = Z[i];
           }
         }
-        if (wv == 1 && j + 1 < nch) {
+        if (wv == 2 && j + 1 < nch) {
           decay(tf + C, (int)((j + 1) % NDB));
           if (j + 2 < nch) load_dt(tf + 2 * C);
         }
