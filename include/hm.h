@@ -68,7 +68,8 @@
  *                (d, f, dv) = (32, 16, 32), and dv = 32 at (64, 32) and (128, 64)
  *                (hm_linattn_fwd: dv = 32 at every (d, f) of the first line, and
  *                (32, 16, 64) as two 32-column workgroups, dsplit 2)
- *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}
+ *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}; and d = 64 with
+ *                (f, dv) in {(16, 16), (16, 32), (32, 32), (32, 64)}
  *       Not built, and why:
  *         f32 at d = 128, f = 64: the full pass keeps W_q^T, W_k^T, two blocks of
  *           phi(q) rows and of phi(k)^T, the score tile and the output rows in LDS:

@@ -40,7 +40,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
 
 struct Tables {
-  hm::Table parts[9];
+  hm::Table parts[10];
   Tables() {
     parts[0] = hm::table_fwd_bf16();
     parts[1] = hm::table_fwd_bf16_decay();
@@ -51,6 +51,7 @@ struct Tables {
     parts[6] = hm::table_fwd_rope_bf16_decay();
     parts[7] = hm::table_fwd_rope_f32();
     parts[8] = hm::table_fwd_c128();
+    parts[9] = hm::table_fwd_f32_d64();
   }
 };
 const Tables &tables() {

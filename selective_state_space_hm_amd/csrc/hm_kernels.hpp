@@ -71,6 +71,7 @@ Table table_train();
 Table table_fwd_bf16();
 Table table_fwd_bf16_decay();
 Table table_fwd_f32();
+Table table_fwd_f32_d64();
 Table table_fwd_rope_bf16();
 Table table_fwd_rope_bf16_decay();
 Table table_fwd_rope_f32();

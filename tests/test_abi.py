@@ -164,6 +164,11 @@ def test_plans():
     st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=16, f=16, dv=16, dtype=hm.HM_F32))
     expect(st, hm.HM_OK)
     assert plan[2] == 1                                 # dv=16 cannot be split
+    for f_, dv_ in ((16, 16), (16, 32), (32, 32), (32, 64)):   # float32 at d = 64
+        st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=64, f=f_, dv=dv_, dtype=hm.HM_F32))
+        expect(st, hm.HM_OK)
+    st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=64, f=64, dv=64, dtype=hm.HM_F32))
+    expect(st, hm.HM_ERR_UNSUPPORTED)                   # float32 (64, 64, 64) is not built
 
 
 def test_alias_needs_init_copy_workspace():

@@ -105,6 +105,31 @@ def test_fp32_plans_with_initial_state(dv, segments, dsplit):
     assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
 
 
+@pytest.mark.parametrize("f,dv", [(16, 16), (16, 32), (32, 32), (32, 64)])
+@pytest.mark.parametrize("segments,dsplit", [(1, 1), (3, 1), (2, 2)])
+def test_fp32_d64(f, dv, segments, dsplit):
+    """float32 at d = 64: ragged n (five chunks and a tail), Mamba decay, a non-zero
+    initial state, segmented and column-split plans, against the oracle (output and
+    final state).  Column halves exist where the half width is built."""
+    if dsplit == 2 and (f, dv) not in ((16, 32), (32, 64)):
+        pytest.skip("no float32 d=64 kernel at half this width")
+    c = inputs.small(n=333, decay="mamba", dtype=torch.float32, d=64, f=f, dv=dv, B=2, H=2, seed=f + dv)
+    F = 2 * f
+    r = np.random.default_rng(7)
+    kk = r.random((2, 2, 9, F))
+    kk /= kk.sum(-1, keepdims=True)
+    S0 = np.einsum("bhjf,bhjd->bhfd", kk, r.normal(size=(2, 2, 9, dv)))
+    z0 = kk.sum(2)
+    s_init = torch.tensor(orc.pack_state(S0, z0), dtype=torch.float32, device="cuda")
+    s_final = torch.empty_like(s_init)
+    o = run_fwd(c, s_init=s_init, s_final=s_final, segments=segments, dsplit=dsplit)
+    torch.cuda.synchronize()
+    ref, S, z = full_oracle(c, S0, z0)
+    assert report(f"fp32 d=64 f={f} dv={dv} segs={segments} dsplit={dsplit}", f64(o), ref) <= FP32_TOL
+    Sg, zg = orc.unpack_state(f64(s_final), F, dv)
+    assert rel_l2(Sg, S) <= FP32_TOL and rel_l2(zg, z) <= FP32_TOL
+
+
 @pytest.mark.parametrize("decay", ["mild", "mamba"])
 @pytest.mark.parametrize("segments,dsplit", [(2, 1), (2, 2), (4, 1), (3, 1)])
 def test_fp32_segment_pass_slots(decay, segments, dsplit):
@@ -228,6 +253,7 @@ def test_split_handoff_with_aliased_state(segments, dsplit):
 
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("dtype,shape", [(torch.float32, (16, 16, 16)), (torch.float32, (32, 16, 32)),
+                                         (torch.float32, (64, 32, 64)), (torch.float32, (64, 16, 16)),
                                          (torch.bfloat16, (128, 64, 128)), (torch.bfloat16, (64, 32, 64)),
                                          (torch.bfloat16, (32, 16, 32)), (torch.bfloat16, (128, 64, 32))])
 @pytest.mark.parametrize("decay", [True, False])
