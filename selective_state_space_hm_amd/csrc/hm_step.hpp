@@ -316,6 +316,14 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   __shared__ double sRev[FH];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+  const int64_t c0 = (int64_t)blockIdx.x * 64 * kFeatBlocks + 16 * wv + col;  // this lane's token in block 0
+  const T *X0 = (const T *)p.x + b * p.sx_b + h * p.sx_h;
+  frag xf[KD], xn[KD];
+  auto load_x = [&](frag *x, int64_t c) {
+#pragma unroll
+    for (int s = 0; s < KD; ++s) x[s] = c < p.n ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g) : frag{};
+  };
+  load_x(xf, c0);  // the first block's rows go out before W^T is staged
   {
     // W^T: sW[f][d] = W[d][f], W read as 16-byte vectors, all issued before the first LDS write
     constexpr int EP = 16 / (int)sizeof(T), NV = DK * FH / EP, VPT = (NV + 255) / 256;
@@ -338,14 +346,6 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
     }
   }
   if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
-  const int64_t c0 = (int64_t)blockIdx.x * 64 * kFeatBlocks + 16 * wv + col;  // this lane's token in block 0
-  const T *X0 = (const T *)p.x + b * p.sx_b + h * p.sx_h;
-  frag xf[KD], xn[KD];
-  auto load_x = [&](frag *x, int64_t c) {
-#pragma unroll
-    for (int s = 0; s < KD; ++s) x[s] = c < p.n ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g) : frag{};
-  };
-  load_x(xf, c0);
   __syncthreads();
   for (int r = 0; r < kFeatBlocks; ++r) {
     const int64_t c = c0 + 64 * r;
