@@ -614,7 +614,7 @@ __global__ __launch_bounds__(256) void bwd_prep(const BwdParams p) {
 //   S <- e^{Lam} S + sum_j e^{Lam - L_j} phik_j v_j^T,   z likewise with v_j = 1,
 // (the forward's state update, on the phik rows bwd_prep wrote), S_c in the dtype
 // and z_c in float32 to the workspace before each chunk's update.  S [F][DV/DS]
-// lives in accumulators, tile tt = wave + 4m, as G in bwd_gstate; in the first
+// lives in accumulators, tile tt = wave + 8m, as G in bwd_gstate; in the first
 // share thread 2f owns z[f].  The shares of one (b, h, range) go to one XCD
 // (they read the same phik rows through its L2).  The next chunk's operands are
 // fetched while the current chunk's products run.
@@ -719,7 +719,7 @@ __global__ __launch_bounds__(kChainWaves * 64) void bwd_states(const BwdParams p
 // One workgroup per (b, h) and share of the value columns (DS shares of DV/DS;
 // the columns of G are independent), chunks from last to first: G and g at every
 // chunk's end go to the workspace; after chunk 0 they are the gradient of the
-// initial state.  G [F][DV/DS] lives in accumulators, tile tt = wave + 4m; the
+// initial state.  G [F][DV/DS] lives in accumulators, tile tt = wave + 8m; the
 // first share also carries g.  With DS > 1, consecutive workgroups go to
 // different XCDs and the shares of one (b, h) share an XCD (and its copy of phi(q)
 // in L2).
