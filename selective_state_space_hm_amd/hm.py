@@ -17,6 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhm.so")
 
+# HM_ABI_VERSION of include/hm.h that the argument structs below are laid out for
+ABI_VERSION = 8
 HM_OK, HM_ERR_NULL, HM_ERR_SHAPE, HM_ERR_DTYPE, HM_ERR_ALIGN, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(8)
 HM_F32, HM_BF16 = 0, 1
 CHUNK = 64
@@ -159,6 +161,9 @@ def lib():
         L.hm_abi_version.restype = C.c_int
         L.hm_args_size.argtypes = [C.c_int]
         L.hm_args_size.restype = C.c_size_t
+        if L.hm_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.hm_abi_version()}, this binding {ABI_VERSION}: "
+                               "rebuild with __graft_entry__.build()")
         _lib = L
     return _lib
 

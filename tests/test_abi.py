@@ -44,7 +44,9 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 8
+    assert hm.lib().hm_abi_version() == 8 == hm.ABI_VERSION
+    with open(os.path.join(ROOT, "include", "hm.h")) as fh:
+        assert re.search(r"#define HM_ABI_VERSION (\d+)", fh.read()).group(1) == str(hm.ABI_VERSION)
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
                                  "HM_ERR_UNSUPPORTED", "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
         assert hm.status_string(code) == name
