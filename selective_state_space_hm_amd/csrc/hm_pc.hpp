@@ -299,13 +299,101 @@ struct PcStepParams {
   int64_t sdt_b, sdt_h, sa_h;
 };
 
+// phi(q_t) and phi(k_t) of (b, h) into sphi[0] and sphi[1], worked by all 256
+// threads: the token rows are staged as floats (through the short causal conv when
+// one is given), then thread (part, group) multiplies its DPART rows of W, read as
+// 16-byte pieces of EPL consecutive outputs, into partial sums; the parts are added
+// in LDS and waves 0 (q) and 1 (k) turn the projections into softmax rows (and,
+// with rope_dims > 0, the rotary encoding turns both).  Ends with a barrier.
+template <typename T, int DK, int FH>
+struct PcFeat {
+  static constexpr int NT = 256, EPL = 16 / (int)sizeof(T), G = 2 * FH / EPL;  // G output groups
+  static constexpr int P = NT / G < DK ? NT / G : DK, DPART = DK / P;          // P parts of DK
+  static_assert(FH % EPL == 0 && DK % P == 0 && FH <= 64 && G * P <= NT, "feature mapping");
+};
+template <typename T, int DK, int FH>
+__device__ __forceinline__ void pc_step_features(const StepParams &p, int64_t b, int64_t h, float (*sx)[DK],
+                                                 float *su, float (*sphi)[2 * FH]) {
+  using PF = PcFeat<T, DK, FH>;
+  constexpr int NT = PF::NT, EPL = PF::EPL, G = PF::G, P = PF::P, DPART = PF::DPART;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 2 * DK; i += NT) sx[i / DK][i % DK] = step_input<T, DK>(p, b, h, i / DK, i % DK, nullptr);
+  __syncthreads();
+  if (tid < G * P) {
+    const int grp = tid % G, part = tid / G;
+    const int proj = grp * EPL / FH, j0 = grp * EPL % FH;
+    const T *W = (const T *)(proj == 0 ? p.wq : p.wk) + h * p.sw_h + j0;
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    // W rows in batches of WB pieces
+    constexpr int WB = DPART < 4 ? DPART : 4;
+#pragma unroll
+    for (int i0 = 0; i0 < DPART; i0 += WB) {
+      f32x4 wr[WB];
+#pragma unroll
+      for (int i = 0; i < WB; ++i)
+        wr[i] = *reinterpret_cast<const f32x4 *>(W + (int64_t)(part * DPART + i0 + i) * FH);
+#pragma unroll
+      for (int i = 0; i < WB; ++i) {
+        const T *wv = reinterpret_cast<const T *>(&wr[i]);
+        const float x = sx[proj][part * DPART + i0 + i];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(x, (float)wv[e], acc[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4)
+      *reinterpret_cast<f32x4 *>(&su[part * 2 * FH + proj * FH + j0 + e]) =
+          f32x4{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  }
+  __syncthreads();
+  {
+    const int w = tid >> 6, lane = tid & 63;
+    if (w < 2) {
+      float u = 0.f;
+      if (lane < FH) {
+#pragma unroll 8
+        for (int part = 0; part < P; ++part) u += su[part * 2 * FH + w * FH + lane];
+      }
+      float m = lane < FH ? fabsf(u) : 0.f;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      const float ep = lane < FH ? __expf(u - m) : 0.f, em = lane < FH ? __expf(-u - m) : 0.f;
+      float sum = ep + em;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      const float inv = 1.f / sum;
+      if (lane < FH) {
+        sphi[w][lane] = ep * inv;
+        sphi[w][FH + lane] = em * inv;
+      }
+    }
+  }
+  __syncthreads();
+  if (p.rope_dims > 0) {
+    // rotary encoding (HedgeMamba explainer §5.2 step 3): thread (row w, pair i)
+    // turns features i and i + dims/2 of phi(q) (w = 0) or phi(k) (w = 1)
+    const int hr = p.rope_dims / 2;
+    if (tid < 2 * hr) {
+      const int w = tid / hr, i = tid % hr;
+      float c, s, x1 = sphi[w][i], x2 = sphi[w][i + hr];
+      rope_cs(rope_rev(i, p.rope_dims, p.rope_base), (double)p.rope_pos[b], c, s);
+      rope_turn<false>(x1, x2, c, s);
+      sphi[w][i] = x1;
+      sphi[w][i + hr] = x2;
+    }
+    __syncthreads();
+  }
+}
+
 // One workgroup of 256 threads per (b, h, group of CPS channels): every thread
 // issues the loads of its PER (channel, 4 states) items of both copies and of A
 // first, featurizes while they are in flight (each group recomputes phi(q), phi(k)
-// of its (b, h): a few thousand FMAs against 2 x 2 x CPS x F x 4 bytes of state),
-// then updates, reads out (sum over the QPC lanes of a channel) and stores in place.
-// Small workgroups let several groups share a CU, so one group's featurization
-// overlaps another's state traffic.  Bound by the state's HBM traffic.
+// of its (b, h), reading W as 16-byte pieces), then updates, reads out (sum over
+// the QPC lanes of a channel) and stores in place.  Small workgroups let four share
+// a CU, so one group's featurization overlaps another's state traffic.  Bound by
+// the state's HBM traffic.
 template <typename T, int DK, int FH, int DV, int CPS>
 __global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
   constexpr int NT = 256, F = 2 * FH, QPC = F / 4;  // float4 per channel row
@@ -315,7 +403,7 @@ __global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
   static_assert(DV % CPS == 0 && 64 % QPC == 0, "channel groups");
   const StepParams &p = pp.s;
   __shared__ float sx[2][DK];
-  __shared__ float su[256 / (2 * FH)][2 * FH];
+  __shared__ __align__(16) float su[PcFeat<T, DK, FH>::P * F];
   __shared__ __align__(16) float sphi[2][F];
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x / NG, b = bh / p.H, h = bh % p.H;
@@ -333,7 +421,7 @@ __global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
       va[m] = reinterpret_cast<const f32x4 *>(AL)[idx];
     }
   }
-  step_features<T, DK, FH>(p, b, h, sx, su, sphi);
+  pc_step_features<T, DK, FH>(p, b, h, sx, su, sphi);
   const T *vp = (const T *)p.v + b * p.sv_b + h * p.sv_h + c0;
   const float *dtp = pp.dt + b * pp.sdt_b + h * pp.sdt_h + c0;
 #pragma unroll

@@ -39,6 +39,36 @@ struct StepParams {
 
 template <typename T> __device__ __forceinline__ float ldf(const T *p) { return (float)*p; }
 
+// Channel c of the token row of projection proj (0 = q, 1 = k) of (b, h) as a
+// float: through the mixer's short causal conv when one is given (in the order of
+// the standalone conv: bias, then taps oldest first, rounded to the input type; the
+// conv state shifts by one row in place), else the input value.  xpre, when given,
+// is the already loaded input value.
+template <typename T, int DK>
+__device__ __forceinline__ float step_input(const StepParams &p, int64_t b, int64_t h, int proj, int c,
+                                            const T *xpre) {
+  const int64_t bh = b * p.H + h;
+  const T *xq = (const T *)p.q + b * p.sq_b + h * p.sq_h;
+  const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
+  const T xt = xpre ? *xpre : (proj == 0 ? xq : xk)[c];
+  float xv = (float)xt;
+  if (p.cwidth > 0) {
+    const int K = p.cwidth;
+    const float *w = (proj == 0 ? p.cwq : p.cwk) + h * p.scw_h + (int64_t)c * K;
+    const float *bias = proj == 0 ? p.cbq : p.cbk;
+    T *cs = (T *)(proj == 0 ? p.csq : p.csk) + bh * (int64_t)(K - 1) * DK + c;
+    T prev[3];
+    for (int r = 0; r < K - 1; ++r) prev[r] = cs[r * DK];
+    float acc = bias ? bias[h * p.scb_h + c] : 0.f;
+    for (int r = 0; r < K - 1; ++r) acc = __builtin_fmaf(w[r], (float)prev[r], acc);
+    acc = __builtin_fmaf(w[K - 1], xv, acc);
+    for (int r = 0; r + 1 < K - 1; ++r) cs[r * DK] = prev[r + 1];
+    if (K > 1) cs[(K - 2) * DK] = xt;
+    xv = (float)to_elem<T>(acc);
+  }
+  return xv;
+}
+
 // phi(q_t) and phi(k_t) of one (b, h) into sphi[0], sphi[1], worked by the first
 // 256 threads of the workgroup: the token rows are staged as floats (through the
 // short causal conv when one is given), projected by W split over PARTS threads
@@ -57,31 +87,9 @@ __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, in
   constexpr int DPART = DK / PARTS;
   static_assert(NT % (2 * FH) == 0 && DK % PARTS == 0, "step mapping");
   const int tid = threadIdx.x;
-  const int64_t bh = b * p.H + h;
-  const T *xq = (const T *)p.q + b * p.sq_b + h * p.sq_h;
-  const T *xk = (const T *)p.k + b * p.sk_b + h * p.sk_h;
   for (int i = tid; i < 2 * DK; i += NT) {
     const int proj = i / DK, c = i % DK;
-    const T xt = xpre ? *xpre : (proj == 0 ? xq : xk)[c];
-    float xv = (float)xt;
-    if (p.cwidth > 0) {
-      // the mixer's short causal conv on this channel, in the order of the
-      // standalone conv (bias, then taps oldest first), rounded to the input type;
-      // the conv state shifts by one row in place
-      const int K = p.cwidth;
-      const float *w = (proj == 0 ? p.cwq : p.cwk) + h * p.scw_h + (int64_t)c * K;
-      const float *bias = proj == 0 ? p.cbq : p.cbk;
-      T *cs = (T *)(proj == 0 ? p.csq : p.csk) + bh * (int64_t)(K - 1) * DK + c;
-      T prev[3];
-      for (int r = 0; r < K - 1; ++r) prev[r] = cs[r * DK];
-      float acc = bias ? bias[h * p.scb_h + c] : 0.f;
-      for (int r = 0; r < K - 1; ++r) acc = __builtin_fmaf(w[r], (float)prev[r], acc);
-      acc = __builtin_fmaf(w[K - 1], xv, acc);
-      for (int r = 0; r + 1 < K - 1; ++r) cs[r * DK] = prev[r + 1];
-      if (K > 1) cs[(K - 2) * DK] = xt;
-      xv = (float)to_elem<T>(acc);
-    }
-    sx[proj][c] = xv;
+    sx[proj][c] = step_input<T, DK>(p, b, h, proj, c, xpre);
   }
   __syncthreads();
   if (tid < NT) {
