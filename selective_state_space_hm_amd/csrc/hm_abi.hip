@@ -15,6 +15,7 @@
 #include "hm_bwd_params.hpp"
 #include "hm_kernels.hpp"
 #include "hm_pc.hpp"
+#include "hm_cp.hpp"
 
 namespace {
 
@@ -86,6 +87,18 @@ const hm::FeatEntry *find_feat(int dt, int pdt, int64_t dk, int64_t fh) {
   return nullptr;
 }
 
+// The chunk-parallel prefill (any d in {16, 32, 64, 128}; its kernels take d at run time)
+const hm::CpEntry *find_cp(int dt, int64_t d, int64_t fh, int64_t dv) {
+  if (d != 16 && d != 32 && d != 64 && d != 128) return nullptr;
+  const hm::CpTable parts[] = {hm::table_cp_bf16(), hm::table_cp_f32()};
+  for (const auto &part : parts)
+    for (int i = 0; i < part.ncp; ++i) {
+      const auto &e = part.cp[i];
+      if (e.dtype == dt && e.fh == fh && e.dv == dv) return &e;
+    }
+  return nullptr;
+}
+
 // MODE_ROPE when the rotary encoding is on
 template <typename A> int rmode(const A *a) { return a->rope_dims ? hm::MODE_ROPE : 0; }
 
@@ -109,6 +122,8 @@ hm_status check_launch(const char *what) {
 
 // ------------------------------------------------------------------ prefill
 struct Plan {
+  bool cp;              // the chunk-parallel path (chunk 256, or sizes without a fused kernel)
+  int64_t nc;           // cp: chunks per sequence
   int chunk, segments, dsplit;
   int lsub;             // segment-pass slots per segment (pieces of seg_len / lsub tokens)
   int64_t seg_len;
@@ -117,6 +132,9 @@ struct Plan {
   size_t ws_state_floats, ws_lam_floats, ws_init_floats;
   size_t bytes() const { return 4 * (ws_state_floats + ws_lam_floats + ws_init_floats); }
 };
+
+hm_status validate_cp(const hm_linattn_fwd_args *a);
+hm_status validate_fused(const hm_linattn_fwd_args *a);
 
 hm_status validate_fwd(const hm_linattn_fwd_args *a) {
   if (!a) return fail(HM_ERR_NULL, "args is NULL");
@@ -148,21 +166,43 @@ hm_status validate_fwd(const hm_linattn_fwd_args *a) {
     return fail(HM_ERR_ALIGN, "state buffers must be 16-byte aligned");
   for (int64_t s : strides)
     if (!stride_ok(s, a->dtype)) return fail(HM_ERR_ALIGN, "every stride times the element size must be a multiple of 16 bytes");
-  if (a->chunk == 256)
-    return fail(HM_ERR_UNSUPPORTED,
-                "chunk 256 is not built: a 256-token chunk's phi(q), phi(k) and v alone take 192 KB of LDS "
-                "in bf16 at 2f = dv = 128, above the 160 KB of a compute unit (built: 0 = auto, 64, 128)");
-  if (a->chunk != 0 && a->chunk != 64 && a->chunk != 128)
-    return fail(HM_ERR_UNSUPPORTED, "chunk %d: built are 0 (auto), 64 and 128", a->chunk);
-  if (a->chunk == 128 && (a->save || a->gate || a->rope_dims))
-    return fail(HM_ERR_UNSUPPORTED, "chunk 128 is built for the plain prefill: no training saves, gate or rotary "
-                                    "encoding (use chunk 64 for those)");
+  if (a->chunk != 0 && a->chunk != 64 && a->chunk != 128 && a->chunk != 256)
+    return fail(HM_ERR_UNSUPPORTED, "chunk %d: built are 0 (auto), 64, 128 and 256", a->chunk);
+  if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0");
+  if (a->dsplit < 0 || a->dsplit > 2) return fail(HM_ERR_UNSUPPORTED, "dsplit must be 0, 1 or 2");
   {
     const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
     if (rs != HM_OK) return rs;
   }
-  if (a->segments < 0) return fail(HM_ERR_SHAPE, "segments must be >= 0");
-  if (a->dsplit < 0 || a->dsplit > 2) return fail(HM_ERR_UNSUPPORTED, "dsplit must be 0, 1 or 2");
+  if (a->chunk == 256) return validate_cp(a);
+  const hm_status fs = validate_fused(a);
+  // sizes without a fused kernel run the chunk-parallel path when nothing else asks for one
+  if (fs == HM_ERR_UNSUPPORTED && !a->dsplit && !a->segments && !a->gate && !a->rope_dims && !a->save &&
+      find_cp(a->dtype, a->d, a->f, a->dv))
+    return validate_cp(a);
+  return fs;
+}
+
+// The plain prefill on the chunk-parallel path: no gate, rotary encoding or
+// training saves, one workgroup per (b, h, chunk) and no segments.
+hm_status validate_cp(const hm_linattn_fwd_args *a) {
+  if (!find_cp(a->dtype, a->d, a->f, a->dv))
+    return fail(HM_ERR_UNSUPPORTED, "no chunk-parallel kernel for dtype=%d d=%lld f=%lld dv=%lld", a->dtype,
+                (long long)a->d, (long long)a->f, (long long)a->dv);
+  if (a->gate || a->rope_dims || a->save)
+    return fail(HM_ERR_UNSUPPORTED, "chunk 256 and the sizes without a fused kernel run the chunk-parallel "
+                                    "path, which is built for the plain prefill: no gate, rotary encoding or "
+                                    "training saves");
+  if (a->segments) return fail(HM_ERR_UNSUPPORTED, "the chunk-parallel path takes segments = 0 (every chunk is one)");
+  if (a->dsplit > 1) return fail(HM_ERR_UNSUPPORTED, "the chunk-parallel path takes dsplit 0 or 1");
+  return ok();
+}
+
+// The fused kernels (chunk 64 or 128): whether one is built for the request.
+hm_status validate_fused(const hm_linattn_fwd_args *a) {
+  if (a->chunk == 128 && (a->save || a->gate || a->rope_dims))
+    return fail(HM_ERR_UNSUPPORTED, "chunk 128 is built for the plain prefill: no training saves, gate or rotary "
+                                    "encoding (use chunk 64 for those)");
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int ch = a->chunk ? a->chunk : hm::CHUNK;
   // the full-pass kernel for dsplit 1 must exist for the size to count as supported
@@ -221,12 +261,34 @@ SaveLayout save_layout(int dtype, int64_t BH, int64_t n, int64_t f, int64_t dv) 
   return l;
 }
 
+// Whether a validated request runs on the chunk-parallel path.
+bool is_cp(const hm_linattn_fwd_args *a) {
+  if (a->chunk == 256) return true;
+  const int decay = a->dt != nullptr && a->a_log != nullptr;
+  const int ch = a->chunk ? a->chunk : hm::CHUNK;
+  return !find_fwd(a->dtype, a->d, a->f, a->dv, decay, hm::MODE_FULL | rmode(a), ch) &&
+         !find_fwd(a->dtype, a->d, a->f, a->dv / 2, decay, hm::MODE_FULL | rmode(a), ch);
+}
+
 Plan make_plan(const hm_linattn_fwd_args *a) {
   Plan p{};
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int64_t BH = a->B * a->H;
   const int64_t F = 2 * a->f;
   const int64_t BLK = F * a->dv + F;
+  if (is_cp(a)) {
+    // chunk-parallel: every chunk's local state, then its start state, in the workspace
+    p.cp = true;
+    p.chunk = a->chunk ? a->chunk : hm::CHUNK;
+    p.nc = (a->n + p.chunk - 1) / p.chunk;
+    p.segments = p.nc > 0 ? (int)p.nc : 1;
+    p.dsplit = 1;
+    p.lsub = 1;
+    p.seg_len = p.chunk;
+    p.ws_state_floats = (size_t)(BH * p.nc) * BLK;
+    p.ws_lam_floats = ((size_t)(BH * p.nc) + 3) / 4 * 4;
+    return p;
+  }
   // chunk: 64 unless asked (128-token chunks add intra-chunk work for fewer state passes)
   const int C = a->chunk ? a->chunk : hm::CHUNK;
   p.chunk = C;
@@ -314,11 +376,45 @@ hm_status hm_linattn_fwd_plan(const hm_linattn_fwd_args *a, int32_t *chunk, int3
 namespace {
 // The prefill after validation and planning, with the workspace `wsp` (at least
 // pl.bytes() bytes, 16-byte aligned; NULL when that is 0).
+// The chunk-parallel path: local states, their scan over the chunks, outputs.
+hm_status run_cp(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, hipStream_t s) {
+  hm_status st = HM_OK;
+  const int64_t BH = a->B * a->H, F = 2 * a->f, BLK = F * a->dv + F;
+  const hm::CpEntry *e = find_cp(a->dtype, a->d, a->f, a->dv);
+  if (!e) return fail(HM_ERR_UNSUPPORTED, "no chunk-parallel kernel");
+  hm::CpParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.wq = a->w_q; p.wk = a->w_k;
+  p.dt = a->dt; p.a_log = a->a_log;
+  p.s_init = a->s_init; p.s_final = a->s_final;
+  p.o = a->o;
+  p.ws_state = (float *)wsp;
+  p.ws_lam = wsp ? (float *)wsp + pl.ws_state_floats : nullptr;
+  p.B = a->B; p.H = a->H; p.n = a->n; p.nc = pl.nc;
+  p.d = (int)a->d; p.chunk = pl.chunk;
+  p.sq_b = a->sq_b; p.sq_h = a->sq_h; p.sq_t = a->sq_t;
+  p.sk_b = a->sk_b; p.sk_h = a->sk_h; p.sk_t = a->sk_t;
+  p.sv_b = a->sv_b; p.sv_h = a->sv_h; p.sv_t = a->sv_t;
+  p.so_b = a->so_b; p.so_h = a->so_h; p.so_t = a->so_t;
+  p.sw_h = a->sw_h; p.sdt_b = a->sdt_b; p.sdt_h = a->sdt_h; p.sdt_t = a->sdt_t;
+  if (pl.nc > 0) {
+    e->local(p, (unsigned)(BH * pl.nc), s);
+    if ((st = check_launch("chunk-parallel local states")) != HM_OK) return st;
+  }
+  hipLaunchKernelGGL(hm::cp_scan_kernel, dim3((unsigned)((BLK + 255) / 256), (unsigned)BH), dim3(256), 0, s, p, BLK);
+  if ((st = check_launch("chunk-parallel state scan")) != HM_OK) return st;
+  if (pl.nc > 0) {
+    e->out(p, (unsigned)(BH * pl.nc * (pl.chunk / hm::CP_BLK)), s);
+    if ((st = check_launch("chunk-parallel outputs")) != HM_OK) return st;
+  }
+  return ok();
+}
+
 hm_status run_fwd(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, void *stream) {
   hm_status st = HM_OK;
   const int64_t BH = a->B * a->H;
   if (BH == 0) return ok();
   if (a->n == 0 && !a->s_final) return ok();
+  if (pl.cp) return run_cp(a, pl, wsp, (hipStream_t)stream);
   const int decay = a->dt != nullptr && a->a_log != nullptr;
   const int64_t dw = a->dv / pl.dsplit;
   // the full pass at the plan's chunk length; the segment pass works in 64-token

@@ -63,7 +63,20 @@ struct PcTable {
   int npc;
 };
 
+struct CpParams;
+struct CpEntry {
+  int dtype, fh, dv;
+  void (*local)(const CpParams &, unsigned grid, hipStream_t);
+  void (*out)(const CpParams &, unsigned grid, hipStream_t);
+};
+struct CpTable {
+  const CpEntry *cp;
+  int ncp;
+};
+
 // one per kernel translation unit
+CpTable table_cp_bf16();
+CpTable table_cp_f32();
 PcTable table_pc();
 ConvTable table_conv();
 BwdTable table_bwd();

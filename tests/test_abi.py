@@ -93,16 +93,26 @@ def test_fwd_validation_errors():
     expect(hm.call_fwd(fwd(s_init=A + 4)), hm.HM_ERR_ALIGN)
     expect(hm.call_fwd(fwd(d=96)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(f=48)), hm.HM_ERR_UNSUPPORTED)
-    expect(hm.call_fwd(fwd(dtype=hm.HM_F32)), hm.HM_ERR_UNSUPPORTED)  # f32 at d=128 not built
-    # the small bf16 shapes are built (their plans resolve); d = 16 is not
+    # sizes without a fused kernel (float32 at d=128, bf16 at d=16) run the chunk-parallel
+    # path: one "segment" per 64-token chunk, no column split
+    assert hm.call_plan(fwd(dtype=hm.HM_F32)) == (hm.HM_OK, (64, 32, 1))
+    assert hm.call_plan(fwd(d=16, f=16, dv=32)) == (hm.HM_OK, (64, 32, 1))
+    # the small bf16 shapes have fused kernels
     expect(hm.call_plan(fwd(d=32, f=16, dv=32))[0], hm.HM_OK)
     expect(hm.call_plan(fwd(dv=32))[0], hm.HM_OK)
-    expect(hm.call_fwd(fwd(d=16, f=16, dv=32)), hm.HM_ERR_UNSUPPORTED)
     assert hm.call_plan(fwd(d=32, f=16, dv=64)) == (hm.HM_OK, (64, 4, 2))  # two 32-column workgroups
     expect(hm.call_fwd(fwd(d=32, f=16, dv=64, dsplit=1)), hm.HM_ERR_UNSUPPORTED)
+    # what the chunk-parallel path does not take: gate, rotary, saves, segments, column splits
+    G0 = dict(gate=A + 0xa000000, sg_b=16 * 2048 * 128, sg_h=2048 * 128, sg_t=128)
+    expect(hm.call_fwd(fwd(dtype=hm.HM_F32, **G0)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(d=16, f=16, dv=32, segments=2)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=96)), hm.HM_ERR_UNSUPPORTED)
-    expect(hm.call_fwd(fwd(chunk=256)), hm.HM_ERR_UNSUPPORTED)
-    assert "192 KB" in hm.last_error()                 # the stated reason: LDS per compute unit
+    assert hm.call_plan(fwd(chunk=256)) == (hm.HM_OK, (256, 8, 1))
+    expect(hm.call_fwd(fwd(chunk=256, **G0)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(chunk=256, rope_dims=32, rope_base=1e4)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(chunk=256, segments=4)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(chunk=256, dsplit=2)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_fwd(fwd(chunk=256, d=96)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=128, gate=A + 0xa000000, sg_t=128)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=128, rope_dims=32, rope_base=1e4)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_fwd(fwd(chunk=128, d=16, f=16, dv=16, dtype=hm.HM_F32, save=A + 0xb000000, save_bytes=1 << 30)),
@@ -145,6 +155,17 @@ def test_workspace_is_linear_not_quadratic():
     assert hm.call_workspace_size(fwd(B=8, H=16, n=2048, segments=1))[1] == 0
 
 
+def test_chunk_parallel_workspace():
+    # every chunk's state and summed log-decay: O(B*H*(n/C)*F*dv), linear in n
+    F, dv = 128, 128
+    for n, C in ((2048, 256), (1000, 256), (4096, 64)):
+        st, nbytes = hm.call_workspace_size(fwd(B=2, H=16, n=n, chunk=C, decay=True) if C == 256 else
+                                            fwd(B=2, H=16, n=n, dtype=hm.HM_F32, decay=True))
+        expect(st, hm.HM_OK)
+        nc = -(-n // C)
+        assert nbytes == 32 * nc * (F * dv + F) * 4 + 4 * ((32 * nc + 3) // 4 * 4)
+
+
 def test_plans():
     st, plan = hm.call_plan(fwd(B=8, H=16, n=2048))
     expect(st, hm.HM_OK)
@@ -169,8 +190,8 @@ def test_plans():
     for f_, dv_ in ((16, 16), (16, 32), (32, 32), (32, 64)):   # float32 at d = 64
         st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=64, f=f_, dv=dv_, dtype=hm.HM_F32))
         expect(st, hm.HM_OK)
-    st, plan = hm.call_plan(fwd(B=1, H=2, n=256, d=64, f=64, dv=64, dtype=hm.HM_F32))
-    expect(st, hm.HM_ERR_UNSUPPORTED)                   # float32 (64, 64, 64) is not built
+    # float32 (64, 64, 64) has no fused kernel: the chunk-parallel path, 4 chunks of 64
+    assert hm.call_plan(fwd(B=1, H=2, n=256, d=64, f=64, dv=64, dtype=hm.HM_F32)) == (hm.HM_OK, (64, 4, 1))
 
 
 def test_alias_needs_init_copy_workspace():
