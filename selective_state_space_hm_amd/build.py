@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhm.so")
 SOURCES = ["hm_abi.hip", "k_fwd_bf16.hip", "k_fwd_bf16_decay.hip", "k_fwd_f32.hip", "k_step_feat.hip",
            "k_conv.hip", "k_bwd.hip", "k_fwd_rope_bf16.hip", "k_fwd_rope_bf16_decay.hip", "k_fwd_rope_f32.hip",
-           "k_pc.hip", "k_fwd_c128.hip", "k_fwd_f32_d64.hip", "k_cp_bf16.hip", "k_cp_f32.hip"]
+           "k_pc.hip", "k_fwd_c128.hip", "k_fwd_f32_d64.hip", "k_cp_bf16.hip", "k_cp_f32.hip", "k_step_bf16.hip", "k_step_f32.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

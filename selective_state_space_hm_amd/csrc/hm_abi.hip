@@ -41,7 +41,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 bool stride_ok(int64_t s, int dt) { return s >= 0 && ((size_t)s * esize(dt)) % 16 == 0; }
 
 struct Tables {
-  hm::Table parts[10];
+  hm::Table parts[12];
   Tables() {
     parts[0] = hm::table_fwd_bf16();
     parts[1] = hm::table_fwd_bf16_decay();
@@ -53,6 +53,8 @@ struct Tables {
     parts[7] = hm::table_fwd_rope_f32();
     parts[8] = hm::table_fwd_c128();
     parts[9] = hm::table_fwd_f32_d64();
+    parts[10] = hm::table_step_bf16();
+    parts[11] = hm::table_step_f32();
   }
 };
 const Tables &tables() {
@@ -400,7 +402,8 @@ hm_status run_cp(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, hipStr
     e->local(p, (unsigned)(BH * pl.nc), s);
     if ((st = check_launch("chunk-parallel local states")) != HM_OK) return st;
   }
-  hipLaunchKernelGGL(hm::cp_scan_kernel, dim3((unsigned)((BLK + 255) / 256), (unsigned)BH), dim3(256), 0, s, p, BLK);
+  hipLaunchKernelGGL(hm::cp_scan_kernel, dim3((unsigned)((BLK + 255) / 256), (unsigned)BH), dim3(256), 0, s, p, BLK,
+                     (int)F, (int)a->dv);
   if ((st = check_launch("chunk-parallel state scan")) != HM_OK) return st;
   if (pl.nc > 0) {
     e->out(p, (unsigned)(BH * pl.nc * (pl.chunk / hm::CP_BLK)), s);

@@ -32,7 +32,7 @@ struct CpParams {
   const float *s_init;      // [B*H][F*dv + F] or NULL
   float *s_final;           // same layout, or NULL (may alias s_init)
   void *o;
-  float *ws_state;          // [B*H][nc][F*dv + F]: local states, then start states
+  float *ws_state;          // [B*H][nc][dv*F + F]: local states, then start states, S^T [dv][F] then z [F]
   float *ws_lam;            // [B*H][nc]: summed log-decay of each chunk
   int64_t B, H, n, nc;
   int d, chunk;
@@ -58,14 +58,24 @@ __device__ __forceinline__ void cp_decay_prefix(const CpParams &p, int64_t b, in
   const bool decay = p.dt != nullptr;
   const float *DT = decay ? p.dt + b * p.sdt_b + h * p.sdt_h : nullptr;
   const float expA = decay ? expf(p.a_log[h]) : 0.f;
+  constexpr int NI = CP_CHMAX / 64;
+  float dtv[NI];  // every dt of the range requested before the scan
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t t = t0 + 64 * i + lane;
+    dtv[i] = decay && 64 * i + lane < cnt && t < p.n ? DT[t * p.sdt_t] : 0.f;
+  }
   double carry = 0.0;
-  for (int i0 = 0; i0 < cnt; i0 += 64) {
-    const int64_t t = t0 + i0 + lane;
-    const bool valid = decay && i0 + lane < cnt && t < p.n;
-    const double x = valid ? (double)(-softplus_f32(DT[t * p.sdt_t]) * expA) : 0.0;
-    const double L = wave_inclusive_scan(x) + carry;
-    if (i0 + lane < cnt) sL[i0 + lane] = L;
-    carry = lane63(L);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (64 * i < cnt) {
+      const int64_t t = t0 + 64 * i + lane;
+      const bool valid = decay && 64 * i + lane < cnt && t < p.n;
+      const double x = valid ? (double)(-softplus_f32(dtv[i]) * expA) : 0.0;
+      const double L = wave_inclusive_scan(x) + carry;
+      if (64 * i + lane < cnt) sL[64 * i + lane] = L;
+      carry = lane63(L);
+    }
   }
 }
 
@@ -74,38 +84,75 @@ __device__ __forceinline__ void cp_decay_prefix(const CpParams &p, int64_t b, in
 template <typename T, int FH>
 __device__ __forceinline__ void cp_stage_wt(const T *W, int d, T *sW) {
   using L = CpLds<T>;
+  constexpr int EPL = 16 / (int)sizeof(T), PR = FH / EPL;  // 16-byte pieces per row of W
+  constexpr int NI = (CP_DKMAX * PR + 255) / 256;
+  // rows of W as 16-byte pieces (consecutive threads read consecutive pieces), all
+  // requested before any is written
+  f32x4 raw[NI];
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int i = threadIdx.x + 256 * m;
+    if (i < d * PR) raw[m] = *reinterpret_cast<const f32x4 *>(W + (int64_t)(i / PR) * FH + (i % PR) * EPL);
+  }
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int i = threadIdx.x + 256 * m;
+    if (i < d * PR) {
+      const int dd = i / PR, j0 = (i % PR) * EPL;
+      const T *e = reinterpret_cast<const T *>(&raw[m]);
+#pragma unroll
+      for (int x = 0; x < EPL; ++x) sW[(j0 + x) * L::LDW + dd] = e[x];
+    }
+  }
+  // columns d .. KS-1 of W^T are zero when d is below one MFMA K-step
   const int dpad = d < Mma<T>::KS ? Mma<T>::KS : d;
-  for (int i = threadIdx.x; i < FH * dpad; i += blockDim.x) {
-    const int j = i / dpad, dd = i % dpad;
-    sW[j * L::LDW + dd] = dd < d ? W[(int64_t)dd * FH + j] : (T)0.f;
+  for (int i = threadIdx.x; i < FH * (dpad - d); i += 256) sW[(i / (dpad - d)) * L::LDW + d + i % (dpad - d)] = (T)0.f;
+}
+
+// The token row of token tile `wv` of the block at token tb (token tb + 16 wv + col
+// for lane (col, g)) as the MFMA B operands of the projection, every K-step
+// requested at once; zeros at or past n and past d.
+template <typename T> struct CpX {
+  typename Mma<T>::frag x[CP_DKMAX / Mma<T>::KS];
+  bool ok;
+};
+template <typename T>
+__device__ __forceinline__ void cp_load_x(const T *X, int64_t sx_t, int64_t tb, int64_t n, int d, CpX<T> &r, int wv,
+                                          int lane) {
+  using M = Mma<T>;
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t t = tb + 16 * wv + col;
+  r.ok = t < n;
+  const T *row = X + (r.ok ? t : 0) * sx_t;
+#pragma unroll
+  for (int i = 0; i < CP_DKMAX / M::KS; ++i) {
+    const int k0 = i * M::KS;
+    r.x[i] = r.ok && k0 + (M::EPL == 8 ? 8 * g : g) < d ? M::ld_contig(row + k0, g) : typename M::frag{};
   }
 }
 
-// Features of token tile `wv` of the block at token tb: the wave's lane (col, g)
-// gets, for token tb + 16 wv + col, ph[t][r] = phi at feature 16t + 4g + r of the u
-// half (t < FH/16) or of the -u half (t >= FH/16), normalized (softmax over both
-// halves), or 0 for tokens at or past n.  The projection U^T = W^T X^T runs on the
-// MFMA with the token rows read from global memory straight into B operands.
+// Features of the loaded token tile: lane (col, g) gets ph[t][r] = phi at feature
+// 16t + 4g + r of the u half (t < FH/16) or of the -u half (t >= FH/16), normalized
+// (softmax over both halves), or 0 for tokens at or past n.  The projection U^T =
+// W^T X^T runs on the MFMA.
 template <typename T, int FH>
-__device__ __forceinline__ void cp_features(const T *X, int64_t sx_t, int64_t tb, int64_t n, int d, const T *sW,
-                                            f32x4 *ph, int wv, int lane) {
+__device__ __forceinline__ void cp_features(const CpX<T> &xr, int d, const T *sW, f32x4 *ph, int lane) {
   using M = Mma<T>;
-  using frag = typename M::frag;
   using L = CpLds<T>;
   constexpr int NFH = FH / 16;
   constexpr float L2E = 1.4426950408889634f;
   const int col = lane & 15, g = lane >> 4;
-  const int64_t t = tb + 16 * wv + col;
-  const bool ok = t < n;
-  const T *row = X + (ok ? t : 0) * sx_t;
   f32x4 u[NFH];
 #pragma unroll
   for (int ft = 0; ft < NFH; ++ft) u[ft] = zero4();
-  for (int k0 = 0; k0 < d; k0 += M::KS) {
-    const bool in = ok && k0 + (M::EPL == 8 ? 8 * g : g) < d;
-    const frag xb = in ? M::ld_contig(row + k0, g) : frag{};
 #pragma unroll
-    for (int ft = 0; ft < NFH; ++ft) u[ft] = M::mma(M::ld_contig(sW + (16 * ft + col) * L::LDW + k0, g), xb, u[ft]);
+  for (int i = 0; i < CP_DKMAX / M::KS; ++i) {
+    const int k0 = i * M::KS;
+    if (k0 < d) {
+#pragma unroll
+      for (int ft = 0; ft < NFH; ++ft)
+        u[ft] = M::mma(M::ld_contig(sW + (16 * ft + col) * L::LDW + k0, g), xr.x[i], u[ft]);
+    }
   }
   float m = 0.f;
 #pragma unroll
@@ -124,25 +171,43 @@ __device__ __forceinline__ void cp_features(const T *X, int64_t sx_t, int64_t tb
       ph[NFH + ft][r] = em;
       sum += ep + em;
     }
-  const float inv = ok ? 1.f / group_sum(sum) : 0.f;
+  const float inv = xr.ok ? 1.f / group_sum(sum) : 0.f;
 #pragma unroll
   for (int ft = 0; ft < 2 * NFH; ++ft) ph[ft] *= inv;
 }
 
-// v rows [tb, tb+64) of one (b, h) into sVt[c][t] (transposed, LDB elements per
-// row), zeros past n; all threads, 16-byte loads.
+// v rows [tb, tb+64) of one (b, h) in 16-byte pieces, one per thread and NI rounds: a
+// wave's lanes take the 64 tokens of one piece (so the transposed LDS writes of a
+// wave fill one row); zeros past n.
+template <typename T, int DV> struct CpV {
+  static constexpr int EPL = 16 / (int)sizeof(T), PR = DV / EPL, NI = CP_BLK * PR / 256 > 0 ? CP_BLK * PR / 256 : 1;
+  f32x4 raw[NI];
+};
 template <typename T, int DV>
-__device__ __forceinline__ void cp_stage_vt(const T *V, int64_t sv_t, int64_t tb, int64_t n, T *sVt) {
-  using L = CpLds<T>;
-  constexpr int EPL = 16 / (int)sizeof(T), PR = DV / EPL;  // 16-byte pieces per row
-  for (int i = threadIdx.x; i < CP_BLK * PR; i += blockDim.x) {
-    const int tt = i / PR, c0 = (i % PR) * EPL;
-    const int64_t t = tb + tt;
-    f32x4 raw = zero4();
-    if (t < n) raw = *reinterpret_cast<const f32x4 *>(V + t * sv_t + c0);
-    const T *e = reinterpret_cast<const T *>(&raw);
+__device__ __forceinline__ void cp_load_v(const T *V, int64_t sv_t, int64_t tb, int64_t n, CpV<T, DV> &r) {
+  using VV = CpV<T, DV>;
 #pragma unroll
-    for (int x = 0; x < EPL; ++x) sVt[(c0 + x) * L::LDB + tt] = e[x];
+  for (int m = 0; m < VV::NI; ++m) {
+    const int i = threadIdx.x + 256 * m, tt = i % CP_BLK, c0 = (i / CP_BLK) * VV::EPL;
+    r.raw[m] = i < CP_BLK * VV::PR && tb + tt < n ? *reinterpret_cast<const f32x4 *>(V + (tb + tt) * sv_t + c0)
+                                                  : zero4();
+  }
+}
+// ... into sVt[c][t] (transposed, LDB elements per row), the keys in tile order
+// (TILE) or in order.
+template <typename T, int DV, bool TILE>
+__device__ __forceinline__ void cp_write_vt(const CpV<T, DV> &r, T *sVt) {
+  using VV = CpV<T, DV>;
+  using L = CpLds<T>;
+#pragma unroll
+  for (int m = 0; m < VV::NI; ++m) {
+    const int i = threadIdx.x + 256 * m, tt = i % CP_BLK, c0 = (i / CP_BLK) * VV::EPL;
+    const int tp = TILE ? Mma<T>::tpos(tt) : tt;
+    if (i < CP_BLK * VV::PR) {
+      const T *e = reinterpret_cast<const T *>(&r.raw[m]);
+#pragma unroll
+      for (int x = 0; x < VV::EPL; ++x) sVt[(c0 + x) * L::LDB + tp] = e[x];
+    }
   }
 }
 
@@ -170,11 +235,15 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = zero4();
   float zsum = 0.f;  // thread f < F: dz[f]
+  CpX<T> xk;
+  CpV<T, DV> vr;
+  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
+  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
   for (int kb = 0; kb * CP_BLK < cnt; ++kb) {
     const int64_t tb = t0 + kb * CP_BLK;
     {
       f32x4 ph[2 * (FH / 16)];
-      cp_features<T, FH>(K, p.sk_t, tb, p.n, p.d, sW, ph, wv, lane);
+      cp_features<T, FH>(xk, p.d, sW, ph, lane);
       const int lt = kb * CP_BLK + 16 * wv + col;  // token within the chunk
       const float w = lt < cnt ? __expf((float)(lam - sL[lt])) : 0.f;
 #pragma unroll
@@ -182,23 +251,34 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) sKt[(16 * ft + 4 * g + r) * L::LDB + 16 * wv + col] = (T)(ph[ft][r] * w);
     }
-    cp_stage_vt<T, DV>(V, p.sv_t, tb, p.n, sVt);
+    cp_write_vt<T, DV, false>(vr, sVt);
+    // the next block's rows are in flight during this block's products
+    if ((kb + 1) * CP_BLK < cnt) {
+      cp_load_x<T>(K, p.sk_t, tb + CP_BLK, p.n, p.d, xk, wv, lane);
+      cp_load_v<T, DV>(V, p.sv_t, tb + CP_BLK, p.n, vr);
+    }
     __syncthreads();
-    // dS[f][c] += sum_t Kt[f][t] Vt[c][t]: tile i of this wave is (tile row, tile column)
+    // dS^T[c][f] += sum_t Vt[c][t] Kt[f][t]: tile i of this wave is (value tile, feature tile)
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tile = 4 * i + wv;
       if (tile < NTL) {
-        const int ft = tile / NCT, ct = tile % NCT;
+        const int ft = tile % NFT, ct = tile / NFT;
 #pragma unroll
         for (int k0 = 0; k0 < CP_BLK; k0 += M::KS)
-          acc[i] = M::mma(M::ld_contig(sKt + (16 * ft + col) * L::LDB + k0, g),
-                          M::ld_contig(sVt + (16 * ct + col) * L::LDB + k0, g), acc[i]);
+          acc[i] = M::mma(M::ld_contig(sVt + (16 * ct + col) * L::LDB + k0, g),
+                          M::ld_contig(sKt + (16 * ft + col) * L::LDB + k0, g), acc[i]);
       }
     }
     if (tid < F) {
-#pragma unroll 8
-      for (int t = 0; t < CP_BLK; ++t) zsum += (float)sKt[tid * L::LDB + t];
+      constexpr int EPL = 16 / (int)sizeof(T);
+#pragma unroll
+      for (int t = 0; t < CP_BLK; t += EPL) {
+        const f32x4 raw = *reinterpret_cast<const f32x4 *>(&sKt[tid * L::LDB + t]);
+        const T *e = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+        for (int x = 0; x < EPL; ++x) zsum += (float)e[x];
+      }
     }
     __syncthreads();
   }
@@ -208,9 +288,9 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
   for (int i = 0; i < TPW; ++i) {
     const int tile = 4 * i + wv;
     if (tile < NTL) {
-      const int ft = tile / NCT, ct = tile % NCT;
+      const int ft = tile % NFT, ct = tile / NFT;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[(int64_t)(16 * ft + 4 * g + r) * DV + 16 * ct + col] = acc[i][r];
+      for (int r = 0; r < 4; ++r) st[(int64_t)(16 * ct + 4 * g + r) * F + 16 * ft + col] = acc[i][r];
     }
   }
   if (tid < F) st[(int64_t)F * DV + tid] = zsum;
@@ -220,37 +300,72 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
 // Pass 2: thread e of (b, h) walks the chunks, replacing each local state by the
 // chunk's start state; s_init is read before s_final is written (same element,
 // same thread), so the two may alias.
-static __global__ __launch_bounds__(256) void cp_scan_kernel(const CpParams p, int64_t BLK) {
+// The workspace holds S^T: its element e = c*F + f is S[f][c], at f*dv + c in the
+// state layout of s_init and s_final.
+static __global__ __launch_bounds__(256) void cp_scan_kernel(const CpParams p, int64_t BLK, int F, int dv) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x, bh = blockIdx.y;
   if (e >= BLK) return;
-  float s = p.s_init ? p.s_init[bh * BLK + e] : 0.f;
+  const int64_t es = e < (int64_t)F * dv ? (e % F) * dv + e / F : e;  // the same element in the state layout
+  float s = p.s_init ? p.s_init[bh * BLK + es] : 0.f;
   float *st = p.ws_state + bh * p.nc * BLK + e;
   const float *lam = p.ws_lam + bh * p.nc;
-  for (int64_t c = 0; c < p.nc; ++c) {
-    const float loc = st[c * BLK];
-    st[c * BLK] = s;
-    s = __builtin_fmaf(__expf(lam[c]), s, loc);
+  // the local states of UNR chunks are requested together, so only the carry is serial
+  constexpr int UNR = 16;
+  for (int64_t c0 = 0; c0 < p.nc; c0 += UNR) {
+    float loc[UNR], dec[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      loc[u] = c0 + u < p.nc ? st[(c0 + u) * BLK] : 0.f;
+      dec[u] = c0 + u < p.nc ? lam[c0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (c0 + u < p.nc) {
+        st[(c0 + u) * BLK] = s;
+        s = __builtin_fmaf(__expf(dec[u]), s, loc[u]);
+      }
+    }
   }
-  if (p.s_final) p.s_final[bh * BLK + e] = s;
+  if (p.s_final) p.s_final[bh * BLK + es] = s;
 }
 
+// A K-step (tile order) of a float32 row in global memory, as an MFMA operand of
+// type T: bf16 slots e take k = 32s + 16(e/4) + 4g + e%4 (two 16-byte loads), f32
+// step s takes k = 16(s/4) + 4g + s%4.
+template <typename T> __device__ __forceinline__ typename Mma<T>::frag cp_row_tile(const float *row, int s, int g);
+template <> __device__ __forceinline__ bf16x8 cp_row_tile<bf16>(const float *row, int s, int g) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 32 * s + 4 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 32 * s + 16 + 4 * g);
+  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+template <> __device__ __forceinline__ float cp_row_tile<float>(const float *row, int s, int g) {
+  return row[16 * (s >> 2) + 4 * g + (s & 3)];
+}
+
+// Four consecutive values of an accumulator column as T, at p (8 or 16 bytes).
+__device__ __forceinline__ void cp_store4(bf16 *p, f32x4 v) {
+  *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
+__device__ __forceinline__ void cp_store4(float *p, f32x4 v) { *reinterpret_cast<f32x4 *>(p) = v; }
+
 // Pass 3: one workgroup (4 waves) per (b, h, chunk, 64-query block); wave w owns
-// query tile w (16 tokens) and all dv columns of its output.
+// query tile w (16 tokens, one per lane column).  The products run transposed, with
+// the queries as MFMA columns, so phi(q) and the weighted scores stay in registers as
+// B operands (tile order) and each lane ends with its token's outputs, numerator
+// and denominator:
+//   O^T = e^{L} S^T phiQ^T + V^T Pt,   Pt[s][t] = e^{L_t - L_s} [s <= t] phiK_s . phiQ_t,
+//   den_t = e^{L_t} phiQ_t . z + sum_s Pt[s][t].
 template <typename T, int FH, int DV>
 __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   using M = Mma<T>;
+  using frag = typename M::frag;
   using L = CpLds<T>;
   constexpr int F = 2 * FH, NFT = F / 16, NCT = DV / 16, LDF = F + L::PAD;
-  // the read-out copy of the start state (S^T, dv rows of F) shares space with the
-  // key block's phi(k) rows, v^T and the weighted score rows, used after it
-  constexpr int KV = CP_BLK * LDF + DV * L::LDB + CP_BLK * L::LDB, ST = DV * LDF;
+  constexpr int KF = M::steps(NFT), KB = M::steps(4);  // K-steps over the features, over a block's keys
   __shared__ __align__(16) T sW[FH * L::LDW];
-  __shared__ __align__(16) T sQ[CP_BLK * LDF];
-  __shared__ __align__(16) T sU[KV > ST ? KV : ST];
-  __shared__ float sZ[F];
-  __shared__ float sDen[CP_BLK];
+  __shared__ __align__(16) T sK[CP_BLK * LDF];  // phi(k) rows of a key block, features in tile order
+  __shared__ __align__(16) T sVt[DV * L::LDB];  // v^T of a key block, keys in tile order
   __shared__ double sL[CP_CHMAX];
-  T *sSt = sU, *sK = sU, *sVt = sU + CP_BLK * LDF, *sP = sVt + DV * L::LDB;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int nqb = p.chunk / CP_BLK;
   const int64_t qb = blockIdx.x % nqb, c = (blockIdx.x / nqb) % p.nc, bh = blockIdx.x / nqb / p.nc;
@@ -258,106 +373,97 @@ __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   if (tq >= p.n) return;  // the whole block is past the sequence's end (uniform)
   const int cnt = (int)((qb + 1) * CP_BLK);  // chunk tokens up to this block's end
   const int64_t BLK = (int64_t)F * DV + F;
-  const float *st = p.ws_state + (bh * p.nc + c) * BLK;
+  const float *st = p.ws_state + (bh * p.nc + c) * BLK;  // start state: S^T [DV][F], then z [F]
   if (wv == 0) cp_decay_prefix(p, b, h, t0, cnt, sL, lane);
   cp_stage_wt<T, FH>((const T *)p.wq + h * p.sw_h, p.d, sW);
-  for (int i = tid; i < F * DV / 4; i += 256) {  // S^T, rounded to the operand type
-    const int f = i / (DV / 4), c4 = 4 * (i % (DV / 4));
-    const f32x4 s4 = *reinterpret_cast<const f32x4 *>(st + (int64_t)f * DV + c4);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) sSt[(c4 + x) * LDF + f] = (T)s4[x];
-  }
-  for (int i = tid; i < F; i += 256) sZ[i] = st[(int64_t)F * DV + i];
   __syncthreads();
-  // phi(q) rows of the block
+  const int lq = (int)qb * CP_BLK + 16 * wv + col;  // this lane's query within the chunk
+  frag qf[KF];
+  float den;
   {
     f32x4 ph[NFT];
-    cp_features<T, FH>((const T *)p.q + b * p.sq_b + h * p.sq_h, p.sq_t, tq, p.n, p.d, sW, ph, wv, lane);
+    CpX<T> xq;
+    cp_load_x<T>((const T *)p.q + b * p.sq_b + h * p.sq_h, p.sq_t, tq, p.n, p.d, xq, wv, lane);
+    cp_features<T, FH>(xq, p.d, sW, ph, lane);
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft)
+    for (int s = 0; s < KF; ++s) qf[s] = M::from_acc(ph, s);
+    // e^{L} phiQ . z on the rounded features the products use
+    float dz = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sQ[(16 * wv + col) * LDF + 16 * ft + 4 * g + r] = (T)ph[ft][r];
+    for (int ft = 0; ft < NFT; ++ft) {
+      const f32x4 z4 = *reinterpret_cast<const f32x4 *>(st + (int64_t)F * DV + 16 * ft + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dz = __builtin_fmaf((float)(T)ph[ft][r], z4[r], dz);
+    }
+    den = group_sum(dz);
   }
-  __syncthreads();
-  // inter-chunk read-out: O = diag(e^{L}) phiQ S, den = e^{L} phiQ . z
+  const float eLq = __expf((float)sL[lq]);
+  den *= eLq;
+  // inter-chunk read-out: O^T[c][t] = e^{L_t} sum_f S^T[c][f] phiQ[t][f], S^T rows from global memory
   f32x4 O[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     O[ct] = zero4();
+    const float *row = st + (int64_t)(16 * ct + col) * F;
 #pragma unroll
-    for (int k0 = 0; k0 < F; k0 += M::KS)
-      O[ct] = M::mma(M::ld_contig(sQ + (16 * wv + col) * LDF + k0, g), M::ld_contig(sSt + (16 * ct + col) * LDF + k0, g),
-                     O[ct]);
+    for (int s = 0; s < KF; ++s) O[ct] = M::mma(cp_row_tile<T>(row, s, g), qf[s], O[ct]);
+    O[ct] *= eLq;
   }
-  float eL[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) eL[r] = __expf((float)sL[qb * CP_BLK + 16 * wv + 4 * g + r]);
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) O[ct][r] *= eL[r];
-  float den = 0.f;  // thread t < 64: query t's denominator
-  if (tid < CP_BLK) {
-    for (int f = 0; f < F; ++f) den = __builtin_fmaf((float)sQ[tid * LDF + f], sZ[f], den);
-    den *= __expf((float)sL[qb * CP_BLK + tid]);
-  }
-  __syncthreads();  // the start state's copy is done with; W^T of k replaces W^T of q
-  cp_stage_wt<T, FH>((const T *)p.wk + h * p.sw_h, p.d, sW);
   const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
   const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h;
+  CpX<T> xk;
+  CpV<T, DV> vr;
+  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
+  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
+  __syncthreads();  // every wave is done with W_q^T
+  cp_stage_wt<T, FH>((const T *)p.wk + h * p.sw_h, p.d, sW);
   __syncthreads();
   for (int kb = 0; kb <= qb; ++kb) {
     const int64_t tb = t0 + kb * CP_BLK;
     {
       f32x4 ph[NFT];
-      cp_features<T, FH>(K, p.sk_t, tb, p.n, p.d, sW, ph, wv, lane);
+      cp_features<T, FH>(xk, p.d, sW, ph, lane);
 #pragma unroll
-      for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sK[(16 * wv + col) * LDF + 16 * ft + 4 * g + r] = (T)ph[ft][r];
+      for (int ft = 0; ft < NFT; ++ft) cp_store4(&sK[(16 * wv + col) * LDF + M::tpos(16 * ft + 4 * g)], ph[ft]);
     }
-    cp_stage_vt<T, DV>(V, p.sv_t, tb, p.n, sVt);
+    cp_write_vt<T, DV, true>(vr, sVt);
+    // the next key block's rows are in flight during this block's products
+    if (kb < qb) {
+      cp_load_x<T>(K, p.sk_t, tb + CP_BLK, p.n, p.d, xk, wv, lane);
+      cp_load_v<T, DV>(V, p.sv_t, tb + CP_BLK, p.n, vr);
+    }
     __syncthreads();
-    // weighted scores of query tile wv against the block's four key tiles
+    // weighted scores Pt[s][t] of the block's four key tiles against this wave's queries
+    f32x4 pt[4];
+    float dsum = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x4 s = zero4();
+      f32x4 a = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < F; k0 += M::KS)
-        s = M::mma(M::ld_contig(sQ + (16 * wv + col) * LDF + k0, g), M::ld_contig(sK + (16 * j + col) * LDF + k0, g), s);
-      const int ls = kb * CP_BLK + 16 * j + col;  // key within the chunk
+      for (int s = 0; s < KF; ++s) a = M::mma(M::ld_tile(sK + (16 * j + col) * LDF, s, g), qf[s], a);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int lq = qb * CP_BLK + 16 * wv + 4 * g + r;  // query within the chunk
-        const float w = ls <= lq ? s[r] * __expf((float)(sL[lq] - sL[ls])) : 0.f;
-        sP[(16 * wv + 4 * g + r) * L::LDB + 16 * j + col] = (T)w;
+        const int ls = kb * CP_BLK + 16 * j + 4 * g + r;  // key within the chunk
+        const float w = ls <= lq ? a[r] * __expf((float)(sL[lq] - sL[ls])) : 0.f;
+        pt[j][r] = (float)(T)w;  // the weight as the product with V sees it
+        dsum += pt[j][r];
       }
     }
-    __syncthreads();
-    if (tid < CP_BLK) {
-#pragma unroll 8
-      for (int s = 0; s < CP_BLK; ++s) den += (float)sP[tid * L::LDB + s];
-    }
+    den += group_sum(dsum);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int k0 = 0; k0 < CP_BLK; k0 += M::KS)
-        O[ct] = M::mma(M::ld_contig(sP + (16 * wv + col) * L::LDB + k0, g), M::ld_contig(sVt + (16 * ct + col) * L::LDB + k0, g),
-                       O[ct]);
+      for (int s = 0; s < KB; ++s)
+        O[ct] = M::mma(M::ld_tile(sVt + (16 * ct + col) * L::LDB, s, g), M::from_acc(pt, s), O[ct]);
     __syncthreads();
   }
-  if (tid < CP_BLK) sDen[tid] = den;
-  __syncthreads();
-  T *Ob = (T *)p.o + b * p.so_b + h * p.so_h;
+  // lane (col, g) holds columns 16ct + 4g .. +3 of query tq + 16 wv + col
+  const int64_t t = tq + 16 * wv + col;
+  if (t < p.n) {
+    const float inv = 1.f / den;
+    T *orow = (T *)p.o + b * p.so_b + h * p.so_h + t * p.so_t;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int lt = 16 * wv + 4 * g + r;
-    const int64_t t = tq + lt;
-    if (t < p.n) {
-      const float inv = 1.f / sDen[lt];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) Ob[t * p.so_t + 16 * ct + col] = (T)(O[ct][r] * inv);
-    }
+    for (int ct = 0; ct < NCT; ++ct) cp_store4(orow + 16 * ct + 4 * g, O[ct] * inv);
   }
 }
 

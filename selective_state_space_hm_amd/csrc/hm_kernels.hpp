@@ -90,6 +90,8 @@ Table table_fwd_rope_bf16_decay();
 Table table_fwd_rope_f32();
 Table table_fwd_c128();
 Table table_step_feat();
+Table table_step_bf16();
+Table table_step_f32();
 
 template <typename T, int DK, int FH, int DW, bool DECAY, int MODE, int CH>
 void launch_fwd(const FwdParams &p, unsigned grid, hipStream_t s) {

@@ -148,7 +148,8 @@ __device__ __forceinline__ void step_features(const StepParams &p, int64_t b, in
 template <typename T, int DK, int FH>
 __device__ __forceinline__ void stage_w_lds(const StepParams &p, int64_t h, T *sW) {
   constexpr int EP = 16 / (int)sizeof(T), PER_MAT = DK * FH / EP, NP = 2 * PER_MAT, NIT = (NP + 255) / 256;
-  static_assert(PER_MAT % 64 == 0, "whole waves of pieces");
+  // every wave loads 64 whole pieces (a wave may take the end of W_q and the start of W_k)
+  static_assert(NP % 64 == 0, "whole waves of pieces");
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid >= 256) return;

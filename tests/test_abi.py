@@ -228,7 +228,8 @@ def test_step_validation_errors():
     expect(hm.call_step(step(state=A + 8)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(sq_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(d=48)), hm.HM_ERR_UNSUPPORTED)
-    expect(hm.call_step(step(d=64, f=64, dv=32)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(f=48)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_step(step(dv=96)), hm.HM_ERR_UNSUPPORTED)
     expect(hm.call_step(step(gate=A + 0xa000008, sg_b=16 * 128, sg_h=128)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=16 * 128, sg_h=100)), hm.HM_ERR_ALIGN)
     expect(hm.call_step(step(gate=A + 0xa000000, sg_b=-1, sg_h=128)), hm.HM_ERR_SHAPE)

@@ -288,6 +288,34 @@ def test_decode_steps(dtype, shape, decay, per_head):
     assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("f", [16, 32, 64])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_decode_size_matrix(dtype, d, f, dv):
+    """Every (dtype, d, f, dv) of the size matrix: 6 decayed steps from a 30-token
+    prefix state, each step's output and the final state against the oracle."""
+    B, H, steps = 2, 2, 6
+    dc = inputs.decode_setup(B, H, d, f, dv, prefix=30, steps=steps, decay=True, dtype=dtype, seed=d + f + dv)
+    pk = orc.hedgehog_features(f64(dc.prefix_k), f64(dc.w_k))
+    S, z = orc.prefix_state(pk, f64(dc.prefix_v), orc.log_decay(f64(dc.prefix_dt), f64(dc.a_log)))
+    state = torch.tensor(orc.pack_state(S, z), dtype=torch.float32, device="cuda")
+    wq, wk, a_log = dc.w_q.cuda(), dc.w_k.cuda(), dc.a_log.cuda()
+    worst = 0.0
+    for t in range(steps):
+        q, k, v, dt = inputs.decode_step_inputs(dc, t, dtype)
+        o = hm.hm_linattn_step(q.cuda(), k.cuda(), v.cuda(), wq, wk, state, dt.cuda(), a_log)
+        torch.cuda.synchronize()
+        ot, S, z = orc.step(S, z, f64(q), f64(k), f64(v), f64(dc.w_q), f64(dc.w_k), f64(dt), f64(dc.a_log))
+        worst = max(worst, rel_l2(f64(o), ot))
+    Sg, zg = orc.unpack_state(f64(state), 2 * f, dv)
+    print(f"[parity] decode {dtype} ({d}, {f}, {dv}): worst step rel-L2 {worst:.3e}, state rel-L2 "
+          f"{rel_l2(Sg, S):.3e}", flush=True)
+    assert worst <= tol_for(dtype)
+    assert rel_l2(Sg, S) <= (1e-6 if dtype == torch.float32 else 1e-5)
+    assert rel_l2(zg, z) <= (1e-6 if dtype == torch.float32 else 1e-5)
+
+
 def test_prefill_then_decode_handoff():
     c = inputs.make_prefill("pd", 2, 2, 300, 128, 64, 128, torch.bfloat16, None, "mamba", seed=12)
     st = torch.empty((2, 2, hm.state_numel(64, 128)), device="cuda")
