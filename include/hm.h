@@ -63,21 +63,22 @@
  *     next synchronization.  NaN/Inf in the inputs are not checked; they
  *     propagate to the outputs.
  *   - Supported sizes (anything else is HM_ERR_UNSUPPORTED):
- *       hm_linattn_fwd, hm_linattn_step:
- *         bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}; also
- *                (d, f, dv) = (32, 16, 32), and dv = 32 at (64, 32) and (128, 64)
- *                (hm_linattn_fwd: dv = 32 at every (d, f) of the first line, and
- *                (32, 16, 64) as two 32-column workgroups, dsplit 2)
- *         f32:   d in {16, 32},  f = 16,        dv in {16, 32}; and d = 64 with
- *                (f, dv) in {(16, 16), (16, 32), (32, 32), (32, 64)}
- *       Not built, and why:
- *         f32 at d = 128, f = 64: the full pass keeps W_q^T, W_k^T, two blocks of
- *           phi(q) rows and of phi(k)^T, the score tile and the output rows in LDS:
- *           157 KB in bf16, twice that in f32 (the bf16 path is the one measured);
- *         bf16 at d = 16: the bf16 MFMA (16x16x32) takes K in steps of 32, so d
- *           must be a multiple of 32;
- *         f = 16 in bf16 with d > 32 or dv > 32: not instantiated (the widths
- *           the pages measure are built, plus the one small bf16 shape).
+ *       hm_linattn_fwd, hm_linattn_step: d in {16, 32, 64, 128}, f in {16, 32, 64},
+ *         dv in {16, 32, 64, 128}, bf16 and f32.  The prefill runs fused kernels
+ *         (chunk 64 or 128; segments, column splits, gate, rotary, saves) at
+ *           bf16:  d in {64, 128}, f in {32, 64}, dv in {64, 128}; (d, f, dv) =
+ *                  (32, 16, 32); dv = 32 at every (d, f) of this line; and
+ *                  (32, 16, 64) as two 32-column workgroups (dsplit 2)
+ *           f32:   d in {16, 32}, f = 16, dv in {16, 32}; and d = 64 with
+ *                  (f, dv) in {(16, 16), (16, 32), (32, 32), (32, 64)}
+ *         and every other size, and chunk 256 at every size, on the
+ *         chunk-parallel path (see hm_linattn_fwd): the plain prefill only (no
+ *         gate, rotary encoding or training saves; segments 0; dsplit 0 or 1).
+ *         The fused kernels hold W_q^T, W_k^T, phi(q), phi(k)^T, the score tile
+ *         and the output rows of a 64-token chunk in LDS (157 KB at bf16, d = 128,
+ *         f = 64), which float32 at that size would double; bf16 d = 16 is below
+ *         one 32-deep bf16 MFMA step; f = 16 at the larger d and dv is not
+ *         instantiated.  The decode step is built at every size and dtype.
  *       hm_featurize:
  *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
  *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}
@@ -145,21 +146,27 @@ hm_status hm_featurize(const hm_featurize_args *args, void *stream);
  *   w_q, w_k: [d, f] each (head stride sw_h).
  *   s_init: optional initial state (NULL = zeros); s_final: optional, receives the
  *   state after token n-1.  They may point to the same buffer.
- *   chunk: the chunk length of the chunk-wise form, 0 = automatic (64), 64 or
- *   128.  A 128-token chunk reads its outputs against the state at the chunk's
- *   start plus the masked, decayed scores of all its earlier tokens, and passes the
- *   state once per chunk; it is built for the plain prefill (no `save`, gate or
- *   rotary encoding: HM_ERR_UNSUPPORTED) at every size below.  256 is
- *   HM_ERR_UNSUPPORTED: a 256-token chunk's phi(q), phi(k) and v alone take 192 KB of
- *   LDS in bf16 at 2f = dv = 128, above the 160 KB of a compute unit.
+ *   chunk: the chunk length of the chunk-wise form, 0 = automatic (64), 64, 128
+ *   or 256.  A chunk's outputs read the state at the chunk's start plus the
+ *   masked, decayed scores of all its earlier tokens, and the state passes once
+ *   per chunk.  128 runs the fused kernels for the plain prefill (no `save`, gate
+ *   or rotary encoding: HM_ERR_UNSUPPORTED).  256, and every size without a fused
+ *   kernel, run the chunk-parallel path: one pass writes every chunk's local end
+ *   state and summed log-decay to the workspace, a scan over the chunks turns
+ *   them into start states (and s_final), and a last pass forms each 64-query
+ *   block's outputs from its chunk's start state and the chunk's earlier keys.
+ *   That path takes the plain prefill only, segments = 0 and dsplit 0 or 1
+ *   (else HM_ERR_UNSUPPORTED); its workspace is B*H*ceil(n/chunk)*(F*dv + F + 1)
+ *   floats (rounded up), linear in n, and the plan reports one segment per chunk.
  *   segments: 0 = automatic, else the number of sequence segments scanned in
  *   parallel (their start states are joined by the affine composition of
  *   [SSM] §4.2).  dsplit: 0 = automatic, 1 or 2 = number of workgroups that
  *   share one (b, h), each owning dv/dsplit value columns.
  *   workspace: device scratch of at least hm_linattn_fwd_workspace_size() bytes
- *   (it may be NULL when that size is 0).  Its size grows with B*H*segments (up
- *   to 4 state blocks per segment: the segment pass may cut a segment into
- *   equal pieces when that fills more of the GPU), never with n^2.
+ *   (it may be NULL when that size is 0).  On the fused kernels its size grows
+ *   with B*H*segments (up to 4 state blocks per segment: the segment pass may cut
+ *   a segment into equal pieces when that fills more of the GPU); on the
+ *   chunk-parallel path with B*H*chunks; never with n^2.
  *   save: optional (NULL = inference), hm_linattn_save_size() bytes: the forward
  *   also keeps what hm_linattn_bwd reads (a float32 state checkpoint at the start
  *   of each of the backward's chunk ranges, at most 256 / (B*H) of them per
@@ -218,9 +225,10 @@ hm_status hm_linattn_fwd(const hm_linattn_fwd_args *args, void *stream);
  * hm_linattn_fwd (the caller still passes all inputs and outputs, `save` included).
  *   - The scratch is HM_NOALLOC_SCRATCH_BYTES (40 MiB) per GPU, a static device
  *     array that each GPU the library runs on holds until the process ends.  Every
- *     automatic plan fits (its segment states stay within 256 state blocks plus a
- *     copy of s_init); a plan that needs more (many explicit `segments` with many
- *     heads) returns HM_ERR_WORKSPACE and launches nothing.
+ *     automatic plan of the fused kernels fits (its segment states stay within 256
+ *     state blocks plus a copy of s_init); a plan that needs more (many explicit
+ *     `segments` with many heads, or a chunk-parallel plan whose B*H*chunks state
+ *     blocks exceed it) returns HM_ERR_WORKSPACE and launches nothing.
  *   - The first call with a device current looks up that device's scratch address
  *     (hipGetSymbolAddress); a failure there returns HM_ERR_HIP.  No call allocates
  *     or frees memory.
