@@ -80,7 +80,7 @@
  *         one 32-deep bf16 MFMA step; f = 16 at the larger d and dv is not
  *         instantiated.  The decode step is built at every size and dtype.
  *       hm_featurize:
- *         bf16 x: d in {32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
+ *         bf16 x: d in {16, 32, 64, 128}, f in {16, 32, 64} (phi bf16 or f32)
  *         f32 x:  d in {16, 32, 64, 128}, f in {16, 32, 64}
  *       with rope_dims > 0, hm_linattn_fwd is built for bf16 (d, f) in
  *       {(128, 64), (64, 32)} and f32 (d, f) in {(16, 16), (32, 16)}; the step and

@@ -283,7 +283,8 @@ struct FeatParams {
 template <typename T, int DK, int FH>
 __device__ __forceinline__ float feature_tiles(const typename Mma<T>::frag *xf, const T *sW, f32x4 *ph) {
   using M = Mma<T>;
-  constexpr int NFH = FH / 16, KD = DK / M::KS, LDW = DK + M::PAD;
+  // K padded to one MFMA step when d is shorter (bf16 d = 16: W^T columns and operand slices past d are zero)
+  constexpr int DKP = DK < M::KS ? M::KS : DK, NFH = FH / 16, KD = DKP / M::KS, LDW = DKP + M::PAD;
   const int lane = threadIdx.x & 63, col = lane & 15, g = lane >> 4;
   f32x4 u[NFH];
 #pragma unroll
@@ -320,7 +321,8 @@ template <typename T, typename TO, int DK, int FH>
 __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int NFH = FH / 16, NFT = 2 * NFH, KD = DK / M::KS, LDW = DK + M::PAD;
+  constexpr int DKP = DK < M::KS ? M::KS : DK;  // K padded to one MFMA step (bf16 d = 16)
+  constexpr int NFH = FH / 16, NFT = 2 * NFH, KD = DKP / M::KS, LDW = DKP + M::PAD;
   __shared__ __align__(16) T sW[FH * LDW];
   __shared__ double sRev[FH];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
@@ -330,7 +332,9 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   frag xf[KD], xn[KD];
   auto load_x = [&](frag *x, int64_t c) {
 #pragma unroll
-    for (int s = 0; s < KD; ++s) x[s] = c < p.n ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g) : frag{};
+    for (int s = 0; s < KD; ++s)
+      x[s] = c < p.n && s * M::KS + (M::EPL == 8 ? 8 * g : g) < DK ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g)
+                                                                   : frag{};
   };
   load_x(xf, c0);  // the first block's rows go out before W^T is staged
   {
@@ -352,6 +356,9 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
 #pragma unroll
         for (int e = 0; e < EP; ++e) sW[(f0 + e) * LDW + d] = wv4[i][e];
       }
+    }
+    if constexpr (DKP > DK) {
+      for (int i = tid; i < FH * (DKP - DK); i += 256) sW[(i / (DKP - DK)) * LDW + DK + i % (DKP - DK)] = (T)0.f;
     }
   }
   if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);

@@ -6,6 +6,7 @@ namespace hm {
 #define HM_FEAT_F(T, TC, TO, TOC, DK) \
   HM_FEAT(T, TC, TO, TOC, DK, 16), HM_FEAT(T, TC, TO, TOC, DK, 32), HM_FEAT(T, TC, TO, TOC, DK, 64)
 static const FeatEntry kFeat[] = {
+    HM_FEAT_F(bf16, HM_DT_BF16, bf16, HM_DT_BF16, 16),  HM_FEAT_F(bf16, HM_DT_BF16, float, HM_DT_F32, 16),
     HM_FEAT_F(bf16, HM_DT_BF16, bf16, HM_DT_BF16, 32),  HM_FEAT_F(bf16, HM_DT_BF16, bf16, HM_DT_BF16, 64),
     HM_FEAT_F(bf16, HM_DT_BF16, bf16, HM_DT_BF16, 128), HM_FEAT_F(bf16, HM_DT_BF16, float, HM_DT_F32, 32),
     HM_FEAT_F(bf16, HM_DT_BF16, float, HM_DT_F32, 64),  HM_FEAT_F(bf16, HM_DT_BF16, float, HM_DT_F32, 128),

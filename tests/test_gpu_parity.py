@@ -34,6 +34,8 @@ def full_oracle(case, s_init=None, z_init=None, form="recurrent"):
     (torch.float32, torch.float32, 16, 16, 77), (torch.float32, torch.float32, 128, 64, 77),
     (torch.float32, torch.float32, 64, 32, 77), (torch.bfloat16, torch.bfloat16, 128, 64, 77),
     (torch.bfloat16, torch.float32, 128, 64, 77), (torch.bfloat16, torch.float32, 32, 16, 77),
+    # bf16 at d = 16: one MFMA K-step padded past d
+    (torch.bfloat16, torch.float32, 16, 16, 77), (torch.bfloat16, torch.bfloat16, 16, 64, 300),
     # several workgroups of four 64-token blocks, the last one ragged
     (torch.bfloat16, torch.bfloat16, 128, 64, 600), (torch.float32, torch.float32, 64, 32, 600)])
 def test_featurize(dtype, phi_dtype, d, f, n):
