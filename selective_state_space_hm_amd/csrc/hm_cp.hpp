@@ -50,28 +50,34 @@ template <typename T> struct CpLds {
   static constexpr int LDB = CP_BLK + PAD;    // rows over a block's tokens
 };
 
-// The inclusive log-decay prefix over tokens t0 .. t0+cnt-1 of one (b, h), from t0
-// on, into sL[0 .. cnt), by one wave, in float64 (differences of large prefix sums
-// lose ~|L| 2^-24 in float32); tokens at or past n add 0.
-__device__ __forceinline__ void cp_decay_prefix(const CpParams &p, int64_t b, int64_t h, int64_t t0, int cnt,
-                                                double *sL, int lane) {
+// The dt values of tokens t0 .. t0+cnt-1 of one (b, h) for one wave (lane + 64 i),
+// requested together; then their inclusive log-decay prefix from t0 on, into
+// sL[0 .. cnt), in float64 (differences of large prefix sums lose ~|L| 2^-24 in
+// float32); tokens at or past n add 0.
+struct CpDt {
+  float v[CP_CHMAX / 64];
+};
+__device__ __forceinline__ void cp_load_dt(const CpParams &p, int64_t b, int64_t h, int64_t t0, int cnt, CpDt &r,
+                                           int lane) {
   const bool decay = p.dt != nullptr;
   const float *DT = decay ? p.dt + b * p.sdt_b + h * p.sdt_h : nullptr;
-  const float expA = decay ? expf(p.a_log[h]) : 0.f;
-  constexpr int NI = CP_CHMAX / 64;
-  float dtv[NI];  // every dt of the range requested before the scan
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int i = 0; i < CP_CHMAX / 64; ++i) {
     const int64_t t = t0 + 64 * i + lane;
-    dtv[i] = decay && 64 * i + lane < cnt && t < p.n ? DT[t * p.sdt_t] : 0.f;
+    r.v[i] = decay && 64 * i + lane < cnt && t < p.n ? DT[t * p.sdt_t] : 0.f;
   }
+}
+__device__ __forceinline__ void cp_decay_scan(const CpParams &p, int64_t h, int64_t t0, int cnt, const CpDt &r,
+                                              double *sL, int lane) {
+  const bool decay = p.dt != nullptr;
+  const float expA = decay ? expf(p.a_log[h]) : 0.f;
   double carry = 0.0;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
+  for (int i = 0; i < CP_CHMAX / 64; ++i) {
     if (64 * i < cnt) {
       const int64_t t = t0 + 64 * i + lane;
       const bool valid = decay && 64 * i + lane < cnt && t < p.n;
-      const double x = valid ? (double)(-softplus_f32(dtv[i]) * expA) : 0.0;
+      const double x = valid ? (double)(-softplus_f32(r.v[i]) * expA) : 0.0;
       const double L = wave_inclusive_scan(x) + carry;
       if (64 * i + lane < cnt) sL[64 * i + lane] = L;
       carry = lane63(L);
@@ -79,32 +85,38 @@ __device__ __forceinline__ void cp_decay_prefix(const CpParams &p, int64_t b, in
   }
 }
 
-// W^T (W is [d][FH] row-major, head stride sw_h) into sW rows of LDW elements,
-// columns past d up to one MFMA K-step zero-filled; all threads.
-template <typename T, int FH>
-__device__ __forceinline__ void cp_stage_wt(const T *W, int d, T *sW) {
-  using L = CpLds<T>;
-  constexpr int EPL = 16 / (int)sizeof(T), PR = FH / EPL;  // 16-byte pieces per row of W
-  constexpr int NI = (CP_DKMAX * PR + 255) / 256;
-  // rows of W as 16-byte pieces (consecutive threads read consecutive pieces), all
-  // requested before any is written
+// W (W is [d][FH] row-major, head stride sw_h) as 16-byte pieces, one per thread and
+// NI rounds (consecutive threads read consecutive pieces of a row) ...
+template <typename T, int FH> struct CpW {
+  static constexpr int EPL = 16 / (int)sizeof(T), PR = FH / EPL, NI = (CP_DKMAX * PR + 255) / 256;
   f32x4 raw[NI];
+};
+template <typename T, int FH>
+__device__ __forceinline__ void cp_load_w(const T *W, int d, CpW<T, FH> &r) {
+  using WW = CpW<T, FH>;
 #pragma unroll
-  for (int m = 0; m < NI; ++m) {
+  for (int m = 0; m < WW::NI; ++m) {
     const int i = threadIdx.x + 256 * m;
-    if (i < d * PR) raw[m] = *reinterpret_cast<const f32x4 *>(W + (int64_t)(i / PR) * FH + (i % PR) * EPL);
+    if (i < d * WW::PR)
+      r.raw[m] = *reinterpret_cast<const f32x4 *>(W + (int64_t)(i / WW::PR) * FH + (i % WW::PR) * WW::EPL);
   }
+}
+// ... into sW as W^T (rows of LDW elements), columns d .. KS-1 zero when d is below
+// one MFMA K-step.
+template <typename T, int FH>
+__device__ __forceinline__ void cp_write_wt(const CpW<T, FH> &r, int d, T *sW) {
+  using WW = CpW<T, FH>;
+  using L = CpLds<T>;
 #pragma unroll
-  for (int m = 0; m < NI; ++m) {
+  for (int m = 0; m < WW::NI; ++m) {
     const int i = threadIdx.x + 256 * m;
-    if (i < d * PR) {
-      const int dd = i / PR, j0 = (i % PR) * EPL;
-      const T *e = reinterpret_cast<const T *>(&raw[m]);
+    if (i < d * WW::PR) {
+      const int dd = i / WW::PR, j0 = (i % WW::PR) * WW::EPL;
+      const T *e = reinterpret_cast<const T *>(&r.raw[m]);
 #pragma unroll
-      for (int x = 0; x < EPL; ++x) sW[(j0 + x) * L::LDW + dd] = e[x];
+      for (int x = 0; x < WW::EPL; ++x) sW[(j0 + x) * L::LDW + dd] = e[x];
     }
   }
-  // columns d .. KS-1 of W^T are zero when d is below one MFMA K-step
   const int dpad = d < Mma<T>::KS ? Mma<T>::KS : d;
   for (int i = threadIdx.x; i < FH * (dpad - d); i += 256) sW[(i / (dpad - d)) * L::LDW + d + i % (dpad - d)] = (T)0.f;
 }
@@ -227,18 +239,24 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
   const int cnt = (int)(p.n - t0 < p.chunk ? p.n - t0 : p.chunk);
   const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
   const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h;
-  if (wv == 0) cp_decay_prefix(p, b, h, t0, cnt, sL, lane);
-  cp_stage_wt<T, FH>((const T *)p.wk + h * p.sw_h, p.d, sW);
+  // every load of the setup is requested before the first is used: dt (wave 0), W_k,
+  // the first block's k rows and v pieces
+  CpDt dtr;
+  if (wv == 0) cp_load_dt(p, b, h, t0, cnt, dtr, lane);
+  CpW<T, FH> wk;
+  cp_load_w<T, FH>((const T *)p.wk + h * p.sw_h, p.d, wk);
+  CpX<T> xk;
+  CpV<T, DV> vr;
+  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
+  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
+  if (wv == 0) cp_decay_scan(p, h, t0, cnt, dtr, sL, lane);
+  cp_write_wt<T, FH>(wk, p.d, sW);
   __syncthreads();
   const double lam = sL[cnt - 1];
   f32x4 acc[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = zero4();
   float zsum = 0.f;  // thread f < F: dz[f]
-  CpX<T> xk;
-  CpV<T, DV> vr;
-  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
-  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
   for (int kb = 0; kb * CP_BLK < cnt; ++kb) {
     const int64_t tb = t0 + kb * CP_BLK;
     {
@@ -329,19 +347,6 @@ static __global__ __launch_bounds__(256) void cp_scan_kernel(const CpParams p, i
   if (p.s_final) p.s_final[bh * BLK + es] = s;
 }
 
-// A K-step (tile order) of a float32 row in global memory, as an MFMA operand of
-// type T: bf16 slots e take k = 32s + 16(e/4) + 4g + e%4 (two 16-byte loads), f32
-// step s takes k = 16(s/4) + 4g + s%4.
-template <typename T> __device__ __forceinline__ typename Mma<T>::frag cp_row_tile(const float *row, int s, int g);
-template <> __device__ __forceinline__ bf16x8 cp_row_tile<bf16>(const float *row, int s, int g) {
-  const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 32 * s + 4 * g);
-  const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 32 * s + 16 + 4 * g);
-  return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-}
-template <> __device__ __forceinline__ float cp_row_tile<float>(const float *row, int s, int g) {
-  return row[16 * (s >> 2) + 4 * g + (s & 3)];
-}
-
 // Four consecutive values of an accumulator column as T, at p (8 or 16 bytes).
 __device__ __forceinline__ void cp_store4(bf16 *p, f32x4 v) {
   *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
@@ -362,10 +367,16 @@ __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   using L = CpLds<T>;
   constexpr int F = 2 * FH, NFT = F / 16, NCT = DV / 16, LDF = F + L::PAD;
   constexpr int KF = M::steps(NFT), KB = M::steps(4);  // K-steps over the features, over a block's keys
-  __shared__ __align__(16) T sW[FH * L::LDW];
-  __shared__ __align__(16) T sK[CP_BLK * LDF];  // phi(k) rows of a key block, features in tile order
-  __shared__ __align__(16) T sVt[DV * L::LDB];  // v^T of a key block, keys in tile order
+  // LDS: W_q^T, W_k^T; the start state's read-out copy S^T (dv rows of F, features in
+  // tile order) shares space with one key block's phi(k) rows and v^T, used after it
+  constexpr int KV = CP_BLK * LDF + DV * L::LDB, ST = DV * LDF;
+  constexpr int NS = (DV * F / 4 + 255) / 256;  // 16-byte pieces of S^T per thread
+  __shared__ __align__(16) T sWq[FH * L::LDW];
+  __shared__ __align__(16) T sWk[FH * L::LDW];
+  __shared__ __align__(16) T sU[KV > ST ? KV : ST];
+  __shared__ __align__(16) float sZ[F];
   __shared__ double sL[CP_CHMAX];
+  T *sSt = sU, *sK = sU, *sVt = sU + CP_BLK * LDF;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int nqb = p.chunk / CP_BLK;
   const int64_t qb = blockIdx.x % nqb, c = (blockIdx.x / nqb) % p.nc, bh = blockIdx.x / nqb / p.nc;
@@ -374,24 +385,52 @@ __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   const int cnt = (int)((qb + 1) * CP_BLK);  // chunk tokens up to this block's end
   const int64_t BLK = (int64_t)F * DV + F;
   const float *st = p.ws_state + (bh * p.nc + c) * BLK;  // start state: S^T [DV][F], then z [F]
-  if (wv == 0) cp_decay_prefix(p, b, h, t0, cnt, sL, lane);
-  cp_stage_wt<T, FH>((const T *)p.wq + h * p.sw_h, p.d, sW);
+  // every load of the setup is requested before the first is used: dt (wave 0), the
+  // query rows, W_q and W_k, the start state
+  CpDt dtr;
+  if (wv == 0) cp_load_dt(p, b, h, t0, cnt, dtr, lane);
+  CpX<T> xq;
+  cp_load_x<T>((const T *)p.q + b * p.sq_b + h * p.sq_h, p.sq_t, tq, p.n, p.d, xq, wv, lane);
+  CpW<T, FH> wq, wk;
+  cp_load_w<T, FH>((const T *)p.wq + h * p.sw_h, p.d, wq);
+  cp_load_w<T, FH>((const T *)p.wk + h * p.sw_h, p.d, wk);
+  f32x4 sr[NS];
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    const int i = tid + 256 * m;
+    if (i < DV * F / 4) sr[m] = *reinterpret_cast<const f32x4 *>(st + 4 * i);
+  }
+  const f32x4 zr = tid < F / 4 ? *reinterpret_cast<const f32x4 *>(st + (int64_t)F * DV + 4 * tid) : zero4();
+  if (wv == 0) cp_decay_scan(p, h, t0, cnt, dtr, sL, lane);
+  cp_write_wt<T, FH>(wq, p.d, sWq);
+  cp_write_wt<T, FH>(wk, p.d, sWk);
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    const int i = tid + 256 * m;  // S^T[cc][f0 .. f0+3] -> its tile-order place in row cc
+    if (i < DV * F / 4) cp_store4(&sSt[(i / (F / 4)) * LDF + M::tpos(4 * (i % (F / 4)))], sr[m]);
+  }
+  if (tid < F / 4) *reinterpret_cast<f32x4 *>(&sZ[4 * tid]) = zr;
   __syncthreads();
+  // the first key block's rows are in flight during the query features and the read-out
+  const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
+  const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h;
+  CpX<T> xk;
+  CpV<T, DV> vr;
+  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
+  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
   const int lq = (int)qb * CP_BLK + 16 * wv + col;  // this lane's query within the chunk
   frag qf[KF];
   float den;
   {
     f32x4 ph[NFT];
-    CpX<T> xq;
-    cp_load_x<T>((const T *)p.q + b * p.sq_b + h * p.sq_h, p.sq_t, tq, p.n, p.d, xq, wv, lane);
-    cp_features<T, FH>(xq, p.d, sW, ph, lane);
+    cp_features<T, FH>(xq, p.d, sWq, ph, lane);
 #pragma unroll
     for (int s = 0; s < KF; ++s) qf[s] = M::from_acc(ph, s);
     // e^{L} phiQ . z on the rounded features the products use
     float dz = 0.f;
 #pragma unroll
     for (int ft = 0; ft < NFT; ++ft) {
-      const f32x4 z4 = *reinterpret_cast<const f32x4 *>(st + (int64_t)F * DV + 16 * ft + 4 * g);
+      const f32x4 z4 = *reinterpret_cast<const f32x4 *>(&sZ[16 * ft + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) dz = __builtin_fmaf((float)(T)ph[ft][r], z4[r], dz);
     }
@@ -399,30 +438,21 @@ __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   }
   const float eLq = __expf((float)sL[lq]);
   den *= eLq;
-  // inter-chunk read-out: O^T[c][t] = e^{L_t} sum_f S^T[c][f] phiQ[t][f], S^T rows from global memory
+  // inter-chunk read-out: O^T[c][t] = e^{L_t} sum_f S^T[c][f] phiQ[t][f]
   f32x4 O[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     O[ct] = zero4();
-    const float *row = st + (int64_t)(16 * ct + col) * F;
 #pragma unroll
-    for (int s = 0; s < KF; ++s) O[ct] = M::mma(cp_row_tile<T>(row, s, g), qf[s], O[ct]);
+    for (int s = 0; s < KF; ++s) O[ct] = M::mma(M::ld_tile(sSt + (16 * ct + col) * LDF, s, g), qf[s], O[ct]);
     O[ct] *= eLq;
   }
-  const T *K = (const T *)p.k + b * p.sk_b + h * p.sk_h;
-  const T *V = (const T *)p.v + b * p.sv_b + h * p.sv_h;
-  CpX<T> xk;
-  CpV<T, DV> vr;
-  cp_load_x<T>(K, p.sk_t, t0, p.n, p.d, xk, wv, lane);
-  cp_load_v<T, DV>(V, p.sv_t, t0, p.n, vr);
-  __syncthreads();  // every wave is done with W_q^T
-  cp_stage_wt<T, FH>((const T *)p.wk + h * p.sw_h, p.d, sW);
-  __syncthreads();
+  __syncthreads();  // the read-out copy's space goes to the key blocks
   for (int kb = 0; kb <= qb; ++kb) {
     const int64_t tb = t0 + kb * CP_BLK;
     {
       f32x4 ph[NFT];
-      cp_features<T, FH>(xk, p.d, sW, ph, lane);
+      cp_features<T, FH>(xk, p.d, sWk, ph, lane);
 #pragma unroll
       for (int ft = 0; ft < NFT; ++ft) cp_store4(&sK[(16 * wv + col) * LDF + M::tpos(16 * ft + 4 * g)], ph[ft]);
     }
