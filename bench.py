@@ -45,7 +45,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
 MFMA_FLOP = 16 * 16 * 32 * 2   # one v_mfma_f32_16x16x32_bf16
 METRIC = "prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM BW (1 MI355X)"
-KERNEL_SOURCES = ["hm_device.hpp", "hm_prefill.hpp", "hm_step.hpp", "hm_abi.hip"]  # kernels and launch plans
+KERNEL_SOURCES = ["hm_device.hpp", "hm_prefill.hpp", "hm_step.hpp", "hm_cp.hpp", "hm_abi.hip"]  # kernels and plans
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
 CPU_WORKERS_MAX = 12           # oracle processes: the GPU machine allows 16 processes per GPU
 

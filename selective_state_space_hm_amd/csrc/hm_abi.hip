@@ -406,7 +406,8 @@ hm_status run_cp(const hm_linattn_fwd_args *a, const Plan &pl, void *wsp, hipStr
                      (int)F, (int)a->dv);
   if ((st = check_launch("chunk-parallel state scan")) != HM_OK) return st;
   if (pl.nc > 0) {
-    e->out(p, (unsigned)(BH * pl.nc * (pl.chunk / hm::CP_BLK)), s);
+    // chunks padded to a multiple of 8: the kernel maps a chunk's query blocks onto one XCD
+    e->out(p, (unsigned)((BH * pl.nc + 7) / 8 * 8 * (pl.chunk / hm::CP_BLK)), s);
     if ((st = check_launch("chunk-parallel outputs")) != HM_OK) return st;
   }
   return ok();

@@ -378,8 +378,13 @@ __global__ __launch_bounds__(256) void cp_out_kernel(const CpParams p) {
   __shared__ double sL[CP_CHMAX];
   T *sSt = sU, *sK = sU, *sVt = sU + CP_BLK * LDF;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
+  // workgroup -> (chunk, query block): consecutive workgroups go to different XCDs (bid % 8), so the nqb
+  // query blocks of chunk ci = 8m + x take workgroups 8 (m nqb + qb) + x, all on XCD x, where they share
+  // the chunk's start state, k and v through that XCD's L2
   const int nqb = p.chunk / CP_BLK;
-  const int64_t qb = blockIdx.x % nqb, c = (blockIdx.x / nqb) % p.nc, bh = blockIdx.x / nqb / p.nc;
+  const int64_t x8 = blockIdx.x % 8, r8 = blockIdx.x / 8, qb = r8 % nqb, ci = (r8 / nqb) * 8 + x8;
+  if (ci >= p.B * p.H * p.nc) return;  // grid padding (uniform)
+  const int64_t c = ci % p.nc, bh = ci / p.nc;
   const int64_t b = bh / p.H, h = bh % p.H, t0 = c * p.chunk, tq = t0 + qb * CP_BLK;
   if (tq >= p.n) return;  // the whole block is past the sequence's end (uniform)
   const int cnt = (int)((qb + 1) * CP_BLK);  // chunk tokens up to this block's end
