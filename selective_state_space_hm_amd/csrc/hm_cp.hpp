@@ -16,10 +16,11 @@
 // phi = softmax([x W, -x W]) (HedgeMamba explainer §2.1, §5.3); log a_t =
 // -softplus(dt_t) exp(A_log[h]) (quant67 §3.2), and a_t = 1 without dt.
 // Every product (projections, scores, the masked and decayed score tiles times V,
-// the read-out of the start state, the local state) is a 16x16 MFMA tile on LDS
-// rows that are contiguous in K; for bf16 inputs the MFMA operands (phi, the
-// weighted scores, the start state's read-out copy) are rounded to bf16 and
-// accumulated in float32.  The carried states are float32 in the workspace.
+// the read-out of the start state, the local state) is a 16x16 MFMA tile, its
+// operands read from LDS rows or kept in registers in the same K order; for bf16
+// inputs the MFMA operands (phi, the weighted scores, the start state's read-out
+// copy) are rounded to bf16 and accumulated in float32.  The carried states are
+// float32 in the workspace.
 #pragma once
 
 #include "hm_device.hpp"
