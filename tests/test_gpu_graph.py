@@ -5,7 +5,7 @@ a decode step that advances the prefill's end state in place is captured once an
 replayed.  Every replay, with eager work and synchronizations between replays,
 must give the eager result bit for bit: the kernels are deterministic and record no
 memset, copy or allocation.  The entry point without allocation is captured the
-same way (it is meant for callers that capture).
+same way (it is meant for callers that capture), and so is the chunk-parallel path.
 """
 import pytest
 import torch
@@ -84,3 +84,26 @@ def test_noalloc_prefill_replays_in_a_graph():
                                   o=o)
 
     _replays_match(run, [o, state])
+
+
+def test_chunk_parallel_prefill_replays_in_a_graph():
+    """The chunk-parallel path (chunk 256: local states, their scan, outputs) with an
+    initial state that the same buffer receives back as s_final, then a decode step
+    on it; the replays must equal the eager run."""
+    c, g, s = _case()
+    B, H = c.B, c.H
+    o = torch.empty_like(g["v"])
+    gen = torch.Generator().manual_seed(33)
+    s0 = (torch.rand((B, H, hm.state_numel(64, 128)), generator=gen) + 0.5).cuda()
+    state = torch.empty_like(s0)
+    o1 = torch.empty((B, H, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    assert hm.hm_linattn_fwd_plan(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], chunk=256)[0] == 256
+
+    def run():
+        torch.mul(s0, 1.0, out=state)  # the state starts from s0 at every replay (an element-wise kernel, no memcpy node)
+        hm.hm_linattn_fwd(g["q"], g["k"], g["v"], g["w_q"], g["w_k"], g["dt"], g["a_log"], s_init=state,
+                          s_final=state, o=o, chunk=256, workspace=ws)
+        hm.hm_linattn_step(s["q"], s["k"], s["v"], g["w_q"], g["w_k"], state, s["dt"], g["a_log"], o=o1)
+
+    _replays_match(run, [o, state, o1])
