@@ -388,8 +388,9 @@ __device__ __forceinline__ void pc_step_features(const StepParams &p, int64_t b,
 }
 
 // One workgroup of 256 threads per (b, h, group of CPS channels): every thread
-// issues the loads of its PER (channel, 4 states) items of both copies and of A
-// first, featurizes while they are in flight (each group recomputes phi(q), phi(k)
+// issues the loads of its PER (channel, 4 states) items of both copies (non-temporal:
+// the state streams through once per step) and of A (temporal: every batch row of the
+// head reads it) first, featurizes while they are in flight (each group recomputes phi(q), phi(k)
 // of its (b, h), reading W as 16-byte pieces), then updates, reads out (sum over
 // the QPC lanes of a channel) and stores in place.  Small workgroups let four share
 // a CU, so one group's featurization overlaps another's state traffic.  Bound by
@@ -416,8 +417,8 @@ __global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
   for (int m = 0; m < PER; ++m) {
     const int idx = tid + NT * m;
     if (idx < ITEMS) {
-      vn[m] = reinterpret_cast<const f32x4 *>(Sn)[idx];
-      vd[m] = reinterpret_cast<const f32x4 *>(Sd)[idx];
+      vn[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sn) + idx);
+      vd[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sd) + idx);
       va[m] = reinterpret_cast<const f32x4 *>(AL)[idx];
     }
   }
@@ -441,8 +442,8 @@ __global__ __launch_bounds__(256) void pc_step_kernel(const PcStepParams pp) {
         num = __builtin_fmaf(q4[e], vn[m][e], num);
         den = __builtin_fmaf(q4[e], vd[m][e], den);
       }
-      reinterpret_cast<f32x4 *>(Sn)[idx] = vn[m];
-      reinterpret_cast<f32x4 *>(Sd)[idx] = vd[m];
+      __builtin_nontemporal_store(vn[m], reinterpret_cast<f32x4 *>(Sn) + idx);
+      __builtin_nontemporal_store(vd[m], reinterpret_cast<f32x4 *>(Sd) + idx);
     }
     // the QPC lanes of channel c are consecutive and aligned
     if constexpr (QPC == 32) {
