@@ -957,7 +957,8 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
         }
       }
       if constexpr (FULL) __syncthreads();
-      // ---- half B: output rows of chunk j-1 to HBM, state update over chunk j-1
+      // ---- half B: output rows of chunk j-1 to HBM (non-temporal: nothing here reads them
+      //      back), state update over chunk j-1
       if (FULL && j >= 1) {
         if constexpr (FULL) {
           constexpr int EP = 16 / (int)sizeof(T);          // elements per 16-byte piece
@@ -981,7 +982,8 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
               for (int u = 0; u < GB; ++u) {
                 const int i = ((i0 + u) * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
-                if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[u];
+                if (ts + row < t1)
+                  __builtin_nontemporal_store(piece[u], reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP));
               }
               __builtin_amdgcn_sched_barrier(0);
             }
@@ -995,7 +997,8 @@ __global__ __launch_bounds__(fwd_waves(DW) * 64) void fwd_kernel(const FwdParams
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
               const int i = (it * NS + sw) * 64 + lane, row = i / PPR, pc = i % PPR;
-              if (ts + row < t1) *reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP) = piece[it];
+              if (ts + row < t1)
+                __builtin_nontemporal_store(piece[it], reinterpret_cast<f32x4 *>(ob + (int64_t)row * p.so_t + pc * EP));
             }
           }
         }
