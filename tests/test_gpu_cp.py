@@ -208,3 +208,31 @@ def test_long_context_chunk256_windows():
                     BF16_TOL)
         Sg, zg = orc.unpack_state(f64(st[0:1, h:h + 1]), 128, 128)
         assert rel_l2(Sg, S[..., :128]) <= BF16_TOL and rel_l2(zg, z) <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_strided_layouts_and_per_head_weights(dtype):
+    """q, k, v as [B, n, H, d] views (token stride H*d), o as a view of a [B, n, H, dv]
+    buffer, one W per head ([H, d, f]), chunk 256 and a ragged tail: every stride the
+    chunk-parallel kernels take, against the oracle head by head."""
+    B, H, n, d, f, dv = 2, 3, 333, 128, 64, 128
+    c = inputs.make_prefill("cstr", B, H, n, d, f, dv, dtype, None, "mild", seed=21)
+    gw = torch.Generator().manual_seed(22)
+    wq = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
+    wk = (torch.randn((H, d, f), generator=gw) / d ** 0.5).to(dtype)
+    lay = lambda t: t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3).cuda()   # [B, H, n, x] view of [B, n, H, x]
+    q, k, v = lay(c.q), lay(c.k), lay(c.v)
+    assert q.stride(2) == H * d
+    obuf = torch.full((B, n, H, dv), float("nan"), dtype=dtype, device="cuda")
+    o = obuf.permute(0, 2, 1, 3)
+    st = torch.full((B, H, hm.state_numel(f, dv)), float("nan"), device="cuda")
+    hm.hm_linattn_fwd(q, k, v, wq.cuda(), wk.cuda(), c.dt.cuda(), c.a_log.cuda(), s_final=st, o=o, chunk=256)
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    for h in range(H):
+        sl = lambda t: f64(t[:, h:h + 1])
+        ref, S, z = orc.forward(sl(c.q), sl(c.k), with_abs(sl(c.v)), f64(wq[h]), f64(wk[h]), sl(c.dt),
+                                f64(c.a_log[h:h + 1]))
+        check_bound(f"chunk256 strided per-head W {dtype} h={h}", f64(o[:, h:h + 1]), ref[..., :dv], ref[..., dv:], tol)
+        Sg, zg = orc.unpack_state(f64(st[:, h:h + 1]), 2 * f, dv)
+        assert rel_l2(Sg, S[..., :dv]) <= tol and rel_l2(zg, z) <= tol
