@@ -309,7 +309,8 @@ __global__ __launch_bounds__(256) void cp_local_kernel(const CpParams p) {
     if (tile < NTL) {
       const int ft = tile % NFT, ct = tile / NFT;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[(int64_t)(16 * ct + 4 * g + r) * F + 16 * ft + col] = acc[i][r];
+      for (int r = 0; r < 4; ++r)
+        __builtin_nontemporal_store(acc[i][r], st + (int64_t)(16 * ct + 4 * g + r) * F + 16 * ft + col);
     }
   }
   if (tid < F) st[(int64_t)F * DV + tid] = zsum;
@@ -328,19 +329,20 @@ static __global__ __launch_bounds__(256) void cp_scan_kernel(const CpParams p, i
   float s = p.s_init ? p.s_init[bh * BLK + es] : 0.f;
   float *st = p.ws_state + bh * p.nc * BLK + e;
   const float *lam = p.ws_lam + bh * p.nc;
-  // the local states of UNR chunks are requested together, so only the carry is serial
+  // the local states of UNR chunks are requested together, so only the carry is serial; the
+  // states stream through once (non-temporal: no cache level holds B*H*chunks of them)
   constexpr int UNR = 16;
   for (int64_t c0 = 0; c0 < p.nc; c0 += UNR) {
     float loc[UNR], dec[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      loc[u] = c0 + u < p.nc ? st[(c0 + u) * BLK] : 0.f;
+      loc[u] = c0 + u < p.nc ? __builtin_nontemporal_load(st + (c0 + u) * BLK) : 0.f;
       dec[u] = c0 + u < p.nc ? lam[c0 + u] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       if (c0 + u < p.nc) {
-        st[(c0 + u) * BLK] = s;
+        __builtin_nontemporal_store(s, st + (c0 + u) * BLK);
         s = __builtin_fmaf(__expf(dec[u]), s, loc[u]);
       }
     }
