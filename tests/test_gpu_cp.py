@@ -236,3 +236,17 @@ def test_strided_layouts_and_per_head_weights(dtype):
         check_bound(f"chunk256 strided per-head W {dtype} h={h}", f64(o[:, h:h + 1]), ref[..., :dv], ref[..., dv:], tol)
         Sg, zg = orc.unpack_state(f64(st[:, h:h + 1]), 2 * f, dv)
         assert rel_l2(Sg, S[..., :dv]) <= tol and rel_l2(zg, z) <= tol
+
+
+@pytest.mark.parametrize("chunk", [0, 256])
+@pytest.mark.parametrize("decay", ["mild", None])
+def test_fp32_long_sequence(chunk, decay):
+    """float32 at (128, 64, 128), n = 20000 (313 chunks of 64, or 79 of 256): the scan
+    carries float32 states through every chunk; outputs element-wise against the
+    float64 oracle at the float32 bar, and the final state."""
+    c = inputs.make_prefill("cfp32long", 1, 2, 20000, 128, 64, 128, torch.float32, None, decay, seed=41)
+    st = torch.full((1, 2, hm.state_numel(64, 128)), float("nan"), device="cuda")
+    o = run_fwd(c, s_final=st, chunk=chunk)
+    torch.cuda.synchronize()
+    ref, S, z = oracle(c)
+    check_prefill(f"chunk-parallel fp32 n=20000 chunk={chunk} decay={decay}", c, o, st, ref, S, z, FP32_TOL)
