@@ -97,7 +97,7 @@
 extern "C" {
 #endif
 
-#define HM_ABI_VERSION 8
+#define HM_ABI_VERSION 9
 
 typedef enum {
   HM_OK = 0,
@@ -119,6 +119,13 @@ typedef enum { HM_F32 = 0, HM_BF16 = 1 } hm_dtype;
  * x: [B, H, n, d] in `dtype` (strides sx_*); w: [d, f] in `dtype` (head stride
  * sw_h); phi: [B, H, n, 2f] in `phi_dtype` (strides sp_*).  The projection is
  * accumulated in float32, the softmax is evaluated in float32.
+ * With conv_width K > 0 the mixer's short causal conv (the one hm_causal_conv
+ * computes, [HM] §2.3 item 4) is applied to x in the featurizer's load prologue:
+ * each loaded row slice becomes bias + sum_j w[c][j] x[t-K+1+j][c] (float32, bias
+ * then taps oldest first, rows before token 0 from conv_prev or zero), rounded to
+ * `dtype`, before the projection: phi equals hm_featurize of hm_causal_conv's
+ * output bit for bit, without writing the convolved x.  conv_width above 4 is
+ * HM_ERR_UNSUPPORTED; K > 0 with conv_w NULL is HM_ERR_NULL.
  */
 typedef struct {
   const void *x;
@@ -133,6 +140,13 @@ typedef struct {
   int32_t rope_dims;        /* 0 = off (see the rotary fields above) */
   float rope_base;
   const int64_t *rope_pos0; /* [B] position of token 0 of each row, or NULL */
+  /* optional short causal conv applied to x as it is loaded (conv_width 0 = none) */
+  int32_t conv_width;       /* K taps, 0..4 */
+  int32_t reserved;
+  const float *conv_w;      /* float32 [d][K] (head stride scw_h), tap K-1 on the current token */
+  const float *conv_b;      /* float32 [d] (head stride scb_h) or NULL */
+  const void *conv_prev;    /* [B, H, K-1, d] in dtype, contiguous: the rows before token 0, or NULL (zeros) */
+  int64_t scw_h, scb_h;
 } hm_featurize_args;
 
 hm_status hm_featurize(const hm_featurize_args *args, void *stream);

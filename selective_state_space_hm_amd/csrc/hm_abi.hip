@@ -1063,6 +1063,11 @@ hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
     const hm_status rs = validate_rope(a->rope_dims, a->rope_base, a->rope_pos0, a->f, false);
     if (rs != HM_OK) return rs;
   }
+  if (a->conv_width < 0 || a->conv_width > 4)
+    return fail(HM_ERR_UNSUPPORTED, "conv_width %d: built are 0 (none) to 4", a->conv_width);
+  if (a->conv_width > 0 && a->B * a->H * a->n > 0 && !a->conv_w) return fail(HM_ERR_NULL, "conv_width > 0 needs conv_w");
+  if (a->scw_h < 0 || a->scb_h < 0) return fail(HM_ERR_SHAPE, "conv strides must be non-negative");
+  if (a->conv_prev && !aligned16(a->conv_prev)) return fail(HM_ERR_ALIGN, "conv_prev must be 16-byte aligned");
   const hm::FeatEntry *e = find_feat(a->dtype, a->phi_dtype, a->d, a->f);
   if (!e)
     return fail(HM_ERR_UNSUPPORTED, "no featurize kernel for dtype=%d phi_dtype=%d d=%lld f=%lld", a->dtype,
@@ -1075,6 +1080,8 @@ hm_status hm_featurize(const hm_featurize_args *a, void *stream) {
   p.sx_b = a->sx_b; p.sx_h = a->sx_h; p.sx_t = a->sx_t; p.sw_h = a->sw_h;
   p.sp_b = a->sp_b; p.sp_h = a->sp_h; p.sp_t = a->sp_t;
   p.rope_dims = a->rope_dims; p.rope_base = a->rope_base; p.rope_pos0 = a->rope_pos0;
+  p.cwidth = a->conv_width; p.cw = a->conv_w; p.cb = a->conv_b; p.cprev = a->conv_prev;
+  p.scw_h = a->scw_h; p.scb_h = a->scb_h;
   const int64_t per = 64 * hm::kFeatBlocks;  // tokens per workgroup
   e->launch(p, dim3((unsigned)((a->n + per - 1) / per), (unsigned)BH), (hipStream_t)stream);
   return check_launch("featurize");

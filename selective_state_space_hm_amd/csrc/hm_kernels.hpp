@@ -107,7 +107,8 @@ void launch_conv(const ConvParams &p, dim3 grid, hipStream_t s) {
 }
 template <typename T, typename TO, int DK, int FH>
 void launch_feat(const FeatParams &p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((featurize_kernel<T, TO, DK, FH>), grid, dim3(256), 0, s, p);
+  if (p.cwidth > 0) hipLaunchKernelGGL((featurize_kernel<T, TO, DK, FH, true>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((featurize_kernel<T, TO, DK, FH, false>), grid, dim3(256), 0, s, p);
 }
 
 }  // namespace hm

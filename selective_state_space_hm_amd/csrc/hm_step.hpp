@@ -272,6 +272,12 @@ struct FeatParams {
   int rope_dims;              // rotary encoding of phi (0 = off)
   float rope_base;
   const int64_t *rope_pos0;   // position of token 0 per batch row (NULL = 0)
+  // optional short causal conv on x (cwidth 0 = none): taps [d][K] (head stride
+  // scw_h), bias [d] (scb_h) or NULL, rows before token 0 [B, H, K-1, d] or NULL
+  int cwidth;
+  const float *cw, *cb;
+  const void *cprev;
+  int64_t scw_h, scb_h;
 };
 
 // Hedgehog features of 16 tokens per wave (gsyq.cn HedgeMamba explainer §2.1,
@@ -317,7 +323,7 @@ __device__ __forceinline__ float feature_tiles(const typename Mma<T>::frag *xf, 
 // tokens; wave w featurizes token tile w of each block, the next block's x rows in
 // flight meanwhile, and stores phi rows with 8/16-byte vector stores.
 constexpr int kFeatBlocks = 4;
-template <typename T, typename TO, int DK, int FH>
+template <typename T, typename TO, int DK, int FH, bool CONV>
 __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   using M = Mma<T>;
   using frag = typename M::frag;
@@ -330,11 +336,53 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   const int64_t c0 = (int64_t)blockIdx.x * 64 * kFeatBlocks + 16 * wv + col;  // this lane's token in block 0
   const T *X0 = (const T *)p.x + b * p.sx_b + h * p.sx_h;
   frag xf[KD], xn[KD];
+  const int K = CONV ? p.cwidth : 0;
+  const T *CP = CONV && p.cprev ? (const T *)p.cprev + bh * (int64_t)(K - 1) * DK : nullptr;
   auto load_x = [&](frag *x, int64_t c) {
+    if constexpr (!CONV) {
 #pragma unroll
-    for (int s = 0; s < KD; ++s)
-      x[s] = c < p.n && s * M::KS + (M::EPL == 8 ? 8 * g : g) < DK ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g)
-                                                                   : frag{};
+      for (int s = 0; s < KD; ++s)
+        x[s] = c < p.n && s * M::KS + (M::EPL == 8 ? 8 * g : g) < DK ? M::ld_contig(X0 + c * p.sx_t + s * M::KS, g)
+                                                                     : frag{};
+    } else {
+    // the short causal conv in the load prologue: the lane's channels of rows c-K+1 .. c
+    // (rows before token 0 from the conv state), bias then taps oldest first in float32,
+    // rounded to T as the standalone conv stores it
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      const int ch0 = s * M::KS + (M::EPL == 8 ? 8 * g : g);  // first channel of this lane's slice
+      frag out{};
+      if (c < p.n && ch0 < DK) {
+        frag rows[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t t = c - (K - 1) + j;
+          rows[j] = frag{};
+          if (j < K) {
+            if (t >= 0) rows[j] = M::ld_contig(X0 + t * p.sx_t + s * M::KS, g);
+            else if (CP) rows[j] = M::ld_contig(CP + (K - 1 + t) * DK + s * M::KS, g);
+          }
+        }
+        const float *wt = p.cw + h * p.scw_h + (int64_t)ch0 * K;
+#pragma unroll
+        for (int e = 0; e < M::EPL; ++e) {
+          float acc = p.cb ? p.cb[h * p.scb_h + ch0 + e] : 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (j < K) {
+              float xv;
+              if constexpr (M::EPL == 8) xv = (float)rows[j][e];
+              else xv = (float)rows[j];
+              acc = __builtin_fmaf(wt[e * K + j], xv, acc);
+            }
+          }
+          if constexpr (M::EPL == 8) out[e] = (T)acc;
+          else out = (T)acc;
+        }
+      }
+      x[s] = out;
+    }
+    }
   };
   load_x(xf, c0);  // the first block's rows go out before W^T is staged
   {

@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhm.so")
 
 # HM_ABI_VERSION of include/hm.h that the argument structs below are laid out for
-ABI_VERSION = 8
+ABI_VERSION = 9
 HM_OK, HM_ERR_NULL, HM_ERR_SHAPE, HM_ERR_DTYPE, HM_ERR_ALIGN, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(8)
 HM_F32, HM_BF16 = 0, 1
 CHUNK = 64
@@ -33,7 +33,9 @@ class FeaturizeArgs(C.Structure):
                 ("B", i64), ("H", i64), ("n", i64), ("d", i64), ("f", i64),
                 ("sx_b", i64), ("sx_h", i64), ("sx_t", i64), ("sw_h", i64),
                 ("sp_b", i64), ("sp_h", i64), ("sp_t", i64),
-                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void)]
+                ("rope_dims", i32), ("rope_base", C.c_float), ("rope_pos0", p_void),
+                ("conv_width", i32), ("reserved", i32), ("conv_w", p_void), ("conv_b", p_void),
+                ("conv_prev", p_void), ("scw_h", i64), ("scb_h", i64)]
 
 
 class FwdArgs(C.Structure):
@@ -361,9 +363,12 @@ def _check_attn(q, k, v, w_q, w_k, o=None, gate=None, token_axis=True):
 
 
 def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Tensor | None = None,
-                 rope_dims=0, rope_base=10000.0, rope_pos0=None):
+                 rope_dims=0, rope_base=10000.0, rope_pos0=None, conv_w=None, conv_b=None, conv_prev=None):
     """phi = softmax([x W, -x W]) for x [B, H, n, d], W [d, f] or [H, d, f]; with
-    rope_dims > 0 turned by the rotary encoding at positions rope_pos0[b] + t."""
+    rope_dims > 0 turned by the rotary encoding at positions rope_pos0[b] + t; with
+    conv_w (float32 [d, K] or [H, d, K]) x first goes through the short causal conv
+    (conv_b float32 [d] or [H, d] or None; conv_prev [B, H, K-1, d] or None), fused
+    into the featurizer's loads."""
     _need(x.dim() == 4, f"x must be [B, H, n, d], got {tuple(x.shape)}")
     B, H, n, d = x.shape
     f = w.shape[-1]
@@ -380,6 +385,22 @@ def hm_featurize(x: torch.Tensor, w: torch.Tensor, phi_dtype=None, phi: torch.Te
     if x.stride(3) != 1 or phi.stride(3) != 1 or w.stride(-1) != 1:
         raise ValueError("inner dimensions must be contiguous")
     _rope(a, B, rope_dims, rope_base, rope_pos0)
+    if conv_w is not None:
+        _need(conv_w.dtype == torch.float32 and conv_w.dim() in (2, 3) and conv_w.shape[-2] == d
+              and conv_w.is_contiguous(), f"conv_w must be contiguous float32 [d, K] or [H, d, K], got {tuple(conv_w.shape)}")
+        K = conv_w.shape[-1]
+        _need(conv_w.dim() == 2 or conv_w.shape[0] == H, "conv_w's head dimension must be H")
+        if conv_b is not None:
+            _need(conv_b.dtype == torch.float32 and conv_b.shape[-1] == d and conv_b.is_contiguous()
+                  and (conv_b.dim() == 1 or (conv_b.dim() == 2 and conv_b.shape[0] == H)),
+                  "conv_b must be contiguous float32 [d] or [H, d]")
+        if conv_prev is not None:
+            _need(conv_prev.dtype == x.dtype and tuple(conv_prev.shape) == (B, H, K - 1, d)
+                  and conv_prev.is_contiguous(), "conv_prev must be contiguous [B, H, K-1, d] in x's dtype")
+        _dev(conv_w, conv_b, conv_prev)
+        a.conv_width, a.conv_w, a.conv_b, a.conv_prev = K, _ptr(conv_w), _ptr(conv_b), _ptr(conv_prev)
+        a.scw_h = d * K if conv_w.dim() == 3 else 0
+        a.scb_h = d if conv_b is not None and conv_b.dim() == 2 else 0
     _check(call_featurize(a, _stream()))
     return phi
 

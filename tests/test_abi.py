@@ -44,7 +44,7 @@ def test_struct_layouts_match_binding():
 
 
 def test_version_and_status_strings():
-    assert hm.lib().hm_abi_version() == 8 == hm.ABI_VERSION
+    assert hm.lib().hm_abi_version() == 9 == hm.ABI_VERSION
     with open(os.path.join(ROOT, "include", "hm.h")) as fh:
         assert re.search(r"#define HM_ABI_VERSION (\d+)", fh.read()).group(1) == str(hm.ABI_VERSION)
     for code, name in enumerate(["HM_OK", "HM_ERR_NULL", "HM_ERR_SHAPE", "HM_ERR_DTYPE", "HM_ERR_ALIGN",
@@ -262,6 +262,11 @@ def test_featurize_validation_errors():
     expect(hm.call_featurize(feat(sp_t=64)), hm.HM_ERR_SHAPE)
     expect(hm.call_featurize(feat(x=A + 6)), hm.HM_ERR_ALIGN)
     expect(hm.call_featurize(feat(d=24)), hm.HM_ERR_UNSUPPORTED)
+    # the fused short conv: widths 0..4, taps required, aligned state
+    expect(hm.call_featurize(feat(conv_width=5, conv_w=A + 0x5000000)), hm.HM_ERR_UNSUPPORTED)
+    expect(hm.call_featurize(feat(conv_width=2)), hm.HM_ERR_NULL)
+    expect(hm.call_featurize(feat(conv_width=2, conv_w=A + 0x5000000, scw_h=-1)), hm.HM_ERR_SHAPE)
+    expect(hm.call_featurize(feat(conv_width=2, conv_w=A + 0x5000000, conv_prev=A + 0x6000008)), hm.HM_ERR_ALIGN)
     expect(hm.call_featurize(feat(n=0)), hm.HM_OK)
 
 

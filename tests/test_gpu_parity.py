@@ -542,3 +542,31 @@ def test_decode_step_with_fused_conv(dtype, shape, K):
     print(f"[parity] decode + fused conv {dtype} {shape} K={K}: worst step rel-L2 {worst:.3e}", flush=True)
     assert worst <= tol_for(dtype)
     assert np.array_equal(f64(sq_a), prev_q) and np.array_equal(f64(sk_a), prev_k)
+
+
+@pytest.mark.parametrize("dtype,d,f", [(torch.bfloat16, 128, 64), (torch.bfloat16, 16, 16), (torch.float32, 64, 32)])
+@pytest.mark.parametrize("K", [1, 2, 4])
+@pytest.mark.parametrize("with_prev", [False, True])
+def test_featurize_with_fused_conv(dtype, d, f, K, with_prev):
+    """hm_featurize with the short causal conv in its load prologue equals hm_causal_conv
+    followed by hm_featurize bit for bit (same operation order and rounding), and the
+    oracle's conv and features to the dtype's bar; per-head taps and bias, ragged n."""
+    B, H, n = 2, 3, 300
+    gen = torch.Generator().manual_seed(K * 7 + d + int(with_prev))
+    x = torch.randn((B, H, n, d), generator=gen).to(dtype)
+    w = (torch.randn((d, f), generator=gen) / d ** 0.5).to(dtype)
+    cw = (torch.randn((H, d, K), generator=gen) * 0.6).float()
+    cb = (torch.randn((H, d), generator=gen) * 0.1).float()
+    prev = torch.randn((B, H, K - 1, d), generator=gen).to(dtype) if with_prev and K > 1 else None
+    xd, wd, cwd, cbd = x.cuda(), w.cuda(), cw.cuda(), cb.cuda()
+    pd = None if prev is None else prev.cuda()
+    fused = hm.hm_featurize(xd, wd, conv_w=cwd, conv_b=cbd, conv_prev=pd)
+    y = hm.hm_causal_conv(xd, cwd, cbd, pd)
+    sep = hm.hm_featurize(y, wd)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, sep), "fused conv + featurize differs from conv then featurize"
+    yr, _ = orc.causal_conv(f64(x), f64(cw), f64(cb), None if prev is None else f64(prev))
+    yr = f64(torch.tensor(yr).to(dtype))  # the conv output rounded as it is stored
+    ref = orc.hedgehog_features(yr, f64(w))
+    r = report(f"featurize+conv {dtype} d={d} f={f} K={K} prev={with_prev}", f64(fused), ref)
+    assert r <= (FP32_TOL if dtype == torch.float32 else 4e-3)
