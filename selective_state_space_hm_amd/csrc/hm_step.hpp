@@ -331,6 +331,7 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   constexpr int NFH = FH / 16, NFT = 2 * NFH, KD = DKP / M::KS, LDW = DKP + M::PAD;
   __shared__ __align__(16) T sW[FH * LDW];
   __shared__ double sRev[FH];
+  __shared__ float sCw[CONV ? DK * 4 : 1], sCb[CONV ? DK : 1];  // conv taps [d][K] and bias of the head
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, col = lane & 15, g = lane >> 4;
   const int64_t bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
   const int64_t c0 = (int64_t)blockIdx.x * 64 * kFeatBlocks + 16 * wv + col;  // this lane's token in block 0
@@ -363,10 +364,10 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
             else if (CP) rows[j] = M::ld_contig(CP + (K - 1 + t) * DK + s * M::KS, g);
           }
         }
-        const float *wt = p.cw + h * p.scw_h + (int64_t)ch0 * K;
+        const float *wt = sCw + ch0 * K;
 #pragma unroll
         for (int e = 0; e < M::EPL; ++e) {
-          float acc = p.cb ? p.cb[h * p.scb_h + ch0 + e] : 0.f;
+          float acc = sCb[ch0 + e];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (j < K) {
@@ -384,7 +385,12 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
     }
     }
   };
-  load_x(xf, c0);  // the first block's rows go out before W^T is staged
+  if constexpr (CONV) {  // the head's conv taps and bias into LDS (read by every load below)
+    for (int i = tid; i < DK * K; i += 256) sCw[i] = p.cw[h * p.scw_h + i];
+    for (int i = tid; i < DK; i += 256) sCb[i] = p.cb ? p.cb[h * p.scb_h + i] : 0.f;
+  } else {
+    load_x(xf, c0);  // the first block's rows go out before W^T is staged
+  }
   {
     // W^T: sW[f][d] = W[d][f], W read as 16-byte vectors, all issued before the first LDS write
     constexpr int EP = 16 / (int)sizeof(T), NV = DK * FH / EP, VPT = (NV + 255) / 256;
@@ -411,6 +417,7 @@ __global__ __launch_bounds__(256) void featurize_kernel(const FeatParams p) {
   }
   if (tid < p.rope_dims / 2) sRev[tid] = rope_rev(tid, p.rope_dims, p.rope_base);
   __syncthreads();
+  if constexpr (CONV) load_x(xf, c0);
   for (int r = 0; r < kFeatBlocks; ++r) {
     const int64_t c = c0 + 64 * r;
     if (c - 16 * wv - col >= p.n) break;  // the workgroup's last block (uniform over the workgroup)
